@@ -1,0 +1,303 @@
+"""fp64 CPU oracle for block-causal ReLU linear attention with RoPE.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and the
+benchmark's CPU-baseline leg may import or run this module.  It shares no code
+with the HIP library and imports nothing from it: callers hand it plain numpy
+arrays (bf16/fp32 values widened exactly to float64).
+
+Pages cited (short tags used below):
+  [ImplBCLA]  "Implementing Block Causal Linear Attention for Long Video
+              Generation with Sana" (instagit.com walkthrough of the Sana repo).
+  [BCLA]      "Block Causal Linear Attention" (happyin.space).
+  [LongSANA]  "[feat] LongSANA: a minute-length real-time video generation
+              model" (huggingface/diffusers pull request 12723).
+  [SANA-WM]   the SANA-WM pipeline pull request (huggingface/diffusers 13881).
+
+What is computed, per (batch b, head h), with phi = ReLU:
+  fq = phi(q), fk = phi(k)                  [ImplBCLA, "The Linear Attention Kernel", steps 3]
+  rq = R(fq), rk = R(fk)  (RoPE after phi)  [ImplBCLA, "Rotary Position Embeddings"]
+  running over blocks j = 0, 1, ... in order:
+     S += v_j^T . rk_j      (d x d)         [ImplBCLA, "The Linear Attention Kernel", vk line]
+     z += sum_n fk_n        (d)             [ImplBCLA, same listing, key-sum in the z line]
+     out_j = (rq_j . S^T) / (fq_j . z + eps)
+  i.e. tokens of block j read the inclusive prefix of blocks <= j
+  [ImplBCLA, "Chunk-Wise Causality" and "Summary"; BCLA, "What SANA-Video Actually
+  Uses": cumulative attention-state and key summaries].
+
+Readings where the pages are silent or ambiguous (each one is restated where it
+is used):
+  - causality is across blocks only; inside a block every token sees the whole
+    block (a block of one token is the token-causal form);
+  - the prefix is inclusive (a block sees itself);
+  - the numerator uses the rotated vectors, the normaliser the un-rotated ones;
+  - RoPE rotates adjacent channel pairs (2i, 2i+1) by +angle; the head dim is
+    split into consecutive sections t, h, w; pair i of a section of width d_s
+    turns by pos * base**(-2i/d_s);  positions are 0-based, tokens are frame-major
+    then raster (row, col) in the frame, t is the absolute latent-frame index;
+    RoPE convention: parity unpinned by the pages (a documented convention,
+    checked only for internal consistency and its textbook special cases);
+  - a last block shorter than the others is allowed;
+  - eps = 1e-8 is added to the normaliser ([ImplBCLA], constructor default).
+"""
+
+import numpy as np
+
+EPS_DEFAULT = 1e-8  # [ImplBCLA, "Architecture and Implementation Details"]
+
+
+# --------------------------------------------------------------------------- RoPE
+
+def token_positions(n_tokens, tokens_per_frame, grid_w, t0=0):
+    """(t, row, col) of each token: frame-major, raster order inside a frame.
+
+    Token n sits in frame n // tpf at raster index n % tpf = row * grid_w + col.
+    t is shifted by t0 (the number of frames already streamed).
+    """
+    n = np.arange(n_tokens, dtype=np.int64)
+    t = n // tokens_per_frame + t0
+    r = n % tokens_per_frame
+    if grid_w > 0:
+        row, col = r // grid_w, r % grid_w
+    else:
+        row, col = np.zeros_like(r), np.zeros_like(r)
+    return t, row, col
+
+
+def rope_rotate(x, pos_t, pos_h, pos_w, split, base):
+    """Rotate adjacent channel pairs of x (n, d) section by section.
+
+    split = (d_t, d_h, d_w): channels [0, d_t) follow t, [d_t, d_t+d_h) follow the
+    row, the rest the column ([SANA-WM] names a 3-D t/h/w rotary embedding).
+    Pair i of a section of width d_s turns by pos * base**(-2 i / d_s); cos and sin
+    are taken in float64.
+    """
+    x = np.array(x, dtype=np.float64, copy=True)
+    off = 0
+    for d_s, pos in zip(split, (pos_t, pos_h, pos_w)):
+        for i in range(d_s // 2):
+            theta = float(base) ** (-2.0 * i / d_s)
+            ang = np.asarray(pos, dtype=np.float64) * theta
+            c, s = np.cos(ang), np.sin(ang)
+            a, b = off + 2 * i, off + 2 * i + 1
+            xa, xb = x[:, a].copy(), x[:, b].copy()
+            x[:, a] = xa * c - xb * s
+            x[:, b] = xa * s + xb * c
+        off += d_s
+    return x
+
+
+def _rotate_tokens(x, rope, tokens_per_frame, t0):
+    """Apply RoPE (or nothing when rope is None) to x (n, d)."""
+    if rope is None:
+        return np.array(x, dtype=np.float64, copy=True)
+    t, row, col = token_positions(x.shape[0], tokens_per_frame, rope["grid"][1], t0)
+    return rope_rotate(x, t, row, col, rope["split"], rope["base"])
+
+
+def _relu(x):
+    # phi = ReLU on queries and keys [ImplBCLA, "What is Block Causal Linear Attention?"]
+    return np.maximum(np.asarray(x, dtype=np.float64), 0.0)
+
+
+# ------------------------------------------------------------------ one-shot forward
+
+def block_bounds(n_tokens, block_tokens):
+    """Token ranges [s, e) of the blocks; the last one may be shorter."""
+    return [(s, min(s + block_tokens, n_tokens)) for s in range(0, n_tokens, block_tokens)]
+
+
+def _head_forward(q, k, v, tokens_per_frame, block_frames, rope, eps, t0, S, z):
+    """One (batch, head) stream: q, k, v are (n, d); S (d, d) and z (d) are updated in place."""
+    fq, fk = _relu(q), _relu(k)
+    rq = _rotate_tokens(fq, rope, tokens_per_frame, t0)
+    rk = _rotate_tokens(fk, rope, tokens_per_frame, t0)
+    v = np.asarray(v, dtype=np.float64)
+    out = np.empty_like(v)
+    for s, e in block_bounds(q.shape[0], block_frames * tokens_per_frame):
+        S += v[s:e].T @ rk[s:e]          # S[e_, f] += sum_n v[n, e_] * rk[n, f]
+        z += fk[s:e].sum(axis=0)         # un-rotated key-sum
+        num = rq[s:e] @ S.T              # num[n, e_] = sum_f S[e_, f] * rq[n, f]
+        den = fq[s:e] @ z + eps          # un-rotated query in the normaliser
+        out[s:e] = num / den[:, None]
+    return out
+
+
+def forward(q, k, v, tokens_per_frame, block_frames, rope=None, eps=EPS_DEFAULT):
+    """Block-causal forward over whole sequences.
+
+    q, k, v: (B, N, H, d) arrays (any float dtype; taken as float64).
+    rope: None (no rotation) or {"split": (d_t, d_h, d_w), "grid": (rows, cols),
+    "base": float}.  Returns out (B, N, H, d) float64.
+    """
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    B, N, H, d = q.shape
+    out = np.empty((B, N, H, d), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            S, z = np.zeros((d, d)), np.zeros(d)
+            out[b, :, h] = _head_forward(q[b, :, h], k[b, :, h], v[b, :, h],
+                                         tokens_per_frame, block_frames, rope, eps, 0, S, z)
+    return out
+
+
+def forward_head(q, k, v, tokens_per_frame, block_frames, rope=None, eps=EPS_DEFAULT):
+    """Same as forward for one (batch, head) slice: q, k, v are (N, d)."""
+    d = q.shape[1]
+    S, z = np.zeros((d, d)), np.zeros(d)
+    return _head_forward(q, k, v, tokens_per_frame, block_frames, rope, eps, 0, S, z)
+
+
+def block_states(k, v, tokens_per_frame, block_frames, rope=None, t0=0):
+    """Inclusive prefix states (S_bar_j, z_bar_j) of every block of one head (k, v: (N, d))."""
+    fk = _relu(k)
+    rk = _rotate_tokens(fk, rope, tokens_per_frame, t0)
+    v = np.asarray(v, dtype=np.float64)
+    d = k.shape[1]
+    S, z = np.zeros((d, d)), np.zeros(d)
+    Ss, zs = [], []
+    for s, e in block_bounds(k.shape[0], block_frames * tokens_per_frame):
+        S = S + v[s:e].T @ rk[s:e]
+        z = z + fk[s:e].sum(axis=0)
+        Ss.append(S.copy())
+        zs.append(z.copy())
+    return np.array(Ss), np.array(zs)
+
+
+def readout_tokens(q, n_idx, S_bar, z_bar, tokens_per_frame, rope=None, eps=EPS_DEFAULT, t0=0):
+    """Outputs of chosen tokens n_idx of one head, given that head's block prefix state.
+
+    q: (m, d) rows of the tokens n_idx; S_bar (d, d), z_bar (d) is the inclusive
+    prefix of the block those tokens sit in.  Used to check sampled outputs of large runs.
+    """
+    fq = _relu(q)
+    if rope is None:
+        rq = fq
+    else:
+        t, row, col = token_positions(int(np.max(n_idx)) + 1, tokens_per_frame, rope["grid"][1], t0)
+        n_idx = np.asarray(n_idx)
+        rq = rope_rotate(fq, t[n_idx], row[n_idx], col[n_idx], rope["split"], rope["base"])
+    return (rq @ S_bar.T) / (fq @ z_bar + eps)[:, None]
+
+
+# ------------------------------------------------------------------------ streaming
+
+class StreamState:
+    """Constant-size cache carried between streamed blocks.
+
+    Holds S (B, H, d, d), z (B, H, d) and the number of frames already committed
+    ([BCLA, "What SANA-Video Actually Uses"]; [LongSANA]: the cache is passed in and
+    returned on every call, an enable-save flag decides whether it is updated).
+    """
+
+    def __init__(self, B, H, d):
+        self.S = np.zeros((B, H, d, d))
+        self.z = np.zeros((B, H, d))
+        self.frames_done = 0
+
+
+def stream_block(state, q, k, v, tokens_per_frame, rope=None, eps=EPS_DEFAULT, save=True):
+    """Process one block (all of q, k, v's N tokens form one block) against the cache.
+
+    The block reads old state + its own contribution (inclusive prefix).  With
+    save, the sum is committed and frames_done advances; without it the cache is
+    left as it was (several denoising steps may reuse one committed cache).
+    """
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    B, N, H, d = q.shape
+    frames = N // tokens_per_frame
+    out = np.empty((B, N, H, d))
+    for b in range(B):
+        for h in range(H):
+            S, z = state.S[b, h].copy(), state.z[b, h].copy()
+            out[b, :, h] = _head_forward(q[b, :, h], k[b, :, h], v[b, :, h], tokens_per_frame,
+                                         frames, rope, eps, state.frames_done, S, z)
+            if save:
+                state.S[b, h], state.z[b, h] = S, z
+    if save:
+        state.frames_done += frames
+    return out
+
+
+# ------------------------------------------------------------- independent checks
+
+def brute_force(q, k, v, tokens_per_frame, block_frames, rope=None, eps=EPS_DEFAULT):
+    """O(N^2) masked form, for tiny inputs.
+
+    out_i = sum_j M_ij <rk_j, rq_i> v_j / (sum_j M_ij <fk_j, fq_i> + eps),
+    M_ij = [block(j) <= block(i)].  Written token by token, with no prefix state.
+    """
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    B, N, H, d = q.shape
+    L = block_frames * tokens_per_frame
+    blk = np.arange(N) // L
+    out = np.empty((B, N, H, d))
+    for b in range(B):
+        for h in range(H):
+            fq, fk = _relu(q[b, :, h]), _relu(k[b, :, h])
+            rq = _rotate_tokens(fq, rope, tokens_per_frame, 0)
+            rk = _rotate_tokens(fk, rope, tokens_per_frame, 0)
+            for i in range(N):
+                num = np.zeros(d)
+                den = 0.0
+                for j in range(N):
+                    if blk[j] <= blk[i]:
+                        num += float(np.dot(rk[j], rq[i])) * v[b, j, h]
+                        den += float(np.dot(fk[j], fq[i]))
+                out[b, i, h] = num / (den + eps)
+    return out
+
+
+def token_causal_cumsum(q, k, v, tokens_per_frame, rope=None, eps=EPS_DEFAULT):
+    """Token-causal linear attention through running sums (np.cumsum over tokens).
+
+    Equals the block form with blocks of one token; written without blocks.
+    """
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    B, N, H, d = q.shape
+    out = np.empty((B, N, H, d))
+    for b in range(B):
+        for h in range(H):
+            fq, fk = _relu(q[b, :, h]), _relu(k[b, :, h])
+            rq = _rotate_tokens(fq, rope, tokens_per_frame, 0)
+            rk = _rotate_tokens(fk, rope, tokens_per_frame, 0)
+            outer = v[b, :, h][:, :, None] * rk[:, None, :]      # (N, d, d)
+            Sc = np.cumsum(outer, axis=0)
+            zc = np.cumsum(fk, axis=0)
+            num = np.einsum("nef,nf->ne", Sc, rq)
+            den = np.einsum("nf,nf->n", zc, fq) + eps
+            out[b, :, h] = num / den[:, None]
+    return out
+
+
+def lite_la_single_block(q, k, v, tokens_per_frame, rope=None, eps=EPS_DEFAULT):
+    """Non-causal ReLU linear attention over the whole sequence, in (B, h, d, N) layout.
+
+    Follows the normalised readout as [ImplBCLA, "The Linear Attention Kernel"] states
+    it for one block: z = 1 / (sum_n k^T . q + eps), vk = v . k_rot^T, out = vk . q_rot,
+    output = out * z, with k, q already through phi.  A block that spans the whole
+    sequence must give this.
+    """
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    B, N, H, d = q.shape
+    out = np.empty((B, N, H, d))
+    for b in range(B):
+        for h in range(H):
+            fq, fk = _relu(q[b, :, h]), _relu(k[b, :, h])
+            rq = _rotate_tokens(fq, rope, tokens_per_frame, 0).T   # (d, N)
+            rk = _rotate_tokens(fk, rope, tokens_per_frame, 0).T
+            qd, kd, vd = fq.T, fk.T, v[b, :, h].T                 # (d, N)
+            zz = 1.0 / (kd.sum(axis=-1, keepdims=True).T @ qd + eps)   # (1, N)
+            vk = vd @ rk.T                                         # (d, d)
+            o = (vk @ rq) * zz                                     # (d, N)
+            out[b, :, h] = o.T
+    return out
+
+
+def rel_err(got, ref):
+    """max |got - ref| / RMS(ref) over the whole tensor (the parity metric)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    if rms == 0.0:
+        return float(np.max(np.abs(got - ref))) if got.size else 0.0
+    return float(np.max(np.abs(got - ref))) / rms
