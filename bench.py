@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Throughput of block-causal ReLU linear attention with RoPE on one MI355X.
+
+One step = one whole forward pass (block states, block prefix, readout) over
+the workload's synthetic bf16 inputs, already resident in HBM.  Prints one JSON
+line: token-heads/s for the whole step, the roofline of the dominant kernel
+(algorithmic bytes / its HIP-event duration against 8 TB/s), per-kernel times,
+the streaming per-block latency, and the fp64 oracle timed on a bounded
+sample on the host cores.
+"""
+
+import argparse
+import ctypes
+import json
+import multiprocessing as mp
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from linear_attention_video_relu_amd import workloads as W  # noqa: E402
+
+METRIC = "tokens·heads/s and achieved HBM GB/s (% peak), block-causal LA fwd"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+REC_BYTES = (32 * 32 + 32) * 4  # one fp32 (S, z) record
+
+
+# ------------------------------------------------------------- CPU baseline leg
+
+_CPU_JOB = {}
+
+
+def _oracle_task(h):
+    cfg, arrs = _CPU_JOB["cfg"], _CPU_JOB["arrs"]
+    try:
+        from threadpoolctl import threadpool_limits
+        ctx = threadpool_limits(1)
+    except Exception:
+        ctx = None
+    import oracle
+    t = time.perf_counter()
+    q, k, v = (W.to_f64(cfg, arrs[x][0, :, h]) for x in W.TENSORS)
+    oracle.forward_head(q, k, v, cfg["tokens_per_frame"], cfg["block_frames"], W.oracle_rope(cfg))
+    if ctx is not None:
+        ctx.unregister()
+    return time.perf_counter() - t
+
+
+def cpu_baseline(cfg, arrs, n_heads):
+    """Time the fp64 oracle on heads 0 .. n_heads-1 of batch row 0, one process per head.
+
+    Runs before anything touches the GPU, so the forked workers inherit the drawn
+    inputs without copying them."""
+    _CPU_JOB.update(cfg=cfg, arrs=arrs)
+    workers = max(1, min(n_heads, len(os.sched_getaffinity(0)), 16))
+    ctxm = mp.get_context("fork")
+    t = time.perf_counter()
+    with ctxm.Pool(workers) as pool:
+        per = pool.map(_oracle_task, list(range(n_heads)))
+    wall = time.perf_counter() - t
+    _CPU_JOB.clear()
+    N = W.n_tokens(cfg)
+    return {"value": n_heads * N / wall, "unit": "tokens·heads/s", "cores": workers,
+            "kind": "oracle",
+            "sample": f"{n_heads} of {cfg['B'] * cfg['H']} (batch, head) streams of {cfg['name']}, "
+                      f"full length {N} tokens, fp64 numpy oracle (inputs widened from bf16 inside "
+                      f"the timed work), one process per stream, 1 BLAS thread each; "
+                      f"{sum(per):.1f} s of CPU work in {wall:.1f} s wall",
+            "cpu_seconds": round(sum(per), 2), "wall_seconds": round(wall, 2)}
+
+
+# ------------------------------------------------------------------- GPU timing
+
+class HipEvents:
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.ev = (ctypes.c_void_p * n)()
+        for i in range(n):
+            e = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed: {rc}")
+            self.ev[i] = e.value
+
+    def ptr(self, i):
+        return ctypes.cast(ctypes.byref(self.ev, i * ctypes.sizeof(ctypes.c_void_p)),
+                           ctypes.POINTER(ctypes.c_void_p))
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.ev[a]),
+                                          ctypes.c_void_p(self.ev[b]))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return ms.value
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="minute_bf16", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--cpu-heads", type=int, default=30, help="oracle sample size (0 = skip)")
+    ap.add_argument("--stream-reps", type=int, default=3, help="timed 40-call streaming runs (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the path is measured on a single MI355X "
+              "(--gpus 1); multi-GPU runs are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    cfg = W.workload(args.workload)
+    B, H, N = cfg["B"], cfg["H"], W.n_tokens(cfg)
+    tpf, bf = cfg["tokens_per_frame"], cfg["block_frames"]
+    t = time.perf_counter()
+    arrs = {x: W.draw(cfg, x) for x in W.TENSORS}
+    print(f"[bench] drew {cfg['name']} inputs in {time.perf_counter() - t:.1f}s", file=sys.stderr, flush=True)
+
+    cpu = None
+    if args.cpu_heads > 0:
+        cpu = cpu_baseline(cfg, arrs, args.cpu_heads)
+        print(f"[bench] cpu baseline {cpu['value']:.3e} token-heads/s on {cpu['cores']} cores",
+              file=sys.stderr, flush=True)
+
+    import torch
+    import __graft_entry__
+    __graft_entry__.ensure_built()
+    from linear_attention_video_relu_amd import lavr
+
+    dev = torch.device("cuda:0")
+    q, k, v = (W.to_torch(cfg, arrs[x], dev) for x in W.TENSORS)
+    del arrs
+    dt = q.dtype
+    rope = lavr.RopeTable(cfg["rope"]["split"], cfg["grid"], cfg["frames"], cfg["rope"]["base"], dev)
+    out = torch.empty_like(q)
+    need = lavr.workspace_bytes(B, H, cfg["frames"], tpf, bf)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    code = lavr._dtype_code(dt)
+    ptrs = [ctypes.c_void_p(x.data_ptr()) for x in (q, k, v, out)]
+
+    def fwd():
+        rc = lavr.lib.la_block_causal_forward(*ptrs, code, code, B, H, 32, cfg["frames"], tpf, bf,
+                                              ctypes.byref(rope.desc), 1e-8,
+                                              ctypes.c_void_p(ws.data_ptr()), need, stream)
+        if rc:
+            raise RuntimeError(lavr.status_string(rc))
+
+    ev = HipEvents(4 * args.steps)
+
+    def fwd_timed(i):
+        rc = lavr.lib.la_block_causal_forward_timed(*ptrs, code, code, B, H, 32, cfg["frames"], tpf,
+                                                    bf, ctypes.byref(rope.desc), 1e-8,
+                                                    ctypes.c_void_p(ws.data_ptr()), need, stream,
+                                                    ev.ptr(4 * i))
+        if rc:
+            raise RuntimeError(lavr.status_string(rc))
+
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize(dev)
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        fwd_timed(i)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    ph = np.array([[ev.elapsed_ms(4 * i + a, 4 * i + a + 1) for a in range(3)] for i in range(args.steps)])
+    ev_step = np.array([ev.elapsed_ms(4 * i, 4 * i + 3) for i in range(args.steps)])
+    k_state, k_prefix, k_read = (float(x) for x in ph.mean(axis=0))
+
+    th = B * N * H
+    esz = 2 if dt == torch.bfloat16 else 4
+    nb = -(-cfg["frames"] // bf)
+    state_io = B * H * nb * REC_BYTES
+    bytes_state = 2 * th * 32 * esz + state_io          # K, V read; block states out
+    bytes_read = 2 * th * 32 * esz + state_io           # Q read, O written; block prefixes in
+    bytes_step = 4 * th * 32 * esz + 2 * state_io
+    kernels = {
+        "k_block_state": {"ms": k_state, "alg_bytes": bytes_state,
+                          "gbs": bytes_state / (k_state * 1e6)},
+        "k_prefix": {"ms": k_prefix},
+        "k_readout": {"ms": k_read, "alg_bytes": bytes_read, "gbs": bytes_read / (k_read * 1e6)},
+    }
+    dom = "k_block_state" if k_state >= k_read else "k_readout"
+    ach = kernels[dom]["gbs"]
+
+    result = {
+        "metric": METRIC,
+        "value": th / (ms_step / 1e3),
+        "unit": "tokens·heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if dt == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg["name"], "B": B, "N": N, "H": H, "head_dim": 32,
+                   "frames": cfg["frames"], "tokens_per_frame": tpf, "block_frames": bf,
+                   "grid": list(cfg["grid"]), "rope_split": list(cfg["rope"]["split"]),
+                   "rope_base": cfg["rope"]["base"], "eps": 1e-8},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None},
+        "step_hbm_gbs": bytes_step / (ms_step * 1e6),
+        "step_frac_of_peak": bytes_step / (ms_step * 1e6) / HBM_PEAK_GBS,
+        "event_ms_per_step": float(ev_step.mean()),
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+
+    if args.stream_reps > 0:
+        result["streaming"] = bench_streaming(lavr, torch, dev, args.stream_reps)
+
+    print(json.dumps(result), flush=True)
+
+
+def bench_streaming(lavr, torch, dev, reps):
+    """Per-block latency of 40 la_stream_block calls (B=2, 70 heads, 3 frames of 30x52)."""
+    cfg = W.workload("stream_bf16")
+    tpf, bf = cfg["tokens_per_frame"], cfg["block_frames"]
+    L = bf * tpf
+    arrs = {x: W.draw(cfg, x) for x in W.TENSORS}
+    q, k, v = (W.to_torch(cfg, arrs[x], dev) for x in W.TENSORS)
+    del arrs
+    nblk = cfg["frames"] // bf
+    # one contiguous buffer per block, as a streaming caller would hold them
+    blocks = [tuple(x[:, j * L:(j + 1) * L].contiguous() for x in (q, k, v)) for j in range(nblk)]
+    del q, k, v
+    outs = [torch.empty_like(blocks[0][0]) for _ in range(nblk)]
+    rope = lavr.RopeTable(cfg["rope"]["split"], cfg["grid"], cfg["frames"], cfg["rope"]["base"], dev)
+    need = lavr.workspace_bytes(cfg["B"], cfg["H"], bf, tpf, bf)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    times = []
+    for rep in range(reps + 1):
+        st = lavr.StreamState(cfg["B"], cfg["H"], device=dev)
+        torch.cuda.synchronize(dev)
+        t0 = time.perf_counter()
+        for j in range(nblk):
+            st.step(*blocks[j], tpf, rope, out=outs[j], workspace=ws)
+        torch.cuda.synchronize(dev)
+        if rep > 0:
+            times.append((time.perf_counter() - t0) / nblk)
+    per_call = float(np.median(times))
+    th = cfg["B"] * L * cfg["H"]
+    call_bytes = 4 * th * 32 * 2 + 2 * cfg["B"] * cfg["H"] * REC_BYTES
+    return {"workload": cfg["name"], "calls": nblk, "ms_per_block": per_call * 1e3,
+            "tokens_heads_per_s": th / per_call, "hbm_gbs": call_bytes / (per_call * 1e9),
+            "reps": reps}
+
+
+if __name__ == "__main__":
+    main()

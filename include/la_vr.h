@@ -1,0 +1,165 @@
+/*
+ * la_vr.h -- C ABI of liblavr: block-causal ReLU linear attention with RoPE
+ * (forward, one-shot and streaming) on AMD MI355X (gfx950).
+ *
+ * What is computed.  For every batch row b and head h, with phi = ReLU applied
+ * elementwise to queries and keys ("Implementing Block Causal Linear Attention
+ * for Long Video Generation with Sana", sections "What is Block Causal Linear
+ * Attention?" and "The Linear Attention Kernel"), and R the rotary embedding
+ * applied to phi(q) and phi(k) right after the ReLU (same page, "Rotary
+ * Position Embeddings"):
+ *
+ *   block j of the sequence adds   S_j = sum_{n in j} v_n (R phi(k_n))^T   (d x d)
+ *                                  z_j = sum_{n in j} phi(k_n)             (d)
+ *   the prefix over blocks <= j    Sbar_j = sum_{j' <= j} S_j',  zbar_j likewise
+ *   a token n of block j reads     out_n = Sbar_j (R phi(q_n)) / (zbar_j . phi(q_n) + eps)
+ *
+ * Tokens of block j see every token of blocks <= j, their own block included,
+ * and nothing later (same page, "Chunk-Wise Causality"; "Block Causal Linear
+ * Attention", happyin.space, "What SANA-Video Actually Uses": a block needs the
+ * cumulative attention state and key summaries of earlier blocks).  The
+ * normaliser uses the un-rotated phi(q), phi(k).  A streaming caller carries the
+ * constant-size (S, z) cache between calls ("[feat] LongSANA: a minute-length
+ * real-time video generation model", diffusers pull request 12723: the cache is
+ * passed in and handed back on every call and an enable-save flag decides
+ * whether a call updates it).
+ *
+ * Layouts.  q, k, v and out are contiguous row-major (B, N, H, head_dim) with
+ * N = frames * tokens_per_frame; tokens are frame-major, then raster order
+ * (row, col) inside a frame.  This is the (B, N, C) activation with C = H *
+ * head_dim.  Only head_dim == 32 is built.
+ *
+ * RoPE.  head_dim is split into consecutive sections of d_t, d_h and d_w
+ * channels that follow the token's frame index t, row and column.  Pair i
+ * (channels 2i, 2i+1 of a section of width d_s) turns by the angle
+ * pos * base^(-2i/d_s):  (x_a, x_b) -> (x_a cos - x_b sin, x_a sin + x_b cos).
+ * A 1-D RoPE over the token index is tokens_per_frame = 1, d_t = head_dim,
+ * d_h = d_w = 0.  The pages fix neither pairing nor frequencies; this is the
+ * library's convention.
+ *
+ * Calling convention.  Every pointer argument named *_dev, q, k, v, out, ws,
+ * S, z or table is device memory owned by the caller; the library never
+ * allocates or frees device memory and keeps no global state.  Every call
+ * checks its arguments on the host first and returns an error code without
+ * touching the GPU if they are wrong; otherwise it enqueues its kernels on
+ * `stream` (a hipStream_t, NULL = default stream) and returns at once.  The
+ * library never aborts and never prints.
+ */
+#ifndef LA_VR_H
+#define LA_VR_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LA_OK = 0,
+  LA_ERR_INVALID_ARG = 1,     /* null/misaligned pointer, bad size, overlap, small workspace */
+  LA_ERR_UNSUPPORTED = 2,     /* valid request the library does not build (head_dim != 32, ...) */
+  LA_ERR_STATE_MISMATCH = 3,  /* la_state shape does not match the call */
+  LA_ERR_HIP = 4              /* a HIP launch or runtime call failed */
+} la_status;
+
+typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
+
+/* Description of a rotary table built by rope_table_build.  table == NULL turns
+ * RoPE off (identity rotation). */
+typedef struct {
+  const float* table;          /* device; (cos, sin) float pairs, see rope_table_bytes */
+  int d_t, d_h, d_w;           /* even section widths, d_t + d_h + d_w == head_dim */
+  int max_frames;              /* rows of the t section: frames 0 .. max_frames-1 */
+  int grid_h, grid_w;          /* rows / columns of a frame (1, 1 for 1-D RoPE) */
+} la_rope;
+
+/* Streaming cache of one generation stream ("Block Causal Linear Attention",
+ * happyin.space, "Integration Contract": one cache per stream, never shared).
+ * S is [B][H][head_dim][head_dim] fp32 (S[e][f] multiplies channel f of the
+ * rotated query), z is [B][H][head_dim] fp32, frames_done counts committed
+ * frames and is the frame offset of the next call's RoPE.  (S, z, frames_done)
+ * is the complete resumable state. */
+typedef struct {
+  float* S;
+  float* z;
+  int B, H, head_dim;
+  long long frames_done;
+} la_state;
+
+/* Bytes of the rotary table: 8 * (max_frames*d_t/2 + grid_h*d_h/2 + grid_w*d_w/2).
+ * Returns 0 for invalid sizes. */
+size_t rope_table_bytes(int d_t, int d_h, int d_w, int max_frames, int grid_h, int grid_w);
+
+/* Fill `table_dev` (bytes >= rope_table_bytes(...), 16-byte aligned) with cos and
+ * sin of every (section, position, pair) angle, computed in float64 on the GPU
+ * and rounded to float32, and describe it in *out.  The t section covers frames
+ * 0 .. max_frames-1, the h section rows 0 .. grid_h-1, the w section columns
+ * 0 .. grid_w-1.  base > 0 (10000 in every SANA configuration).  Layout: the
+ * t section as [max_frames][d_t/2] pairs, then h as [grid_h][d_h/2], then w as
+ * [grid_w][d_w/2]; a pair is (cos, sin). */
+int rope_table_build(la_rope* out, float* table_dev, size_t bytes, int head_dim,
+                     int d_t, int d_h, int d_w, int max_frames, int grid_h, int grid_w,
+                     double base, void* stream);
+
+/* Workspace bytes needed by la_block_causal_forward for this shape (for
+ * la_stream_block pass frames = block_frames).  0 for invalid sizes. */
+size_t la_workspace_bytes(int B, int H, int head_dim, int frames, int tokens_per_frame,
+                          int block_frames);
+
+/* One-shot block-causal forward over `frames` frames, blocks of block_frames
+ * frames (the last block may be shorter), starting from an empty cache.
+ * q, k, v have dtype in_dt, out has dtype out_dt (LA_BF16 out is rounded to
+ * nearest even from the fp32 result).  All accumulation is fp32.  eps >= 0 is
+ * added to the normaliser (1e-8 in SANA).  ws (256-byte aligned, ws_bytes >=
+ * la_workspace_bytes) is scratch owned by the caller and must not be touched
+ * by other work until the call's kernels finish.  out must not overlap q, k, v.
+ * If rope->table is non-NULL, frames <= rope->max_frames and, when d_h + d_w >
+ * 0, grid_h * grid_w == tokens_per_frame.  rope may be NULL (RoPE off). */
+int la_block_causal_forward(const void* q, const void* k, const void* v, void* out,
+                            la_dtype in_dt, la_dtype out_dt,
+                            int B, int H, int head_dim, int frames, int tokens_per_frame,
+                            int block_frames, const la_rope* rope, float eps,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* la_block_causal_forward that also records four caller-created hipEvent_t
+ * events[0..3] on `stream`: before the block-state kernel, after it, after
+ * the prefix kernel and after the readout kernel, so a caller can time each
+ * phase with hipEventElapsedTime.  events must not be NULL. */
+int la_block_causal_forward_timed(const void* q, const void* k, const void* v, void* out,
+                                  la_dtype in_dt, la_dtype out_dt,
+                                  int B, int H, int head_dim, int frames, int tokens_per_frame,
+                                  int block_frames, const la_rope* rope, float eps,
+                                  void* ws, size_t ws_bytes, void* stream, void* const* events);
+
+/* Bind the caller's device buffers S_dev ([B][H][d][d] fp32) and z_dev
+ * ([B][H][d] fp32), both 16-byte aligned, to *st, zero them on `stream`, and set
+ * frames_done = 0. */
+int la_state_init(la_state* st, float* S_dev, float* z_dev, int B, int H, int head_dim,
+                  void* stream);
+
+/* Streaming step: q, k, v, out hold exactly one block of block_frames frames,
+ * shape (B, block_frames * tokens_per_frame, H, head_dim); (B, H, head_dim) must
+ * equal the state's, else LA_ERR_STATE_MISMATCH.  The block
+ * reads the cache plus its own contribution; RoPE frame offset is
+ * st->frames_done.  With save != 0 the cache becomes cache + this block and
+ * st->frames_done advances by block_frames (on the host, at enqueue time);
+ * with save == 0 the cache is left unchanged (several denoising steps of one
+ * block may reuse it, [feat] LongSANA pull request: timesteps per chunk).
+ * The result is the one-shot result of the concatenated blocks.  Workspace as
+ * for la_block_causal_forward with frames = block_frames. */
+int la_stream_block(la_state* st, const void* q, const void* k, const void* v, void* out,
+                    la_dtype in_dt, la_dtype out_dt, int B, int H, int head_dim,
+                    int block_frames, int tokens_per_frame, const la_rope* rope, float eps,
+                    int save, void* ws, size_t ws_bytes, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* la_status_string(int status);
+
+/* Library version as "major.minor.patch". */
+const char* la_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LA_VR_H */

@@ -1,0 +1,277 @@
+// Host side of liblavr: argument checks, launch planning, workspace sizing and
+// the C entry points declared in include/la_vr.h.  Every check runs before any
+// HIP call, so a bad call returns a status without touching the GPU.
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "la_internal.h"
+#include "la_vr.h"
+
+using lavr::Plan;
+
+namespace {
+
+constexpr int kStateTarget = 1024;     // tokens per block-state chunk (target)
+constexpr int kReadTarget = 512;       // tokens per readout tile (target)
+constexpr int kTabLdsMax = 32768;      // LDS bytes for a staged rotary window
+constexpr int kStep = 64;              // block-state kernel step (tokens)
+constexpr long long kTwo42 = 1LL << 42;
+constexpr long long kMaxTokens = 1LL << 30;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
+
+long long round_up(long long a, long long m) { return cdiv(a, m) * m; }
+
+bool rope_on(const la_rope* r) { return r != nullptr && r->table != nullptr; }
+
+int esize(la_dtype dt) { return dt == LA_BF16 ? 2 : 4; }
+
+bool valid_dtype(int dt) { return dt == LA_F32 || dt == LA_BF16; }
+
+// Validate the rotary description for a call covering frames [t0, t0 + frames).
+int check_rope(const la_rope* r, int head_dim, int tpf, long long t0, long long frames) {
+  if (!rope_on(r)) return LA_OK;
+  if (!aligned(r->table, 16)) return LA_ERR_INVALID_ARG;
+  if (r->d_t < 0 || r->d_h < 0 || r->d_w < 0) return LA_ERR_INVALID_ARG;
+  if ((r->d_t | r->d_h | r->d_w) & 1) return LA_ERR_INVALID_ARG;
+  if (r->d_t + r->d_h + r->d_w != head_dim) return LA_ERR_INVALID_ARG;
+  if (r->max_frames < 1 || r->grid_h < 1 || r->grid_w < 1) return LA_ERR_INVALID_ARG;
+  if (r->d_h + r->d_w > 0 && (long long)r->grid_h * r->grid_w != tpf) return LA_ERR_INVALID_ARG;
+  if (t0 < 0 || t0 + frames > r->max_frames) return LA_ERR_INVALID_ARG;
+  return LA_OK;
+}
+
+// Pairs of the rotary table a workgroup covering `tokens` consecutive tokens stages.
+long long tab_pairs(const la_rope* r, int tpf, int tokens) {
+  if (!rope_on(r)) return 0;
+  const long long nf = (tokens - 1) / tpf + 2;
+  return nf * (r->d_t / 2) + (long long)r->grid_h * (r->d_h / 2) + (long long)r->grid_w * (r->d_w / 2);
+}
+
+// Split a block of L tokens into chunks of about `target` tokens (a multiple of
+// `mult`) whose rotary window fits in LDS.  Returns false if none fits.
+bool split_block(int L, int target, int mult, const la_rope* r, int tpf, int* n_out, int* T_out) {
+  long long n = cdiv(L, target);
+  for (;;) {
+    long long T = round_up(cdiv(L, n), mult);
+    if (tab_pairs(r, tpf, (int)T) * 8 <= kTabLdsMax) {
+      *n_out = (int)n;
+      *T_out = (int)T;
+      return true;
+    }
+    if (T <= mult) return false;
+    ++n;
+  }
+}
+
+int make_plan(Plan* p, int B, int H, int head_dim, int frames, int tpf, int block_frames,
+              const la_rope* rope, long long t0, la_dtype in_dt) {
+  if (B < 1 || H < 1 || head_dim < 1 || frames < 1 || tpf < 1 || block_frames < 1)
+    return LA_ERR_INVALID_ARG;
+  if (head_dim != lavr::kHeadDim) return LA_ERR_UNSUPPORTED;
+  if (B > 65535 || H > 65535 || (long long)B * H > (1LL << 24)) return LA_ERR_UNSUPPORTED;
+  const long long N = (long long)frames * tpf;
+  if (N > kMaxTokens || N * tpf >= kTwo42) return LA_ERR_UNSUPPORTED;
+  int st = check_rope(rope, head_dim, tpf, t0, frames);
+  if (st != LA_OK) return st;
+  const int gw_div = (rope_on(rope) && rope->d_h + rope->d_w > 0) ? rope->grid_w : 1;
+  if ((long long)tpf * gw_div >= kTwo42) return LA_ERR_UNSUPPORTED;
+
+  std::memset(p, 0, sizeof(*p));
+  p->B = B;
+  p->H = H;
+  p->N = (int)N;
+  p->tpf = tpf;
+  p->gw_div = gw_div;
+  p->L = (int)((long long)(block_frames < frames ? block_frames : frames) * tpf);
+  p->nb = (int)cdiv(N, p->L);
+  p->hg = (H + lavr::kHeadsPerGroup - 1) / lavr::kHeadsPerGroup;
+  p->t0 = t0;
+  p->mag_tpf = (uint64_t)(kTwo42 / tpf) + 1;
+  p->mag_gw = (uint64_t)(kTwo42 / gw_div) + 1;
+  if (!split_block(p->L, kStateTarget, kStep, rope, tpf, &p->cpb, &p->Tc)) return LA_ERR_UNSUPPORTED;
+  if (!split_block(p->L, kReadTarget, 32, rope, tpf, &p->rpb, &p->Tr)) return LA_ERR_UNSUPPORTED;
+  if ((long long)p->hg * p->nb * p->cpb > 0x7fffffffLL || (long long)p->hg * p->nb * p->rpb > 0x7fffffffLL)
+    return LA_ERR_UNSUPPORTED;
+
+  if (rope_on(rope)) {
+    p->rope.table = rope->table;
+    p->rope.pt = rope->d_t / 2;
+    p->rope.ph = rope->d_h / 2;
+    p->rope.pw = rope->d_w / 2;
+    p->rope.max_frames = rope->max_frames;
+    p->rope.gh = rope->grid_h;
+    p->rope.gw = rope->grid_w;
+  }
+  const int tiles = (in_dt == LA_BF16 ? 3 : 2) * kStep * 2 * lavr::kHeadDim * esize(in_dt);
+  p->lds_state = tiles + (int)(tab_pairs(rope, tpf, p->Tc) * 8);
+  p->lds_read = (int)(tab_pairs(rope, tpf, p->Tr) * 8);
+
+  const size_t rec = (size_t)lavr::kRec * sizeof(float);
+  const size_t part = (size_t)B * H * p->nb * p->cpb * rec;
+  const size_t prefix = (size_t)B * H * p->nb * rec;
+  p->ws_part = 0;
+  p->ws_prefix = align256(part);
+  p->ws_total = p->ws_prefix + align256(prefix);
+  return LA_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+int check_tensors(const void* q, const void* k, const void* v, void* out, la_dtype in_dt,
+                  la_dtype out_dt, const Plan& p) {
+  if (!q || !k || !v || !out) return LA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return LA_ERR_INVALID_ARG;
+  const size_t elems = (size_t)p.B * p.N * p.H * lavr::kHeadDim;
+  const size_t nin = elems * esize(in_dt), nout = elems * esize(out_dt);
+  if (overlaps(out, nout, q, nin) || overlaps(out, nout, k, nin) || overlaps(out, nout, v, nin))
+    return LA_ERR_INVALID_ARG;
+  return LA_OK;
+}
+
+int hip_status(int e) { return e == 0 ? LA_OK : LA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t rope_table_bytes(int d_t, int d_h, int d_w, int max_frames, int grid_h, int grid_w) {
+  if (d_t < 0 || d_h < 0 || d_w < 0 || ((d_t | d_h | d_w) & 1)) return 0;
+  if (max_frames < 1 || grid_h < 1 || grid_w < 1) return 0;
+  return 8 * ((size_t)max_frames * (d_t / 2) + (size_t)grid_h * (d_h / 2) + (size_t)grid_w * (d_w / 2));
+}
+
+int rope_table_build(la_rope* out, float* table_dev, size_t bytes, int head_dim, int d_t, int d_h,
+                     int d_w, int max_frames, int grid_h, int grid_w, double base, void* stream) {
+  if (!out || !table_dev || !aligned(table_dev, 16)) return LA_ERR_INVALID_ARG;
+  if (head_dim < 1) return LA_ERR_INVALID_ARG;
+  if (head_dim != lavr::kHeadDim) return LA_ERR_UNSUPPORTED;
+  if (d_t + d_h + d_w != head_dim) return LA_ERR_INVALID_ARG;
+  const size_t need = rope_table_bytes(d_t, d_h, d_w, max_frames, grid_h, grid_w);
+  if (need == 0 || bytes < need) return LA_ERR_INVALID_ARG;
+  if (!(base > 0.0) || !std::isfinite(base)) return LA_ERR_INVALID_ARG;
+  if ((long long)max_frames * (d_t / 2) > 0x7fffffffLL) return LA_ERR_UNSUPPORTED;
+  const int e = lavr::launch_rope_table(table_dev, d_t / 2, d_h / 2, d_w / 2, max_frames, grid_h,
+                                        grid_w, base, stream);
+  if (e != 0) return LA_ERR_HIP;
+  out->table = table_dev;
+  out->d_t = d_t;
+  out->d_h = d_h;
+  out->d_w = d_w;
+  out->max_frames = max_frames;
+  out->grid_h = grid_h;
+  out->grid_w = grid_w;
+  return LA_OK;
+}
+
+size_t la_workspace_bytes(int B, int H, int head_dim, int frames, int tokens_per_frame,
+                          int block_frames) {
+  Plan p;
+  if (make_plan(&p, B, H, head_dim, frames, tokens_per_frame, block_frames, nullptr, 0, LA_BF16) != LA_OK)
+    return 0;
+  return p.ws_total;
+}
+
+int la_block_causal_forward(const void* q, const void* k, const void* v, void* out,
+                            la_dtype in_dt, la_dtype out_dt, int B, int H, int head_dim,
+                            int frames, int tokens_per_frame, int block_frames,
+                            const la_rope* rope, float eps, void* ws, size_t ws_bytes,
+                            void* stream) {
+  if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return LA_ERR_INVALID_ARG;
+  if (!std::isfinite(eps) || eps < 0.f) return LA_ERR_INVALID_ARG;
+  Plan p;
+  int st = make_plan(&p, B, H, head_dim, frames, tokens_per_frame, block_frames, rope, 0, in_dt);
+  if (st != LA_OK) return st;
+  st = check_tensors(q, k, v, out, in_dt, out_dt, p);
+  if (st != LA_OK) return st;
+  if (!ws || !aligned(ws, 256) || ws_bytes < p.ws_total) return LA_ERR_INVALID_ARG;
+  return hip_status(lavr::launch_forward(p, q, k, v, out, in_dt == LA_BF16, out_dt == LA_BF16, eps,
+                                         ws, nullptr, nullptr, nullptr, nullptr, stream));
+}
+
+int la_block_causal_forward_timed(const void* q, const void* k, const void* v, void* out,
+                                  la_dtype in_dt, la_dtype out_dt, int B, int H, int head_dim,
+                                  int frames, int tokens_per_frame, int block_frames,
+                                  const la_rope* rope, float eps, void* ws, size_t ws_bytes,
+                                  void* stream, void* const* events) {
+  if (!events || !events[0] || !events[1] || !events[2] || !events[3]) return LA_ERR_INVALID_ARG;
+  if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return LA_ERR_INVALID_ARG;
+  if (!std::isfinite(eps) || eps < 0.f) return LA_ERR_INVALID_ARG;
+  Plan p;
+  int st = make_plan(&p, B, H, head_dim, frames, tokens_per_frame, block_frames, rope, 0, in_dt);
+  if (st != LA_OK) return st;
+  st = check_tensors(q, k, v, out, in_dt, out_dt, p);
+  if (st != LA_OK) return st;
+  if (!ws || !aligned(ws, 256) || ws_bytes < p.ws_total) return LA_ERR_INVALID_ARG;
+  return hip_status(lavr::launch_forward(p, q, k, v, out, in_dt == LA_BF16, out_dt == LA_BF16, eps,
+                                         ws, nullptr, nullptr, nullptr, nullptr, stream, events));
+}
+
+int la_state_init(la_state* st, float* S_dev, float* z_dev, int B, int H, int head_dim,
+                  void* stream) {
+  if (!st || !S_dev || !z_dev || !aligned(S_dev, 16) || !aligned(z_dev, 16)) return LA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || head_dim < 1) return LA_ERR_INVALID_ARG;
+  if (head_dim != lavr::kHeadDim) return LA_ERR_UNSUPPORTED;
+  if (B > 65535 || H > 65535 || (long long)B * H > (1LL << 24)) return LA_ERR_UNSUPPORTED;
+  const size_t nS = (size_t)B * H * head_dim * head_dim, nz = (size_t)B * H * head_dim;
+  if (overlaps(S_dev, nS * 4, z_dev, nz * 4)) return LA_ERR_INVALID_ARG;
+  int e = lavr::launch_zero(S_dev, nS, stream);
+  if (e == 0) e = lavr::launch_zero(z_dev, nz, stream);
+  if (e != 0) return LA_ERR_HIP;
+  st->S = S_dev;
+  st->z = z_dev;
+  st->B = B;
+  st->H = H;
+  st->head_dim = head_dim;
+  st->frames_done = 0;
+  return LA_OK;
+}
+
+int la_stream_block(la_state* st, const void* q, const void* k, const void* v, void* out,
+                    la_dtype in_dt, la_dtype out_dt, int B, int H, int head_dim,
+                    int block_frames, int tokens_per_frame, const la_rope* rope, float eps,
+                    int save, void* ws, size_t ws_bytes, void* stream) {
+  if (!st || !st->S || !st->z) return LA_ERR_INVALID_ARG;
+  if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return LA_ERR_INVALID_ARG;
+  if (!std::isfinite(eps) || eps < 0.f) return LA_ERR_INVALID_ARG;
+  if (st->frames_done < 0) return LA_ERR_INVALID_ARG;
+  if (B != st->B || H != st->H || head_dim != st->head_dim) return LA_ERR_STATE_MISMATCH;
+  Plan p;
+  int rc = make_plan(&p, B, H, head_dim, block_frames, tokens_per_frame, block_frames, rope,
+                     st->frames_done, in_dt);
+  if (rc != LA_OK) return rc;
+  rc = check_tensors(q, k, v, out, in_dt, out_dt, p);
+  if (rc != LA_OK) return rc;
+  if (!ws || !aligned(ws, 256) || ws_bytes < p.ws_total) return LA_ERR_INVALID_ARG;
+  const int e = lavr::launch_forward(p, q, k, v, out, in_dt == LA_BF16, out_dt == LA_BF16, eps, ws,
+                                     st->S, st->z, save ? st->S : nullptr, save ? st->z : nullptr,
+                                     stream);
+  if (e != 0) return LA_ERR_HIP;
+  if (save) st->frames_done += block_frames;
+  return LA_OK;
+}
+
+const char* la_status_string(int status) {
+  switch (status) {
+    case LA_OK: return "LA_OK";
+    case LA_ERR_INVALID_ARG: return "LA_ERR_INVALID_ARG: invalid argument";
+    case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED: not supported by this library";
+    case LA_ERR_STATE_MISMATCH: return "LA_ERR_STATE_MISMATCH: state shape does not match the call";
+    case LA_ERR_HIP: return "LA_ERR_HIP: HIP launch or runtime error";
+    default: return "unknown la_status";
+  }
+}
+
+const char* la_version(void) { return "0.1.0"; }
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// Internal interface between the host API layer (la_api.cpp) and the HIP
+// kernels (la_kernels.hip).  Not installed; the public ABI is include/la_vr.h.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lavr {
+
+constexpr int kHeadDim = 32;                       // the only head dim built
+constexpr int kRec = kHeadDim * kHeadDim + kHeadDim;  // floats of one (S, z) record
+constexpr int kHeadsPerGroup = 2;                  // heads handled by one workgroup
+
+// Rotary table as the kernels see it.
+struct RopeDev {
+  const float* table;   // (cos, sin) pairs; nullptr = RoPE off
+  int pt, ph, pw;       // pairs per section (d_t/2, d_h/2, d_w/2)
+  int max_frames;       // rows of the t section
+  int gh, gw;           // rows of the h and w sections
+};
+
+// Everything a launch needs; filled by the host planner.
+struct Plan {
+  int B, H;
+  int N;                // tokens per sequence in this call
+  int tpf;              // tokens per frame
+  int gw_div;           // divisor for row/col (grid_w, or 1 without spatial sections)
+  int L;                // tokens per block
+  int nb;               // blocks in this call
+  int hg;               // head groups = ceil(H / 2)
+  int cpb, Tc;          // block-state chunks per block, tokens per chunk
+  int rpb, Tr;          // readout tiles per block, tokens per tile
+  long long t0;         // frame offset of token 0 (frames already streamed)
+  uint64_t mag_tpf;     // floor(2^42 / tpf) + 1
+  uint64_t mag_gw;      // floor(2^42 / gw_div) + 1
+  RopeDev rope;
+  int lds_state;        // dynamic LDS bytes of the block-state kernel
+  int lds_read;         // dynamic LDS bytes of the readout kernel
+  size_t ws_part;       // byte offset of the per-chunk partial states
+  size_t ws_prefix;     // byte offset of the per-block prefix states
+  size_t ws_total;      // workspace bytes
+};
+
+// Launchers; each returns a hipError_t value (0 = success).
+int launch_rope_table(float* table, int pt, int ph, int pw, int max_frames, int gh, int gw,
+                      double base, void* stream);
+int launch_forward(const Plan& p, const void* q, const void* k, const void* v, void* out,
+                   int in_bf16, int out_bf16, float eps, void* ws,
+                   const float* S_init, const float* z_init, float* S_save, float* z_save,
+                   void* stream, void* const* events = nullptr);
+int launch_zero(float* p, size_t n, void* stream);
+
+}  // namespace lavr

@@ -1,0 +1,233 @@
+"""ctypes binding of liblavr (include/la_vr.h).
+
+Argument marshalling only: every step of the attention runs in the library's
+HIP kernels.  Torch supplies device memory and the current stream.  If the
+library is not built this module raises ImportError on import; there is no
+fallback path.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblavr.so")
+
+LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_STATE_MISMATCH, LA_ERR_HIP = range(5)
+LA_F32, LA_BF16 = 0, 1
+HEAD_DIM = 32
+EPS_DEFAULT = 1e-8
+
+
+class LaRope(ctypes.Structure):
+    _fields_ = [("table", ctypes.c_void_p), ("d_t", ctypes.c_int), ("d_h", ctypes.c_int),
+                ("d_w", ctypes.c_int), ("max_frames", ctypes.c_int), ("grid_h", ctypes.c_int),
+                ("grid_w", ctypes.c_int)]
+
+
+class LaState(ctypes.Structure):
+    _fields_ = [("S", ctypes.c_void_p), ("z", ctypes.c_void_p), ("B", ctypes.c_int),
+                ("H", ctypes.c_int), ("head_dim", ctypes.c_int), ("frames_done", ctypes.c_longlong)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(LIB_PATH)
+    c_int, c_size, c_vp, c_float, c_double = (ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p,
+                                             ctypes.c_float, ctypes.c_double)
+    sig = {
+        "rope_table_bytes": (c_size, [c_int] * 6),
+        "rope_table_build": (c_int, [ctypes.POINTER(LaRope), c_vp, c_size, c_int, c_int, c_int,
+                                     c_int, c_int, c_int, c_int, c_double, c_vp]),
+        "la_workspace_bytes": (c_size, [c_int] * 6),
+        "la_block_causal_forward": (c_int, [c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int,
+                                            c_int, c_int, c_int, c_int, ctypes.POINTER(LaRope),
+                                            c_float, c_vp, c_size, c_vp]),
+        "la_block_causal_forward_timed": (c_int, [c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int,
+                                                  c_int, c_int, c_int, c_int, c_int,
+                                                  ctypes.POINTER(LaRope), c_float, c_vp, c_size,
+                                                  c_vp, ctypes.POINTER(c_vp)]),
+        "la_state_init": (c_int, [ctypes.POINTER(LaState), c_vp, c_vp, c_int, c_int, c_int, c_vp]),
+        "la_stream_block": (c_int, [ctypes.POINTER(LaState), c_vp, c_vp, c_vp, c_vp, c_int, c_int,
+                                    c_int, c_int, c_int, c_int, c_int, ctypes.POINTER(LaRope),
+                                    c_float, c_int, c_vp, c_size, c_vp]),
+        "la_status_string": (ctypes.c_char_p, [c_int]),
+        "la_version": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+EXPORTS = ("rope_table_bytes", "rope_table_build", "la_workspace_bytes", "la_block_causal_forward",
+           "la_block_causal_forward_timed", "la_state_init", "la_stream_block", "la_status_string", "la_version")
+
+
+def status_string(code):
+    return lib.la_status_string(int(code)).decode()
+
+
+def _check(code, what):
+    if code == LA_OK:
+        return
+    msg = f"{what}: {status_string(code)}"
+    if code == LA_ERR_HIP:
+        raise RuntimeError(msg)
+    raise ValueError(msg)
+
+
+def _dtype_code(dt):
+    if dt == torch.bfloat16:
+        return LA_BF16
+    if dt == torch.float32:
+        return LA_F32
+    raise ValueError(f"unsupported dtype {dt}; use torch.bfloat16 or torch.float32")
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+# ---------------------------------------------------------------------- RoPE
+
+class RopeTable:
+    """Device rotary table built by rope_table_build, plus its la_rope description.
+
+    split = (d_t, d_h, d_w), grid = (rows, cols) of a frame; max_frames rows of the
+    t section.  A 1-D RoPE over the token index is split (32, 0, 0), grid (1, 1).
+    """
+
+    def __init__(self, split, grid, max_frames, base=10000.0, device="cuda"):
+        d_t, d_h, d_w = (int(s) for s in split)
+        gh, gw = (int(g) for g in grid)
+        nbytes = lib.rope_table_bytes(d_t, d_h, d_w, int(max_frames), gh, gw)
+        if nbytes == 0:
+            raise ValueError(f"invalid rotary table shape split={split} grid={grid} max_frames={max_frames}")
+        self.device = torch.device(device)
+        self.buffer = torch.empty(nbytes // 4, dtype=torch.float32, device=self.device)
+        self.desc = LaRope()
+        _check(lib.rope_table_build(ctypes.byref(self.desc), _ptr(self.buffer), nbytes, HEAD_DIM,
+                                    d_t, d_h, d_w, int(max_frames), gh, gw, float(base),
+                                    _stream(self.device)), "rope_table_build")
+        self.split, self.grid, self.max_frames, self.base = (d_t, d_h, d_w), (gh, gw), int(max_frames), float(base)
+
+
+def _rope_ptr(rope):
+    return ctypes.byref(rope.desc) if rope is not None else None
+
+
+# ------------------------------------------------------------------ one-shot
+
+def workspace_bytes(B, H, frames, tokens_per_frame, block_frames, head_dim=HEAD_DIM):
+    n = lib.la_workspace_bytes(int(B), int(H), int(head_dim), int(frames), int(tokens_per_frame),
+                               int(block_frames))
+    if n == 0:
+        raise ValueError("invalid shape for la_workspace_bytes")
+    return n
+
+
+_ws_cache = {}
+
+
+def _workspace(device, nbytes):
+    key = (device, torch.cuda.current_stream(device).cuda_stream)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf
+
+
+def _check_qkv(q, k, v):
+    for t in (q, k, v):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise ValueError("q, k, v must be CUDA (HIP) tensors")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous (B, N, H, head_dim) tensors")
+    if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share shape and dtype")
+    if q.device != k.device or q.device != v.device:
+        raise ValueError("q, k, v must be on one device")
+
+
+def block_causal_forward(q, k, v, block_frames, tokens_per_frame, rope=None, eps=EPS_DEFAULT,
+                         out=None, out_dtype=None, workspace=None):
+    """One-shot block-causal forward.  q, k, v: (B, N, H, 32), N = frames * tokens_per_frame."""
+    _check_qkv(q, k, v)
+    B, N, H, d = q.shape
+    if N % tokens_per_frame:
+        raise ValueError("N must be a multiple of tokens_per_frame")
+    frames = N // tokens_per_frame
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, N, H, d), dtype=out_dtype, device=q.device)
+    elif out.shape != q.shape or out.dtype != out_dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor of q's shape and out_dtype on q's device")
+    need = lib.la_workspace_bytes(B, H, d, frames, int(tokens_per_frame), int(block_frames))
+    ws = _workspace(q.device, need) if workspace is None else workspace
+    _check(lib.la_block_causal_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(q.dtype),
+                                       _dtype_code(out_dtype), B, H, d, frames,
+                                       int(tokens_per_frame), int(block_frames), _rope_ptr(rope),
+                                       float(eps), _ptr(ws), ws.numel() * ws.element_size(),
+                                       _stream(q.device)), "la_block_causal_forward")
+    return out
+
+
+# ----------------------------------------------------------------- streaming
+
+class StreamState:
+    """Constant-size (S, z) cache of one generation stream, on one device."""
+
+    def __init__(self, B, H, head_dim=HEAD_DIM, device="cuda"):
+        self.device = torch.device(device)
+        self.S = torch.empty((B, H, head_dim, head_dim), dtype=torch.float32, device=self.device)
+        self.z = torch.empty((B, H, head_dim), dtype=torch.float32, device=self.device)
+        self.desc = LaState()
+        _check(lib.la_state_init(ctypes.byref(self.desc), _ptr(self.S), _ptr(self.z), int(B), int(H),
+                                 int(head_dim), _stream(self.device)), "la_state_init")
+
+    @property
+    def frames_done(self):
+        return int(self.desc.frames_done)
+
+    def snapshot(self):
+        """Host copy of the full resumable state (S, z, frames_done)."""
+        return self.S.cpu(), self.z.cpu(), self.frames_done
+
+    def restore(self, snap):
+        S, z, frames_done = snap
+        self.S.copy_(S)
+        self.z.copy_(z)
+        self.desc.frames_done = int(frames_done)
+
+    def step(self, q, k, v, tokens_per_frame, rope=None, eps=EPS_DEFAULT, save=True, out=None,
+             out_dtype=None, workspace=None):
+        """Run one block (all of q's tokens) against the cache; see la_stream_block."""
+        _check_qkv(q, k, v)
+        B, N, H, d = q.shape
+        if N % tokens_per_frame:
+            raise ValueError("N must be a multiple of tokens_per_frame")
+        frames = N // tokens_per_frame
+        out_dtype = q.dtype if out_dtype is None else out_dtype
+        if out is None:
+            out = torch.empty((B, N, H, d), dtype=out_dtype, device=q.device)
+        elif out.shape != q.shape or out.dtype != out_dtype or not out.is_contiguous():
+            raise ValueError("out must be a contiguous tensor of q's shape and out_dtype")
+        need = lib.la_workspace_bytes(B, H, d, frames, int(tokens_per_frame), frames)
+        ws = _workspace(q.device, need) if workspace is None else workspace
+        _check(lib.la_stream_block(ctypes.byref(self.desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                   _dtype_code(q.dtype), _dtype_code(out_dtype), B, H, d, frames,
+                                   int(tokens_per_frame), _rope_ptr(rope), float(eps), int(bool(save)),
+                                   _ptr(ws), ws.numel() * ws.element_size(), _stream(q.device)),
+               "la_stream_block")
+        return out

@@ -1,0 +1,155 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+header declares, sizes its buffers, and rejects bad arguments with the right
+status before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lavr():
+    import __graft_entry__
+    __graft_entry__.ensure_built()
+    from linear_attention_video_relu_amd import lavr
+    return lavr
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "la_vr.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_function(lavr):
+    names = header_functions()
+    assert set(names) == set(lavr.EXPORTS), names
+    raw = ctypes.CDLL(lavr.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_version_and_status_strings(lavr):
+    assert lavr.lib.la_version() == b"0.1.0"
+    for code in range(5):
+        assert lavr.status_string(code).startswith("LA_")
+    assert "unknown" in lavr.status_string(99)
+
+
+def test_rope_table_bytes(lavr):
+    assert lavr.lib.rope_table_bytes(8, 12, 12, 240, 30, 52) == 8 * (240 * 4 + 30 * 6 + 52 * 6)
+    assert lavr.lib.rope_table_bytes(32, 0, 0, 256, 1, 1) == 8 * 256 * 16
+    assert lavr.lib.rope_table_bytes(7, 13, 12, 10, 30, 52) == 0     # odd section
+    assert lavr.lib.rope_table_bytes(8, 12, 12, 0, 30, 52) == 0      # no frames
+
+
+def test_workspace_bytes(lavr):
+    # minute config: 30 blocks of 12480 tokens, 70 heads
+    n = lavr.workspace_bytes(1, 70, 240, 1560, 8)
+    rec = (32 * 32 + 32) * 4
+    assert n >= 70 * 30 * rec            # at least the per-block prefix states
+    assert n < 0.05 * 1 * 374400 * 70 * 32 * 2 * 4   # small next to q, k, v, out
+    assert lavr.lib.la_workspace_bytes(1, 70, 64, 240, 1560, 8) == 0   # head_dim 64 not built
+    assert lavr.lib.la_workspace_bytes(0, 70, 32, 240, 1560, 8) == 0
+
+
+FAKE = 0x100000          # 16- and 256-byte aligned, never dereferenced: every call below fails validation
+
+
+def call_forward(lavr, **kw):
+    args = dict(q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, out=FAKE + 0x3000000,
+                in_dt=lavr.LA_BF16, out_dt=lavr.LA_BF16, B=1, H=2, d=32, frames=4, tpf=6,
+                bf=2, rope=None, eps=1e-8, ws=FAKE + 0x4000000, ws_bytes=1 << 20)
+    args.update(kw)
+    return lavr.lib.la_block_causal_forward(
+        ctypes.c_void_p(args["q"]), ctypes.c_void_p(args["k"]), ctypes.c_void_p(args["v"]),
+        ctypes.c_void_p(args["out"]), args["in_dt"], args["out_dt"], args["B"], args["H"],
+        args["d"], args["frames"], args["tpf"], args["bf"], args["rope"], args["eps"],
+        ctypes.c_void_p(args["ws"]), args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), 1),                      # null pointer
+    (dict(k=FAKE + 2), 1),               # misaligned
+    (dict(B=0), 1),
+    (dict(H=-1), 1),
+    (dict(frames=0), 1),
+    (dict(tpf=0), 1),
+    (dict(bf=0), 1),
+    (dict(d=64), 2),                     # head_dim 64 is not built
+    (dict(in_dt=7), 1),
+    (dict(eps=-1.0), 1),
+    (dict(eps=float("inf")), 1),
+    (dict(ws_bytes=16), 1),              # workspace too small
+    (dict(ws=FAKE + 8), 1),              # workspace misaligned
+    (dict(out=FAKE + 0x1000000 + 64), 1),  # out overlaps k
+])
+def test_forward_rejects_bad_arguments(lavr, kw, code):
+    assert call_forward(lavr, **kw) == code
+
+
+def rope_desc(lavr, **kw):
+    r = lavr.LaRope()
+    d = dict(table=FAKE + 0x5000000, d_t=8, d_h=12, d_w=12, max_frames=4, grid_h=2, grid_w=3)
+    d.update(kw)
+    for k_, v_ in d.items():
+        setattr(r, k_, v_)
+    return r
+
+
+@pytest.mark.parametrize("kw", [
+    dict(d_t=7, d_h=13),                 # odd section
+    dict(d_t=8, d_h=12, d_w=10),         # sections do not sum to head_dim
+    dict(grid_h=3),                      # grid does not match tokens per frame
+    dict(max_frames=3),                  # frames past the table
+    dict(table=FAKE + 0x5000000 + 4),    # misaligned table
+])
+def test_forward_rejects_bad_rope(lavr, kw):
+    r = rope_desc(lavr, **kw)
+    assert call_forward(lavr, rope=ctypes.byref(r)) == lavr.LA_ERR_INVALID_ARG
+
+
+def test_rope_table_build_rejects(lavr):
+    r = lavr.LaRope()
+    f = lavr.lib.rope_table_build
+    ok = dict(dt=8, dh=12, dw=12, mf=4, gh=2, gw=3)
+    assert f(ctypes.byref(r), ctypes.c_void_p(FAKE), 8, 32, 8, 12, 12, 4, 2, 3, 10000.0, None) == 1   # bytes
+    assert f(ctypes.byref(r), ctypes.c_void_p(FAKE), 1 << 20, 64, 8, 12, 12, 4, 2, 3, 10000.0, None) == 2
+    assert f(ctypes.byref(r), ctypes.c_void_p(FAKE), 1 << 20, 32, 8, 12, 12, 4, 2, 3, -1.0, None) == 1
+    assert f(ctypes.byref(r), ctypes.c_void_p(0), 1 << 20, 32, 8, 12, 12, 4, 2, 3, 10000.0, None) == 1
+    assert f(None, ctypes.c_void_p(FAKE), 1 << 20, 32, 8, 12, 12, 4, 2, 3, 10000.0, None) == 1
+    assert ok
+
+
+def test_stream_block_state_checks(lavr):
+    st = lavr.LaState()
+    st.S, st.z, st.B, st.H, st.head_dim, st.frames_done = FAKE, FAKE + 0x100000, 2, 4, 32, 0
+    f = lavr.lib.la_stream_block
+    p = [ctypes.c_void_p(FAKE + i * 0x1000000) for i in range(1, 5)]
+    ws = ctypes.c_void_p(FAKE + 0x6000000)
+    # batch / heads / head_dim that differ from the state's
+    assert f(ctypes.byref(st), *p, 1, 1, 1, 4, 32, 3, 6, None, 1e-8, 1, ws, 1 << 24, None) == 3
+    assert f(ctypes.byref(st), *p, 1, 1, 2, 5, 32, 3, 6, None, 1e-8, 1, ws, 1 << 24, None) == 3
+    # small workspace
+    assert f(ctypes.byref(st), *p, 1, 1, 2, 4, 32, 3, 6, None, 1e-8, 1, ws, 64, None) == 1
+    # frames past the rotary table at this offset
+    st.frames_done = 3
+    r = rope_desc(lavr, max_frames=5)
+    assert f(ctypes.byref(st), *p, 1, 1, 2, 4, 32, 3, 6, ctypes.byref(r), 1e-8, 1, ws, 1 << 24, None) == 1
+    st.S = 0
+    assert f(ctypes.byref(st), *p, 1, 1, 2, 4, 32, 3, 6, None, 1e-8, 1, ws, 1 << 24, None) == 1
+    assert st.frames_done == 3           # nothing committed by a rejected call
+
+
+def test_state_init_rejects(lavr):
+    st = lavr.LaState()
+    f = lavr.lib.la_state_init
+    assert f(ctypes.byref(st), ctypes.c_void_p(0), ctypes.c_void_p(FAKE), 1, 1, 32, None) == 1
+    assert f(ctypes.byref(st), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 4), 1, 1, 32, None) == 1
+    assert f(ctypes.byref(st), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 4096), 1, 1, 64, None) == 2
+    assert f(ctypes.byref(st), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 64), 1, 1, 32, None) == 1  # overlap

@@ -1,0 +1,301 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small cases compare every element; the full-size workloads compare whole
+(batch, head) slices the oracle computes in seconds.  bf16 outputs are scored
+with the output's own rounding allowed (see helpers.err_bf16_out); bf16 inputs
+with fp32 outputs are scored with the plain metric.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import (TOL_BF16, TOL_F32, device_inputs, err_bf16_out, oracle_head, to_f64_torch)
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def lavr():
+    import __graft_entry__
+    __graft_entry__.ensure_built()
+    from linear_attention_video_relu_amd import lavr
+    return lavr
+
+
+def W():
+    from linear_attention_video_relu_amd import workloads
+    return workloads
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def rope_for(lavr, cfg, frames=None):
+    if cfg.get("rope") is None:
+        return None
+    return lavr.RopeTable(cfg["rope"]["split"], cfg["grid"], frames or cfg["frames"],
+                          cfg["rope"]["base"], DEV)
+
+
+def small_cfg(**kw):
+    """A small 3-D RoPE workload: frames of 6 x 10 tokens, ragged last block."""
+    base = dict(index=100, B=2, H=3, head_dim=32, frames=11, tokens_per_frame=60, grid=(6, 10),
+                block_frames=3, dtype="bf16", rope={"split": (8, 12, 12), "base": 10000.0},
+                scale=1.0, outlier_frac=0.05, outlier_scale=8.0, name="small3d")
+    base.update(kw)
+    return base
+
+
+def full_oracle(cfg, arrs):
+    w = W()
+    return oracle.forward(*(w.to_f64(cfg, arrs[t]) for t in w.TENSORS), cfg["tokens_per_frame"],
+                          cfg["block_frames"], w.oracle_rope(cfg))
+
+
+# -------------------------------------------------------------- small, every element
+
+def test_tiny_f32_matches_oracle(lavr):
+    w = W()
+    cfg = w.workload("tiny_f32")
+    say("case tiny_f32 one-shot")
+    arrs, (q, k, v) = device_inputs(cfg, DEV)
+    out = lavr.block_causal_forward(q, k, v, cfg["block_frames"], 1, rope_for(lavr, cfg))
+    torch.cuda.synchronize()
+    err = oracle.rel_err(to_f64_torch(out), full_oracle(cfg, arrs))
+    say(f"tiny_f32 rel err {err:.3e}")
+    assert err <= TOL_F32
+
+
+@pytest.mark.parametrize("kw", [
+    dict(),                                           # B=2, H=3 (odd: a half-empty head group)
+    dict(frames=12, block_frames=4, H=1, B=1),        # whole blocks, one head
+    dict(frames=5, block_frames=8),                   # one block shorter than block_frames
+    dict(frames=40, block_frames=3, H=2, B=1, tokens_per_frame=48, grid=(6, 8)),  # many tiles
+])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_small_bf16_matches_oracle(lavr, kw, out_dtype):
+    cfg = small_cfg(**kw)
+    say(f"case small bf16 {kw} out={out_dtype}")
+    arrs, (q, k, v) = device_inputs(cfg, DEV)
+    od = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    out = lavr.block_causal_forward(q, k, v, cfg["block_frames"], cfg["tokens_per_frame"],
+                                    rope_for(lavr, cfg), out_dtype=od)
+    torch.cuda.synchronize()
+    ref = full_oracle(cfg, arrs)
+    got = to_f64_torch(out)
+    if out_dtype == "f32":
+        err = oracle.rel_err(got, ref)
+        say(f"  rel err {err:.3e}")
+        assert err <= TOL_BF16
+        assert err <= 1e-4          # the hi/lo operand split keeps ~17-bit accuracy
+    else:
+        err = err_bf16_out(got, ref)
+        say(f"  rel err beyond bf16 rounding {err:.3e} (plain {oracle.rel_err(got, ref):.3e})")
+        assert err <= TOL_BF16
+
+
+def test_bf16_output_is_rne_of_f32_output(lavr):
+    """bf16 outputs are the fp32 results rounded to nearest even, bit for bit."""
+    cfg = small_cfg(frames=9)
+    say("case bf16 out == rne(f32 out)")
+    _, (q, k, v) = device_inputs(cfg, DEV)
+    rope = rope_for(lavr, cfg)
+    o32 = lavr.block_causal_forward(q, k, v, 3, cfg["tokens_per_frame"], rope, out_dtype=torch.float32)
+    o16 = lavr.block_causal_forward(q, k, v, 3, cfg["tokens_per_frame"], rope, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+
+
+def test_f32_small_3d(lavr):
+    cfg = small_cfg(dtype="f32")
+    say("case small f32 3-D RoPE")
+    arrs, (q, k, v) = device_inputs(cfg, DEV)
+    out = lavr.block_causal_forward(q, k, v, cfg["block_frames"], cfg["tokens_per_frame"], rope_for(lavr, cfg))
+    torch.cuda.synchronize()
+    err = oracle.rel_err(to_f64_torch(out), full_oracle(cfg, arrs))
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL_F32
+
+
+def test_rope_off_constant_v(lavr):
+    """RoPE off and v constant: out == v up to eps / D."""
+    cfg = small_cfg(dtype="f32", rope=None)
+    say("case rope off, v constant")
+    arrs, (q, k, v) = device_inputs(cfg, DEV)
+    q, k = q.abs() + 0.1, k.abs() + 0.1
+    c = torch.linspace(-2, 3, 32, device=DEV)
+    v = c.expand_as(q).contiguous()
+    out = lavr.block_causal_forward(q, k, v, cfg["block_frames"], cfg["tokens_per_frame"], None)
+    torch.cuda.synchronize()
+    assert torch.max(torch.abs(out - v)).item() <= 1e-5
+
+
+def test_one_token_blocks_and_zero_queries(lavr):
+    """Blocks of one token (token-causal form) and tokens whose phi(q) is all zero."""
+    cfg = small_cfg(dtype="f32", frames=40, tokens_per_frame=1, grid=(1, 1), block_frames=1,
+                    rope={"split": (32, 0, 0), "base": 10000.0}, B=1, H=2)
+    say("case one-token blocks, zero queries")
+    arrs, _ = device_inputs(cfg, DEV)
+    arrs["q"][:, 7] = -np.abs(arrs["q"][:, 7])
+    w = W()
+    q, k, v = (w.to_torch(cfg, arrs[t], DEV) for t in w.TENSORS)
+    out = lavr.block_causal_forward(q, k, v, 1, 1, rope_for(lavr, cfg))
+    torch.cuda.synchronize()
+    got = to_f64_torch(out)
+    ref = oracle.token_causal_cumsum(*(w.to_f64(cfg, arrs[t]) for t in w.TENSORS), 1, w.oracle_rope(cfg))
+    assert oracle.rel_err(got, ref) <= TOL_F32
+    assert np.all(got[:, 7] == 0.0)
+
+
+def test_causality_bitwise(lavr):
+    cfg = small_cfg(frames=9)
+    say("case causality")
+    arrs, (q, k, v) = device_inputs(cfg, DEV)
+    rope = rope_for(lavr, cfg)
+    o1 = lavr.block_causal_forward(q, k, v, 3, cfg["tokens_per_frame"], rope).clone()
+    L = 3 * cfg["tokens_per_frame"]
+    q2, k2, v2 = q.clone(), k.clone(), v.clone()
+    q2[:, L:] = -q2[:, L:]
+    k2[:, L:] = 3 * k2[:, L:]
+    v2[:, L:] = 1.0
+    o2 = lavr.block_causal_forward(q2, k2, v2, 3, cfg["tokens_per_frame"], rope)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[:, :L], o2[:, :L])
+    assert not torch.equal(o1[:, L:], o2[:, L:])
+
+
+def test_deterministic(lavr):
+    cfg = small_cfg(frames=9)
+    say("case determinism")
+    _, (q, k, v) = device_inputs(cfg, DEV)
+    rope = rope_for(lavr, cfg)
+    a = lavr.block_causal_forward(q, k, v, 3, cfg["tokens_per_frame"], rope).clone()
+    b = lavr.block_causal_forward(q, k, v, 3, cfg["tokens_per_frame"], rope)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+# ----------------------------------------------------------------------- streaming
+
+def stream_run(lavr, st, q, k, v, cfg, rope, nblk, L, save=True, out_dtype=None):
+    outs = []
+    for j in range(nblk):
+        sl = slice(j * L, (j + 1) * L)
+        outs.append(st.step(q[:, sl].contiguous(), k[:, sl].contiguous(), v[:, sl].contiguous(),
+                            cfg["tokens_per_frame"], rope, save=save, out_dtype=out_dtype))
+    return torch.cat(outs, dim=1)
+
+
+def test_streaming_equals_one_shot_small(lavr):
+    cfg = small_cfg(frames=12)
+    say("case streaming small")
+    arrs, (q, k, v) = device_inputs(cfg, DEV)
+    rope = rope_for(lavr, cfg)
+    L = 3 * cfg["tokens_per_frame"]
+    one = lavr.block_causal_forward(q, k, v, 3, cfg["tokens_per_frame"], rope, out_dtype=torch.float32)
+    st = lavr.StreamState(cfg["B"], cfg["H"], device=DEV)
+    got = stream_run(lavr, st, q, k, v, cfg, rope, 4, L, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert st.frames_done == 12
+    assert torch.equal(got, one)
+    assert oracle.rel_err(to_f64_torch(got), full_oracle(cfg, arrs)) <= 1e-4
+
+
+def test_streaming_save_flag_and_resume(lavr):
+    cfg = small_cfg(frames=12, B=1, H=2)
+    say("case streaming save/resume/isolation")
+    _, (q, k, v) = device_inputs(cfg, DEV)
+    rope = rope_for(lavr, cfg)
+    tpf = cfg["tokens_per_frame"]
+    L = 3 * tpf
+    ref_state = lavr.StreamState(1, 2, device=DEV)
+    ref = stream_run(lavr, ref_state, q, k, v, cfg, rope, 4, L)
+
+    st = lavr.StreamState(1, 2, device=DEV)
+    stream_run(lavr, st, q[:, :2 * L], k[:, :2 * L], v[:, :2 * L], cfg, rope, 2, L)
+    snap = st.snapshot()
+    # save=0: several steps of one block read the cache without changing it
+    sl = slice(2 * L, 3 * L)
+    a = st.step(q[:, sl].contiguous(), k[:, sl].contiguous(), v[:, sl].contiguous(), tpf, rope, save=False)
+    b = st.step(q[:, sl].contiguous(), k[:, sl].contiguous(), v[:, sl].contiguous(), tpf, rope, save=False)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and st.frames_done == 6
+    assert torch.equal(st.S.cpu(), snap[0]) and torch.equal(st.z.cpu(), snap[1])
+    # resume from the host snapshot in a fresh state object; interleave with another stream
+    st2 = lavr.StreamState(1, 2, device=DEV)
+    st2.restore(snap)
+    other = lavr.StreamState(1, 2, device=DEV)
+    outs = []
+    for j in (2, 3):
+        sl = slice(j * L, (j + 1) * L)
+        outs.append(st2.step(q[:, sl].contiguous(), k[:, sl].contiguous(), v[:, sl].contiguous(), tpf, rope))
+        other.step(v[:, sl].contiguous(), q[:, sl].contiguous(), k[:, sl].contiguous(), tpf, rope)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], a)
+    assert torch.equal(torch.cat(outs, 1), ref[:, 2 * L:])
+    assert torch.equal(st2.S, ref_state.S) and st2.frames_done == 12
+
+
+def test_stream_state_mismatch_raises(lavr):
+    st = lavr.StreamState(1, 2, device=DEV)
+    x = torch.zeros((2, 60, 2, 32), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError, match="STATE_MISMATCH"):
+        st.step(x, x.clone(), x.clone(), 60, None)
+    with pytest.raises(ValueError, match="INVALID_ARG"):
+        lavr.block_causal_forward(x, x.clone(), x.clone(), 1, 60, None, eps=-1.0)
+
+
+# ------------------------------------------------------------- full-size workloads
+
+def check_heads(cfg, arrs, out, heads, label):
+    worst = 0.0
+    for b, h in heads:
+        ref = oracle_head(cfg, arrs, b, h)
+        got = to_f64_torch(out[b, :, h])
+        e = err_bf16_out(got, ref) if out.dtype == torch.bfloat16 else oracle.rel_err(got, ref)
+        say(f"  {label} b={b} h={h} err {e:.3e} (plain {oracle.rel_err(got, ref):.3e})")
+        worst = max(worst, e)
+    return worst
+
+
+@pytest.mark.parametrize("name,heads", [
+    ("clip480p_bf16", [(0, 0), (0, 1), (0, 34), (0, 69)]),
+    ("clip720p_bf16", [(0, 0), (1, 37), (1, 69)]),
+    ("minute_bf16", [(0, 0), (0, 41)]),
+])
+def test_full_size_one_shot(lavr, name, heads):
+    w = W()
+    cfg = w.workload(name)
+    say(f"case full-size {name}")
+    arrs, (q, k, v) = device_inputs(cfg, DEV)
+    rope = rope_for(lavr, cfg)
+    out = lavr.block_causal_forward(q, k, v, cfg["block_frames"], cfg["tokens_per_frame"], rope)
+    torch.cuda.synchronize()
+    assert check_heads(cfg, arrs, out, heads, name) <= TOL_BF16
+    # the whole output is finite and a sampled token of every head agrees too
+    assert torch.isfinite(out).all().item()
+    del out, q, k, v
+    torch.cuda.empty_cache()
+
+
+def test_full_size_streaming(lavr):
+    """40 streamed 3-frame blocks (B=2, 70 heads) == one-shot over 120 frames, bit for bit."""
+    w = W()
+    cfg = w.workload("stream_bf16")
+    say("case full-size streaming 40 x 3 frames")
+    arrs, (q, k, v) = device_inputs(cfg, DEV)
+    rope = rope_for(lavr, cfg)
+    tpf = cfg["tokens_per_frame"]
+    L = 3 * tpf
+    one = lavr.block_causal_forward(q, k, v, 3, tpf, rope)
+    st = lavr.StreamState(cfg["B"], cfg["H"], device=DEV)
+    got = stream_run(lavr, st, q, k, v, cfg, rope, 40, L)
+    torch.cuda.synchronize()
+    assert st.frames_done == 120
+    assert torch.equal(got, one)
+    assert check_heads(cfg, arrs, got, [(0, 5), (1, 60)], "stream") <= TOL_BF16
