@@ -13,8 +13,22 @@ using lavr::Plan;
 
 namespace {
 
-constexpr int kStateTarget = 1024;     // tokens per block-state chunk (target)
-constexpr int kReadTarget = 512;       // tokens per readout tile (target)
+// Work split.  A block-state chunk or readout tile holds at most kStateMax /
+// kReadMax tokens (long chunks keep the partial-state traffic and the prefix
+// kernel small), and the launch is split finer until it has at least kMinWg
+// workgroups (a single streamed block must still fill 256 CUs).
+#ifndef LAVR_STATE_MAX
+#define LAVR_STATE_MAX 3200
+#endif
+#ifndef LAVR_READ_MAX
+#define LAVR_READ_MAX 1024
+#endif
+#ifndef LAVR_MIN_WG
+#define LAVR_MIN_WG 1024
+#endif
+constexpr int kStateMax = LAVR_STATE_MAX;
+constexpr int kReadMax = LAVR_READ_MAX;
+constexpr int kMinWg = LAVR_MIN_WG;
 constexpr int kTabLdsMax = 32768;      // LDS bytes for a staged rotary window
 constexpr int kStep = 64;              // block-state kernel step (tokens)
 constexpr long long kTwo42 = 1LL << 42;
@@ -54,19 +68,24 @@ long long tab_pairs(const la_rope* r, int tpf, int tokens) {
   return nf * (r->d_t / 2) + (long long)r->grid_h * (r->d_h / 2) + (long long)r->grid_w * (r->d_w / 2);
 }
 
-// Split a block of L tokens into chunks of about `target` tokens (a multiple of
-// `mult`) whose rotary window fits in LDS.  Returns false if none fits.
-bool split_block(int L, int target, int mult, const la_rope* r, int tpf, int* n_out, int* T_out) {
-  long long n = cdiv(L, target);
+// Split a block of L tokens into n chunks of T tokens (a multiple of `mult`):
+// at most max_tokens per chunk, at least min_n chunks, the rotary window of a
+// chunk fits in LDS and its byte span (plus the 256 tokens a kernel may run
+// ahead) stays within the 32-bit buffer offsets the kernels use; row_bytes is
+// the widest token row (fp32).  Returns false if no split fits.
+bool split_block(int L, int max_tokens, long long min_n, int mult, const la_rope* r, int tpf,
+                 long long row_bytes, int* n_out, int* T_out) {
+  long long n = cdiv(L, max_tokens);
+  if (n < min_n) n = min_n;
   for (;;) {
-    long long T = round_up(cdiv(L, n), mult);
-    if (tab_pairs(r, tpf, (int)T) * 8 <= kTabLdsMax) {
-      *n_out = (int)n;
+    const long long T = round_up(cdiv(L, n), mult);
+    if (tab_pairs(r, tpf, (int)T) * 8 <= kTabLdsMax && (T + 256) * row_bytes < (1LL << 31)) {
+      *n_out = (int)cdiv(L, T);
       *T_out = (int)T;
       return true;
     }
     if (T <= mult) return false;
-    ++n;
+    n = cdiv(L, T - mult);
   }
 }
 
@@ -95,8 +114,12 @@ int make_plan(Plan* p, int B, int H, int head_dim, int frames, int tpf, int bloc
   p->t0 = t0;
   p->mag_tpf = (uint64_t)(kTwo42 / tpf) + 1;
   p->mag_gw = (uint64_t)(kTwo42 / gw_div) + 1;
-  if (!split_block(p->L, kStateTarget, kStep, rope, tpf, &p->cpb, &p->Tc)) return LA_ERR_UNSUPPORTED;
-  if (!split_block(p->L, kReadTarget, 32, rope, tpf, &p->rpb, &p->Tr)) return LA_ERR_UNSUPPORTED;
+  const long long row_bytes = (long long)H * head_dim * 4;
+  const long long min_n = cdiv(kMinWg, (long long)B * p->hg * p->nb);
+  if (!split_block(p->L, kStateMax, min_n, kStep, rope, tpf, row_bytes, &p->cpb, &p->Tc))
+    return LA_ERR_UNSUPPORTED;
+  if (!split_block(p->L, kReadMax, min_n, 64, rope, tpf, row_bytes, &p->rpb, &p->Tr))
+    return LA_ERR_UNSUPPORTED;
   if ((long long)p->hg * p->nb * p->cpb > 0x7fffffffLL || (long long)p->hg * p->nb * p->rpb > 0x7fffffffLL)
     return LA_ERR_UNSUPPORTED;
 

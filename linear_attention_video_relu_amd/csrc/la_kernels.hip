@@ -18,8 +18,11 @@
 //
 // Data in HBM: q, k, v, out are (B, N, H, 32) row-major.  A token's two-head
 // slice is 128 contiguous bytes in bf16 (256 in fp32), so each workgroup owns
-// a pair of heads and every global access is a whole 16-byte lane chunk of a
-// fully used 128-byte line.
+// a pair of heads and a lane moves 16-byte pieces of fully used 128-byte
+// lines.  Q, K, V and out are reached through buffer resources that span one
+// workgroup's token range: the hardware range check turns reads past the end
+// into zeros and drops writes past the end, so ragged tails need no branches,
+// and lane offsets stay 32-bit.
 //
 // bf16 arithmetic: bf16 MFMA operands that are not exact bf16 values (the
 // rotated keys and queries, the prefix state) are split as x = hi + lo with
@@ -41,21 +44,31 @@ constexpr int REC = kRec;
 constexpr int NT = 256;              // threads of the state and readout workgroups
 constexpr int STEP = 64;             // tokens per step of the state kernel
 constexpr int TCOLS = 2 * D;         // an LDS tile row holds two heads
-constexpr int SCAN_NT = 64;          // threads of the prefix workgroups
+constexpr int RSRC_WORD3 = 0x00020000;  // gfx9 raw buffer: 32-bit data, range checked
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// Token position bookkeeping shared by the kernels: how to split a token index
+// into (frame, row, col), and the step that advances it by 64 tokens.
+struct PosArgs {
+  int tpf, gw, ghd;          // tokens per frame, row length, rows per frame
+  int adv_f, adv_r, adv_c;   // 64 tokens = adv_f frames + adv_r rows + adv_c tokens
+  long long t0;              // frame offset (frames already streamed)
+  uint64_t mag_tpf, mag_gw;
+};
 
 struct StateArgs {
   const void* k;
   const void* v;
   float* part;
-  int H, N, L, nb, cpb, Tc, hg, tpf, gw;
-  long long t0;
-  uint64_t mag_tpf, mag_gw;
+  int H, N, L, nb, cpb, Tc, hg;
+  PosArgs pos;
   RopeDev rope;
 };
 
@@ -74,9 +87,8 @@ struct ReadArgs {
   void* out;
   const float* prefix;
   float eps;
-  int H, N, L, nb, rpb, Tr, hg, tpf, gw;
-  long long t0;
-  uint64_t mag_tpf, mag_gw;
+  int H, N, L, nb, rpb, Tr, hg;
+  PosArgs pos;
   RopeDev rope;
 };
 
@@ -86,8 +98,6 @@ __device__ __forceinline__ uint32_t fast_div(uint32_t n, uint64_t mag) {
   // floor(n / d) with mag = floor(2^42 / d) + 1; exact while n * d < 2^42.
   return (uint32_t)(((uint64_t)n * mag) >> 42);
 }
-
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 // Two floats rounded to bf16 (nearest, ties to even; v_cvt_pk_bf16_f32), packed
 // low = a, high = b.
@@ -111,27 +121,45 @@ __device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 
-// Loads 16 bytes of element type T and widens them to floats.
-template <typename T> struct Vec16;
-template <> struct Vec16<uint16_t> {
-  static constexpr int N = 8;
-  __device__ static void widen(u32x4 r, float* x) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = __uint_as_float(r[i] << 16);
-      x[2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
-    }
-  }
-};
-template <> struct Vec16<float> {
-  static constexpr int N = 4;
-  __device__ static void widen(u32x4 r, float* x) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(r[i]);
-  }
-};
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, RSRC_WORD3);
+}
 
-__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+// ------------------------------------------------------------ lane chunks
+//
+// Both the block-state loader and the readout give a lane channels 8c .. 8c+7
+// (c = 0..3) of one token, for each of the two heads of its group.  A chunk of
+// 8 elements is one 16-byte load in bf16 and two in fp32.
+
+template <typename T> struct Raw8 { u32x4 r[sizeof(T) / 2]; };
+
+template <typename T>
+__device__ __forceinline__ Raw8<T> bload8(__amdgpu_buffer_rsrc_t rs, int off) {
+  Raw8<T> o;
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 2); ++i) o.r[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16 * i, 0, 0);
+  return o;
+}
+
+// phi = ReLU on the raw bits (a sign bit set means <= 0; the integer max with 0
+// clears it), then widen to fp32.
+__device__ __forceinline__ void relu_widen(const Raw8<uint16_t>& r, float* x) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // copy the element to a scalar first: bit-casting a subscripted vector
+    // element directly reads element 0 with this compiler
+    const uint32_t ri = r.r[0][i];
+    const s16x2 z = {0, 0};
+    const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(s16x2, ri), z));
+    x[2 * i] = __uint_as_float(w << 16);
+    x[2 * i + 1] = __uint_as_float(w & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void relu_widen(const Raw8<float>& r, float* x) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    x[i] = __uint_as_float((uint32_t)__builtin_elementwise_max((int)r.r[i >> 2][i & 3], 0));
+}
 
 // --------------------------------------------------------------------- RoPE
 //
@@ -160,65 +188,108 @@ __device__ __forceinline__ TabWindow stage_table(float2* lds, const RopeDev& r, 
   return w;
 }
 
-template <int NP>
-struct PairLut {
-  int base[NP], stride[NP], sel[NP];
-  __device__ void init(const RopeDev& r, const TabWindow& w, int p0) {
+// (frame, row, col) of a lane's token, advanced 64 tokens at a time without
+// divisions: the carries are at most one row and one frame per step.
+struct TokPos {
+  int f, row, col;
+  __device__ void init(int n, const PosArgs& p) {
+    f = (int)fast_div((uint32_t)n, p.mag_tpf);
+    const int rem = n - f * p.tpf;
+    row = (int)fast_div((uint32_t)rem, p.mag_gw);
+    col = rem - row * p.gw;
+  }
+  __device__ void advance(const PosArgs& p) {
+    col += p.adv_c;
+    const bool c1 = col >= p.gw;
+    col = c1 ? col - p.gw : col;
+    row += p.adv_r + (int)c1;
+    const bool c2 = row >= p.ghd;
+    row = c2 ? row - p.ghd : row;
+    f += p.adv_f + (int)c2;
+  }
+};
+
+struct RopeLane {
+  // Per pair: table index = base + fl * sf + row * sr + col * sc, where only the
+  // stride of the pair's own section is non-zero (no per-lane branches).
+  int base[4], sf[4], sr[4], sc[4];
+
+  __device__ void init(const RopeDev& r, const TabWindow& w, int c) {
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const int gp = p0 + i;
-      if (gp < r.pt) {
-        sel[i] = 0; base[i] = gp; stride[i] = r.pt;
-      } else if (gp < r.pt + r.ph) {
-        sel[i] = 1; base[i] = w.nf * r.pt + (gp - r.pt); stride[i] = r.ph;
-      } else {
-        sel[i] = 2; base[i] = w.nf * r.pt + r.gh * r.ph + (gp - r.pt - r.ph); stride[i] = r.pw;
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int gp = 4 * c + i;
+      const bool in_t = gp < r.pt, in_h = !in_t && gp < r.pt + r.ph, in_w = !in_t && !in_h;
+      base[i] = in_t ? gp : (in_h ? w.nf * r.pt + (gp - r.pt) : w.nf * r.pt + r.gh * r.ph + (gp - r.pt - r.ph));
+      sf[i] = in_t ? r.pt : 0;
+      sr[i] = in_h ? r.ph : 0;
+      sc[i] = in_w ? r.pw : 0;
     }
   }
-  // Rotate NP adjacent pairs x[0..2NP) of token n (local index in the call).
-  __device__ void rotate(float* x, const float2* lds, int n, int f_lo, int tpf, int gw,
-                         uint64_t mag_tpf, uint64_t mag_gw) const {
-    const int f = (int)fast_div((uint32_t)n, mag_tpf);
-    const int rem = n - f * tpf;
-    const int row = (int)fast_div((uint32_t)rem, mag_gw);
-    const int col = rem - row * gw;
-    const int pos3[3] = {f - f_lo, row, col};
+
+  // (cos, sin) of the lane's 4 pairs at the token's local frame (clamped into
+  // the staged window, so tokens past the range read valid rows), row and
+  // column.  pairs2: every section has an even number of pairs, so the pairs
+  // (4c, 4c+1) and (4c+2, 4c+3) share a section, sit side by side in the
+  // table, and one 16-byte LDS read fetches both.
+  __device__ void fetch(const float2* lds, const TokPos& tp, const TabWindow& w, bool pairs2,
+                        float2* cs) const {
+    const int fl = min(tp.f - w.f_lo, w.nf - 1);
+    if (pairs2) {
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const int pos = sel[i] == 0 ? pos3[0] : (sel[i] == 1 ? pos3[1] : pos3[2]);
-      const float2 cs = lds[base[i] + pos * stride[i]];
-      const float a = x[2 * i], b = x[2 * i + 1];
-      x[2 * i] = a * cs.x - b * cs.y;
-      x[2 * i + 1] = a * cs.y + b * cs.x;
+      for (int i = 0; i < 4; i += 2) {
+        const int idx = base[i] + __umul24(fl, sf[i]) + __umul24(tp.row, sr[i]) + __umul24(tp.col, sc[i]);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(lds + idx);
+        cs[i] = make_float2(v[0], v[1]);
+        cs[i + 1] = make_float2(v[2], v[3]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int idx = base[i] + __umul24(fl, sf[i]) + __umul24(tp.row, sr[i]) + __umul24(tp.col, sc[i]);
+        cs[i] = lds[idx];
+      }
     }
   }
 };
 
+__device__ __forceinline__ void rotate8(float* x, const float2* cs) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = x[2 * i], b = x[2 * i + 1];
+    x[2 * i] = a * cs[i].x - b * cs[i].y;
+    x[2 * i + 1] = a * cs[i].y + b * cs[i].x;
+  }
+}
+
+// Sum over the four lanes l, l^16, l^32, l^48 that hold one token's chunks.
+__device__ __forceinline__ float sum4_lanes(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // --------------------------------------------------------- k_block_state
 //
 // Grid: x = chunk * hg + head group, y = batch.  256 threads.  Each 64-token
-// step: every thread loads 16-byte chunks of K and V (8 lanes cover one
-// token's two-head bf16 row), applies ReLU, adds to its key-sum, rotates, and
-// writes V and R phi(K) into LDS tiles [token][2 heads x 32].  Then wave w
-// takes head (w & 1) and tokens 32*(w >> 1) .. +31 of the step and feeds
-// MFMA: A[e][n] = V[n][e], B[n][f] = R phi(K)[n][f], so C = S (32 x 32).
-// A lane supplies one channel over 8 tokens, read across LDS rows.  Odd
-// groups of 8 rows store the two heads swapped, so the two half-waves read
-// disjoint LDS banks.
+// step: thread t loads channels 8(t&3) .. +7 of token (t>>2) for both heads of
+// K and V, applies ReLU, adds to its key sums, rotates (one table fetch for
+// both heads), and writes V and R phi(K) into LDS tiles [token][2 heads x 32].
+// Loads run two steps ahead of the tiles.  Then wave w takes head (w & 1) and
+// tokens 32*(w >> 1) .. +31 of the step and feeds MFMA: A[e][n] = V[n][e],
+// B[n][f] = R phi(K)[n][f], so C = S (32 x 32).  A lane supplies one channel
+// over 8 tokens, read across LDS rows; odd groups of 8 rows store the two
+// heads swapped, so the two half-waves read disjoint LDS banks.  Tokens past
+// the chunk read as zeros (buffer range check) and add nothing.
 
 template <typename TIn>
 __global__ __launch_bounds__(NT) void k_block_state(StateArgs a) {
   constexpr bool BF = sizeof(TIn) == 2;
-  constexpr int VEC = Vec16<TIn>::N;     // elements per 16 bytes
-  constexpr int CPH = D / VEC;           // 16-byte chunks per head row
-  constexpr int LPR = 2 * CPH;           // lanes per two-head row
-  constexpr int TPP = NT / LPR;          // tokens per load pass
-  constexpr int NPASS = STEP / TPP;
-  constexpr int NP = VEC / 2;            // rotary pairs per chunk
+  constexpr int ES = (int)sizeof(TIn);
   constexpr int NTILE = BF ? 3 : 2;      // V, R phi(K) (hi, lo for bf16)
   constexpr int TILE_ELEMS = STEP * TCOLS;
-  constexpr int TILE_BYTES = NTILE * TILE_ELEMS * (int)sizeof(TIn);
+  constexpr int TILE_BYTES = NTILE * TILE_ELEMS * ES;
+  constexpr int W16 = 16 / ES;           // elements per 16 bytes
 
   extern __shared__ __align__(16) unsigned char smem[];
   TIn* tV = reinterpret_cast<TIn*>(smem);
@@ -237,63 +308,80 @@ __global__ __launch_bounds__(NT) void k_block_state(StateArgs a) {
   const int c1 = min(c0 + a.Tc, blk1);
   const int h0 = g * kHeadsPerGroup;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-
-  // loader role of this thread
-  const int lr = t % LPR, ltok = t / LPR, lhh = lr / CPH, lcc = lr % CPH;
-  const bool lhead_ok = h0 + lhh < a.H;
+  const int lrow = t >> 2, lc = t & 3;   // loader: token row of the step, channel chunk
+  const int nh = min(kHeadsPerGroup, a.H - h0);
   const bool rope_on = a.rope.table != nullptr;
+  const bool pairs2 = ((a.rope.pt | a.rope.ph | a.rope.pw) & 1) == 0;
 
-  const TabWindow win = stage_table(tab, a.rope, a.t0, c0, c1, a.mag_tpf);
-  PairLut<NP> lut;
-  if (rope_on) lut.init(a.rope, win, lcc * NP);
+  // K and V of this chunk: rows c0 .. c1-1 of batch b.
+  const int RB = a.H * D * ES;
+  const size_t base = ((size_t)b * a.N + c0) * RB;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const char*>(a.k) + base, (uint32_t)(c1 - c0) * RB);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const char*>(a.v) + base, (uint32_t)(c1 - c0) * RB);
+  int voff = lrow * RB + (h0 * D + 8 * lc) * ES;
+
+  struct Buf { Raw8<TIn> k[2], v[2]; };
+  auto load_step = [&](Buf& bf) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bf.k[h] = bload8<TIn>(rk, voff + h * D * ES);
+      bf.v[h] = bload8<TIn>(rv, voff + h * D * ES);
+    }
+    voff += STEP * RB;
+  };
+  // Two register buffers: loads run two steps ahead of the LDS tiles.
+  Buf b0, b1;
+  if (c0 < c1) load_step(b0);
+  if (c0 + STEP < c1) load_step(b1);
+
+  const TabWindow win = stage_table(tab, a.rope, a.pos.t0, c0, c1, a.pos.mag_tpf);
+  RopeLane rl;
+  TokPos tp;
+  if (rope_on) {
+    rl.init(a.rope, win, lc);
+    tp.init(c0 + lrow, a.pos);
+  }
   __syncthreads();
 
-  const size_t tok_stride = (size_t)a.H * D;
-  const size_t off = ((size_t)b * a.N) * tok_stride + (size_t)(h0 + lhh) * D + lcc * VEC;
-  const TIn* kp = reinterpret_cast<const TIn*>(a.k) + off;
-  const TIn* vp = reinterpret_cast<const TIn*>(a.v) + off;
-
-  float zacc[VEC];
+  float zacc[2][8];
 #pragma unroll
-  for (int i = 0; i < VEC; ++i) zacc[i] = 0.f;
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) zacc[h][i] = 0.f;
   f32x16 acc = {};
-
   const int hh = w & 1, th = w >> 1, cl = lane & 31, q = lane >> 5;
 
-  for (int s0 = c0; s0 < c1; s0 += STEP) {
+  auto run_step = [&](const Buf& bf) {
+    float2 cs[4];
+    if (rope_on) {
+      rl.fetch(tab, tp, win, pairs2, cs);
+      tp.advance(a.pos);
+    }
 #pragma unroll
-    for (int p = 0; p < NPASS; ++p) {
-      const int row = p * TPP + ltok;
-      const int tok = s0 + row;
-      const bool ok = tok < c1 && lhead_ok;
-      u32x4 kr = {0u, 0u, 0u, 0u}, vr = {0u, 0u, 0u, 0u};
-      if (ok) {
-        kr = ld16(kp + (size_t)tok * tok_stride);
-        vr = ld16(vp + (size_t)tok * tok_stride);
-      }
-      float x[VEC];
-      Vec16<TIn>::widen(kr, x);
+    for (int h = 0; h < 2; ++h) {
+      float x[8];
+      relu_widen(bf.k[h], x);
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) {
-        x[i] = fmaxf(x[i], 0.f);
-        zacc[i] += x[i];
-      }
-      if (rope_on && ok) lut.rotate(x, tab, tok, win.f_lo, a.tpf, a.gw, a.mag_tpf, a.mag_gw);
-      const int col = (lhh * D + lcc * VEC) ^ (((row >> 3) & 1) << 5);
-      *reinterpret_cast<u32x4*>(tV + row * TCOLS + col) = vr;
+      for (int i = 0; i < 8; ++i) zacc[h][i] += x[i];
+      if (rope_on) rotate8(x, cs);
+      const int col = (h * D + 8 * lc) ^ (((lrow >> 3) & 1) << 5);
+      TIn* dv = tV + lrow * TCOLS + col;
+#pragma unroll
+      for (int i = 0; i < ES / 2; ++i) *reinterpret_cast<u32x4*>(dv + i * W16) = bf.v[h].r[i];
       if constexpr (BF) {
         u32x4 hi, lo;
         split8(x, hi, lo);
-        *reinterpret_cast<u32x4*>(tK + row * TCOLS + col) = hi;
-        *reinterpret_cast<u32x4*>(tKl + row * TCOLS + col) = lo;
+        *reinterpret_cast<u32x4*>(tK + lrow * TCOLS + col) = hi;
+        *reinterpret_cast<u32x4*>(tKl + lrow * TCOLS + col) = lo;
       } else {
-        u32x4 xr;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xr[i] = __float_as_uint(x[i]);
-        *reinterpret_cast<u32x4*>(tK + row * TCOLS + col) = xr;
+        f32x4* dk = reinterpret_cast<f32x4*>(tK + lrow * TCOLS + col);
+        dk[0] = f32x4{x[0], x[1], x[2], x[3]};
+        dk[1] = f32x4{x[4], x[5], x[6], x[7]};
       }
     }
-    __syncthreads();
+  };
+
+  auto mfma_step = [&]() {
     if constexpr (BF) {
       const uint16_t* V16 = reinterpret_cast<const uint16_t*>(tV);
       const uint16_t* Kh16 = reinterpret_cast<const uint16_t*>(tK);
@@ -323,22 +411,38 @@ __global__ __launch_bounds__(NT) void k_block_state(StateArgs a) {
         acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Vf[i0], Kf[i0], acc, 0, 0, 0);
       }
     }
+  };
+
+  for (int s0 = c0; s0 < c1; s0 += 2 * STEP) {
+    run_step(b0);
     __syncthreads();
+    if (s0 + 2 * STEP < c1) load_step(b0);
+    mfma_step();
+    __syncthreads();
+    if (s0 + STEP < c1) {
+      run_step(b1);
+      __syncthreads();
+      if (s0 + 3 * STEP < c1) load_step(b1);
+      mfma_step();
+      __syncthreads();
+    }
   }
 
   // Combine the two waves of each head, and the key-sum lanes, through LDS.
   float* red = reinterpret_cast<float*>(smem);   // [2 waves][16][64]
-  float* zred = red + 2 * 16 * 64;               // [NT][VEC]
+  float* zred = red + 2 * 16 * 64;               // [NT][16]
   if (w >= 2) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) red[((w - 2) * 16 + v) * 64 + lane] = acc[v];
   }
 #pragma unroll
-  for (int i = 0; i < VEC; ++i) zred[t * VEC + i] = zacc[i];
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) zred[t * 16 + h * 8 + i] = zacc[h][i];
   __syncthreads();
 
   const int nchunk = a.nb * a.cpb;
-  if (w < 2 && h0 + w < a.H) {
+  if (w < 2 && w < nh) {
     float* dst = a.part + ((size_t)(b * a.H + h0 + w) * nchunk + ci) * REC;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -346,11 +450,11 @@ __global__ __launch_bounds__(NT) void k_block_state(StateArgs a) {
       dst[e * D + (lane & 31)] = acc[v] + red[(w * 16 + v) * 64 + lane];
     }
   }
-  if (t < 2 * D && h0 + t / D < a.H) {
+  if (t < 2 * D && t / D < nh) {
     const int hd = t / D, ch = t % D;
-    const int r = hd * CPH + ch / VEC, el = ch % VEC;
+    const int lc2 = ch >> 3, el = ch & 7;
     float s = 0.f;
-    for (int tp = 0; tp < TPP; ++tp) s += zred[(tp * LPR + r) * VEC + el];
+    for (int r = 0; r < STEP; ++r) s += zred[(r * 4 + lc2) * 16 + hd * 8 + el];
     a.part[((size_t)(b * a.H + h0 + hd) * nchunk + ci) * REC + D * D + ch] = s;
   }
 }
@@ -358,28 +462,47 @@ __global__ __launch_bounds__(NT) void k_block_state(StateArgs a) {
 // -------------------------------------------------------------- k_prefix
 //
 // Grid: x = element group (17 x 64 covers the 1056 floats of a record),
-// y = head, z = batch.  One thread owns one element of (S, z) for one head
-// and walks the blocks in order: block sum = p_0 + p_1 + ... (chunk order),
-// prefix = previous prefix + block sum.  A streaming call starts from the
-// carried cache, so one block streamed on top of a cache adds exactly as the
-// one-shot prefix does.
+// y = head, z = batch; 256 threads.  For each run of 32 blocks, the four waves
+// form block sums p_0 + p_1 + ... (chunk order) for blocks w, w+4, ... of the
+// run into LDS; then wave 0 walks the run in block order: prefix = previous
+// prefix + block sum.  A streaming call starts from the carried cache, so one
+// block streamed on top of a cache adds exactly as the one-shot prefix does.
 
-__global__ __launch_bounds__(SCAN_NT) void k_prefix(PrefixArgs a) {
-  const int el = blockIdx.x * SCAN_NT + threadIdx.x;
-  if (el >= REC) return;
+constexpr int PFX_NT = 256;
+constexpr int PFX_RUN = 32;
+
+__global__ __launch_bounds__(PFX_NT) void k_prefix(PrefixArgs a) {
+  __shared__ float bs[PFX_RUN][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int el = blockIdx.x * 64 + lane;
+  const bool ok = el < REC;
   const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
-  float acc = 0.f;
-  if (a.S_init != nullptr) acc = el < D * D ? a.S_init[bh * D * D + el] : a.z_init[bh * D + el - D * D];
-  const float* p = a.part + bh * a.nb * a.cpb * REC + el;
+  const float* part = a.part + bh * a.nb * a.cpb * REC + el;
   float* o = a.prefix + bh * a.nb * REC + el;
-  for (int j = 0; j < a.nb; ++j) {
-    float bs = p[0];
-    for (int c = 1; c < a.cpb; ++c) bs += p[(size_t)c * REC];
-    p += (size_t)a.cpb * REC;
-    acc += bs;
-    o[(size_t)j * REC] = acc;
+  float acc = 0.f;
+  if (w == 0 && ok && a.S_init != nullptr)
+    acc = el < D * D ? a.S_init[bh * D * D + el] : a.z_init[bh * D + el - D * D];
+  for (int r0 = 0; r0 < a.nb; r0 += PFX_RUN) {
+    const int nr = min(PFX_RUN, a.nb - r0);
+    for (int jj = w; jj < nr; jj += 4) {
+      float s = 0.f;
+      if (ok) {
+        const float* p = part + (size_t)(r0 + jj) * a.cpb * REC;
+        s = p[0];
+        for (int c = 1; c < a.cpb; ++c) s += p[(size_t)c * REC];
+      }
+      bs[jj][lane] = s;
+    }
+    __syncthreads();
+    if (w == 0 && ok) {
+      for (int jj = 0; jj < nr; ++jj) {
+        acc += bs[jj][lane];
+        o[(size_t)(r0 + jj) * REC] = acc;
+      }
+    }
+    __syncthreads();
   }
-  if (a.S_save != nullptr) {
+  if (w == 0 && ok && a.S_save != nullptr) {
     if (el < D * D) a.S_save[bh * D * D + el] = acc;
     else a.z_save[bh * D + el - D * D] = acc;
   }
@@ -387,17 +510,19 @@ __global__ __launch_bounds__(SCAN_NT) void k_prefix(PrefixArgs a) {
 
 // ------------------------------------------------------------- k_readout
 //
-// Grid: x = tile * hg + head group, y = batch.  256 threads; wave w takes head
-// (w & 1) and every other 16-token group of the tile starting at (w >> 1).
-// MFMA 16x16x32: A = Sbar rows (e) x channels (f), B = channels (f) x tokens:
-// lane l holds channels 8(l>>4) .. +7 of token (l & 15), which is one 16-byte
-// load of bf16 q.  The output lane holds channels 4(l>>4) .. +3 of each 16-row
-// half for token (l & 15), so the normaliser of that token, summed over the
-// four lanes that share it, is already in place.
+// Grid: x = tile * hg + head group, y = batch.  256 threads; wave w takes the
+// tile's 16-token groups w, w+4, ... for both heads of the group, with loads
+// two groups ahead.  MFMA 16x16x32: A = Sbar rows (e) x channels (f), B =
+// channels (f) x tokens: lane l holds channels 8(l>>4) .. +7 of token (l & 15),
+// one 16-byte load of bf16 q.  The output lane holds channels 4(l>>4) .. +3 of
+// each 16-row half for token (l & 15), so the normaliser of that token, summed
+// over the four lanes that share it, is already in place.  Tokens past the
+// tile read as zeros and their stores are dropped by the buffer range check.
 
 template <typename TIn, typename TOut>
 __global__ __launch_bounds__(NT) void k_readout(ReadArgs a) {
   constexpr bool BF = sizeof(TIn) == 2;
+  constexpr int ES = (int)sizeof(TIn), EO = (int)sizeof(TOut);
   extern __shared__ __align__(16) unsigned char smem[];
   float2* tab = reinterpret_cast<float2*>(smem);
 
@@ -410,114 +535,142 @@ __global__ __launch_bounds__(NT) void k_readout(ReadArgs a) {
   const int blk1 = min(blk0 + a.L, a.N);
   const int t0 = min(blk0 + r * a.Tr, blk1);
   const int t1 = min(t0 + a.Tr, blk1);
+  if (t0 >= t1) return;
   const bool rope_on = a.rope.table != nullptr;
-
-  const TabWindow win = stage_table(tab, a.rope, a.t0, t0, t1, a.mag_tpf);
-  __syncthreads();
+  const bool pairs2 = ((a.rope.pt | a.rope.ph | a.rope.pw) & 1) == 0;
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int hh = w & 1, sub = w >> 1;
-  const int head = g * kHeadsPerGroup + hh;
-  if (head >= a.H || t0 >= t1) return;
   const int tl = lane & 15, ch = lane >> 4;
+  const int h0 = g * kHeadsPerGroup;
+  const int nh = min(kHeadsPerGroup, a.H - h0);
+  const int ngroups = (t1 - t0 + 15) >> 4;
 
-  PairLut<4> lut;
-  if (rope_on) lut.init(a.rope, win, 4 * ch);
+  const int RB = a.H * D * ES, RO = a.H * D * EO;
+  const __amdgpu_buffer_rsrc_t rq =
+      make_rsrc(static_cast<const char*>(a.q) + ((size_t)b * a.N + t0) * RB, (uint32_t)(t1 - t0) * RB);
+  const __amdgpu_buffer_rsrc_t ro =
+      make_rsrc(static_cast<char*>(a.out) + ((size_t)b * a.N + t0) * RO, (uint32_t)(t1 - t0) * RO);
+  int qoff = (w * 16 + tl) * RB + (h0 * D + 8 * ch) * ES;
+  int ooff = (w * 16 + tl) * RO + (h0 * D + 4 * ch) * EO;
 
-  const float* pre = a.prefix + ((size_t)(b * a.H + head) * a.nb + j) * REC;
-  float zb[8];
-  {
+  struct Buf { Raw8<TIn> x[2]; };
+  auto load_group = [&](Buf& bf) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) bf.x[h] = bload8<TIn>(rq, qoff + h * D * ES);
+    qoff += 64 * RB;
+  };
+  // Two register buffers: loads run two groups ahead of the arithmetic.
+  Buf b0, b1;
+  load_group(b0);
+  load_group(b1);
+
+  // Per head: key-sum slice and Sbar operands (row e = 16 half + tl, channels 8ch .. +7).
+  float zb[2][8];
+  u32x4 Ah[2][2], Al[2][2];
+  float As[2][2][8];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int hd = min(h, nh - 1);
+    const float* pre = a.prefix + ((size_t)(b * a.H + h0 + hd) * a.nb + j) * REC;
     const f32x4 z0 = *reinterpret_cast<const f32x4*>(pre + D * D + 8 * ch);
     const f32x4 z1 = *reinterpret_cast<const f32x4*>(pre + D * D + 8 * ch + 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { zb[i] = z0[i]; zb[4 + i] = z1[i]; }
-  }
-  // Sbar operands: row e = 16 * half + tl, channels 8 ch .. 8 ch + 7.
-  u32x4 Ah[2], Al[2];
-  float As[2][8];
+    for (int i = 0; i < 4; ++i) { zb[h][i] = z0[i]; zb[h][4 + i] = z1[i]; }
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    const float* srow = pre + (16 * hf + tl) * D + 8 * ch;
-    const f32x4 s0 = *reinterpret_cast<const f32x4*>(srow);
-    const f32x4 s1 = *reinterpret_cast<const f32x4*>(srow + 4);
-    float sv[8];
+    for (int hf = 0; hf < 2; ++hf) {
+      const float* srow = pre + (16 * hf + tl) * D + 8 * ch;
+      const f32x4 s0 = *reinterpret_cast<const f32x4*>(srow);
+      const f32x4 s1 = *reinterpret_cast<const f32x4*>(srow + 4);
+      float sv[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { sv[i] = s0[i]; sv[4 + i] = s1[i]; }
-    if constexpr (BF) {
-      split8(sv, Ah[hf], Al[hf]);
-    } else {
+      for (int i = 0; i < 4; ++i) { sv[i] = s0[i]; sv[4 + i] = s1[i]; }
+      if constexpr (BF) {
+        split8(sv, Ah[h][hf], Al[h][hf]);
+      } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) As[hf][i] = sv[i];
+        for (int i = 0; i < 8; ++i) As[h][hf][i] = sv[i];
+      }
     }
   }
 
-  const size_t tok_stride = (size_t)a.H * D;
-  const TIn* qp = reinterpret_cast<const TIn*>(a.q) + (size_t)b * a.N * tok_stride + (size_t)head * D + 8 * ch;
-  TOut* op = reinterpret_cast<TOut*>(a.out) + (size_t)b * a.N * tok_stride + (size_t)head * D + 4 * ch;
+  const TabWindow win = stage_table(tab, a.rope, a.pos.t0, t0, t1, a.pos.mag_tpf);
+  RopeLane rl;
+  TokPos tp;
+  if (rope_on) {
+    rl.init(a.rope, win, ch);
+    tp.init(t0 + w * 16 + tl, a.pos);
+  }
+  __syncthreads();
 
-  for (int gi = sub; t0 + gi * 16 < t1; gi += 2) {
-    const int tok = t0 + gi * 16 + tl;
-    const bool ok = tok < t1;
-    float x[8];
-    if constexpr (BF) {
-      u32x4 qr = {0u, 0u, 0u, 0u};
-      if (ok) qr = ld16(qp + (size_t)tok * tok_stride);
-      Vec16<uint16_t>::widen(qr, x);
-    } else {
-      u32x4 q0 = {0u, 0u, 0u, 0u}, q1 = {0u, 0u, 0u, 0u};
-      if (ok) {
-        q0 = ld16(qp + (size_t)tok * tok_stride);
-        q1 = ld16(qp + (size_t)tok * tok_stride + 4);
-      }
-      Vec16<float>::widen(q0, x);
-      Vec16<float>::widen(q1, x + 4);
+  auto run_group = [&](const Buf& bf) {
+    float2 cs[4];
+    if (rope_on) {
+      rl.fetch(tab, tp, win, pairs2, cs);
+      tp.advance(a.pos);
     }
-    float den = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      x[i] = fmaxf(x[i], 0.f);
-      den += zb[i] * x[i];
-    }
-    if (rope_on && ok) lut.rotate(x, tab, tok, win.f_lo, a.tpf, a.gw, a.mag_tpf, a.mag_gw);
-
-    f32x4 o[2];
-    if constexpr (BF) {
-      u32x4 bh, bl;
-      split8(x, bh, bl);
+    for (int h = 0; h < 2; ++h) {
+      if (h >= nh) break;
+      float x[8];
+      relu_widen(bf.x[h], x);
+      float den = 0.f;
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        f32x4 c = {0.f, 0.f, 0.f, 0.f};
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Ah[hf]), as_bf16x8(bh), c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Ah[hf]), as_bf16x8(bl), c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Al[hf]), as_bf16x8(bh), c, 0, 0, 0);
-        o[hf] = c;
-      }
-    } else {
+      for (int i = 0; i < 8; ++i) den += zb[h][i] * x[i];
+      if (rope_on) rotate8(x, cs);
+      f32x4 o[2];
+      if constexpr (BF) {
+        u32x4 bh, bl;
+        split8(x, bh, bl);
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+        for (int hf = 0; hf < 2; ++hf) {
+          f32x4 cc = {0.f, 0.f, 0.f, 0.f};
+          cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Ah[h][hf]), as_bf16x8(bh), cc, 0, 0, 0);
+          cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Ah[h][hf]), as_bf16x8(bl), cc, 0, 0, 0);
+          cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Al[h][hf]), as_bf16x8(bh), cc, 0, 0, 0);
+          o[hf] = cc;
+        }
+      } else {
 #pragma unroll
-        for (int s = 0; s < 8; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(As[hf][s], x[s], c, 0, 0, 0);
-        o[hf] = c;
-      }
-    }
-    den += __shfl_xor(den, 16);
-    den += __shfl_xor(den, 32);
-    const float inv = 1.0f / (den + a.eps);
-    if (ok) {
-      TOut* dst = op + (size_t)tok * tok_stride;
+        for (int hf = 0; hf < 2; ++hf) {
+          f32x4 cc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        if constexpr (sizeof(TOut) == 2) {
-          u32x2 pk;
-          pk[0] = pack_bf16(o[hf][0] * inv, o[hf][1] * inv);
-          pk[1] = pack_bf16(o[hf][2] * inv, o[hf][3] * inv);
-          *reinterpret_cast<u32x2*>(dst + 16 * hf) = pk;
-        } else {
-          f32x4 ov = o[hf] * inv;
-          *reinterpret_cast<f32x4*>(dst + 16 * hf) = ov;
+          for (int s = 0; s < 8; ++s) cc = __builtin_amdgcn_mfma_f32_16x16x4f32(As[h][hf][s], x[s], cc, 0, 0, 0);
+          o[hf] = cc;
         }
       }
+      den = sum4_lanes(den);
+      const float inv = __builtin_amdgcn_rcpf(den + a.eps);
+      if constexpr (EO == 2) {
+        // Lane row ch holds channels 4ch..4ch+3 of each 16-channel half.  One
+        // permlane16 swap per dword trades the halves between rows ch and ch^1,
+        // so an even row ends up with channels 4ch..4ch+7 and an odd row with
+        // 12+4ch..19+4ch: one 16-byte store per lane.
+        const uint32_t p00 = pack_bf16(o[0][0] * inv, o[0][1] * inv);
+        const uint32_t p01 = pack_bf16(o[0][2] * inv, o[0][3] * inv);
+        const uint32_t p10 = pack_bf16(o[1][0] * inv, o[1][1] * inv);
+        const uint32_t p11 = pack_bf16(o[1][2] * inv, o[1][3] * inv);
+        const auto s0 = __builtin_amdgcn_permlane16_swap(p00, p10, false, false);
+        const auto s1 = __builtin_amdgcn_permlane16_swap(p01, p11, false, false);
+        const u32x4 pk = {s0[0], s1[0], s0[1], s1[1]};
+        __builtin_amdgcn_raw_buffer_store_b128(pk, ro, ooff + (h * D + ((ch & 1) ? 12 : 0)) * EO, 0, 0);
+      } else {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const f32x4 ov = o[hf] * inv;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ov), ro,
+                                                 ooff + (h * D + 16 * hf) * EO, 0, 0);
+        }
+      }
+    }
+    ooff += 64 * RO;
+  };
+
+  for (int gi = w; gi < ngroups; gi += 8) {
+    run_group(b0);
+    if (gi + 8 < ngroups) load_group(b0);
+    if (gi + 4 < ngroups) {
+      run_group(b1);
+      if (gi + 12 < ngroups) load_group(b1);
     }
   }
 }
@@ -555,6 +708,21 @@ hipError_t launch_readout(const ReadArgs& ra, dim3 grid, int lds, hipStream_t s)
   return hipGetLastError();
 }
 
+PosArgs pos_args(const Plan& p) {
+  PosArgs q;
+  q.tpf = p.tpf;
+  q.gw = p.gw_div;
+  q.ghd = p.tpf / p.gw_div;
+  q.adv_f = 64 / p.tpf;
+  const int rr = 64 % p.tpf;
+  q.adv_r = rr / p.gw_div;
+  q.adv_c = rr % p.gw_div;
+  q.t0 = p.t0;
+  q.mag_tpf = p.mag_tpf;
+  q.mag_gw = p.mag_gw;
+  return q;
+}
+
 }  // namespace
 
 int launch_rope_table(float* table, int pt, int ph, int pw, int max_frames, int gh, int gw,
@@ -588,11 +756,12 @@ int launch_forward(const Plan& p, const void* q, const void* k, const void* v, v
   if (e != hipSuccess) return (int)e;
   float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.ws_part);
   float* prefix = reinterpret_cast<float*>(static_cast<char*>(ws) + p.ws_prefix);
+  const PosArgs pa_pos = pos_args(p);
 
   StateArgs sa;
   sa.k = k; sa.v = v; sa.part = part;
   sa.H = p.H; sa.N = p.N; sa.L = p.L; sa.nb = p.nb; sa.cpb = p.cpb; sa.Tc = p.Tc; sa.hg = p.hg;
-  sa.tpf = p.tpf; sa.gw = p.gw_div; sa.t0 = p.t0; sa.mag_tpf = p.mag_tpf; sa.mag_gw = p.mag_gw;
+  sa.pos = pa_pos;
   sa.rope = p.rope;
   const dim3 gs((unsigned)(p.hg * p.nb * p.cpb), (unsigned)p.B);
   if (in_bf16) hipLaunchKernelGGL(k_block_state<uint16_t>, gs, dim3(NT), p.lds_state, s, sa);
@@ -604,8 +773,8 @@ int launch_forward(const Plan& p, const void* q, const void* k, const void* v, v
   PrefixArgs pa;
   pa.part = part; pa.prefix = prefix; pa.S_init = S_init; pa.z_init = z_init;
   pa.S_save = S_save; pa.z_save = z_save; pa.H = p.H; pa.nb = p.nb; pa.cpb = p.cpb;
-  const dim3 gp((REC + SCAN_NT - 1) / SCAN_NT, (unsigned)p.H, (unsigned)p.B);
-  hipLaunchKernelGGL(k_prefix, gp, dim3(SCAN_NT), 0, s, pa);
+  const dim3 gp((REC + 63) / 64, (unsigned)p.H, (unsigned)p.B);
+  hipLaunchKernelGGL(k_prefix, gp, dim3(PFX_NT), 0, s, pa);
   e = hipGetLastError();
   if (e == hipSuccess) e = mark(2);
   if (e != hipSuccess) return (int)e;
@@ -613,7 +782,7 @@ int launch_forward(const Plan& p, const void* q, const void* k, const void* v, v
   ReadArgs ra;
   ra.q = q; ra.out = out; ra.prefix = prefix; ra.eps = eps;
   ra.H = p.H; ra.N = p.N; ra.L = p.L; ra.nb = p.nb; ra.rpb = p.rpb; ra.Tr = p.Tr; ra.hg = p.hg;
-  ra.tpf = p.tpf; ra.gw = p.gw_div; ra.t0 = p.t0; ra.mag_tpf = p.mag_tpf; ra.mag_gw = p.mag_gw;
+  ra.pos = pa_pos;
   ra.rope = p.rope;
   const dim3 gr((unsigned)(p.hg * p.nb * p.rpb), (unsigned)p.B);
   if (in_bf16 && out_bf16) e = launch_readout<uint16_t, uint16_t>(ra, gr, p.lds_read, s);

@@ -12,7 +12,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblavr.so")
+# LAVR_LIBRARY may name another build of the same library (e.g. a tuning build).
+LIB_PATH = os.environ.get("LAVR_LIBRARY") or os.path.join(_HERE, "liblavr.so")
 
 LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_STATE_MISMATCH, LA_ERR_HIP = range(5)
 LA_F32, LA_BF16 = 0, 1
