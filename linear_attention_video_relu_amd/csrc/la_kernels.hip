@@ -45,6 +45,12 @@ constexpr int NT = 256;              // threads of the state and readout workgro
 constexpr int STEP = 64;             // tokens per step of the state kernel
 constexpr int TCOLS = 2 * D;         // an LDS tile row holds two heads
 constexpr int RSRC_WORD3 = 0x00020000;  // gfx9 raw buffer: 32-bit data, range checked
+#ifndef LAVR_STATE_PF
+#define LAVR_STATE_PF 2   // block-state: 64-token steps of K/V loads in flight
+#endif
+#ifndef LAVR_READ_PF
+#define LAVR_READ_PF 2    // readout: 16-token groups of Q loads in flight per wave
+#endif
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
@@ -161,6 +167,18 @@ __device__ __forceinline__ void relu_widen(const Raw8<float>& r, float* x) {
     x[i] = __uint_as_float((uint32_t)__builtin_elementwise_max((int)r.r[i >> 2][i & 3], 0));
 }
 
+// Two transposing LDS reads (ds_read_b64_tr_b16) at element offsets e0 and
+// e1 of a bf16 tile, joined into one 8-element MFMA operand.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+template <typename T>
+__device__ __forceinline__ u32x4 tr_pair(const T* tile, int e0, int e1) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + e0));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + e1));
+  const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+  return u32x4{ua[0], ua[1], ub[0], ub[1]};
+}
+
 // --------------------------------------------------------------------- RoPE
 //
 // A workgroup stages the rows of the rotary table it needs in LDS: the t rows
@@ -209,15 +227,20 @@ struct TokPos {
   }
 };
 
+// Per lookup: table index = base + fl * sf + row * sr + col * sc, where only
+// the stride of the lookup's own section is non-zero (no per-lane branches).
+// P2: every section has an even number of pairs, so the pairs (4c, 4c+1) and
+// (4c+2, 4c+3) share a section, sit side by side in the table, and one
+// 16-byte LDS read fetches a couple; otherwise each pair is read on its own.
+template <bool P2>
 struct RopeLane {
-  // Per pair: table index = base + fl * sf + row * sr + col * sc, where only the
-  // stride of the pair's own section is non-zero (no per-lane branches).
-  int base[4], sf[4], sr[4], sc[4];
+  static constexpr int NL = P2 ? 2 : 4;   // lookups per lane
+  int base[NL], sf[NL], sr[NL], sc[NL];
 
   __device__ void init(const RopeDev& r, const TabWindow& w, int c) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int gp = 4 * c + i;
+    for (int i = 0; i < NL; ++i) {
+      const int gp = 4 * c + (P2 ? 2 * i : i);
       const bool in_t = gp < r.pt, in_h = !in_t && gp < r.pt + r.ph, in_w = !in_t && !in_h;
       base[i] = in_t ? gp : (in_h ? w.nf * r.pt + (gp - r.pt) : w.nf * r.pt + r.gh * r.ph + (gp - r.pt - r.ph));
       sf[i] = in_t ? r.pt : 0;
@@ -227,25 +250,17 @@ struct RopeLane {
   }
 
   // (cos, sin) of the lane's 4 pairs at the token's local frame (clamped into
-  // the staged window, so tokens past the range read valid rows), row and
-  // column.  pairs2: every section has an even number of pairs, so the pairs
-  // (4c, 4c+1) and (4c+2, 4c+3) share a section, sit side by side in the
-  // table, and one 16-byte LDS read fetches both.
-  __device__ void fetch(const float2* lds, const TokPos& tp, const TabWindow& w, bool pairs2,
-                        float2* cs) const {
+  // the staged window, so tokens past the range read valid rows), row and column.
+  __device__ void fetch(const float2* lds, const TokPos& tp, const TabWindow& w, float2* cs) const {
     const int fl = min(tp.f - w.f_lo, w.nf - 1);
-    if (pairs2) {
 #pragma unroll
-      for (int i = 0; i < 4; i += 2) {
-        const int idx = base[i] + __umul24(fl, sf[i]) + __umul24(tp.row, sr[i]) + __umul24(tp.col, sc[i]);
+    for (int i = 0; i < NL; ++i) {
+      const int idx = base[i] + __umul24(fl, sf[i]) + __umul24(tp.row, sr[i]) + __umul24(tp.col, sc[i]);
+      if constexpr (P2) {
         const f32x4 v = *reinterpret_cast<const f32x4*>(lds + idx);
-        cs[i] = make_float2(v[0], v[1]);
-        cs[i + 1] = make_float2(v[2], v[3]);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int idx = base[i] + __umul24(fl, sf[i]) + __umul24(tp.row, sr[i]) + __umul24(tp.col, sc[i]);
+        cs[2 * i] = make_float2(v[0], v[1]);
+        cs[2 * i + 1] = make_float2(v[2], v[3]);
+      } else {
         cs[i] = lds[idx];
       }
     }
@@ -269,6 +284,51 @@ __device__ __forceinline__ float sum4_lanes(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Sum over the 16 lanes of a wave that share (lane mod 4): two DPP rotations
+// inside each 16-lane row (row_ror 4, 8), then the four rows.
+__device__ __forceinline__ float sum16_lanes_mod4(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false));
+  return sum4_lanes(v);
+}
+
+// Rotary window staged in two phases: the global reads go to registers
+// first, so K/V loads can be issued before the LDS writes wait for them.
+struct TabStage {
+  static constexpr int PER = 4;   // entries a thread holds in registers
+  float2 v[PER];
+  int nt, tot;
+  TabWindow w;
+  const float2* tsrc;
+  const float2* hwsrc;
+
+  __device__ void issue(const RopeDev& r, long long t0, int n0, int n1, uint64_t mag_tpf) {
+    w = TabWindow{0, 0};
+    nt = tot = 0;
+    if (r.table == nullptr || n1 <= n0) return;
+    w.f_lo = (int)fast_div((uint32_t)n0, mag_tpf);
+    w.nf = (int)fast_div((uint32_t)(n1 - 1), mag_tpf) - w.f_lo + 1;
+    const float2* tab = reinterpret_cast<const float2*>(r.table);
+    tsrc = tab + (size_t)(t0 + w.f_lo) * r.pt;
+    hwsrc = tab + (size_t)r.max_frames * r.pt;
+    nt = w.nf * r.pt;
+    tot = nt + r.gh * r.ph + r.gw * r.pw;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = threadIdx.x + k * NT;
+      if (i < tot) v[k] = i < nt ? tsrc[i] : hwsrc[i - nt];
+    }
+  }
+  __device__ void commit(float2* lds) const {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = threadIdx.x + k * NT;
+      if (i < tot) lds[i] = v[k];
+    }
+    for (int i = threadIdx.x + PER * NT; i < tot; i += NT) lds[i] = i < nt ? tsrc[i] : hwsrc[i - nt];
+  }
+};
+
 // --------------------------------------------------------- k_block_state
 //
 // Grid: x = chunk * hg + head group, y = batch.  256 threads.  Each 64-token
@@ -282,14 +342,15 @@ __device__ __forceinline__ float sum4_lanes(float v) {
 // heads swapped, so the two half-waves read disjoint LDS banks.  Tokens past
 // the chunk read as zeros (buffer range check) and add nothing.
 
-template <typename TIn>
-__global__ __launch_bounds__(NT) void k_block_state(StateArgs a) {
+template <typename TIn, bool P2>
+__global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? (P2 ? 4 : 3) : 2) void k_block_state(StateArgs a) {
   constexpr bool BF = sizeof(TIn) == 2;
   constexpr int ES = (int)sizeof(TIn);
   constexpr int NTILE = BF ? 3 : 2;      // V, R phi(K) (hi, lo for bf16)
   constexpr int TILE_ELEMS = STEP * TCOLS;
   constexpr int TILE_BYTES = NTILE * TILE_ELEMS * ES;
   constexpr int W16 = 16 / ES;           // elements per 16 bytes
+  constexpr int PF = (BF && P2) ? LAVR_STATE_PF : 2;   // steps of loads in flight
 
   extern __shared__ __align__(16) unsigned char smem[];
   TIn* tV = reinterpret_cast<TIn*>(smem);
@@ -311,7 +372,6 @@ __global__ __launch_bounds__(NT) void k_block_state(StateArgs a) {
   const int lrow = t >> 2, lc = t & 3;   // loader: token row of the step, channel chunk
   const int nh = min(kHeadsPerGroup, a.H - h0);
   const bool rope_on = a.rope.table != nullptr;
-  const bool pairs2 = ((a.rope.pt | a.rope.ph | a.rope.pw) & 1) == 0;
 
   // K and V of this chunk: rows c0 .. c1-1 of batch b.
   const int RB = a.H * D * ES;
@@ -329,13 +389,23 @@ __global__ __launch_bounds__(NT) void k_block_state(StateArgs a) {
     }
     voff += STEP * RB;
   };
-  // Two register buffers: loads run two steps ahead of the LDS tiles.
-  Buf b0, b1;
-  if (c0 < c1) load_step(b0);
-  if (c0 + STEP < c1) load_step(b1);
+  // Rotary window reads first, then the K/V loads, then the window's LDS
+  // writes: the writes wait only for the window reads.
+  TabStage ts;
+  ts.issue(a.rope, a.pos.t0, c0, c1, a.pos.mag_tpf);
+  const TabWindow win = ts.w;
 
-  const TabWindow win = stage_table(tab, a.rope, a.pos.t0, c0, c1, a.pos.mag_tpf);
-  RopeLane rl;
+  // Register buffers: loads run PF steps ahead of the LDS tiles.  Every load
+  // is issued, also past the chunk (those read zeros and touch no memory), so
+  // the number of loads in flight is fixed and each wait covers only the
+  // oldest step.
+  Buf b0, b1, b2;
+  load_step(b0);
+  load_step(b1);
+  if constexpr (PF > 2) load_step(b2);
+
+  ts.commit(tab);
+  RopeLane<P2> rl;
   TokPos tp;
   if (rope_on) {
     rl.init(a.rope, win, lc);
@@ -354,7 +424,7 @@ __global__ __launch_bounds__(NT) void k_block_state(StateArgs a) {
   auto run_step = [&](const Buf& bf) {
     float2 cs[4];
     if (rope_on) {
-      rl.fetch(tab, tp, win, pairs2, cs);
+      rl.fetch(tab, tp, win, cs);
       tp.advance(a.pos);
     }
 #pragma unroll
@@ -383,21 +453,21 @@ __global__ __launch_bounds__(NT) void k_block_state(StateArgs a) {
 
   auto mfma_step = [&]() {
     if constexpr (BF) {
-      const uint16_t* V16 = reinterpret_cast<const uint16_t*>(tV);
-      const uint16_t* Kh16 = reinterpret_cast<const uint16_t*>(tK);
-      const uint16_t* Kl16 = reinterpret_cast<const uint16_t*>(tKl);
-      const int col = (hh * D + cl) ^ (q << 5);  // rows 8q..8q+7 of a 16-row group
+      // ds_read_b64_tr_b16: in each 16-lane group, lane 4r+s reads channels
+      // c0+4s .. +3 of token row r, and the hardware hands lane i channel c0+i
+      // of the 4 rows.  Group G = lane >> 4 takes channels 16(G&1) .. +15 of its
+      // head and tokens 8(G>>1) .. +7 of the 16-token MFMA step (two reads of 4
+      // rows), which is the 32x32x16 operand layout: lane l holds channel l%32
+      // over tokens 8(l/32) .. +7.
+      const int G = lane >> 4, jr = (lane >> 2) & 3, js = lane & 3;
+      const int colb = ((hh * D) ^ ((G >> 1) << 5)) + 16 * (G & 1) + 4 * js;
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        const int r0 = th * 32 + m * 16 + 8 * q;
-        u32x4 av, bh, bl;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i0 = (r0 + 2 * e) * TCOLS + col, i1 = i0 + TCOLS;
-          av[e] = (uint32_t)V16[i0] | ((uint32_t)V16[i1] << 16);
-          bh[e] = (uint32_t)Kh16[i0] | ((uint32_t)Kh16[i1] << 16);
-          bl[e] = (uint32_t)Kl16[i0] | ((uint32_t)Kl16[i1] << 16);
-        }
+        const int row0 = th * 32 + m * 16 + 8 * (G >> 1) + jr;
+        const int e0 = row0 * TCOLS + colb, e1 = e0 + 4 * TCOLS;
+        const u32x4 av = tr_pair(tV, e0, e1);
+        const u32x4 bh = tr_pair(tK, e0, e1);
+        const u32x4 bl = tr_pair(tKl, e0, e1);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(bh), acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(bl), acc, 0, 0, 0);
       }
@@ -413,24 +483,25 @@ __global__ __launch_bounds__(NT) void k_block_state(StateArgs a) {
     }
   };
 
-  for (int s0 = c0; s0 < c1; s0 += 2 * STEP) {
-    run_step(b0);
+  // Whole rounds of PF steps; steps past the chunk hold zeros and add nothing.
+  auto one_step = [&](Buf& bf) {
+    run_step(bf);
     __syncthreads();
-    if (s0 + 2 * STEP < c1) load_step(b0);
+    load_step(bf);
     mfma_step();
     __syncthreads();
-    if (s0 + STEP < c1) {
-      run_step(b1);
-      __syncthreads();
-      if (s0 + 3 * STEP < c1) load_step(b1);
-      mfma_step();
-      __syncthreads();
-    }
+  };
+  for (int s0 = c0; s0 < c1; s0 += PF * STEP) {
+    one_step(b0);
+    one_step(b1);
+    if constexpr (PF > 2) one_step(b2);
   }
 
-  // Combine the two waves of each head, and the key-sum lanes, through LDS.
+  // Combine the two waves of each head through LDS.  Key sums: first across
+  // the 16 lanes of a wave that hold the same channel chunk (cross-lane adds),
+  // then across the four waves through LDS.
   float* red = reinterpret_cast<float*>(smem);   // [2 waves][16][64]
-  float* zred = red + 2 * 16 * 64;               // [NT][16]
+  float* zred = red + 2 * 16 * 64;               // [4 waves][4 chunks][16]
   if (w >= 2) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) red[((w - 2) * 16 + v) * 64 + lane] = acc[v];
@@ -438,7 +509,10 @@ __global__ __launch_bounds__(NT) void k_block_state(StateArgs a) {
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) zred[t * 16 + h * 8 + i] = zacc[h][i];
+    for (int i = 0; i < 8; ++i) {
+      const float zs = sum16_lanes_mod4(zacc[h][i]);
+      if (lane < 4) zred[(w * 4 + lane) * 16 + h * 8 + i] = zs;
+    }
   __syncthreads();
 
   const int nchunk = a.nb * a.cpb;
@@ -454,7 +528,8 @@ __global__ __launch_bounds__(NT) void k_block_state(StateArgs a) {
     const int hd = t / D, ch = t % D;
     const int lc2 = ch >> 3, el = ch & 7;
     float s = 0.f;
-    for (int r = 0; r < STEP; ++r) s += zred[(r * 4 + lc2) * 16 + hd * 8 + el];
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) s += zred[(ww * 4 + lc2) * 16 + hd * 8 + el];
     a.part[((size_t)(b * a.H + h0 + hd) * nchunk + ci) * REC + D * D + ch] = s;
   }
 }
@@ -519,7 +594,7 @@ __global__ __launch_bounds__(PFX_NT) void k_prefix(PrefixArgs a) {
 // over the four lanes that share it, is already in place.  Tokens past the
 // tile read as zeros and their stores are dropped by the buffer range check.
 
-template <typename TIn, typename TOut>
+template <typename TIn, typename TOut, bool P2>
 __global__ __launch_bounds__(NT) void k_readout(ReadArgs a) {
   constexpr bool BF = sizeof(TIn) == 2;
   constexpr int ES = (int)sizeof(TIn), EO = (int)sizeof(TOut);
@@ -537,7 +612,6 @@ __global__ __launch_bounds__(NT) void k_readout(ReadArgs a) {
   const int t1 = min(t0 + a.Tr, blk1);
   if (t0 >= t1) return;
   const bool rope_on = a.rope.table != nullptr;
-  const bool pairs2 = ((a.rope.pt | a.rope.ph | a.rope.pw) & 1) == 0;
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int tl = lane & 15, ch = lane >> 4;
@@ -553,16 +627,15 @@ __global__ __launch_bounds__(NT) void k_readout(ReadArgs a) {
   int qoff = (w * 16 + tl) * RB + (h0 * D + 8 * ch) * ES;
   int ooff = (w * 16 + tl) * RO + (h0 * D + 4 * ch) * EO;
 
-  struct Buf { Raw8<TIn> x[2]; };
-  auto load_group = [&](Buf& bf) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) bf.x[h] = bload8<TIn>(rq, qoff + h * D * ES);
-    qoff += 64 * RB;
-  };
-  // Two register buffers: loads run two groups ahead of the arithmetic.
-  Buf b0, b1;
-  load_group(b0);
-  load_group(b1);
+  // Prologue order: rotary window, then the prefix state, then the first Q
+  // loads, so that no wait before the loop drains the Q prefetch.
+  const TabWindow win = stage_table(tab, a.rope, a.pos.t0, t0, t1, a.pos.mag_tpf);
+  RopeLane<P2> rl;
+  TokPos tp;
+  if (rope_on) {
+    rl.init(a.rope, win, ch);
+    tp.init(t0 + w * 16 + tl, a.pos);
+  }
 
   // Per head: key-sum slice and Sbar operands (row e = 16 half + tl, channels 8ch .. +7).
   float zb[2][8];
@@ -593,19 +666,27 @@ __global__ __launch_bounds__(NT) void k_readout(ReadArgs a) {
     }
   }
 
-  const TabWindow win = stage_table(tab, a.rope, a.pos.t0, t0, t1, a.pos.mag_tpf);
-  RopeLane rl;
-  TokPos tp;
-  if (rope_on) {
-    rl.init(a.rope, win, ch);
-    tp.init(t0 + w * 16 + tl, a.pos);
-  }
+  struct Buf { Raw8<TIn> x[2]; };
+  auto load_group = [&](Buf& bf) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) bf.x[h] = bload8<TIn>(rq, qoff + h * D * ES);
+    qoff += 64 * RB;
+  };
+  // Register buffers: loads run RPF groups ahead of the arithmetic.  Every
+  // load is issued, also past the tile (those read zeros and touch no memory),
+  // so the number of loads in flight is fixed.
+  constexpr int RPF = BF ? LAVR_READ_PF : 2;
+  Buf b0, b1, b2;
+  load_group(b0);
+  load_group(b1);
+  if constexpr (RPF > 2) load_group(b2);
+
   __syncthreads();
 
   auto run_group = [&](const Buf& bf) {
     float2 cs[4];
     if (rope_on) {
-      rl.fetch(tab, tp, win, pairs2, cs);
+      rl.fetch(tab, tp, win, cs);
       tp.advance(a.pos);
     }
 #pragma unroll
@@ -665,12 +746,16 @@ __global__ __launch_bounds__(NT) void k_readout(ReadArgs a) {
     ooff += 64 * RO;
   };
 
-  for (int gi = w; gi < ngroups; gi += 8) {
+  // Whole rounds of RPF groups; groups past the tile read zeros and their
+  // stores are dropped by the range check.
+  for (int gi = w; gi < ngroups; gi += 4 * RPF) {
     run_group(b0);
-    if (gi + 8 < ngroups) load_group(b0);
-    if (gi + 4 < ngroups) {
-      run_group(b1);
-      if (gi + 12 < ngroups) load_group(b1);
+    load_group(b0);
+    run_group(b1);
+    load_group(b1);
+    if constexpr (RPF > 2) {
+      run_group(b2);
+      load_group(b2);
     }
   }
 }
@@ -703,8 +788,9 @@ __global__ void k_fill_zero(float* p, size_t n) {
 }
 
 template <typename TIn, typename TOut>
-hipError_t launch_readout(const ReadArgs& ra, dim3 grid, int lds, hipStream_t s) {
-  hipLaunchKernelGGL((k_readout<TIn, TOut>), grid, dim3(NT), lds, s, ra);
+hipError_t launch_readout(const ReadArgs& ra, bool p2, dim3 grid, int lds, hipStream_t s) {
+  if (p2) hipLaunchKernelGGL((k_readout<TIn, TOut, true>), grid, dim3(NT), lds, s, ra);
+  else hipLaunchKernelGGL((k_readout<TIn, TOut, false>), grid, dim3(NT), lds, s, ra);
   return hipGetLastError();
 }
 
@@ -764,8 +850,11 @@ int launch_forward(const Plan& p, const void* q, const void* k, const void* v, v
   sa.pos = pa_pos;
   sa.rope = p.rope;
   const dim3 gs((unsigned)(p.hg * p.nb * p.cpb), (unsigned)p.B);
-  if (in_bf16) hipLaunchKernelGGL(k_block_state<uint16_t>, gs, dim3(NT), p.lds_state, s, sa);
-  else hipLaunchKernelGGL(k_block_state<float>, gs, dim3(NT), p.lds_state, s, sa);
+  const bool p2 = ((p.rope.pt | p.rope.ph | p.rope.pw) & 1) == 0;
+  if (in_bf16 && p2) hipLaunchKernelGGL((k_block_state<uint16_t, true>), gs, dim3(NT), p.lds_state, s, sa);
+  else if (in_bf16) hipLaunchKernelGGL((k_block_state<uint16_t, false>), gs, dim3(NT), p.lds_state, s, sa);
+  else if (p2) hipLaunchKernelGGL((k_block_state<float, true>), gs, dim3(NT), p.lds_state, s, sa);
+  else hipLaunchKernelGGL((k_block_state<float, false>), gs, dim3(NT), p.lds_state, s, sa);
   e = hipGetLastError();
   if (e == hipSuccess) e = mark(1);
   if (e != hipSuccess) return (int)e;
@@ -785,10 +874,10 @@ int launch_forward(const Plan& p, const void* q, const void* k, const void* v, v
   ra.pos = pa_pos;
   ra.rope = p.rope;
   const dim3 gr((unsigned)(p.hg * p.nb * p.rpb), (unsigned)p.B);
-  if (in_bf16 && out_bf16) e = launch_readout<uint16_t, uint16_t>(ra, gr, p.lds_read, s);
-  else if (in_bf16) e = launch_readout<uint16_t, float>(ra, gr, p.lds_read, s);
-  else if (out_bf16) e = launch_readout<float, uint16_t>(ra, gr, p.lds_read, s);
-  else e = launch_readout<float, float>(ra, gr, p.lds_read, s);
+  if (in_bf16 && out_bf16) e = launch_readout<uint16_t, uint16_t>(ra, p2, gr, p.lds_read, s);
+  else if (in_bf16) e = launch_readout<uint16_t, float>(ra, p2, gr, p.lds_read, s);
+  else if (out_bf16) e = launch_readout<float, uint16_t>(ra, p2, gr, p.lds_read, s);
+  else e = launch_readout<float, float>(ra, p2, gr, p.lds_read, s);
   if (e == hipSuccess) e = mark(3);
   return (int)e;
 }

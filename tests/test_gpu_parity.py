@@ -76,6 +76,7 @@ def test_tiny_f32_matches_oracle(lavr):
     dict(frames=12, block_frames=4, H=1, B=1),        # whole blocks, one head
     dict(frames=5, block_frames=8),                   # one block shorter than block_frames
     dict(frames=40, block_frames=3, H=2, B=1, tokens_per_frame=48, grid=(6, 8)),  # many tiles
+    dict(rope={"split": (6, 14, 12), "base": 10000.0}),   # odd pair counts: per-pair table reads
 ])
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 def test_small_bf16_matches_oracle(lavr, kw, out_dtype):
@@ -111,8 +112,9 @@ def test_bf16_output_is_rne_of_f32_output(lavr):
     assert torch.equal(o16, o32.to(torch.bfloat16))
 
 
-def test_f32_small_3d(lavr):
-    cfg = small_cfg(dtype="f32")
+@pytest.mark.parametrize("split", [(8, 12, 12), (6, 14, 12)])
+def test_f32_small_3d(lavr, split):
+    cfg = small_cfg(dtype="f32", rope={"split": split, "base": 10000.0})
     say("case small f32 3-D RoPE")
     arrs, (q, k, v) = device_inputs(cfg, DEV)
     out = lavr.block_causal_forward(q, k, v, cfg["block_frames"], cfg["tokens_per_frame"], rope_for(lavr, cfg))
@@ -202,7 +204,8 @@ def test_streaming_equals_one_shot_small(lavr):
     got = stream_run(lavr, st, q, k, v, cfg, rope, 4, L, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert st.frames_done == 12
-    assert torch.allclose(got, one, rtol=1e-5, atol=1e-6 * one.abs().max().item())
+    # one-shot and streamed launches may sum a block's partials in another order
+    assert oracle.rel_err(to_f64_torch(got), to_f64_torch(one)) <= 1e-4
     assert oracle.rel_err(to_f64_torch(got), full_oracle(cfg, arrs)) <= 1e-4
 
 
