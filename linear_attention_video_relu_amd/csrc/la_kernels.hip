@@ -625,7 +625,15 @@ __global__ __launch_bounds__(NT) void k_readout(ReadArgs a) {
   const __amdgpu_buffer_rsrc_t ro =
       make_rsrc(static_cast<char*>(a.out) + ((size_t)b * a.N + t0) * RO, (uint32_t)(t1 - t0) * RO);
   int qoff = (w * 16 + tl) * RB + (h0 * D + 8 * ch) * ES;
-  int ooff = (w * 16 + tl) * RO + (h0 * D + 4 * ch) * EO;
+  int ooff = (w * 16) * RO + h0 * D * EO;
+  // Output offsets of this lane.  fp32: channels 4ch..+3 of each 16-channel half
+  // of token tl.  bf16 (after the exchange in run_group): a 16-byte piece of
+  // channels co..co+7; with two heads, tokens tl & 7 (first store) and 8 + (tl & 7)
+  // (second store) of head tl >> 3, so each store instruction writes whole
+  // 128-byte lines (8 tokens x both heads of the group).
+  const int co = 4 * ch + ((ch & 1) ? 12 : 0);
+  const int o_one = tl * RO + (EO == 2 ? co : 4 * ch) * EO;
+  const int o_pair = (tl & 7) * RO + ((tl >> 3) * D + co) * EO;
 
   // Prologue order: rotary window, then the prefix state, then the first Q
   // loads, so that no wait before the loop drains the Q prefetch.
@@ -689,6 +697,7 @@ __global__ __launch_bounds__(NT) void k_readout(ReadArgs a) {
       rl.fetch(tab, tp, win, cs);
       tp.advance(a.pos);
     }
+    u32x4 pk[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       if (h >= nh) break;
@@ -732,15 +741,37 @@ __global__ __launch_bounds__(NT) void k_readout(ReadArgs a) {
         const uint32_t p11 = pack_bf16(o[1][2] * inv, o[1][3] * inv);
         const auto s0 = __builtin_amdgcn_permlane16_swap(p00, p10, false, false);
         const auto s1 = __builtin_amdgcn_permlane16_swap(p01, p11, false, false);
-        const u32x4 pk = {s0[0], s1[0], s0[1], s1[1]};
-        __builtin_amdgcn_raw_buffer_store_b128(pk, ro, ooff + (h * D + ((ch & 1) ? 12 : 0)) * EO, 0, 0);
+        pk[h] = u32x4{s0[0], s1[0], s0[1], s1[1]};
       } else {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           const f32x4 ov = o[hf] * inv;
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ov), ro,
-                                                 ooff + (h * D + 16 * hf) * EO, 0, 0);
+                                                 ooff + o_one + (h * D + 16 * hf) * EO, 0, 0);
         }
+      }
+    }
+    if constexpr (EO == 2) {
+      if (nh == 2) {
+        // Lanes tl and tl ^ 8 (DPP row rotate by 8 inside each 16-lane row) trade
+        // one piece: the low lane keeps head 0 of tokens tl and tl + 8, the high
+        // lane head 1 of tokens tl - 8 and tl.
+        const bool lo = tl < 8;
+        uint32_t first[4], second[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t p0 = pk[0][i], p1 = pk[1][i];
+          const uint32_t snd = lo ? p1 : p0;
+          const uint32_t rcv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)snd, 0x128, 0xf, 0xf, false);
+          first[i] = lo ? p0 : rcv;
+          second[i] = lo ? rcv : p1;
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{first[0], first[1], first[2], first[3]}, ro,
+                                               ooff + o_pair, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{second[0], second[1], second[2], second[3]}, ro,
+                                               ooff + o_pair + 8 * RO, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b128(pk[0], ro, ooff + o_one, 0, 0);
       }
     }
     ooff += 64 * RO;

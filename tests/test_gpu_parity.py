@@ -287,7 +287,7 @@ def test_full_size_one_shot(lavr, name, heads):
 
 
 def test_full_size_streaming(lavr):
-    """40 streamed 3-frame blocks (B=2, 70 heads) == one-shot over 120 frames, bit for bit."""
+    """40 streamed 3-frame blocks (B=2, 70 heads) match one-shot over 120 frames to one bf16 step."""
     w = W()
     cfg = w.workload("stream_bf16")
     say("case full-size streaming 40 x 3 frames")
