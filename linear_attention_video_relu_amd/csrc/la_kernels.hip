@@ -539,9 +539,11 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? (P2 ? 4 : 3) : 2) void k_blo
 // Grid: x = element group (17 x 64 covers the 1056 floats of a record),
 // y = head, z = batch; 256 threads.  For each run of 32 blocks, the four waves
 // form block sums p_0 + p_1 + ... (chunk order) for blocks w, w+4, ... of the
-// run into LDS; then wave 0 walks the run in block order: prefix = previous
-// prefix + block sum.  A streaming call starts from the carried cache, so one
-// block streamed on top of a cache adds exactly as the one-shot prefix does.
+// run into LDS, reading the (block, chunk) partials of a wave eight at a time
+// so that their latencies overlap; then wave 0 walks the run in block order:
+// prefix = previous prefix + block sum.  A streaming call starts from the
+// carried cache, so one block streamed on top of a cache adds exactly as the
+// one-shot prefix does.
 
 constexpr int PFX_NT = 256;
 constexpr int PFX_RUN = 32;
@@ -552,21 +554,42 @@ __global__ __launch_bounds__(PFX_NT) void k_prefix(PrefixArgs a) {
   const int el = blockIdx.x * 64 + lane;
   const bool ok = el < REC;
   const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
-  const float* part = a.part + bh * a.nb * a.cpb * REC + el;
+  // (lanes past the record read its last element and discard it)
+  const float* part = a.part + bh * a.nb * a.cpb * REC + min(el, REC - 1);
   float* o = a.prefix + bh * a.nb * REC + el;
   float acc = 0.f;
   if (w == 0 && ok && a.S_init != nullptr)
     acc = el < D * D ? a.S_init[bh * D * D + el] : a.z_init[bh * D + el - D * D];
+  constexpr int BATCH = 8;
   for (int r0 = 0; r0 < a.nb; r0 += PFX_RUN) {
     const int nr = min(PFX_RUN, a.nb - r0);
-    for (int jj = w; jj < nr; jj += 4) {
-      float s = 0.f;
-      if (ok) {
-        const float* p = part + (size_t)(r0 + jj) * a.cpb * REC;
-        s = p[0];
-        for (int c = 1; c < a.cpb; ++c) s += p[(size_t)c * REC];
+    // Items of this wave: (block bi, chunk c) for its blocks r0 + w + 4 bi, in
+    // block-major, chunk-minor order; item q sits at block w + 4 (q / cpb).
+    const int items = (nr > w ? (nr - w + 3) / 4 : 0) * a.cpb;
+    float s = 0.f;
+    int bi = 0, c = 0;                    // (block, chunk) of the next item to add
+    for (int q0 = 0; q0 < items; q0 += BATCH) {
+      // Unconditional loads (items past the end reread the last one) keep the
+      // eight in flight together.
+      float v[BATCH];
+      int lb = bi, lcn = c;               // (block, chunk) of the next item to load
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        v[i] = part[((size_t)(r0 + w + 4 * lb) * a.cpb + lcn) * REC];
+        if (q0 + i + 1 < items && ++lcn == a.cpb) { lcn = 0; ++lb; }
       }
-      bs[jj][lane] = s;
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        if (q0 + i < items) {
+          s += v[i];
+          if (++c == a.cpb) {
+            bs[w + 4 * bi][lane] = s;
+            s = 0.f;
+            c = 0;
+            ++bi;
+          }
+        }
+      }
     }
     __syncthreads();
     if (w == 0 && ok) {
