@@ -180,7 +180,7 @@ def main():
     ptrs = [ctypes.c_void_p(x.data_ptr()) for x in (q, k, v, out)]
 
     def fwd():
-        rc = lavr.lib.la_block_causal_forward(*ptrs, code, code, B, H, 32, cfg["frames"], tpf, bf,
+        rc = lavr.lib.la_block_causal_forward(*ptrs, code, code, B, H, 32, cfg["frames"], tpf, bf, 0,
                                               ctypes.byref(rope.desc), 1e-8,
                                               ctypes.c_void_p(ws.data_ptr()), need, stream)
         if rc:
@@ -190,7 +190,7 @@ def main():
 
     def fwd_timed(i):
         rc = lavr.lib.la_block_causal_forward_timed(*ptrs, code, code, B, H, 32, cfg["frames"], tpf,
-                                                    bf, ctypes.byref(rope.desc), 1e-8,
+                                                    bf, 0, ctypes.byref(rope.desc), 1e-8,
                                                     ctypes.c_void_p(ws.data_ptr()), need, stream,
                                                     ev.ptr(4 * i))
         if rc:

@@ -101,13 +101,20 @@ int rope_table_build(la_rope* out, float* table_dev, size_t bytes, int head_dim,
                      int d_t, int d_h, int d_w, int max_frames, int grid_h, int grid_w,
                      double base, void* stream);
 
-/* Workspace bytes needed by la_block_causal_forward for this shape (for
- * la_stream_block pass frames = block_frames).  0 for invalid sizes. */
+/* Workspace bytes needed by la_block_causal_forward for this shape and block
+ * schedule (for la_stream_block pass frames = block_frames and
+ * first_block_frames = 0).  0 for invalid sizes. */
 size_t la_workspace_bytes(int B, int H, int head_dim, int frames, int tokens_per_frame,
-                          int block_frames);
+                          int block_frames, int first_block_frames);
 
-/* One-shot block-causal forward over `frames` frames, blocks of block_frames
- * frames (the last block may be shorter), starting from an empty cache.
+/* One-shot block-causal forward over `frames` frames, starting from an empty
+ * cache.  Blocks: the first holds first_block_frames frames (0 means
+ * block_frames: a uniform schedule), every later one block_frames frames, and
+ * the last may be shorter.  A first chunk one frame longer than the others is
+ * the schedule the SANA-WM pipeline pull request (huggingface/diffusers 13881,
+ * review thread) names as its configuration; a block of frames sees itself and
+ * every earlier block ("Implementing Block Causal Linear Attention for Long
+ * Video Generation with Sana", "Chunk-Wise Causality").
  * q, k, v have dtype in_dt, out has dtype out_dt (LA_BF16 out is rounded to
  * nearest even from the fp32 result).  All accumulation is fp32.  eps >= 0 is
  * added to the normaliser (1e-8 in SANA).  ws (256-byte aligned, ws_bytes >=
@@ -118,8 +125,8 @@ size_t la_workspace_bytes(int B, int H, int head_dim, int frames, int tokens_per
 int la_block_causal_forward(const void* q, const void* k, const void* v, void* out,
                             la_dtype in_dt, la_dtype out_dt,
                             int B, int H, int head_dim, int frames, int tokens_per_frame,
-                            int block_frames, const la_rope* rope, float eps,
-                            void* ws, size_t ws_bytes, void* stream);
+                            int block_frames, int first_block_frames, const la_rope* rope,
+                            float eps, void* ws, size_t ws_bytes, void* stream);
 
 /* la_block_causal_forward that also records four caller-created hipEvent_t
  * events[0..3] on `stream`: before the block-state kernel, after it, after
@@ -128,8 +135,9 @@ int la_block_causal_forward(const void* q, const void* k, const void* v, void* o
 int la_block_causal_forward_timed(const void* q, const void* k, const void* v, void* out,
                                   la_dtype in_dt, la_dtype out_dt,
                                   int B, int H, int head_dim, int frames, int tokens_per_frame,
-                                  int block_frames, const la_rope* rope, float eps,
-                                  void* ws, size_t ws_bytes, void* stream, void* const* events);
+                                  int block_frames, int first_block_frames, const la_rope* rope,
+                                  float eps, void* ws, size_t ws_bytes, void* stream,
+                                  void* const* events);
 
 /* Bind the caller's device buffers S_dev ([B][H][d][d] fp32) and z_dev
  * ([B][H][d] fp32), both 16-byte aligned, to *st, zero them on `stream`, and set

@@ -89,10 +89,13 @@ bool split_block(int L, int max_tokens, long long min_n, int mult, const la_rope
   }
 }
 
+// first_block_frames: frames of the first block (0 = block_frames).
 int make_plan(Plan* p, int B, int H, int head_dim, int frames, int tpf, int block_frames,
-              const la_rope* rope, long long t0, la_dtype in_dt) {
-  if (B < 1 || H < 1 || head_dim < 1 || frames < 1 || tpf < 1 || block_frames < 1)
+              int first_block_frames, const la_rope* rope, long long t0, la_dtype in_dt) {
+  if (B < 1 || H < 1 || head_dim < 1 || frames < 1 || tpf < 1 || block_frames < 1 ||
+      first_block_frames < 0)
     return LA_ERR_INVALID_ARG;
+  if (first_block_frames == 0) first_block_frames = block_frames;
   if (head_dim != lavr::kHeadDim) return LA_ERR_UNSUPPORTED;
   if (B > 65535 || H > 65535 || (long long)B * H > (1LL << 24)) return LA_ERR_UNSUPPORTED;
   const long long N = (long long)frames * tpf;
@@ -109,16 +112,18 @@ int make_plan(Plan* p, int B, int H, int head_dim, int frames, int tpf, int bloc
   p->tpf = tpf;
   p->gw_div = gw_div;
   p->L = (int)((long long)(block_frames < frames ? block_frames : frames) * tpf);
-  p->nb = (int)cdiv(N, p->L);
+  p->L0 = (int)((long long)(first_block_frames < frames ? first_block_frames : frames) * tpf);
+  p->nb = N <= p->L0 ? 1 : 1 + (int)cdiv(N - p->L0, p->L);
+  const int Lmax = p->L0 > p->L ? p->L0 : p->L;   // chunks and tiles are planned for the longest block
   p->hg = (H + lavr::kHeadsPerGroup - 1) / lavr::kHeadsPerGroup;
   p->t0 = t0;
   p->mag_tpf = (uint64_t)(kTwo42 / tpf) + 1;
   p->mag_gw = (uint64_t)(kTwo42 / gw_div) + 1;
   const long long row_bytes = (long long)H * head_dim * 4;
   const long long min_n = cdiv(kMinWg, (long long)B * p->hg * p->nb);
-  if (!split_block(p->L, kStateMax, min_n, kStep, rope, tpf, row_bytes, &p->cpb, &p->Tc))
+  if (!split_block(Lmax, kStateMax, min_n, kStep, rope, tpf, row_bytes, &p->cpb, &p->Tc))
     return LA_ERR_UNSUPPORTED;
-  if (!split_block(p->L, kReadMax, min_n, 64, rope, tpf, row_bytes, &p->rpb, &p->Tr))
+  if (!split_block(Lmax, kReadMax, min_n, 64, rope, tpf, row_bytes, &p->rpb, &p->Tr))
     return LA_ERR_UNSUPPORTED;
   if ((long long)p->hg * p->nb * p->cpb > 0x7fffffffLL || (long long)p->hg * p->nb * p->rpb > 0x7fffffffLL)
     return LA_ERR_UNSUPPORTED;
@@ -198,9 +203,10 @@ int rope_table_build(la_rope* out, float* table_dev, size_t bytes, int head_dim,
 }
 
 size_t la_workspace_bytes(int B, int H, int head_dim, int frames, int tokens_per_frame,
-                          int block_frames) {
+                          int block_frames, int first_block_frames) {
   Plan p;
-  if (make_plan(&p, B, H, head_dim, frames, tokens_per_frame, block_frames, nullptr, 0, LA_BF16) != LA_OK)
+  if (make_plan(&p, B, H, head_dim, frames, tokens_per_frame, block_frames, first_block_frames,
+                nullptr, 0, LA_BF16) != LA_OK)
     return 0;
   return p.ws_total;
 }
@@ -208,12 +214,13 @@ size_t la_workspace_bytes(int B, int H, int head_dim, int frames, int tokens_per
 int la_block_causal_forward(const void* q, const void* k, const void* v, void* out,
                             la_dtype in_dt, la_dtype out_dt, int B, int H, int head_dim,
                             int frames, int tokens_per_frame, int block_frames,
-                            const la_rope* rope, float eps, void* ws, size_t ws_bytes,
-                            void* stream) {
+                            int first_block_frames, const la_rope* rope, float eps, void* ws,
+                            size_t ws_bytes, void* stream) {
   if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return LA_ERR_INVALID_ARG;
   if (!std::isfinite(eps) || eps < 0.f) return LA_ERR_INVALID_ARG;
   Plan p;
-  int st = make_plan(&p, B, H, head_dim, frames, tokens_per_frame, block_frames, rope, 0, in_dt);
+  int st = make_plan(&p, B, H, head_dim, frames, tokens_per_frame, block_frames, first_block_frames,
+                     rope, 0, in_dt);
   if (st != LA_OK) return st;
   st = check_tensors(q, k, v, out, in_dt, out_dt, p);
   if (st != LA_OK) return st;
@@ -225,13 +232,14 @@ int la_block_causal_forward(const void* q, const void* k, const void* v, void* o
 int la_block_causal_forward_timed(const void* q, const void* k, const void* v, void* out,
                                   la_dtype in_dt, la_dtype out_dt, int B, int H, int head_dim,
                                   int frames, int tokens_per_frame, int block_frames,
-                                  const la_rope* rope, float eps, void* ws, size_t ws_bytes,
-                                  void* stream, void* const* events) {
+                                  int first_block_frames, const la_rope* rope, float eps,
+                                  void* ws, size_t ws_bytes, void* stream, void* const* events) {
   if (!events || !events[0] || !events[1] || !events[2] || !events[3]) return LA_ERR_INVALID_ARG;
   if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return LA_ERR_INVALID_ARG;
   if (!std::isfinite(eps) || eps < 0.f) return LA_ERR_INVALID_ARG;
   Plan p;
-  int st = make_plan(&p, B, H, head_dim, frames, tokens_per_frame, block_frames, rope, 0, in_dt);
+  int st = make_plan(&p, B, H, head_dim, frames, tokens_per_frame, block_frames, first_block_frames,
+                     rope, 0, in_dt);
   if (st != LA_OK) return st;
   st = check_tensors(q, k, v, out, in_dt, out_dt, p);
   if (st != LA_OK) return st;
@@ -270,7 +278,7 @@ int la_stream_block(la_state* st, const void* q, const void* k, const void* v, v
   if (st->frames_done < 0) return LA_ERR_INVALID_ARG;
   if (B != st->B || H != st->H || head_dim != st->head_dim) return LA_ERR_STATE_MISMATCH;
   Plan p;
-  int rc = make_plan(&p, B, H, head_dim, block_frames, tokens_per_frame, block_frames, rope,
+  int rc = make_plan(&p, B, H, head_dim, block_frames, tokens_per_frame, block_frames, 0, rope,
                      st->frames_done, in_dt);
   if (rc != LA_OK) return rc;
   rc = check_tensors(q, k, v, out, in_dt, out_dt, p);
@@ -295,6 +303,6 @@ const char* la_status_string(int status) {
   }
 }
 
-const char* la_version(void) { return "0.1.0"; }
+const char* la_version(void) { return "0.2.0"; }
 
 }  // extern "C"

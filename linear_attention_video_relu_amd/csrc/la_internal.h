@@ -25,7 +25,8 @@ struct Plan {
   int N;                // tokens per sequence in this call
   int tpf;              // tokens per frame
   int gw_div;           // divisor for row/col (grid_w, or 1 without spatial sections)
-  int L;                // tokens per block
+  int L;                // tokens per block (after the first)
+  int L0;               // tokens of the first block
   int nb;               // blocks in this call
   int hg;               // head groups = ceil(H / 2)
   int cpb, Tc;          // block-state chunks per block, tokens per chunk

@@ -73,7 +73,7 @@ struct StateArgs {
   const void* k;
   const void* v;
   float* part;
-  int H, N, L, nb, cpb, Tc, hg;
+  int H, N, L, L0, nb, cpb, Tc, hg;   // L0: tokens of the first block
   PosArgs pos;
   RopeDev rope;
 };
@@ -93,7 +93,7 @@ struct ReadArgs {
   void* out;
   const float* prefix;
   float eps;
-  int H, N, L, nb, rpb, Tr, hg;
+  int H, N, L, L0, nb, rpb, Tr, hg;   // L0: tokens of the first block
   PosArgs pos;
   RopeDev rope;
 };
@@ -126,6 +126,10 @@ __device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+// First token of block j when the first block holds L0 tokens and every later
+// one L.
+__device__ __forceinline__ int block_start(int j, int L0, int L) { return j == 0 ? 0 : L0 + (j - 1) * L; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, RSRC_WORD3);
@@ -363,8 +367,8 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? (P2 ? 4 : 3) : 2) void k_blo
   const int b = blockIdx.y;
   const int j = ci / a.cpb;
   const int c = ci - j * a.cpb;
-  const int blk0 = j * a.L;
-  const int blk1 = min(blk0 + a.L, a.N);
+  const int blk0 = block_start(j, a.L0, a.L);
+  const int blk1 = min(blk0 + (j == 0 ? a.L0 : a.L), a.N);
   const int c0 = min(blk0 + c * a.Tc, blk1);
   const int c1 = min(c0 + a.Tc, blk1);
   const int h0 = g * kHeadsPerGroup;
@@ -629,8 +633,8 @@ __global__ __launch_bounds__(NT) void k_readout(ReadArgs a) {
   const int b = blockIdx.y;
   const int j = ti / a.rpb;
   const int r = ti - j * a.rpb;
-  const int blk0 = j * a.L;
-  const int blk1 = min(blk0 + a.L, a.N);
+  const int blk0 = block_start(j, a.L0, a.L);
+  const int blk1 = min(blk0 + (j == 0 ? a.L0 : a.L), a.N);
   const int t0 = min(blk0 + r * a.Tr, blk1);
   const int t1 = min(t0 + a.Tr, blk1);
   if (t0 >= t1) return;
@@ -900,7 +904,7 @@ int launch_forward(const Plan& p, const void* q, const void* k, const void* v, v
 
   StateArgs sa;
   sa.k = k; sa.v = v; sa.part = part;
-  sa.H = p.H; sa.N = p.N; sa.L = p.L; sa.nb = p.nb; sa.cpb = p.cpb; sa.Tc = p.Tc; sa.hg = p.hg;
+  sa.H = p.H; sa.N = p.N; sa.L = p.L; sa.L0 = p.L0; sa.nb = p.nb; sa.cpb = p.cpb; sa.Tc = p.Tc; sa.hg = p.hg;
   sa.pos = pa_pos;
   sa.rope = p.rope;
   const dim3 gs((unsigned)(p.hg * p.nb * p.cpb), (unsigned)p.B);
@@ -924,7 +928,7 @@ int launch_forward(const Plan& p, const void* q, const void* k, const void* v, v
 
   ReadArgs ra;
   ra.q = q; ra.out = out; ra.prefix = prefix; ra.eps = eps;
-  ra.H = p.H; ra.N = p.N; ra.L = p.L; ra.nb = p.nb; ra.rpb = p.rpb; ra.Tr = p.Tr; ra.hg = p.hg;
+  ra.H = p.H; ra.N = p.N; ra.L = p.L; ra.L0 = p.L0; ra.nb = p.nb; ra.rpb = p.rpb; ra.Tr = p.Tr; ra.hg = p.hg;
   ra.pos = pa_pos;
   ra.rope = p.rope;
   const dim3 gr((unsigned)(p.hg * p.nb * p.rpb), (unsigned)p.B);

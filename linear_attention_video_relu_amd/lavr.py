@@ -42,12 +42,12 @@ def _load():
         "rope_table_bytes": (c_size, [c_int] * 6),
         "rope_table_build": (c_int, [ctypes.POINTER(LaRope), c_vp, c_size, c_int, c_int, c_int,
                                      c_int, c_int, c_int, c_int, c_double, c_vp]),
-        "la_workspace_bytes": (c_size, [c_int] * 6),
+        "la_workspace_bytes": (c_size, [c_int] * 7),
         "la_block_causal_forward": (c_int, [c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int,
-                                            c_int, c_int, c_int, c_int, ctypes.POINTER(LaRope),
-                                            c_float, c_vp, c_size, c_vp]),
+                                            c_int, c_int, c_int, c_int, c_int,
+                                            ctypes.POINTER(LaRope), c_float, c_vp, c_size, c_vp]),
         "la_block_causal_forward_timed": (c_int, [c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int,
-                                                  c_int, c_int, c_int, c_int, c_int,
+                                                  c_int, c_int, c_int, c_int, c_int, c_int,
                                                   ctypes.POINTER(LaRope), c_float, c_vp, c_size,
                                                   c_vp, ctypes.POINTER(c_vp)]),
         "la_state_init": (c_int, [ctypes.POINTER(LaState), c_vp, c_vp, c_int, c_int, c_int, c_vp]),
@@ -129,9 +129,11 @@ def _rope_ptr(rope):
 
 # ------------------------------------------------------------------ one-shot
 
-def workspace_bytes(B, H, frames, tokens_per_frame, block_frames, head_dim=HEAD_DIM):
+def workspace_bytes(B, H, frames, tokens_per_frame, block_frames, head_dim=HEAD_DIM,
+                    first_block_frames=0):
+    """Workspace bytes of a forward call (first_block_frames 0 = uniform blocks)."""
     n = lib.la_workspace_bytes(int(B), int(H), int(head_dim), int(frames), int(tokens_per_frame),
-                               int(block_frames))
+                               int(block_frames), int(first_block_frames or 0))
     if n == 0:
         raise ValueError("invalid shape for la_workspace_bytes")
     return n
@@ -162,8 +164,10 @@ def _check_qkv(q, k, v):
 
 
 def block_causal_forward(q, k, v, block_frames, tokens_per_frame, rope=None, eps=EPS_DEFAULT,
-                         out=None, out_dtype=None, workspace=None):
-    """One-shot block-causal forward.  q, k, v: (B, N, H, 32), N = frames * tokens_per_frame."""
+                         out=None, out_dtype=None, workspace=None, first_block_frames=None):
+    """One-shot block-causal forward.  q, k, v: (B, N, H, 32), N = frames * tokens_per_frame.
+
+    first_block_frames: frames of the first block (None = block_frames)."""
     _check_qkv(q, k, v)
     B, N, H, d = q.shape
     if N % tokens_per_frame:
@@ -174,11 +178,12 @@ def block_causal_forward(q, k, v, block_frames, tokens_per_frame, rope=None, eps
         out = torch.empty((B, N, H, d), dtype=out_dtype, device=q.device)
     elif out.shape != q.shape or out.dtype != out_dtype or not out.is_contiguous() or out.device != q.device:
         raise ValueError("out must be a contiguous tensor of q's shape and out_dtype on q's device")
-    need = lib.la_workspace_bytes(B, H, d, frames, int(tokens_per_frame), int(block_frames))
+    f0 = int(first_block_frames or 0)
+    need = lib.la_workspace_bytes(B, H, d, frames, int(tokens_per_frame), int(block_frames), f0)
     ws = _workspace(q.device, need) if workspace is None else workspace
     _check(lib.la_block_causal_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(q.dtype),
                                        _dtype_code(out_dtype), B, H, d, frames,
-                                       int(tokens_per_frame), int(block_frames), _rope_ptr(rope),
+                                       int(tokens_per_frame), int(block_frames), f0, _rope_ptr(rope),
                                        float(eps), _ptr(ws), ws.numel() * ws.element_size(),
                                        _stream(q.device)), "la_block_causal_forward")
     return out
@@ -224,7 +229,7 @@ class StreamState:
             out = torch.empty((B, N, H, d), dtype=out_dtype, device=q.device)
         elif out.shape != q.shape or out.dtype != out_dtype or not out.is_contiguous():
             raise ValueError("out must be a contiguous tensor of q's shape and out_dtype")
-        need = lib.la_workspace_bytes(B, H, d, frames, int(tokens_per_frame), frames)
+        need = lib.la_workspace_bytes(B, H, d, frames, int(tokens_per_frame), frames, 0)
         ws = _workspace(q.device, need) if workspace is None else workspace
         _check(lib.la_stream_block(ctypes.byref(self.desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                    _dtype_code(q.dtype), _dtype_code(out_dtype), B, H, d, frames,

@@ -101,19 +101,32 @@ def _relu(x):
 
 # ------------------------------------------------------------------ one-shot forward
 
-def block_bounds(n_tokens, block_tokens):
-    """Token ranges [s, e) of the blocks; the last one may be shorter."""
-    return [(s, min(s + block_tokens, n_tokens)) for s in range(0, n_tokens, block_tokens)]
+def block_bounds(n_tokens, block_tokens, first_tokens=None):
+    """Token ranges [s, e) of the blocks; the last one may be shorter.
+
+    first_tokens (default block_tokens) is the length of the first block: a
+    schedule whose first chunk holds one frame more than the others is named in
+    [SANA-WM] (review thread: the configuration uses "first_chunk_plus_one").
+    """
+    first = block_tokens if first_tokens is None else first_tokens
+    bounds = [(0, min(first, n_tokens))]
+    s = first
+    while s < n_tokens:
+        bounds.append((s, min(s + block_tokens, n_tokens)))
+        s += block_tokens
+    return bounds
 
 
-def _head_forward(q, k, v, tokens_per_frame, block_frames, rope, eps, t0, S, z):
+def _head_forward(q, k, v, tokens_per_frame, block_frames, rope, eps, t0, S, z,
+                  first_block_frames=None):
     """One (batch, head) stream: q, k, v are (n, d); S (d, d) and z (d) are updated in place."""
     fq, fk = _relu(q), _relu(k)
     rq = _rotate_tokens(fq, rope, tokens_per_frame, t0)
     rk = _rotate_tokens(fk, rope, tokens_per_frame, t0)
     v = np.asarray(v, dtype=np.float64)
     out = np.empty_like(v)
-    for s, e in block_bounds(q.shape[0], block_frames * tokens_per_frame):
+    first = None if first_block_frames is None else first_block_frames * tokens_per_frame
+    for s, e in block_bounds(q.shape[0], block_frames * tokens_per_frame, first):
         S += v[s:e].T @ rk[s:e]          # S[e_, f] += sum_n v[n, e_] * rk[n, f]
         z += fk[s:e].sum(axis=0)         # un-rotated key-sum
         num = rq[s:e] @ S.T              # num[n, e_] = sum_f S[e_, f] * rq[n, f]
@@ -122,12 +135,14 @@ def _head_forward(q, k, v, tokens_per_frame, block_frames, rope, eps, t0, S, z):
     return out
 
 
-def forward(q, k, v, tokens_per_frame, block_frames, rope=None, eps=EPS_DEFAULT):
+def forward(q, k, v, tokens_per_frame, block_frames, rope=None, eps=EPS_DEFAULT,
+            first_block_frames=None):
     """Block-causal forward over whole sequences.
 
     q, k, v: (B, N, H, d) arrays (any float dtype; taken as float64).
     rope: None (no rotation) or {"split": (d_t, d_h, d_w), "grid": (rows, cols),
-    "base": float}.  Returns out (B, N, H, d) float64.
+    "base": float}.  first_block_frames: frames of the first block (default
+    block_frames).  Returns out (B, N, H, d) float64.
     """
     q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
     B, N, H, d = q.shape
@@ -136,18 +151,21 @@ def forward(q, k, v, tokens_per_frame, block_frames, rope=None, eps=EPS_DEFAULT)
         for h in range(H):
             S, z = np.zeros((d, d)), np.zeros(d)
             out[b, :, h] = _head_forward(q[b, :, h], k[b, :, h], v[b, :, h],
-                                         tokens_per_frame, block_frames, rope, eps, 0, S, z)
+                                         tokens_per_frame, block_frames, rope, eps, 0, S, z,
+                                         first_block_frames)
     return out
 
 
-def forward_head(q, k, v, tokens_per_frame, block_frames, rope=None, eps=EPS_DEFAULT):
+def forward_head(q, k, v, tokens_per_frame, block_frames, rope=None, eps=EPS_DEFAULT,
+                 first_block_frames=None):
     """Same as forward for one (batch, head) slice: q, k, v are (N, d)."""
     d = q.shape[1]
     S, z = np.zeros((d, d)), np.zeros(d)
-    return _head_forward(q, k, v, tokens_per_frame, block_frames, rope, eps, 0, S, z)
+    return _head_forward(q, k, v, tokens_per_frame, block_frames, rope, eps, 0, S, z,
+                         first_block_frames)
 
 
-def block_states(k, v, tokens_per_frame, block_frames, rope=None, t0=0):
+def block_states(k, v, tokens_per_frame, block_frames, rope=None, t0=0, first_block_frames=None):
     """Inclusive prefix states (S_bar_j, z_bar_j) of every block of one head (k, v: (N, d))."""
     fk = _relu(k)
     rk = _rotate_tokens(fk, rope, tokens_per_frame, t0)
@@ -155,7 +173,8 @@ def block_states(k, v, tokens_per_frame, block_frames, rope=None, t0=0):
     d = k.shape[1]
     S, z = np.zeros((d, d)), np.zeros(d)
     Ss, zs = [], []
-    for s, e in block_bounds(k.shape[0], block_frames * tokens_per_frame):
+    first = None if first_block_frames is None else first_block_frames * tokens_per_frame
+    for s, e in block_bounds(k.shape[0], block_frames * tokens_per_frame, first):
         S = S + v[s:e].T @ rk[s:e]
         z = z + fk[s:e].sum(axis=0)
         Ss.append(S.copy())
@@ -220,16 +239,20 @@ def stream_block(state, q, k, v, tokens_per_frame, rope=None, eps=EPS_DEFAULT, s
 
 # ------------------------------------------------------------- independent checks
 
-def brute_force(q, k, v, tokens_per_frame, block_frames, rope=None, eps=EPS_DEFAULT):
+def brute_force(q, k, v, tokens_per_frame, block_frames, rope=None, eps=EPS_DEFAULT,
+                first_block_frames=None):
     """O(N^2) masked form, for tiny inputs.
 
     out_i = sum_j M_ij <rk_j, rq_i> v_j / (sum_j M_ij <fk_j, fq_i> + eps),
-    M_ij = [block(j) <= block(i)].  Written token by token, with no prefix state.
+    M_ij = [block(j) <= block(i)].  Written token by token, with no prefix state;
+    the block of a token comes from its frame index: frames below the first
+    block's end are block 0, then one block per block_frames frames.
     """
     q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
     B, N, H, d = q.shape
-    L = block_frames * tokens_per_frame
-    blk = np.arange(N) // L
+    f0 = block_frames if first_block_frames is None else first_block_frames
+    frame = np.arange(N) // tokens_per_frame
+    blk = np.where(frame < f0, 0, 1 + (frame - f0) // block_frames)
     out = np.empty((B, N, H, d))
     for b in range(B):
         for h in range(H):

@@ -32,7 +32,8 @@ def oracle_head(cfg, arrs, b, h, block_frames=None):
     """fp64 oracle output of one (batch, head) of a drawn workload: (N, 32)."""
     q, k, v = (W.to_f64(cfg, arrs[t][b, :, h]) for t in W.TENSORS)
     bf = cfg["block_frames"] if block_frames is None else block_frames
-    return oracle.forward_head(q, k, v, cfg["tokens_per_frame"], bf, W.oracle_rope(cfg))
+    return oracle.forward_head(q, k, v, cfg["tokens_per_frame"], bf, W.oracle_rope(cfg),
+                               first_block_frames=cfg.get("first_block_frames"))
 
 
 def to_f64_torch(t):

@@ -35,7 +35,7 @@ def test_exports_every_declared_function(lavr):
 
 
 def test_version_and_status_strings(lavr):
-    assert lavr.lib.la_version() == b"0.1.0"
+    assert lavr.lib.la_version() == b"0.2.0"
     for code in range(5):
         assert lavr.status_string(code).startswith("LA_")
     assert "unknown" in lavr.status_string(99)
@@ -54,8 +54,12 @@ def test_workspace_bytes(lavr):
     rec = (32 * 32 + 32) * 4
     assert n >= 70 * 30 * rec            # at least the per-block prefix states
     assert n < 0.05 * 1 * 374400 * 70 * 32 * 2 * 4   # small next to q, k, v, out
-    assert lavr.lib.la_workspace_bytes(1, 70, 64, 240, 1560, 8) == 0   # head_dim 64 not built
-    assert lavr.lib.la_workspace_bytes(0, 70, 32, 240, 1560, 8) == 0
+    assert lavr.lib.la_workspace_bytes(1, 70, 64, 240, 1560, 8, 0) == 0   # head_dim 64 not built
+    assert lavr.lib.la_workspace_bytes(0, 70, 32, 240, 1560, 8, 0) == 0
+    assert lavr.lib.la_workspace_bytes(1, 70, 32, 240, 1560, 8, -1) == 0  # bad first block
+    # a first block of 9 frames: 1 + ceil(231 / 8) = 30 blocks, workspace at least as large
+    assert lavr.workspace_bytes(1, 70, 240, 1560, 8, first_block_frames=9) >= 70 * 30 * rec
+    assert lavr.workspace_bytes(1, 70, 240, 1560, 8, first_block_frames=8) == n
 
 
 FAKE = 0x100000          # 16- and 256-byte aligned, never dereferenced: every call below fails validation
@@ -64,12 +68,12 @@ FAKE = 0x100000          # 16- and 256-byte aligned, never dereferenced: every c
 def call_forward(lavr, **kw):
     args = dict(q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, out=FAKE + 0x3000000,
                 in_dt=lavr.LA_BF16, out_dt=lavr.LA_BF16, B=1, H=2, d=32, frames=4, tpf=6,
-                bf=2, rope=None, eps=1e-8, ws=FAKE + 0x4000000, ws_bytes=1 << 20)
+                bf=2, f0=0, rope=None, eps=1e-8, ws=FAKE + 0x4000000, ws_bytes=1 << 20)
     args.update(kw)
     return lavr.lib.la_block_causal_forward(
         ctypes.c_void_p(args["q"]), ctypes.c_void_p(args["k"]), ctypes.c_void_p(args["v"]),
         ctypes.c_void_p(args["out"]), args["in_dt"], args["out_dt"], args["B"], args["H"],
-        args["d"], args["frames"], args["tpf"], args["bf"], args["rope"], args["eps"],
+        args["d"], args["frames"], args["tpf"], args["bf"], args["f0"], args["rope"], args["eps"],
         ctypes.c_void_p(args["ws"]), args["ws_bytes"], None)
 
 
@@ -81,6 +85,7 @@ def call_forward(lavr, **kw):
     (dict(frames=0), 1),
     (dict(tpf=0), 1),
     (dict(bf=0), 1),
+    (dict(f0=-2), 1),                    # negative first-block length
     (dict(d=64), 2),                     # head_dim 64 is not built
     (dict(in_dt=7), 1),
     (dict(eps=-1.0), 1),

@@ -54,7 +54,8 @@ def small_cfg(**kw):
 def full_oracle(cfg, arrs):
     w = W()
     return oracle.forward(*(w.to_f64(cfg, arrs[t]) for t in w.TENSORS), cfg["tokens_per_frame"],
-                          cfg["block_frames"], w.oracle_rope(cfg))
+                          cfg["block_frames"], w.oracle_rope(cfg),
+                          first_block_frames=cfg.get("first_block_frames"))
 
 
 # -------------------------------------------------------------- small, every element
@@ -182,6 +183,67 @@ def test_deterministic(lavr):
     assert torch.equal(a, b)
 
 
+# ------------------------------------------- block schedule: a first block of other length
+
+@pytest.mark.parametrize("frames,bf,f0", [
+    (11, 3, 4),      # one frame more first: 4 + 3 + 3 + 1
+    (10, 3, 1),      # a shorter first block: 1 + 3 + 3 + 3
+    (5, 3, 7),       # the first block covers the whole clip
+    (12, 3, 3),      # equal to block_frames: the uniform schedule
+])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_first_block_schedule_small(lavr, frames, bf, f0, out_dtype):
+    cfg = small_cfg(frames=frames, block_frames=bf, first_block_frames=f0)
+    say(f"case first-block schedule frames={frames} bf={bf} first={f0} out={out_dtype}")
+    arrs, (q, k, v) = device_inputs(cfg, DEV)
+    od = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    out = lavr.block_causal_forward(q, k, v, bf, cfg["tokens_per_frame"], rope_for(lavr, cfg),
+                                    out_dtype=od, first_block_frames=f0)
+    torch.cuda.synchronize()
+    ref = full_oracle(cfg, arrs)
+    got = to_f64_torch(out)
+    if out_dtype == "f32":
+        err = oracle.rel_err(got, ref)
+        assert err <= 1e-4
+    else:
+        err = err_bf16_out(got, ref)
+    say(f"  err {err:.3e}")
+    assert err <= TOL_BF16
+
+
+def test_first_block_schedule_equals_uniform_when_equal(lavr):
+    cfg = small_cfg(frames=9)
+    say("case first block == block_frames is the uniform schedule, bit for bit")
+    _, (q, k, v) = device_inputs(cfg, DEV)
+    rope = rope_for(lavr, cfg)
+    a = lavr.block_causal_forward(q, k, v, 3, cfg["tokens_per_frame"], rope).clone()
+    b = lavr.block_causal_forward(q, k, v, 3, cfg["tokens_per_frame"], rope, first_block_frames=3)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_streaming_first_block_plus_one(lavr):
+    """A 4-frame first call, then 3-frame calls == one-shot with first_block_frames=4."""
+    cfg = small_cfg(frames=13, block_frames=3, first_block_frames=4)
+    say("case streaming with a longer first block")
+    arrs, (q, k, v) = device_inputs(cfg, DEV)
+    rope = rope_for(lavr, cfg)
+    tpf = cfg["tokens_per_frame"]
+    one = lavr.block_causal_forward(q, k, v, 3, tpf, rope, out_dtype=torch.float32, first_block_frames=4)
+    st = lavr.StreamState(cfg["B"], cfg["H"], device=DEV)
+    outs, s0 = [], 0
+    for f in (4, 3, 3, 3):
+        sl = slice(s0, s0 + f * tpf)
+        outs.append(st.step(q[:, sl].contiguous(), k[:, sl].contiguous(), v[:, sl].contiguous(),
+                            tpf, rope, out_dtype=torch.float32))
+        s0 += f * tpf
+    got = torch.cat(outs, dim=1)
+    torch.cuda.synchronize()
+    assert st.frames_done == 13
+    assert oracle.rel_err(to_f64_torch(got), to_f64_torch(one)) <= 1e-4
+    assert oracle.rel_err(to_f64_torch(got), full_oracle(cfg, arrs)) <= 1e-4
+
+
 # ----------------------------------------------------------------------- streaming
 
 def stream_run(lavr, st, q, k, v, cfg, rope, nblk, L, save=True, out_dtype=None):
@@ -284,6 +346,53 @@ def test_full_size_one_shot(lavr, name, heads):
     assert torch.isfinite(out).all().item()
     del out, q, k, v
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name,over,heads", [
+    ("clip720p_bf16", dict(first_block_frames=4), [(0, 2), (1, 68)]),   # 4 + 3 x 5 + 2 frames
+    ("minute_bf16", dict(block_frames=16), [(0, 3), (0, 60)]),          # 15 blocks of 16 frames
+])
+def test_full_size_other_schedules(lavr, name, over, heads):
+    w = W()
+    cfg = w.workload(name, **over)
+    say(f"case full-size {name} {over}")
+    arrs, (q, k, v) = device_inputs(cfg, DEV)
+    rope = rope_for(lavr, cfg)
+    out = lavr.block_causal_forward(q, k, v, cfg["block_frames"], cfg["tokens_per_frame"], rope,
+                                    first_block_frames=cfg.get("first_block_frames"))
+    torch.cuda.synchronize()
+    assert check_heads(cfg, arrs, out, heads, name) <= TOL_BF16
+    del out, q, k, v
+    torch.cuda.empty_cache()
+
+
+def test_full_size_streaming_save_off_reuse(lavr):
+    """Each of 40 blocks read twice with save=0 (denoising steps), then committed:
+    the save=0 outputs equal the committed ones bit for bit, the cache only moves
+    on commits, and the committed outputs equal plain streaming."""
+    w = W()
+    cfg = w.workload("stream_bf16")
+    say("case full-size streaming with save=0 reuse")
+    _, (q, k, v) = device_inputs(cfg, DEV)
+    rope = rope_for(lavr, cfg)
+    tpf = cfg["tokens_per_frame"]
+    L = 3 * tpf
+    plain = lavr.StreamState(cfg["B"], cfg["H"], device=DEV)
+    ref = stream_run(lavr, plain, q, k, v, cfg, rope, 40, L)
+    st = lavr.StreamState(cfg["B"], cfg["H"], device=DEV)
+    for j in range(40):
+        sl = slice(j * L, (j + 1) * L)
+        x = tuple(t[:, sl].contiguous() for t in (q, k, v))
+        a = st.step(*x, tpf, rope, save=False)
+        b = st.step(*x, tpf, rope, save=False)
+        c = st.step(*x, tpf, rope, save=True)
+        if j % 13 == 0:
+            torch.cuda.synchronize()
+            assert torch.equal(a, b) and torch.equal(a, c)
+            assert torch.equal(c, ref[:, sl])
+    torch.cuda.synchronize()
+    assert st.frames_done == 120
+    assert torch.equal(st.S, plain.S) and torch.equal(st.z, plain.z)
 
 
 def test_full_size_streaming(lavr):

@@ -288,3 +288,57 @@ def test_rel_err_metric():
     ref = np.array([3.0, -4.0])          # RMS = sqrt(12.5)
     got = np.array([3.5, -4.0])
     assert oracle.rel_err(got, ref) == pytest.approx(0.5 / np.sqrt(12.5))
+
+
+# ------------------------------------------- first block longer than the others (N1)
+
+@pytest.mark.parametrize("tpf,frames,block_frames,first,rope", [
+    (6, 7, 2, 3, ROPE_3D),      # first block one frame longer: 3 + 2 + 2
+    (6, 8, 2, 3, ROPE_3D),      # ... with a ragged last block: 3 + 2 + 2 + 1
+    (1, 21, 4, 5, ROPE_1D),     # 1-D: 5 + 4 + 4 + 4 + 4
+    (6, 5, 2, 1, ROPE_3D),      # first block shorter: 1 + 2 + 2
+    (6, 3, 2, 4, ROPE_3D),      # first block covers the whole clip
+])
+def test_first_block_schedule_matches_brute_force(tpf, frames, block_frames, first, rope):
+    q, k, v = rand_qkv(31, 2, frames * tpf, 2, 8)
+    got = oracle.forward(q, k, v, tpf, block_frames, rope, first_block_frames=first)
+    ref = oracle.brute_force(q, k, v, tpf, block_frames, rope, first_block_frames=first)
+    assert np.max(np.abs(got - ref)) <= 1e-9 * np.max(np.abs(ref))
+
+
+def test_first_block_schedule_bounds():
+    assert oracle.block_bounds(17, 4, 5) == [(0, 5), (5, 9), (9, 13), (13, 17)]
+    assert oracle.block_bounds(18, 4, 5) == [(0, 5), (5, 9), (9, 13), (13, 17), (17, 18)]
+    assert oracle.block_bounds(3, 4, 5) == [(0, 3)]
+    assert oracle.block_bounds(8, 4) == oracle.block_bounds(8, 4, 4) == [(0, 4), (4, 8)]
+
+
+def test_first_block_equal_to_block_is_uniform():
+    q, k, v = rand_qkv(32, 1, 7 * 6, 2, 8)
+    a = oracle.forward(q, k, v, 6, 2, ROPE_3D)
+    b = oracle.forward(q, k, v, 6, 2, ROPE_3D, first_block_frames=2)
+    assert np.array_equal(a, b)
+
+
+def test_first_block_spanning_clip_is_single_block_formula():
+    """A first block holding every frame is the single-block formula as printed."""
+    q, k, v = rand_qkv(33, 1, 4 * 6, 2, 8)
+    got = oracle.forward(q, k, v, 6, 1, ROPE_3D, first_block_frames=4)
+    ref = oracle.lite_la_single_block(q, k, v, 6, ROPE_3D)
+    assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_streaming_first_block_plus_one_equals_one_shot():
+    """Streaming a 3-frame first block, then 2-frame blocks == one-shot with that schedule."""
+    tpf, bf, first, frames = 6, 2, 3, 7
+    q, k, v = rand_qkv(34, 2, frames * tpf, 2, 8)
+    ref = oracle.forward(q, k, v, tpf, bf, ROPE_3D, first_block_frames=first)
+    st = oracle.StreamState(2, 2, 8)
+    outs, s = [], 0
+    for f in (first, bf, bf):
+        e = s + f * tpf
+        outs.append(oracle.stream_block(st, q[:, s:e], k[:, s:e], v[:, s:e], tpf, ROPE_3D))
+        s = e
+    got = np.concatenate(outs, axis=1)
+    assert st.frames_done == frames
+    assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
