@@ -28,7 +28,11 @@ from linear_attention_video_relu_amd import workloads as W  # noqa: E402
 
 METRIC = "tokens·heads/s and achieved HBM GB/s (% peak), block-causal LA fwd"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
-REC_BYTES = (32 * 32 + 32) * 4  # one fp32 (S, z) record
+
+
+def rec_bytes(d):
+    """Bytes of one fp32 (S, z) record at head dim d."""
+    return (d * d + d) * 4
 KERNEL_SOURCES = ("la_kernels.hip", "la_internal.h", "la_api.cpp")
 
 
@@ -150,7 +154,7 @@ def main():
         sys.exit(2)
 
     cfg = W.workload(args.workload)
-    B, H, N = cfg["B"], cfg["H"], W.n_tokens(cfg)
+    B, H, N, d = cfg["B"], cfg["H"], W.n_tokens(cfg), cfg["head_dim"]
     tpf, bf = cfg["tokens_per_frame"], cfg["block_frames"]
     t = time.perf_counter()
     arrs = {x: W.draw(cfg, x) for x in W.TENSORS}
@@ -173,14 +177,14 @@ def main():
     dt = q.dtype
     rope = lavr.RopeTable(cfg["rope"]["split"], cfg["grid"], cfg["frames"], cfg["rope"]["base"], dev)
     out = torch.empty_like(q)
-    need = lavr.workspace_bytes(B, H, cfg["frames"], tpf, bf)
+    need = lavr.workspace_bytes(B, H, cfg["frames"], tpf, bf, head_dim=d)
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     code = lavr._dtype_code(dt)
     ptrs = [ctypes.c_void_p(x.data_ptr()) for x in (q, k, v, out)]
 
     def fwd():
-        rc = lavr.lib.la_block_causal_forward(*ptrs, code, code, B, H, 32, cfg["frames"], tpf, bf, 0,
+        rc = lavr.lib.la_block_causal_forward(*ptrs, code, code, B, H, d, cfg["frames"], tpf, bf, 0,
                                               ctypes.byref(rope.desc), 1e-8,
                                               ctypes.c_void_p(ws.data_ptr()), need, stream)
         if rc:
@@ -189,7 +193,7 @@ def main():
     ev = HipEvents(4 * args.steps)
 
     def fwd_timed(i):
-        rc = lavr.lib.la_block_causal_forward_timed(*ptrs, code, code, B, H, 32, cfg["frames"], tpf,
+        rc = lavr.lib.la_block_causal_forward_timed(*ptrs, code, code, B, H, d, cfg["frames"], tpf,
                                                     bf, 0, ctypes.byref(rope.desc), 1e-8,
                                                     ctypes.c_void_p(ws.data_ptr()), need, stream,
                                                     ev.ptr(4 * i))
@@ -220,10 +224,10 @@ def main():
     th = B * N * H
     esz = 2 if dt == torch.bfloat16 else 4
     nb = -(-cfg["frames"] // bf)
-    state_io = B * H * nb * REC_BYTES
-    bytes_state = 2 * th * 32 * esz + state_io          # K, V read; block states out
-    bytes_read = 2 * th * 32 * esz + state_io           # Q read, O written; block prefixes in
-    bytes_step = 4 * th * 32 * esz + 2 * state_io
+    state_io = B * H * nb * rec_bytes(d)
+    bytes_state = 2 * th * d * esz + state_io           # K, V read; block states out
+    bytes_read = 2 * th * d * esz + state_io            # Q read, O written; block prefixes in
+    bytes_step = 4 * th * d * esz + 2 * state_io
     kernels = {
         "k_block_state": {"ms": k_state, "alg_bytes": bytes_state,
                           "gbs": bytes_state / (k_state * 1e6)},
@@ -246,7 +250,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if dt == torch.bfloat16 else "f32",
         "data": "synthetic",
-        "config": {"workload": cfg["name"], "B": B, "N": N, "H": H, "head_dim": 32,
+        "config": {"workload": cfg["name"], "B": B, "N": N, "H": H, "head_dim": d,
                    "frames": cfg["frames"], "tokens_per_frame": tpf, "block_frames": bf,
                    "grid": list(cfg["grid"]), "rope_split": list(cfg["rope"]["split"]),
                    "rope_base": cfg["rope"]["base"], "eps": 1e-8},
@@ -294,7 +298,8 @@ def bench_streaming(lavr, torch, dev, reps):
             times.append((time.perf_counter() - t0) / nblk)
     per_call = float(np.median(times))
     th = cfg["B"] * L * cfg["H"]
-    call_bytes = 4 * th * 32 * 2 + 2 * cfg["B"] * cfg["H"] * REC_BYTES
+    d = cfg["head_dim"]
+    call_bytes = 4 * th * d * 2 + 2 * cfg["B"] * cfg["H"] * rec_bytes(d)
     return {"workload": cfg["name"], "calls": nblk, "ms_per_block": per_call * 1e3,
             "tokens_heads_per_s": th / per_call, "hbm_gbs": call_bytes / (per_call * 1e9),
             "reps": reps}

@@ -96,7 +96,7 @@ int make_plan(Plan* p, int B, int H, int head_dim, int frames, int tpf, int bloc
       first_block_frames < 0)
     return LA_ERR_INVALID_ARG;
   if (first_block_frames == 0) first_block_frames = block_frames;
-  if (head_dim != lavr::kHeadDim) return LA_ERR_UNSUPPORTED;
+  if (!lavr::head_dim_built(head_dim)) return LA_ERR_UNSUPPORTED;
   if (B > 65535 || H > 65535 || (long long)B * H > (1LL << 24)) return LA_ERR_UNSUPPORTED;
   const long long N = (long long)frames * tpf;
   if (N > kMaxTokens || N * tpf >= kTwo42) return LA_ERR_UNSUPPORTED;
@@ -108,6 +108,8 @@ int make_plan(Plan* p, int B, int H, int head_dim, int frames, int tpf, int bloc
   std::memset(p, 0, sizeof(*p));
   p->B = B;
   p->H = H;
+  p->D = head_dim;
+  p->rec = lavr::rec_floats(head_dim);
   p->N = (int)N;
   p->tpf = tpf;
   p->gw_div = gw_div;
@@ -115,7 +117,7 @@ int make_plan(Plan* p, int B, int H, int head_dim, int frames, int tpf, int bloc
   p->L0 = (int)((long long)(first_block_frames < frames ? first_block_frames : frames) * tpf);
   p->nb = N <= p->L0 ? 1 : 1 + (int)cdiv(N - p->L0, p->L);
   const int Lmax = p->L0 > p->L ? p->L0 : p->L;   // chunks and tiles are planned for the longest block
-  p->hg = (H + lavr::kHeadsPerGroup - 1) / lavr::kHeadsPerGroup;
+  p->hg = head_dim == 32 ? (H + 1) / 2 : H;
   p->t0 = t0;
   p->mag_tpf = (uint64_t)(kTwo42 / tpf) + 1;
   p->mag_gw = (uint64_t)(kTwo42 / gw_div) + 1;
@@ -137,11 +139,11 @@ int make_plan(Plan* p, int B, int H, int head_dim, int frames, int tpf, int bloc
     p->rope.gh = rope->grid_h;
     p->rope.gw = rope->grid_w;
   }
-  const int tiles = (in_dt == LA_BF16 ? 3 : 2) * kStep * 2 * lavr::kHeadDim * esize(in_dt);
+  const int tiles = (in_dt == LA_BF16 ? 3 : 2) * kStep * 64 * esize(in_dt);   // 64 channels per row
   p->lds_state = tiles + (int)(tab_pairs(rope, tpf, p->Tc) * 8);
   p->lds_read = (int)(tab_pairs(rope, tpf, p->Tr) * 8);
 
-  const size_t rec = (size_t)lavr::kRec * sizeof(float);
+  const size_t rec = (size_t)p->rec * sizeof(float);
   const size_t part = (size_t)B * H * p->nb * p->cpb * rec;
   const size_t prefix = (size_t)B * H * p->nb * rec;
   p->ws_part = 0;
@@ -160,7 +162,7 @@ int check_tensors(const void* q, const void* k, const void* v, void* out, la_dty
   if (!q || !k || !v || !out) return LA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
     return LA_ERR_INVALID_ARG;
-  const size_t elems = (size_t)p.B * p.N * p.H * lavr::kHeadDim;
+  const size_t elems = (size_t)p.B * p.N * p.H * p.D;
   const size_t nin = elems * esize(in_dt), nout = elems * esize(out_dt);
   if (overlaps(out, nout, q, nin) || overlaps(out, nout, k, nin) || overlaps(out, nout, v, nin))
     return LA_ERR_INVALID_ARG;
@@ -183,7 +185,7 @@ int rope_table_build(la_rope* out, float* table_dev, size_t bytes, int head_dim,
                      int d_w, int max_frames, int grid_h, int grid_w, double base, void* stream) {
   if (!out || !table_dev || !aligned(table_dev, 16)) return LA_ERR_INVALID_ARG;
   if (head_dim < 1) return LA_ERR_INVALID_ARG;
-  if (head_dim != lavr::kHeadDim) return LA_ERR_UNSUPPORTED;
+  if (!lavr::head_dim_built(head_dim)) return LA_ERR_UNSUPPORTED;
   if (d_t + d_h + d_w != head_dim) return LA_ERR_INVALID_ARG;
   const size_t need = rope_table_bytes(d_t, d_h, d_w, max_frames, grid_h, grid_w);
   if (need == 0 || bytes < need) return LA_ERR_INVALID_ARG;
@@ -252,7 +254,7 @@ int la_state_init(la_state* st, float* S_dev, float* z_dev, int B, int H, int he
                   void* stream) {
   if (!st || !S_dev || !z_dev || !aligned(S_dev, 16) || !aligned(z_dev, 16)) return LA_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || head_dim < 1) return LA_ERR_INVALID_ARG;
-  if (head_dim != lavr::kHeadDim) return LA_ERR_UNSUPPORTED;
+  if (!lavr::head_dim_built(head_dim)) return LA_ERR_UNSUPPORTED;
   if (B > 65535 || H > 65535 || (long long)B * H > (1LL << 24)) return LA_ERR_UNSUPPORTED;
   const size_t nS = (size_t)B * H * head_dim * head_dim, nz = (size_t)B * H * head_dim;
   if (overlaps(S_dev, nS * 4, z_dev, nz * 4)) return LA_ERR_INVALID_ARG;

@@ -7,9 +7,11 @@
 
 namespace lavr {
 
-constexpr int kHeadDim = 32;                       // the only head dim built
-constexpr int kRec = kHeadDim * kHeadDim + kHeadDim;  // floats of one (S, z) record
-constexpr int kHeadsPerGroup = 2;                  // heads handled by one workgroup
+// Head dims built: 32 (two heads per workgroup) and 64 (one head per
+// workgroup).  Either way a workgroup owns 64 channels = 128 bytes of bf16 of
+// every token row.
+constexpr bool head_dim_built(int d) { return d == 32 || d == 64; }
+constexpr int rec_floats(int d) { return d * d + d; }   // floats of one (S, z) record
 
 // Rotary table as the kernels see it.
 struct RopeDev {
@@ -22,13 +24,15 @@ struct RopeDev {
 // Everything a launch needs; filled by the host planner.
 struct Plan {
   int B, H;
+  int D;                // head dim (32 or 64)
+  int rec;              // floats of one (S, z) record: D * D + D
   int N;                // tokens per sequence in this call
   int tpf;              // tokens per frame
   int gw_div;           // divisor for row/col (grid_w, or 1 without spatial sections)
   int L;                // tokens per block (after the first)
   int L0;               // tokens of the first block
   int nb;               // blocks in this call
-  int hg;               // head groups = ceil(H / 2)
+  int hg;               // workgroup head groups: ceil(H / 2) at D = 32, H at D = 64
   int cpb, Tc;          // block-state chunks per block, tokens per chunk
   int rpb, Tr;          // readout tiles per block, tokens per tile
   long long t0;         // frame offset of token 0 (frames already streamed)

@@ -39,8 +39,7 @@
 namespace lavr {
 namespace {
 
-constexpr int D = kHeadDim;
-constexpr int REC = kRec;
+constexpr int D = 32;                // channels of one lane chunk's half (a head at head dim 32)
 constexpr int NT = 256;              // threads of the state and readout workgroups
 constexpr int STEP = 64;             // tokens per step of the state kernel
 constexpr int TCOLS = 2 * D;         // an LDS tile row holds two heads
@@ -86,6 +85,7 @@ struct PrefixArgs {
   float* S_save;
   float* z_save;
   int H, nb, cpb;
+  int hd, rec;               // head dim, floats per record (hd * hd + hd)
 };
 
 struct ReadArgs {
@@ -335,26 +335,32 @@ struct TabStage {
 
 // --------------------------------------------------------- k_block_state
 //
-// Grid: x = chunk * hg + head group, y = batch.  256 threads.  Each 64-token
-// step: thread t loads channels 8(t&3) .. +7 of token (t>>2) for both heads of
-// K and V, applies ReLU, adds to its key sums, rotates (one table fetch for
-// both heads), and writes V and R phi(K) into LDS tiles [token][2 heads x 32].
-// Loads run two steps ahead of the tiles.  Then wave w takes head (w & 1) and
-// tokens 32*(w >> 1) .. +31 of the step and feeds MFMA: A[e][n] = V[n][e],
-// B[n][f] = R phi(K)[n][f], so C = S (32 x 32).  A lane supplies one channel
-// over 8 tokens, read across LDS rows; odd groups of 8 rows store the two
-// heads swapped, so the two half-waves read disjoint LDS banks.  Tokens past
-// the chunk read as zeros (buffer range check) and add nothing.
+// Grid: x = chunk * hg + head group, y = batch.  256 threads.  A workgroup owns
+// 64 channels (128 bytes of bf16) of every token row: two heads at head dim 32,
+// one head at 64, whose two 32-channel halves take the place of the two heads
+// in the loads and tiles.  Each 64-token step: thread t loads channels
+// 8(t&3) .. +7 of each 32-channel half of token (t>>2) of K and V, applies
+// ReLU, adds to its key sums, rotates, and writes V and R phi(K) into LDS tiles
+// [token][64].  Loads run two steps ahead of the tiles.  MFMA with
+// A[e][n] = V[n][e], B[n][f] = R phi(K)[n][f], C = S: at head dim 32, wave w
+// takes head (w & 1) and tokens 32*(w >> 1) .. +31 of the step (two waves per
+// head, added at the end); at 64, wave w takes the quadrant (e half w >> 1,
+// f half w & 1) of S over all 64 tokens.  A lane supplies one channel over 8
+// tokens, read across LDS rows; odd groups of 8 rows store the two halves
+// swapped, so the two half-waves read disjoint LDS banks.  Tokens past the
+// chunk read as zeros (buffer range check) and add nothing.
 
-template <typename TIn, bool P2>
-__global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? (P2 ? 4 : 3) : 2) void k_block_state(StateArgs a) {
+template <typename TIn, bool P2, int DH>
+__global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? ((P2 && DH == 32) ? 4 : 3) : 2) void k_block_state(StateArgs a) {
   constexpr bool BF = sizeof(TIn) == 2;
+  constexpr bool W64 = DH == 64;
+  constexpr int RECN = DH * DH + DH;
   constexpr int ES = (int)sizeof(TIn);
   constexpr int NTILE = BF ? 3 : 2;      // V, R phi(K) (hi, lo for bf16)
   constexpr int TILE_ELEMS = STEP * TCOLS;
   constexpr int TILE_BYTES = NTILE * TILE_ELEMS * ES;
   constexpr int W16 = 16 / ES;           // elements per 16 bytes
-  constexpr int PF = (BF && P2) ? LAVR_STATE_PF : 2;   // steps of loads in flight
+  constexpr int PF = (BF && P2 && !W64) ? LAVR_STATE_PF : 2;   // steps of loads in flight
 
   extern __shared__ __align__(16) unsigned char smem[];
   TIn* tV = reinterpret_cast<TIn*>(smem);
@@ -371,18 +377,18 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? (P2 ? 4 : 3) : 2) void k_blo
   const int blk1 = min(blk0 + (j == 0 ? a.L0 : a.L), a.N);
   const int c0 = min(blk0 + c * a.Tc, blk1);
   const int c1 = min(c0 + a.Tc, blk1);
-  const int h0 = g * kHeadsPerGroup;
+  const int h0 = W64 ? g : 2 * g;        // first head of the group
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int lrow = t >> 2, lc = t & 3;   // loader: token row of the step, channel chunk
-  const int nh = min(kHeadsPerGroup, a.H - h0);
+  const int nh = W64 ? 2 : min(2, a.H - h0);   // 32-channel halves that hold data
   const bool rope_on = a.rope.table != nullptr;
 
   // K and V of this chunk: rows c0 .. c1-1 of batch b.
-  const int RB = a.H * D * ES;
+  const int RB = a.H * DH * ES;
   const size_t base = ((size_t)b * a.N + c0) * RB;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const char*>(a.k) + base, (uint32_t)(c1 - c0) * RB);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const char*>(a.v) + base, (uint32_t)(c1 - c0) * RB);
-  int voff = lrow * RB + (h0 * D + 8 * lc) * ES;
+  int voff = lrow * RB + (g * 64 + 8 * lc) * ES;
 
   struct Buf { Raw8<TIn> k[2], v[2]; };
   auto load_step = [&](Buf& bf) {
@@ -409,10 +415,11 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? (P2 ? 4 : 3) : 2) void k_blo
   if constexpr (PF > 2) load_step(b2);
 
   ts.commit(tab);
-  RopeLane<P2> rl;
+  RopeLane<P2> rl, rl1;                  // rl1: the second half at head dim 64
   TokPos tp;
   if (rope_on) {
     rl.init(a.rope, win, lc);
+    if constexpr (W64) rl1.init(a.rope, win, lc + 4);
     tp.init(c0 + lrow, a.pos);
   }
   __syncthreads();
@@ -424,11 +431,15 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? (P2 ? 4 : 3) : 2) void k_blo
     for (int i = 0; i < 8; ++i) zacc[h][i] = 0.f;
   f32x16 acc = {};
   const int hh = w & 1, th = w >> 1, cl = lane & 31, q = lane >> 5;
+  const int ha = W64 ? (w >> 1) : hh;    // half of the channels feeding A (V, rows e of S)
+  const int hb = W64 ? (w & 1) : hh;     // half of the channels feeding B (R phi(K), columns f)
+  const int rbase = W64 ? 0 : th * 32;   // first token row of the wave's share of a step
 
   auto run_step = [&](const Buf& bf) {
-    float2 cs[4];
+    float2 cs[4], cs1[4];
     if (rope_on) {
       rl.fetch(tab, tp, win, cs);
+      if constexpr (W64) rl1.fetch(tab, tp, win, cs1);
       tp.advance(a.pos);
     }
 #pragma unroll
@@ -437,7 +448,7 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? (P2 ? 4 : 3) : 2) void k_blo
       relu_widen(bf.k[h], x);
 #pragma unroll
       for (int i = 0; i < 8; ++i) zacc[h][i] += x[i];
-      if (rope_on) rotate8(x, cs);
+      if (rope_on) rotate8(x, (W64 && h == 1) ? cs1 : cs);
       const int col = (h * D + 8 * lc) ^ (((lrow >> 3) & 1) << 5);
       TIn* dv = tV + lrow * TCOLS + col;
 #pragma unroll
@@ -459,19 +470,21 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? (P2 ? 4 : 3) : 2) void k_blo
     if constexpr (BF) {
       // ds_read_b64_tr_b16: in each 16-lane group, lane 4r+s reads channels
       // c0+4s .. +3 of token row r, and the hardware hands lane i channel c0+i
-      // of the 4 rows.  Group G = lane >> 4 takes channels 16(G&1) .. +15 of its
-      // head and tokens 8(G>>1) .. +7 of the 16-token MFMA step (two reads of 4
+      // of the 4 rows.  Group G = lane >> 4 takes channels 16(G&1) .. +15 of a
+      // half and tokens 8(G>>1) .. +7 of the 16-token MFMA step (two reads of 4
       // rows), which is the 32x32x16 operand layout: lane l holds channel l%32
       // over tokens 8(l/32) .. +7.
       const int G = lane >> 4, jr = (lane >> 2) & 3, js = lane & 3;
-      const int colb = ((hh * D) ^ ((G >> 1) << 5)) + 16 * (G & 1) + 4 * js;
+      const int sw = (G >> 1) << 5;
+      const int colA = ((ha * D) ^ sw) + 16 * (G & 1) + 4 * js;
+      const int colB = ((hb * D) ^ sw) + 16 * (G & 1) + 4 * js;
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const int row0 = th * 32 + m * 16 + 8 * (G >> 1) + jr;
-        const int e0 = row0 * TCOLS + colb, e1 = e0 + 4 * TCOLS;
-        const u32x4 av = tr_pair(tV, e0, e1);
-        const u32x4 bh = tr_pair(tK, e0, e1);
-        const u32x4 bl = tr_pair(tKl, e0, e1);
+      for (int m = 0; m < (W64 ? 4 : 2); ++m) {
+        const int row0 = rbase + m * 16 + 8 * (G >> 1) + jr;
+        const int eA = row0 * TCOLS + colA, eB = row0 * TCOLS + colB;
+        const u32x4 av = tr_pair(tV, eA, eA + 4 * TCOLS);
+        const u32x4 bh = tr_pair(tK, eB, eB + 4 * TCOLS);
+        const u32x4 bl = tr_pair(tKl, eB, eB + 4 * TCOLS);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(bh), acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(bl), acc, 0, 0, 0);
       }
@@ -479,10 +492,12 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? (P2 ? 4 : 3) : 2) void k_blo
       const float* Vf = reinterpret_cast<const float*>(tV);
       const float* Kf = reinterpret_cast<const float*>(tK);
 #pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        const int row = th * 32 + 2 * s + q;
-        const int i0 = row * TCOLS + ((hh * D + cl) ^ (((row >> 3) & 1) << 5));
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Vf[i0], Kf[i0], acc, 0, 0, 0);
+      for (int s = 0; s < (W64 ? 32 : 16); ++s) {
+        const int row = rbase + 2 * s + q;
+        const int swr = ((row >> 3) & 1) << 5;
+        const int iA = row * TCOLS + ((ha * D + cl) ^ swr);
+        const int iB = row * TCOLS + ((hb * D + cl) ^ swr);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Vf[iA], Kf[iB], acc, 0, 0, 0);
       }
     }
   };
@@ -501,12 +516,12 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? (P2 ? 4 : 3) : 2) void k_blo
     if constexpr (PF > 2) one_step(b2);
   }
 
-  // Combine the two waves of each head through LDS.  Key sums: first across
-  // the 16 lanes of a wave that hold the same channel chunk (cross-lane adds),
-  // then across the four waves through LDS.
+  // Head dim 32: combine the two waves of each head through LDS.  Key sums:
+  // first across the 16 lanes of a wave that hold the same channel chunk
+  // (cross-lane adds), then across the four waves through LDS.
   float* red = reinterpret_cast<float*>(smem);   // [2 waves][16][64]
   float* zred = red + 2 * 16 * 64;               // [4 waves][4 chunks][16]
-  if (w >= 2) {
+  if (!W64 && w >= 2) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) red[((w - 2) * 16 + v) * 64 + lane] = acc[v];
   }
@@ -519,9 +534,17 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? (P2 ? 4 : 3) : 2) void k_blo
     }
   __syncthreads();
 
+  // Records: S (DH x DH, row e, column f) then z (DH).
   const int nchunk = a.nb * a.cpb;
-  if (w < 2 && w < nh) {
-    float* dst = a.part + ((size_t)(b * a.H + h0 + w) * nchunk + ci) * REC;
+  if constexpr (W64) {
+    float* dst = a.part + ((size_t)(b * a.H + h0) * nchunk + ci) * RECN;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int e = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      dst[(ha * D + e) * DH + hb * D + (lane & 31)] = acc[v];
+    }
+  } else if (w < 2 && w < nh) {
+    float* dst = a.part + ((size_t)(b * a.H + h0 + w) * nchunk + ci) * RECN;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int e = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
@@ -534,7 +557,9 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? (P2 ? 4 : 3) : 2) void k_blo
     float s = 0.f;
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) s += zred[(ww * 4 + lc2) * 16 + hd * 8 + el];
-    a.part[((size_t)(b * a.H + h0 + hd) * nchunk + ci) * REC + D * D + ch] = s;
+    const size_t zi = W64 ? ((size_t)(b * a.H + h0) * nchunk + ci) * RECN + DH * DH + hd * D + ch
+                          : ((size_t)(b * a.H + h0 + hd) * nchunk + ci) * RECN + D * D + ch;
+    a.part[zi] = s;
   }
 }
 
@@ -556,6 +581,7 @@ __global__ __launch_bounds__(PFX_NT) void k_prefix(PrefixArgs a) {
   __shared__ float bs[PFX_RUN][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int el = blockIdx.x * 64 + lane;
+  const int REC = a.rec;
   const bool ok = el < REC;
   const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
   // (lanes past the record read its last element and discard it)
@@ -563,7 +589,7 @@ __global__ __launch_bounds__(PFX_NT) void k_prefix(PrefixArgs a) {
   float* o = a.prefix + bh * a.nb * REC + el;
   float acc = 0.f;
   if (w == 0 && ok && a.S_init != nullptr)
-    acc = el < D * D ? a.S_init[bh * D * D + el] : a.z_init[bh * D + el - D * D];
+    acc = el < a.hd * a.hd ? a.S_init[bh * a.hd * a.hd + el] : a.z_init[bh * a.hd + el - a.hd * a.hd];
   constexpr int BATCH = 8;
   for (int r0 = 0; r0 < a.nb; r0 += PFX_RUN) {
     const int nr = min(PFX_RUN, a.nb - r0);
@@ -605,26 +631,33 @@ __global__ __launch_bounds__(PFX_NT) void k_prefix(PrefixArgs a) {
     __syncthreads();
   }
   if (w == 0 && ok && a.S_save != nullptr) {
-    if (el < D * D) a.S_save[bh * D * D + el] = acc;
-    else a.z_save[bh * D + el - D * D] = acc;
+    if (el < a.hd * a.hd) a.S_save[bh * a.hd * a.hd + el] = acc;
+    else a.z_save[bh * a.hd + el - a.hd * a.hd] = acc;
   }
 }
 
 // ------------------------------------------------------------- k_readout
 //
-// Grid: x = tile * hg + head group, y = batch.  256 threads; wave w takes the
-// tile's 16-token groups w, w+4, ... for both heads of the group, with loads
-// two groups ahead.  MFMA 16x16x32: A = Sbar rows (e) x channels (f), B =
-// channels (f) x tokens: lane l holds channels 8(l>>4) .. +7 of token (l & 15),
-// one 16-byte load of bf16 q.  The output lane holds channels 4(l>>4) .. +3 of
-// each 16-row half for token (l & 15), so the normaliser of that token, summed
-// over the four lanes that share it, is already in place.  Tokens past the
-// tile read as zeros and their stores are dropped by the buffer range check.
+// Grid: x = tile * hg + head group, y = batch.  256 threads; a workgroup owns
+// 64 channels of every token row (two heads at head dim 32, one at 64, as in
+// the block-state kernel).  Wave w takes the tile's 16-token groups w, w+4, ...
+// with loads two groups ahead.  MFMA 16x16x32: A = Sbar rows (e) x 32 channels
+// (f), B = 32 channels (f) x tokens: lane l holds channels 8(l>>4) .. +7 of
+// each 32-channel half of token (l & 15), one 16-byte load of bf16 q per half.
+// At head dim 32 each half is a head; at 64 every 16-row tile of the output
+// sums the products of both halves.  The output lane holds channels
+// 4(l>>4) .. +3 of each 16-row tile for token (l & 15), so the normaliser of
+// that token, summed over the four lanes that share it, is already in place.
+// Tokens past the tile read as zeros and their stores are dropped by the
+// buffer range check.
 
-template <typename TIn, typename TOut, bool P2>
+template <typename TIn, typename TOut, bool P2, int DH>
 __global__ __launch_bounds__(NT) void k_readout(ReadArgs a) {
   constexpr bool BF = sizeof(TIn) == 2;
+  constexpr bool W64 = DH == 64;
+  constexpr int RECN = DH * DH + DH;
   constexpr int ES = (int)sizeof(TIn), EO = (int)sizeof(TOut);
+  constexpr int NA = W64 ? 8 : 4;        // Sbar tiles of 16 rows x 32 channels a lane holds
   extern __shared__ __align__(16) unsigned char smem[];
   float2* tab = reinterpret_cast<float2*>(smem);
 
@@ -642,22 +675,22 @@ __global__ __launch_bounds__(NT) void k_readout(ReadArgs a) {
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int tl = lane & 15, ch = lane >> 4;
-  const int h0 = g * kHeadsPerGroup;
-  const int nh = min(kHeadsPerGroup, a.H - h0);
+  const int h0 = W64 ? g : 2 * g;        // first head of the group
+  const int nh = W64 ? 2 : min(2, a.H - h0);   // 32-channel halves that hold data
   const int ngroups = (t1 - t0 + 15) >> 4;
 
-  const int RB = a.H * D * ES, RO = a.H * D * EO;
+  const int RB = a.H * DH * ES, RO = a.H * DH * EO;
   const __amdgpu_buffer_rsrc_t rq =
       make_rsrc(static_cast<const char*>(a.q) + ((size_t)b * a.N + t0) * RB, (uint32_t)(t1 - t0) * RB);
   const __amdgpu_buffer_rsrc_t ro =
       make_rsrc(static_cast<char*>(a.out) + ((size_t)b * a.N + t0) * RO, (uint32_t)(t1 - t0) * RO);
-  int qoff = (w * 16 + tl) * RB + (h0 * D + 8 * ch) * ES;
-  int ooff = (w * 16) * RO + h0 * D * EO;
-  // Output offsets of this lane.  fp32: channels 4ch..+3 of each 16-channel half
-  // of token tl.  bf16 (after the exchange in run_group): a 16-byte piece of
-  // channels co..co+7; with two heads, tokens tl & 7 (first store) and 8 + (tl & 7)
-  // (second store) of head tl >> 3, so each store instruction writes whole
-  // 128-byte lines (8 tokens x both heads of the group).
+  int qoff = (w * 16 + tl) * RB + (g * 64 + 8 * ch) * ES;
+  int ooff = (w * 16) * RO + g * 64 * EO;
+  // Output offsets of this lane.  fp32: channels 4ch..+3 of each 16-channel
+  // tile of token tl.  bf16 (after the exchange in run_group): a 16-byte piece
+  // of channels co..co+7; with both halves present, tokens tl & 7 (first store)
+  // and 8 + (tl & 7) (second store) of half tl >> 3, so each store instruction
+  // writes whole 128-byte lines (8 tokens x the group's 64 channels).
   const int co = 4 * ch + ((ch & 1) ? 12 : 0);
   const int o_one = tl * RO + (EO == 2 ? co : 4 * ch) * EO;
   const int o_pair = (tl & 7) * RO + ((tl >> 3) * D + co) * EO;
@@ -665,39 +698,52 @@ __global__ __launch_bounds__(NT) void k_readout(ReadArgs a) {
   // Prologue order: rotary window, then the prefix state, then the first Q
   // loads, so that no wait before the loop drains the Q prefetch.
   const TabWindow win = stage_table(tab, a.rope, a.pos.t0, t0, t1, a.pos.mag_tpf);
-  RopeLane<P2> rl;
+  RopeLane<P2> rl, rl1;                  // rl1: the second half at head dim 64
   TokPos tp;
   if (rope_on) {
     rl.init(a.rope, win, ch);
+    if constexpr (W64) rl1.init(a.rope, win, ch + 4);
     tp.init(t0 + w * 16 + tl, a.pos);
   }
 
-  // Per head: key-sum slice and Sbar operands (row e = 16 half + tl, channels 8ch .. +7).
+  // Key-sum slices zb[h] (channels 32h + 8ch .. +7 of the half's z) and Sbar
+  // tiles.  Head dim 32: tile 2h + hf = rows 16hf + tl, channels 8ch .. +7 of
+  // head h.  Head dim 64: tile 2et + kt = rows 16et + tl, channels 32kt + 8ch .. +7.
   float zb[2][8];
-  u32x4 Ah[2][2], Al[2][2];
-  float As[2][2][8];
+  u32x4 Ah[NA], Al[NA];
+  float As[NA][8];
+  auto take_tile = [&](int i, const float* srow) {
+    const f32x4 s0 = *reinterpret_cast<const f32x4*>(srow);
+    const f32x4 s1 = *reinterpret_cast<const f32x4*>(srow + 4);
+    float sv[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) { sv[k] = s0[k]; sv[4 + k] = s1[k]; }
+    if constexpr (BF) {
+      split8(sv, Ah[i], Al[i]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) As[i][k] = sv[k];
+    }
+  };
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int hd = min(h, nh - 1);
-    const float* pre = a.prefix + ((size_t)(b * a.H + h0 + hd) * a.nb + j) * REC;
-    const f32x4 z0 = *reinterpret_cast<const f32x4*>(pre + D * D + 8 * ch);
-    const f32x4 z1 = *reinterpret_cast<const f32x4*>(pre + D * D + 8 * ch + 4);
+    const int hd = W64 ? 0 : min(h, nh - 1);
+    const float* pre = a.prefix + ((size_t)(b * a.H + h0 + hd) * a.nb + j) * RECN;
+    const float* zp = pre + DH * DH + (W64 ? h * D : 0) + 8 * ch;
+    const f32x4 z0 = *reinterpret_cast<const f32x4*>(zp);
+    const f32x4 z1 = *reinterpret_cast<const f32x4*>(zp + 4);
 #pragma unroll
     for (int i = 0; i < 4; ++i) { zb[h][i] = z0[i]; zb[h][4 + i] = z1[i]; }
+    if constexpr (W64) {
+      // this h: output rows 32h .. 32h+31 = tiles et = 2h, 2h+1
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const float* srow = pre + (16 * hf + tl) * D + 8 * ch;
-      const f32x4 s0 = *reinterpret_cast<const f32x4*>(srow);
-      const f32x4 s1 = *reinterpret_cast<const f32x4*>(srow + 4);
-      float sv[8];
+      for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { sv[i] = s0[i]; sv[4 + i] = s1[i]; }
-      if constexpr (BF) {
-        split8(sv, Ah[h][hf], Al[h][hf]);
-      } else {
+        for (int kt = 0; kt < 2; ++kt)
+          take_tile((2 * h + hf) * 2 + kt, pre + (16 * (2 * h + hf) + tl) * DH + kt * D + 8 * ch);
+    } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) As[h][hf][i] = sv[i];
-      }
+      for (int hf = 0; hf < 2; ++hf) take_tile(2 * h + hf, pre + (16 * hf + tl) * D + 8 * ch);
     }
   }
 
@@ -711,6 +757,7 @@ __global__ __launch_bounds__(NT) void k_readout(ReadArgs a) {
   // load is issued, also past the tile (those read zeros and touch no memory),
   // so the number of loads in flight is fixed.
   constexpr int RPF = BF ? LAVR_READ_PF : 2;
+  static_assert(RPF == 2 || RPF == 3, "readout prefetch depth: two or three buffers");
   Buf b0, b1, b2;
   load_group(b0);
   load_group(b1);
@@ -718,71 +765,123 @@ __global__ __launch_bounds__(NT) void k_readout(ReadArgs a) {
 
   __syncthreads();
 
+  // Output of one 32-channel half h (o: its two 16-row tiles) scaled by inv:
+  // bf16 pieces go to pk[h] for the paired store, fp32 is stored at once.
+  auto emit = [&](int h, const f32x4* o, float inv, u32x4* pk) {
+    if constexpr (EO == 2) {
+      // Lane row ch holds channels 4ch..4ch+3 of each 16-channel tile.  One
+      // permlane16 swap per dword trades the tiles between rows ch and ch^1,
+      // so an even row ends up with channels 4ch..4ch+7 and an odd row with
+      // 12+4ch..19+4ch: one 16-byte store per lane.
+      const uint32_t p00 = pack_bf16(o[0][0] * inv, o[0][1] * inv);
+      const uint32_t p01 = pack_bf16(o[0][2] * inv, o[0][3] * inv);
+      const uint32_t p10 = pack_bf16(o[1][0] * inv, o[1][1] * inv);
+      const uint32_t p11 = pack_bf16(o[1][2] * inv, o[1][3] * inv);
+      const auto s0 = __builtin_amdgcn_permlane16_swap(p00, p10, false, false);
+      const auto s1 = __builtin_amdgcn_permlane16_swap(p01, p11, false, false);
+      pk[h] = u32x4{s0[0], s1[0], s0[1], s1[1]};
+    } else {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const f32x4 ov = o[hf] * inv;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ov), ro,
+                                               ooff + o_one + (h * D + 16 * hf) * EO, 0, 0);
+      }
+    }
+  };
+
   auto run_group = [&](const Buf& bf) {
-    float2 cs[4];
+    float2 cs[4], cs1[4];
     if (rope_on) {
       rl.fetch(tab, tp, win, cs);
+      if constexpr (W64) rl1.fetch(tab, tp, win, cs1);
       tp.advance(a.pos);
     }
     u32x4 pk[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if (h >= nh) break;
-      float x[8];
-      relu_widen(bf.x[h], x);
+    if constexpr (W64) {
+      // one head: den over both halves, every output tile from both halves
       float den = 0.f;
+      u32x4 bh[2], bl[2];
+      float xs[2][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) den += zb[h][i] * x[i];
-      if (rope_on) rotate8(x, cs);
-      f32x4 o[2];
-      if constexpr (BF) {
-        u32x4 bh, bl;
-        split8(x, bh, bl);
+      for (int h = 0; h < 2; ++h) {
+        float x[8];
+        relu_widen(bf.x[h], x);
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          f32x4 cc = {0.f, 0.f, 0.f, 0.f};
-          cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Ah[h][hf]), as_bf16x8(bh), cc, 0, 0, 0);
-          cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Ah[h][hf]), as_bf16x8(bl), cc, 0, 0, 0);
-          cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Al[h][hf]), as_bf16x8(bh), cc, 0, 0, 0);
-          o[hf] = cc;
-        }
-      } else {
+        for (int i = 0; i < 8; ++i) den += zb[h][i] * x[i];
+        if (rope_on) rotate8(x, h ? cs1 : cs);
+        if constexpr (BF) {
+          split8(x, bh[h], bl[h]);
+        } else {
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          f32x4 cc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < 8; ++s) cc = __builtin_amdgcn_mfma_f32_16x16x4f32(As[h][hf][s], x[s], cc, 0, 0, 0);
-          o[hf] = cc;
+          for (int i = 0; i < 8; ++i) xs[h][i] = x[i];
         }
       }
       den = sum4_lanes(den);
       const float inv = __builtin_amdgcn_rcpf(den + a.eps);
-      if constexpr (EO == 2) {
-        // Lane row ch holds channels 4ch..4ch+3 of each 16-channel half.  One
-        // permlane16 swap per dword trades the halves between rows ch and ch^1,
-        // so an even row ends up with channels 4ch..4ch+7 and an odd row with
-        // 12+4ch..19+4ch: one 16-byte store per lane.
-        const uint32_t p00 = pack_bf16(o[0][0] * inv, o[0][1] * inv);
-        const uint32_t p01 = pack_bf16(o[0][2] * inv, o[0][3] * inv);
-        const uint32_t p10 = pack_bf16(o[1][0] * inv, o[1][1] * inv);
-        const uint32_t p11 = pack_bf16(o[1][2] * inv, o[1][3] * inv);
-        const auto s0 = __builtin_amdgcn_permlane16_swap(p00, p10, false, false);
-        const auto s1 = __builtin_amdgcn_permlane16_swap(p01, p11, false, false);
-        pk[h] = u32x4{s0[0], s1[0], s0[1], s1[1]};
-      } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        f32x4 o[2];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          const f32x4 ov = o[hf] * inv;
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ov), ro,
-                                                 ooff + o_one + (h * D + 16 * hf) * EO, 0, 0);
+          const int et = 2 * h + hf;
+          f32x4 cc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            if constexpr (BF) {
+              cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Ah[et * 2 + kt]), as_bf16x8(bh[kt]), cc, 0, 0, 0);
+              cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Ah[et * 2 + kt]), as_bf16x8(bl[kt]), cc, 0, 0, 0);
+              cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Al[et * 2 + kt]), as_bf16x8(bh[kt]), cc, 0, 0, 0);
+            } else {
+#pragma unroll
+              for (int s = 0; s < 8; ++s)
+                cc = __builtin_amdgcn_mfma_f32_16x16x4f32(As[et * 2 + kt][s], xs[kt][s], cc, 0, 0, 0);
+            }
+          }
+          o[hf] = cc;
         }
+        emit(h, o, inv, pk);
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (h >= nh) break;
+        float x[8];
+        relu_widen(bf.x[h], x);
+        float den = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) den += zb[h][i] * x[i];
+        if (rope_on) rotate8(x, cs);
+        f32x4 o[2];
+        if constexpr (BF) {
+          u32x4 bh, bl;
+          split8(x, bh, bl);
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            f32x4 cc = {0.f, 0.f, 0.f, 0.f};
+            cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Ah[2 * h + hf]), as_bf16x8(bh), cc, 0, 0, 0);
+            cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Ah[2 * h + hf]), as_bf16x8(bl), cc, 0, 0, 0);
+            cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Al[2 * h + hf]), as_bf16x8(bh), cc, 0, 0, 0);
+            o[hf] = cc;
+          }
+        } else {
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            f32x4 cc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 8; ++s) cc = __builtin_amdgcn_mfma_f32_16x16x4f32(As[2 * h + hf][s], x[s], cc, 0, 0, 0);
+            o[hf] = cc;
+          }
+        }
+        den = sum4_lanes(den);
+        emit(h, o, __builtin_amdgcn_rcpf(den + a.eps), pk);
       }
     }
     if constexpr (EO == 2) {
       if (nh == 2) {
         // Lanes tl and tl ^ 8 (DPP row rotate by 8 inside each 16-lane row) trade
-        // one piece: the low lane keeps head 0 of tokens tl and tl + 8, the high
-        // lane head 1 of tokens tl - 8 and tl.
+        // one piece: the low lane keeps half 0 of tokens tl and tl + 8, the high
+        // lane half 1 of tokens tl - 8 and tl.
         const bool lo = tl < 8;
         uint32_t first[4], second[4];
 #pragma unroll
@@ -845,11 +944,29 @@ __global__ void k_fill_zero(float* p, size_t n) {
   if (i < n) p[i] = 0.f;
 }
 
-template <typename TIn, typename TOut>
+template <typename TIn, typename TOut, int DH>
 hipError_t launch_readout(const ReadArgs& ra, bool p2, dim3 grid, int lds, hipStream_t s) {
-  if (p2) hipLaunchKernelGGL((k_readout<TIn, TOut, true>), grid, dim3(NT), lds, s, ra);
-  else hipLaunchKernelGGL((k_readout<TIn, TOut, false>), grid, dim3(NT), lds, s, ra);
+  if (p2) hipLaunchKernelGGL((k_readout<TIn, TOut, true, DH>), grid, dim3(NT), lds, s, ra);
+  else hipLaunchKernelGGL((k_readout<TIn, TOut, false, DH>), grid, dim3(NT), lds, s, ra);
   return hipGetLastError();
+}
+
+template <int DH>
+hipError_t launch_state(const StateArgs& sa, bool in_bf16, bool p2, dim3 grid, int lds, hipStream_t s) {
+  if (in_bf16 && p2) hipLaunchKernelGGL((k_block_state<uint16_t, true, DH>), grid, dim3(NT), lds, s, sa);
+  else if (in_bf16) hipLaunchKernelGGL((k_block_state<uint16_t, false, DH>), grid, dim3(NT), lds, s, sa);
+  else if (p2) hipLaunchKernelGGL((k_block_state<float, true, DH>), grid, dim3(NT), lds, s, sa);
+  else hipLaunchKernelGGL((k_block_state<float, false, DH>), grid, dim3(NT), lds, s, sa);
+  return hipGetLastError();
+}
+
+template <int DH>
+hipError_t launch_readouts(const ReadArgs& ra, bool in_bf16, bool out_bf16, bool p2, dim3 grid, int lds,
+                           hipStream_t s) {
+  if (in_bf16 && out_bf16) return launch_readout<uint16_t, uint16_t, DH>(ra, p2, grid, lds, s);
+  if (in_bf16) return launch_readout<uint16_t, float, DH>(ra, p2, grid, lds, s);
+  if (out_bf16) return launch_readout<float, uint16_t, DH>(ra, p2, grid, lds, s);
+  return launch_readout<float, float, DH>(ra, p2, grid, lds, s);
 }
 
 PosArgs pos_args(const Plan& p) {
@@ -909,18 +1026,16 @@ int launch_forward(const Plan& p, const void* q, const void* k, const void* v, v
   sa.rope = p.rope;
   const dim3 gs((unsigned)(p.hg * p.nb * p.cpb), (unsigned)p.B);
   const bool p2 = ((p.rope.pt | p.rope.ph | p.rope.pw) & 1) == 0;
-  if (in_bf16 && p2) hipLaunchKernelGGL((k_block_state<uint16_t, true>), gs, dim3(NT), p.lds_state, s, sa);
-  else if (in_bf16) hipLaunchKernelGGL((k_block_state<uint16_t, false>), gs, dim3(NT), p.lds_state, s, sa);
-  else if (p2) hipLaunchKernelGGL((k_block_state<float, true>), gs, dim3(NT), p.lds_state, s, sa);
-  else hipLaunchKernelGGL((k_block_state<float, false>), gs, dim3(NT), p.lds_state, s, sa);
-  e = hipGetLastError();
+  e = p.D == 64 ? launch_state<64>(sa, in_bf16, p2, gs, p.lds_state, s)
+                : launch_state<32>(sa, in_bf16, p2, gs, p.lds_state, s);
   if (e == hipSuccess) e = mark(1);
   if (e != hipSuccess) return (int)e;
 
   PrefixArgs pa;
   pa.part = part; pa.prefix = prefix; pa.S_init = S_init; pa.z_init = z_init;
   pa.S_save = S_save; pa.z_save = z_save; pa.H = p.H; pa.nb = p.nb; pa.cpb = p.cpb;
-  const dim3 gp((REC + 63) / 64, (unsigned)p.H, (unsigned)p.B);
+  pa.hd = p.D; pa.rec = p.rec;
+  const dim3 gp((unsigned)((p.rec + 63) / 64), (unsigned)p.H, (unsigned)p.B);
   hipLaunchKernelGGL(k_prefix, gp, dim3(PFX_NT), 0, s, pa);
   e = hipGetLastError();
   if (e == hipSuccess) e = mark(2);
@@ -932,10 +1047,8 @@ int launch_forward(const Plan& p, const void* q, const void* k, const void* v, v
   ra.pos = pa_pos;
   ra.rope = p.rope;
   const dim3 gr((unsigned)(p.hg * p.nb * p.rpb), (unsigned)p.B);
-  if (in_bf16 && out_bf16) e = launch_readout<uint16_t, uint16_t>(ra, p2, gr, p.lds_read, s);
-  else if (in_bf16) e = launch_readout<uint16_t, float>(ra, p2, gr, p.lds_read, s);
-  else if (out_bf16) e = launch_readout<float, uint16_t>(ra, p2, gr, p.lds_read, s);
-  else e = launch_readout<float, float>(ra, p2, gr, p.lds_read, s);
+  e = p.D == 64 ? launch_readouts<64>(ra, in_bf16, out_bf16, p2, gr, p.lds_read, s)
+                : launch_readouts<32>(ra, in_bf16, out_bf16, p2, gr, p.lds_read, s);
   if (e == hipSuccess) e = mark(3);
   return (int)e;
 }

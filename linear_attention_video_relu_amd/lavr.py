@@ -104,8 +104,9 @@ def _ptr(t):
 class RopeTable:
     """Device rotary table built by rope_table_build, plus its la_rope description.
 
-    split = (d_t, d_h, d_w), grid = (rows, cols) of a frame; max_frames rows of the
-    t section.  A 1-D RoPE over the token index is split (32, 0, 0), grid (1, 1).
+    split = (d_t, d_h, d_w) with d_t + d_h + d_w = the head dim (32 or 64), grid =
+    (rows, cols) of a frame; max_frames rows of the t section.  A 1-D RoPE over the
+    token index is split (head_dim, 0, 0), grid (1, 1).
     """
 
     def __init__(self, split, grid, max_frames, base=10000.0, device="cuda"):
@@ -117,7 +118,7 @@ class RopeTable:
         self.device = torch.device(device)
         self.buffer = torch.empty(nbytes // 4, dtype=torch.float32, device=self.device)
         self.desc = LaRope()
-        _check(lib.rope_table_build(ctypes.byref(self.desc), _ptr(self.buffer), nbytes, HEAD_DIM,
+        _check(lib.rope_table_build(ctypes.byref(self.desc), _ptr(self.buffer), nbytes, d_t + d_h + d_w,
                                     d_t, d_h, d_w, int(max_frames), gh, gw, float(base),
                                     _stream(self.device)), "rope_table_build")
         self.split, self.grid, self.max_frames, self.base = (d_t, d_h, d_w), (gh, gw), int(max_frames), float(base)
@@ -165,7 +166,8 @@ def _check_qkv(q, k, v):
 
 def block_causal_forward(q, k, v, block_frames, tokens_per_frame, rope=None, eps=EPS_DEFAULT,
                          out=None, out_dtype=None, workspace=None, first_block_frames=None):
-    """One-shot block-causal forward.  q, k, v: (B, N, H, 32), N = frames * tokens_per_frame.
+    """One-shot block-causal forward.  q, k, v: (B, N, H, D) with D = 32 or 64,
+    N = frames * tokens_per_frame.
 
     first_block_frames: frames of the first block (None = block_frames)."""
     _check_qkv(q, k, v)

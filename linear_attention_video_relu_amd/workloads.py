@@ -26,6 +26,7 @@ CHUNK_TOKENS = 4096
 TENSORS = ("q", "k", "v")
 
 ROPE_3D = {"split": (8, 12, 12), "base": 10000.0}
+ROPE_3D_64 = {"split": (16, 24, 24), "base": 10000.0}
 
 WORKLOADS = {
     # 1-D RoPE over the token index: one token per "frame", blocks of 64 tokens.
@@ -46,6 +47,14 @@ WORKLOADS = {
     "minute_bf16": dict(index=4, B=1, H=70, head_dim=32, frames=240, tokens_per_frame=1560,
                         grid=(30, 52), block_frames=8, dtype="bf16", rope=ROPE_3D,
                         scale=1.0, outlier_frac=0.05, outlier_scale=8.0),
+    # The same 2240 channels as 35 heads of 64 (the pages name head dims 32 and
+    # 64); the rotary split keeps the t:h:w = 8:12:12 proportions.
+    "minute_d64_bf16": dict(index=5, B=1, H=35, head_dim=64, frames=240, tokens_per_frame=1560,
+                            grid=(30, 52), block_frames=8, dtype="bf16", rope=ROPE_3D_64,
+                            scale=1.0, outlier_frac=0.05, outlier_scale=8.0),
+    "clip480p_d64_bf16": dict(index=6, B=1, H=35, head_dim=64, frames=12, tokens_per_frame=1560,
+                              grid=(30, 52), block_frames=3, dtype="bf16", rope=ROPE_3D_64,
+                              scale=0.5, outlier_frac=0.0, outlier_scale=1.0),
 }
 
 

@@ -54,7 +54,10 @@ def test_workspace_bytes(lavr):
     rec = (32 * 32 + 32) * 4
     assert n >= 70 * 30 * rec            # at least the per-block prefix states
     assert n < 0.05 * 1 * 374400 * 70 * 32 * 2 * 4   # small next to q, k, v, out
-    assert lavr.lib.la_workspace_bytes(1, 70, 64, 240, 1560, 8, 0) == 0   # head_dim 64 not built
+    assert lavr.lib.la_workspace_bytes(1, 70, 48, 240, 1560, 8, 0) == 0   # head_dim 48 not built
+    # the same channels as 35 heads of 64: records of 64 x 64 + 64 floats
+    n64 = lavr.lib.la_workspace_bytes(1, 35, 64, 240, 1560, 8, 0)
+    assert n64 >= 35 * 30 * (64 * 64 + 64) * 4
     assert lavr.lib.la_workspace_bytes(0, 70, 32, 240, 1560, 8, 0) == 0
     assert lavr.lib.la_workspace_bytes(1, 70, 32, 240, 1560, 8, -1) == 0  # bad first block
     # a first block of 9 frames: 1 + ceil(231 / 8) = 30 blocks, workspace at least as large
@@ -86,7 +89,7 @@ def call_forward(lavr, **kw):
     (dict(tpf=0), 1),
     (dict(bf=0), 1),
     (dict(f0=-2), 1),                    # negative first-block length
-    (dict(d=64), 2),                     # head_dim 64 is not built
+    (dict(d=48), 2),                     # head dims other than 32 and 64 are not built
     (dict(in_dt=7), 1),
     (dict(eps=-1.0), 1),
     (dict(eps=float("inf")), 1),
@@ -124,7 +127,8 @@ def test_rope_table_build_rejects(lavr):
     f = lavr.lib.rope_table_build
     ok = dict(dt=8, dh=12, dw=12, mf=4, gh=2, gw=3)
     assert f(ctypes.byref(r), ctypes.c_void_p(FAKE), 8, 32, 8, 12, 12, 4, 2, 3, 10000.0, None) == 1   # bytes
-    assert f(ctypes.byref(r), ctypes.c_void_p(FAKE), 1 << 20, 64, 8, 12, 12, 4, 2, 3, 10000.0, None) == 2
+    assert f(ctypes.byref(r), ctypes.c_void_p(FAKE), 1 << 20, 48, 16, 16, 16, 4, 2, 3, 10000.0, None) == 2
+    assert f(ctypes.byref(r), ctypes.c_void_p(FAKE), 1 << 20, 64, 8, 12, 12, 4, 2, 3, 10000.0, None) == 1
     assert f(ctypes.byref(r), ctypes.c_void_p(FAKE), 1 << 20, 32, 8, 12, 12, 4, 2, 3, -1.0, None) == 1
     assert f(ctypes.byref(r), ctypes.c_void_p(0), 1 << 20, 32, 8, 12, 12, 4, 2, 3, 10000.0, None) == 1
     assert f(None, ctypes.c_void_p(FAKE), 1 << 20, 32, 8, 12, 12, 4, 2, 3, 10000.0, None) == 1
@@ -156,5 +160,5 @@ def test_state_init_rejects(lavr):
     f = lavr.lib.la_state_init
     assert f(ctypes.byref(st), ctypes.c_void_p(0), ctypes.c_void_p(FAKE), 1, 1, 32, None) == 1
     assert f(ctypes.byref(st), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 4), 1, 1, 32, None) == 1
-    assert f(ctypes.byref(st), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 4096), 1, 1, 64, None) == 2
+    assert f(ctypes.byref(st), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 4096), 1, 1, 48, None) == 2
     assert f(ctypes.byref(st), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 64), 1, 1, 32, None) == 1  # overlap

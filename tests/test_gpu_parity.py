@@ -244,6 +244,84 @@ def test_streaming_first_block_plus_one(lavr):
     assert oracle.rel_err(to_f64_torch(got), full_oracle(cfg, arrs)) <= 1e-4
 
 
+# ---------------------------------------------------------------------- head dim 64
+
+def small64(**kw):
+    """small_cfg at head dim 64 (one head per workgroup); t:h:w split 16:24:24."""
+    base = small_cfg(head_dim=64, rope={"split": (16, 24, 24), "base": 10000.0}, name="small3d64")
+    base.update(kw)
+    return base
+
+
+@pytest.mark.parametrize("kw", [
+    dict(),                                                    # B=2, H=3, ragged last block
+    dict(frames=40, block_frames=3, H=2, B=1, tokens_per_frame=48, grid=(6, 8)),   # many tiles
+    dict(rope={"split": (14, 26, 24), "base": 10000.0}),       # odd pair counts
+    dict(frames=11, block_frames=3, first_block_frames=4),     # longer first block
+    dict(rope=None),                                           # RoPE off
+])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_head_dim_64_small(lavr, kw, out_dtype):
+    cfg = small64(**kw)
+    say(f"case head dim 64 {kw} out={out_dtype}")
+    arrs, (q, k, v) = device_inputs(cfg, DEV)
+    od = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    out = lavr.block_causal_forward(q, k, v, cfg["block_frames"], cfg["tokens_per_frame"],
+                                    rope_for(lavr, cfg), out_dtype=od,
+                                    first_block_frames=cfg.get("first_block_frames"))
+    torch.cuda.synchronize()
+    ref = full_oracle(cfg, arrs)
+    got = to_f64_torch(out)
+    if out_dtype == "f32":
+        err = oracle.rel_err(got, ref)
+        say(f"  rel err {err:.3e}")
+        assert err <= 1e-4
+    else:
+        err = err_bf16_out(got, ref)
+        say(f"  rel err beyond bf16 rounding {err:.3e} (plain {oracle.rel_err(got, ref):.3e})")
+    assert err <= TOL_BF16
+
+
+@pytest.mark.parametrize("split", [(16, 24, 24), (14, 26, 24), (64, 0, 0)])
+def test_head_dim_64_f32_inputs(lavr, split):
+    cfg = small64(dtype="f32", rope={"split": split, "base": 10000.0})
+    if split[1] == 0:
+        cfg.update(tokens_per_frame=1, grid=(1, 1), frames=200, block_frames=48)
+    say(f"case head dim 64 f32 split {split}")
+    arrs, (q, k, v) = device_inputs(cfg, DEV)
+    out = lavr.block_causal_forward(q, k, v, cfg["block_frames"], cfg["tokens_per_frame"], rope_for(lavr, cfg))
+    torch.cuda.synchronize()
+    err = oracle.rel_err(to_f64_torch(out), full_oracle(cfg, arrs))
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL_F32
+
+
+def test_head_dim_64_bf16_output_is_rne_of_f32_output(lavr):
+    cfg = small64(frames=9)
+    say("case head dim 64: bf16 out == rne(f32 out)")
+    _, (q, k, v) = device_inputs(cfg, DEV)
+    rope = rope_for(lavr, cfg)
+    o32 = lavr.block_causal_forward(q, k, v, 3, cfg["tokens_per_frame"], rope, out_dtype=torch.float32)
+    o16 = lavr.block_causal_forward(q, k, v, 3, cfg["tokens_per_frame"], rope, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+
+
+def test_head_dim_64_streaming(lavr):
+    cfg = small64(frames=12)
+    say("case head dim 64 streaming")
+    arrs, (q, k, v) = device_inputs(cfg, DEV)
+    rope = rope_for(lavr, cfg)
+    L = 3 * cfg["tokens_per_frame"]
+    one = lavr.block_causal_forward(q, k, v, 3, cfg["tokens_per_frame"], rope, out_dtype=torch.float32)
+    st = lavr.StreamState(cfg["B"], cfg["H"], head_dim=64, device=DEV)
+    got = stream_run(lavr, st, q, k, v, cfg, rope, 4, L, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert st.frames_done == 12
+    assert oracle.rel_err(to_f64_torch(got), to_f64_torch(one)) <= 1e-4
+    assert oracle.rel_err(to_f64_torch(got), full_oracle(cfg, arrs)) <= 1e-4
+
+
 # ----------------------------------------------------------------------- streaming
 
 def stream_run(lavr, st, q, k, v, cfg, rope, nblk, L, save=True, out_dtype=None):
@@ -332,6 +410,8 @@ def check_heads(cfg, arrs, out, heads, label):
     ("clip480p_bf16", [(0, 0), (0, 1), (0, 34), (0, 69)]),
     ("clip720p_bf16", [(0, 0), (1, 37), (1, 69)]),
     ("minute_bf16", [(0, 0), (0, 41)]),
+    ("clip480p_d64_bf16", [(0, 0), (0, 17), (0, 34)]),
+    ("minute_d64_bf16", [(0, 0), (0, 20)]),
 ])
 def test_full_size_one_shot(lavr, name, heads):
     w = W()
