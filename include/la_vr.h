@@ -27,7 +27,8 @@
  * Layouts.  q, k, v and out are contiguous row-major (B, N, H, head_dim) with
  * N = frames * tokens_per_frame; tokens are frame-major, then raster order
  * (row, col) inside a frame.  This is the (B, N, C) activation with C = H *
- * head_dim.  Only head_dim == 32 is built.
+ * head_dim.  head_dim 32 and 64 are built (the per-head widths the walkthrough
+ * names, "Integration into Sana's Video Backbone").
  *
  * RoPE.  head_dim is split into consecutive sections of d_t, d_h and d_w
  * channels that follow the token's frame index t, row and column.  Pair i
@@ -57,7 +58,7 @@ extern "C" {
 typedef enum {
   LA_OK = 0,
   LA_ERR_INVALID_ARG = 1,     /* null/misaligned pointer, bad size, overlap, small workspace */
-  LA_ERR_UNSUPPORTED = 2,     /* valid request the library does not build (head_dim != 32, ...) */
+  LA_ERR_UNSUPPORTED = 2,     /* valid request the library does not build (head_dim not 32 or 64, ...) */
   LA_ERR_STATE_MISMATCH = 3,  /* la_state shape does not match the call */
   LA_ERR_HIP = 4              /* a HIP launch or runtime call failed */
 } la_status;

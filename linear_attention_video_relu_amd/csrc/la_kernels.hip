@@ -16,10 +16,10 @@
 //                  eps from un-rotated phi(q), rotates phi(q), multiplies by
 //                  Sbar_j on MFMA and writes out = num / den.
 //
-// Data in HBM: q, k, v, out are (B, N, H, 32) row-major.  A token's two-head
-// slice is 128 contiguous bytes in bf16 (256 in fp32), so each workgroup owns
-// a pair of heads and a lane moves 16-byte pieces of fully used 128-byte
-// lines.  Q, K, V and out are reached through buffer resources that span one
+// Data in HBM: q, k, v, out are (B, N, H, D) row-major with D = 32 or 64.  A
+// workgroup owns 64 channels of every token row (a pair of heads at D = 32,
+// one head at D = 64): 128 contiguous bytes in bf16 (256 in fp32), so a lane
+// moves 16-byte pieces of fully used 128-byte lines.  Q, K, V and out are reached through buffer resources that span one
 // workgroup's token range: the hardware range check turns reads past the end
 // into zeros and drops writes past the end, so ragged tails need no branches,
 // and lane offsets stay 32-bit.
