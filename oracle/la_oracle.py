@@ -198,6 +198,86 @@ def readout_tokens(q, n_idx, S_bar, z_bar, tokens_per_frame, rope=None, eps=EPS_
     return (rq @ S_bar.T) / (fq @ z_bar + eps)[:, None]
 
 
+# ------------------------------------------------------------------------ backward
+
+def _unrotate_tokens(y, rope, tokens_per_frame, t0):
+    """R^T y: each pair turns by minus its angle (the transpose of a rotation)."""
+    if rope is None:
+        return np.array(y, dtype=np.float64, copy=True)
+    t, row, col = token_positions(y.shape[0], tokens_per_frame, rope["grid"][1], t0)
+    return rope_rotate(y, -t, -row, -col, rope["split"], rope["base"])
+
+
+def backward_head(q, k, v, g, tokens_per_frame, block_frames, rope=None, eps=EPS_DEFAULT,
+                  first_block_frames=None):
+    """Gradients (dq, dk, dv) of sum(g * out) for one (batch, head); q, k, v, g: (N, d).
+
+    The pages give the forward only; this is its exact derivative, written out
+    from the forward's definition (token n of block j, p = phi(q_n), r = R p,
+    den = zbar_j . p + eps, out = Sbar_j r / den):
+      a = g / den, beta = -(g . out) / den,
+      dq = [q > 0] * (R^T Sbar_j^T a + beta zbar_j),
+      G_j = sum_n a r^T, gz_j = sum_n beta p over block j,
+      dS_i = sum_{j >= i} G_j, dz_i = sum_{j >= i} gz_j (blocks at or after i see block i),
+      dv_m = dS_i kappa_m, dk_m = [k > 0] * (R^T dS_i^T v_m + dz_i), kappa = R phi(k).
+    ReLU's derivative is taken as 0 at 0.
+    """
+    q, k, v, g = (np.asarray(a, dtype=np.float64) for a in (q, k, v, g))
+    N, d = q.shape
+    fq, fk = _relu(q), _relu(k)
+    rq = _rotate_tokens(fq, rope, tokens_per_frame, 0)
+    rk = _rotate_tokens(fk, rope, tokens_per_frame, 0)
+    first = None if first_block_frames is None else first_block_frames * tokens_per_frame
+    bounds = block_bounds(N, block_frames * tokens_per_frame, first)
+    S, z = np.zeros((d, d)), np.zeros(d)
+    Sbar, zbar = [], []
+    for s, e in bounds:
+        S = S + v[s:e].T @ rk[s:e]
+        z = z + fk[s:e].sum(axis=0)
+        Sbar.append(S)
+        zbar.append(z)
+    dr, dp = np.zeros((N, d)), np.zeros((N, d))
+    G, gz = [], []
+    for jb, (s, e) in enumerate(bounds):
+        den = fq[s:e] @ zbar[jb] + eps
+        out = (rq[s:e] @ Sbar[jb].T) / den[:, None]
+        a = g[s:e] / den[:, None]
+        beta = -np.sum(g[s:e] * out, axis=1) / den
+        dr[s:e] = a @ Sbar[jb]                 # row n: Sbar^T a_n
+        dp[s:e] = beta[:, None] * zbar[jb][None, :]
+        G.append(a.T @ rq[s:e])                # G[e, f] = sum_n a_n[e] r_n[f]
+        gz.append(beta @ fq[s:e])
+    nb = len(bounds)
+    dS, dz = [None] * nb, [None] * nb
+    accS, accz = np.zeros((d, d)), np.zeros(d)
+    for i in reversed(range(nb)):
+        accS = accS + G[i]
+        accz = accz + gz[i]
+        dS[i], dz[i] = accS, accz
+    dv, dkr, dku = np.zeros((N, d)), np.zeros((N, d)), np.zeros((N, d))
+    for i, (s, e) in enumerate(bounds):
+        dv[s:e] = rk[s:e] @ dS[i].T            # dv_m[e] = sum_f dS[e, f] kappa_m[f]
+        dkr[s:e] = v[s:e] @ dS[i]              # d kappa_m[f] = sum_e dS[e, f] v_m[e]
+        dku[s:e] = dz[i][None, :]
+    dq = (q > 0) * (_unrotate_tokens(dr, rope, tokens_per_frame, 0) + dp)
+    dk = (k > 0) * (_unrotate_tokens(dkr, rope, tokens_per_frame, 0) + dku)
+    return dq, dk, dv
+
+
+def backward(q, k, v, g, tokens_per_frame, block_frames, rope=None, eps=EPS_DEFAULT,
+             first_block_frames=None):
+    """backward_head over (B, N, H, d) arrays; returns dq, dk, dv (float64)."""
+    q, k, v, g = (np.asarray(a, dtype=np.float64) for a in (q, k, v, g))
+    B, N, H, d = q.shape
+    dq, dk, dv = (np.empty((B, N, H, d)) for _ in range(3))
+    for b in range(B):
+        for h in range(H):
+            dq[b, :, h], dk[b, :, h], dv[b, :, h] = backward_head(
+                q[b, :, h], k[b, :, h], v[b, :, h], g[b, :, h], tokens_per_frame, block_frames,
+                rope, eps, first_block_frames)
+    return dq, dk, dv
+
+
 # ------------------------------------------------------------------------ streaming
 
 class StreamState:
