@@ -140,6 +140,28 @@ int la_block_causal_forward_timed(const void* q, const void* k, const void* v, v
                                   float eps, void* ws, size_t ws_bytes, void* stream,
                                   void* const* events);
 
+/* Workspace bytes needed by la_block_causal_backward for this shape (0 for
+ * invalid sizes and for head dims the backward does not build). */
+size_t la_backward_workspace_bytes(int B, int H, int head_dim, int frames, int tokens_per_frame,
+                                   int block_frames, int first_block_frames);
+
+/* Gradients of sum(dout * out) with respect to q, k and v, where out is what
+ * la_block_causal_forward returns for the same arguments.  The pages state the
+ * forward only ("Implementing Block Causal Linear Attention for Long Video
+ * Generation with Sana", "The Linear Attention Kernel" and "Chunk-Wise
+ * Causality"); this is its exact derivative (ReLU's derivative taken as 0 at
+ * 0), for training.  q, k, v and dout have dtype in_dt and layout (B, N, H,
+ * head_dim); dq, dk, dv have dtype grad_dt and the same layout, and must not
+ * overlap the inputs or each other.  Only head_dim 32 is built (other valid
+ * head dims return LA_ERR_UNSUPPORTED).  The block states are formed again from
+ * k and v.  ws (256-byte aligned, ws_bytes >= la_backward_workspace_bytes) is
+ * caller-owned scratch.  Same status codes and stream semantics as the forward. */
+int la_block_causal_backward(const void* q, const void* k, const void* v, const void* dout,
+                             void* dq, void* dk, void* dv, la_dtype in_dt, la_dtype grad_dt,
+                             int B, int H, int head_dim, int frames, int tokens_per_frame,
+                             int block_frames, int first_block_frames, const la_rope* rope,
+                             float eps, void* ws, size_t ws_bytes, void* stream);
+
 /* Bind the caller's device buffers S_dev ([B][H][d][d] fp32) and z_dev
  * ([B][H][d] fp32), both 16-byte aligned, to *st, zero them on `stream`, and set
  * frames_done = 0. */

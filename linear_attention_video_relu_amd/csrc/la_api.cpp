@@ -140,7 +140,8 @@ int make_plan(Plan* p, int B, int H, int head_dim, int frames, int tpf, int bloc
     p->rope.gw = rope->grid_w;
   }
   const int tiles = (in_dt == LA_BF16 ? 3 : 2) * kStep * 64 * esize(in_dt);   // 64 channels per row
-  p->lds_state = tiles + (int)(tab_pairs(rope, tpf, p->Tc) * 8);
+  p->tab_state = (int)(tab_pairs(rope, tpf, p->Tc) * 8);
+  p->lds_state = tiles + p->tab_state;
   p->lds_read = (int)(tab_pairs(rope, tpf, p->Tr) * 8);
 
   const size_t rec = (size_t)p->rec * sizeof(float);
@@ -149,6 +150,8 @@ int make_plan(Plan* p, int B, int H, int head_dim, int frames, int tpf, int bloc
   p->ws_part = 0;
   p->ws_prefix = align256(part);
   p->ws_total = p->ws_prefix + align256(prefix);
+  p->ws_suffix = p->ws_total;
+  p->ws_total_bw = p->ws_suffix + align256(prefix);
   return LA_OK;
 }
 
@@ -248,6 +251,48 @@ int la_block_causal_forward_timed(const void* q, const void* k, const void* v, v
   if (!ws || !aligned(ws, 256) || ws_bytes < p.ws_total) return LA_ERR_INVALID_ARG;
   return hip_status(lavr::launch_forward(p, q, k, v, out, in_dt == LA_BF16, out_dt == LA_BF16, eps,
                                          ws, nullptr, nullptr, nullptr, nullptr, stream, events));
+}
+
+size_t la_backward_workspace_bytes(int B, int H, int head_dim, int frames, int tokens_per_frame,
+                                   int block_frames, int first_block_frames) {
+  Plan p;
+  if (head_dim != 32) return 0;
+  if (make_plan(&p, B, H, head_dim, frames, tokens_per_frame, block_frames, first_block_frames,
+                nullptr, 0, LA_BF16) != LA_OK)
+    return 0;
+  return p.ws_total_bw;
+}
+
+int la_block_causal_backward(const void* q, const void* k, const void* v, const void* dout,
+                             void* dq, void* dk, void* dv, la_dtype in_dt, la_dtype grad_dt,
+                             int B, int H, int head_dim, int frames, int tokens_per_frame,
+                             int block_frames, int first_block_frames, const la_rope* rope,
+                             float eps, void* ws, size_t ws_bytes, void* stream) {
+  if (!valid_dtype(in_dt) || !valid_dtype(grad_dt)) return LA_ERR_INVALID_ARG;
+  if (!std::isfinite(eps) || eps < 0.f) return LA_ERR_INVALID_ARG;
+  Plan p;
+  int st = make_plan(&p, B, H, head_dim, frames, tokens_per_frame, block_frames, first_block_frames,
+                     rope, 0, in_dt);
+  if (st != LA_OK) return st;
+  if (head_dim != 32) return LA_ERR_UNSUPPORTED;
+  // inputs q, k, v, dout; gradient outputs dq, dk, dv: each output checked
+  // against the inputs (as the forward checks out) and against the others.
+  const void* ins[4] = {q, k, v, dout};
+  void* outs[3] = {dq, dk, dv};
+  const size_t elems = (size_t)p.B * p.N * p.H * p.D;
+  const size_t nin = elems * esize(in_dt), nout = elems * esize(grad_dt);
+  for (const void* x : ins)
+    if (!x || !aligned(x, 16)) return LA_ERR_INVALID_ARG;
+  for (int i = 0; i < 3; ++i) {
+    if (!outs[i] || !aligned(outs[i], 16)) return LA_ERR_INVALID_ARG;
+    for (const void* x : ins)
+      if (overlaps(outs[i], nout, x, nin)) return LA_ERR_INVALID_ARG;
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], nout, outs[j], nout)) return LA_ERR_INVALID_ARG;
+  }
+  if (!ws || !aligned(ws, 256) || ws_bytes < p.ws_total_bw) return LA_ERR_INVALID_ARG;
+  return hip_status(lavr::launch_backward(p, q, k, v, dout, dq, dk, dv, in_dt == LA_BF16,
+                                          grad_dt == LA_BF16, eps, ws, stream));
 }
 
 int la_state_init(la_state* st, float* S_dev, float* z_dev, int B, int H, int head_dim,

@@ -40,9 +40,12 @@ struct Plan {
   uint64_t mag_gw;      // floor(2^42 / gw_div) + 1
   RopeDev rope;
   int lds_state;        // dynamic LDS bytes of the block-state kernel
+  int tab_state;        // of which the rotary window of a chunk
   int lds_read;         // dynamic LDS bytes of the readout kernel
   size_t ws_part;       // byte offset of the per-chunk partial states
   size_t ws_prefix;     // byte offset of the per-block prefix states
+  size_t ws_suffix;     // byte offset of the per-block suffix sums (backward only)
+  size_t ws_total_bw;   // workspace bytes of the backward
   size_t ws_total;      // workspace bytes
 };
 
@@ -54,5 +57,8 @@ int launch_forward(const Plan& p, const void* q, const void* k, const void* v, v
                    const float* S_init, const float* z_init, float* S_save, float* z_save,
                    void* stream, void* const* events = nullptr);
 int launch_zero(float* p, size_t n, void* stream);
+int launch_backward(const Plan& p, const void* q, const void* k, const void* v, const void* dout,
+                    void* dq, void* dk, void* dv, int in_bf16, int grad_bf16, float eps, void* ws,
+                    void* stream);
 
 }  // namespace lavr

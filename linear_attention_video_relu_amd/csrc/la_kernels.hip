@@ -86,6 +86,7 @@ struct PrefixArgs {
   float* z_save;
   int H, nb, cpb;
   int hd, rec;               // head dim, floats per record (hd * hd + hd)
+  int rev;                   // 1: sums over blocks j >= i (last block first)
 };
 
 struct ReadArgs {
@@ -605,7 +606,8 @@ __global__ __launch_bounds__(PFX_NT) void k_prefix(PrefixArgs a) {
       int lb = bi, lcn = c;               // (block, chunk) of the next item to load
 #pragma unroll
       for (int i = 0; i < BATCH; ++i) {
-        v[i] = part[((size_t)(r0 + w + 4 * lb) * a.cpb + lcn) * REC];
+        const int jb = a.rev ? a.nb - 1 - (r0 + w + 4 * lb) : r0 + w + 4 * lb;
+        v[i] = part[((size_t)jb * a.cpb + lcn) * REC];
         if (q0 + i + 1 < items && ++lcn == a.cpb) { lcn = 0; ++lb; }
       }
 #pragma unroll
@@ -625,7 +627,7 @@ __global__ __launch_bounds__(PFX_NT) void k_prefix(PrefixArgs a) {
     if (w == 0 && ok) {
       for (int jj = 0; jj < nr; ++jj) {
         acc += bs[jj][lane];
-        o[(size_t)(r0 + jj) * REC] = acc;
+        o[(size_t)(a.rev ? a.nb - 1 - (r0 + jj) : r0 + jj) * REC] = acc;
       }
     }
     __syncthreads();
@@ -917,6 +919,516 @@ __global__ __launch_bounds__(NT) void k_readout(ReadArgs a) {
   }
 }
 
+// =================================================================== backward
+
+constexpr int REC32 = D * D + D;   // floats of a head-dim-32 record
+//
+// The exact derivative of the forward for an output gradient g, per (batch,
+// head); for token n of block j (p = phi(q_n), r = R p, den = zbar_j . p + eps,
+// out = Sbar_j r / den):
+//   a = g / den, beta = -(g . out) / den,
+//   dq = [q > 0] (R^T Sbar_j^T a + beta zbar_j),
+//   G_j = sum_n a r^T, gz_j = sum_n beta p,
+//   dS_i = sum_{j >= i} G_j, dz_i = sum_{j >= i} gz_j   (block j reads every block <= j),
+//   dv = dS_i kappa, dk = [k > 0] (R^T dS_i^T v + dz_i), kappa = R phi(k).
+// Sbar, zbar come from the forward's block-state and prefix kernels (run again
+// by the backward entry point); dS, dz from the prefix kernel run over the
+// blocks in reverse on the chunk partials of (G, gz).
+
+struct BwQArgs {
+  const void* q;
+  const void* g;
+  void* dq;
+  const float* prefix;       // Sbar_j, zbar_j records
+  float* part;               // out: chunk partials of (G, gz)
+  float eps;
+  int H, N, L, L0, nb, cpb, Tc, hg;
+  PosArgs pos;
+  RopeDev rope;
+};
+
+struct BwKVArgs {
+  const void* k;
+  const void* v;
+  void* dk;
+  void* dv;
+  const float* suffix;       // dS_i, dz_i records
+  int H, N, L, L0, nb, rpb, Tr, hg;
+  PosArgs pos;
+  RopeDev rope;
+};
+
+__device__ __forceinline__ void unrotate8(float* x, const float2* cs) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = x[2 * i], b = x[2 * i + 1];
+    x[2 * i] = a * cs[i].x + b * cs[i].y;
+    x[2 * i + 1] = b * cs[i].x - a * cs[i].y;
+  }
+}
+
+__device__ __forceinline__ void widen8(const Raw8<uint16_t>& r, float* x) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t ri = r.r[0][i];
+    x[2 * i] = __uint_as_float(ri << 16);
+    x[2 * i + 1] = __uint_as_float(ri & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void widen8(const Raw8<float>& r, float* x) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = __uint_as_float(r.r[i >> 2][i & 3]);
+}
+
+// Matrix-vector products in the token layout (lane l: token l & 15, channels
+// 8(l >> 4) .. +7).  MFMA 16x16x32 output row i of tile t is loaded from matrix
+// row 8(i >> 2) + 4t + (i & 3), so the output lane of chunk ch holds channels
+// 8ch + 4t .. +3: with both tiles, exactly the channels its inputs hold.
+__device__ __forceinline__ int perm_row(int t, int i) { return 8 * (i >> 2) + 4 * t + (i & 3); }
+
+// A operands of a 32 x 32 fp32 matrix m (row-major) or of its transpose, for
+// both tiles: bf16 hi/lo pairs, or 8 floats per tile for the fp32 MFMA.
+template <bool BF, bool TR>
+__device__ __forceinline__ void perm_tiles(const float* m, int lane, u32x4* hi, u32x4* lo, float (*fs)[8]) {
+  const int i = lane & 15, kc = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int row = perm_row(t, i);
+    float sv[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) sv[s] = TR ? m[(8 * kc + s) * D + row] : m[row * D + 8 * kc + s];
+    if constexpr (BF) {
+      split8(sv, hi[t], lo[t]);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) fs[t][s] = sv[s];
+    }
+  }
+}
+
+// y = M x for the lane's token: x as bf16 hi/lo (xl may be null: x exact in
+// bf16) or as 8 floats; y in the lane's 8 channels.
+template <bool BF>
+__device__ __forceinline__ void matvec(const u32x4* Mh, const u32x4* Ml, const float (*Mf)[8],
+                                       u32x4 xh, const u32x4* xl, const float* xf, float* y) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (BF) {
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Mh[t]), as_bf16x8(xh), c, 0, 0, 0);
+      if (xl != nullptr) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Mh[t]), as_bf16x8(*xl), c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Ml[t]), as_bf16x8(xh), c, 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(Mf[t][s], xf[s], c, 0, 0, 0);
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) y[4 * t + v] = c[v];
+  }
+}
+
+// Store the 8 channels y of the lane's token for half h: bf16 pieces are
+// collected in pk for the paired store; fp32 goes out at once.
+template <int EO>
+__device__ __forceinline__ void put8(const float* y, int h, u32x4* pk, __amdgpu_buffer_rsrc_t rs, int off) {
+  if constexpr (EO == 2) {
+    pk[h] = u32x4{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7])};
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{y[0], y[1], y[2], y[3]}), rs, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{y[4], y[5], y[6], y[7]}), rs, off + 16, 0, 0);
+  }
+}
+
+// Paired bf16 store of both halves' pieces as whole 128-byte lines (lanes tl
+// and tl ^ 8 trade one piece, as in the readout), or one half alone.
+__device__ __forceinline__ void store_pair(const u32x4* pk, int nh, int tl, __amdgpu_buffer_rsrc_t rs,
+                                           int off_pair, int off_one, int RO) {
+  if (nh == 2) {
+    const bool lo = tl < 8;
+    uint32_t first[4], second[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t p0 = pk[0][i], p1 = pk[1][i];
+      const uint32_t snd = lo ? p1 : p0;
+      const uint32_t rcv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)snd, 0x128, 0xf, 0xf, false);
+      first[i] = lo ? p0 : rcv;
+      second[i] = lo ? rcv : p1;
+    }
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{first[0], first[1], first[2], first[3]}, rs, off_pair, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{second[0], second[1], second[2], second[3]}, rs,
+                                           off_pair + 8 * RO, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b128(pk[0], rs, off_one, 0, 0);
+  }
+}
+
+// ------------------------------------------------------------------ k_bw_kv
+//
+// Grid and token layout as k_readout (tiles of one block, head pairs).  Per
+// token: kappa = R phi(k), dv = dS kappa, dkappa = dS^T v, dk = [k > 0]
+// (R^T dkappa + dz), both products on MFMA with row-permuted A operands.
+
+template <typename TIn, typename TOut, bool P2>
+__global__ __launch_bounds__(NT) void k_bw_kv(BwKVArgs a) {
+  constexpr bool BF = sizeof(TIn) == 2;
+  constexpr int ES = (int)sizeof(TIn), EO = (int)sizeof(TOut);
+  extern __shared__ __align__(16) unsigned char smem[];
+  float2* tab = reinterpret_cast<float2*>(smem);
+
+  const int g = blockIdx.x % a.hg;
+  const int ti = blockIdx.x / a.hg;
+  const int b = blockIdx.y;
+  const int j = ti / a.rpb;
+  const int r = ti - j * a.rpb;
+  const int blk0 = block_start(j, a.L0, a.L);
+  const int blk1 = min(blk0 + (j == 0 ? a.L0 : a.L), a.N);
+  const int t0 = min(blk0 + r * a.Tr, blk1);
+  const int t1 = min(t0 + a.Tr, blk1);
+  if (t0 >= t1) return;
+  const bool rope_on = a.rope.table != nullptr;
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int tl = lane & 15, ch = lane >> 4;
+  const int h0 = 2 * g;
+  const int nh = min(2, a.H - h0);
+  const int ngroups = (t1 - t0 + 15) >> 4;
+
+  const int RB = a.H * D * ES, RO = a.H * D * EO;
+  const size_t row0 = (size_t)b * a.N + t0;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const char*>(a.k) + row0 * RB, (uint32_t)(t1 - t0) * RB);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const char*>(a.v) + row0 * RB, (uint32_t)(t1 - t0) * RB);
+  const __amdgpu_buffer_rsrc_t rdk = make_rsrc(static_cast<char*>(a.dk) + row0 * RO, (uint32_t)(t1 - t0) * RO);
+  const __amdgpu_buffer_rsrc_t rdv = make_rsrc(static_cast<char*>(a.dv) + row0 * RO, (uint32_t)(t1 - t0) * RO);
+  int ioff = (w * 16 + tl) * RB + (h0 * D + 8 * ch) * ES;
+  int ooff = (w * 16) * RO + h0 * D * EO;
+  const int o_one = tl * RO + 8 * ch * EO;
+  const int o_pair = (tl & 7) * RO + ((tl >> 3) * D + 8 * ch) * EO;
+
+  const TabWindow win = stage_table(tab, a.rope, a.pos.t0, t0, t1, a.pos.mag_tpf);
+  RopeLane<P2> rl;
+  TokPos tp;
+  if (rope_on) {
+    rl.init(a.rope, win, ch);
+    tp.init(t0 + w * 16 + tl, a.pos);
+  }
+
+  // dS (for dv) and dS^T (for dkappa) of block j, per head; dz slices.
+  u32x4 Nh[2][2], Nl[2][2], Th[2][2], Tl[2][2];
+  float Nf[2][2][8], Tf[2][2][8];
+  float dzb[2][8];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int hd = min(h, nh - 1);
+    const float* rec = a.suffix + ((size_t)(b * a.H + h0 + hd) * a.nb + j) * REC32;
+    perm_tiles<BF, false>(rec, lane, Nh[h], Nl[h], Nf[h]);
+    perm_tiles<BF, true>(rec, lane, Th[h], Tl[h], Tf[h]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dzb[h][i] = rec[D * D + 8 * ch + i];
+  }
+
+  struct Buf { Raw8<TIn> k[2], v[2]; };
+  auto load_group = [&](Buf& bf) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bf.k[h] = bload8<TIn>(rk, ioff + h * D * ES);
+      bf.v[h] = bload8<TIn>(rv, ioff + h * D * ES);
+    }
+    ioff += 64 * RB;
+  };
+  Buf b0, b1;
+  load_group(b0);
+  load_group(b1);
+  __syncthreads();
+
+  auto run_group = [&](const Buf& bf) {
+    float2 cs[4];
+    if (rope_on) {
+      rl.fetch(tab, tp, win, cs);
+      tp.advance(a.pos);
+    }
+    u32x4 pkk[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}}, pkv[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (h >= nh) break;
+      float kx[8], kap[8], vx[8], dv[8], dka[8];
+      relu_widen(bf.k[h], kx);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) kap[i] = kx[i];
+      if (rope_on) rotate8(kap, cs);
+      widen8(bf.v[h], vx);
+      if constexpr (BF) {
+        u32x4 kh, klo;
+        split8(kap, kh, klo);
+        matvec<true>(Nh[h], Nl[h], nullptr, kh, &klo, nullptr, dv);
+        matvec<true>(Th[h], Tl[h], nullptr, bf.v[h].r[0], nullptr, nullptr, dka);   // v is exact in bf16
+      } else {
+        matvec<false>(nullptr, nullptr, Nf[h], u32x4{}, nullptr, kap, dv);
+        matvec<false>(nullptr, nullptr, Tf[h], u32x4{}, nullptr, vx, dka);
+      }
+      if (rope_on) unrotate8(dka, cs);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dka[i] = kx[i] > 0.f ? dka[i] + dzb[h][i] : 0.f;
+      put8<EO>(dka, h, pkk, rdk, ooff + o_one + h * D * EO);
+      put8<EO>(dv, h, pkv, rdv, ooff + o_one + h * D * EO);
+    }
+    if constexpr (EO == 2) {
+      store_pair(pkk, nh, tl, rdk, ooff + o_pair, ooff + o_one, RO);
+      store_pair(pkv, nh, tl, rdv, ooff + o_pair, ooff + o_one, RO);
+    }
+    ooff += 64 * RO;
+  };
+
+  for (int gi = w; gi < ngroups; gi += 8) {
+    run_group(b0);
+    load_group(b0);
+    run_group(b1);
+    load_group(b1);
+  }
+}
+
+// ------------------------------------------------------------------- k_bw_q
+//
+// Grid as k_block_state (chunks of one block, head pairs); token layout as
+// k_readout, wave w taking the chunk's 16-token groups w, w+4, ...  Per token:
+// num = Sbar r, den, out, a, beta, Sbar^T a (MFMA, row-permuted operands) and
+// dq.  The chunk's G = sum a r^T goes through a per-wave LDS tile [16 tokens]
+// [2 heads x 32] holding a and r (bf16 hi and lo, or fp32), read back
+// transposed into 32x32 MFMAs over the group's tokens; gz = sum beta p stays in
+// registers.  At the end the four waves' partials are added through LDS and
+// written as the chunk's (G, gz) records.
+
+template <typename TIn, typename TOut, bool P2>
+__global__ __launch_bounds__(NT) void k_bw_q(BwQArgs a) {
+  constexpr bool BF = sizeof(TIn) == 2;
+  constexpr int ES = (int)sizeof(TIn), EO = (int)sizeof(TOut);
+  constexpr int WT = 16 * TCOLS;                     // elements of one wave tile array
+  constexpr int WAVE_BYTES = BF ? 4 * WT * 2 : 2 * WT * 4;   // a hi/lo, r hi/lo (bf16) or a, r (fp32)
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* red = reinterpret_cast<float*>(smem);                // [4 waves][2 heads][1024] at the end
+  float* zred = red + 4 * 2 * D * D;                           // [4 waves][2 heads][32]
+  float2* tab = reinterpret_cast<float2*>(zred + 4 * 2 * D);
+
+  const int g = blockIdx.x % a.hg;
+  const int ci = blockIdx.x / a.hg;
+  const int b = blockIdx.y;
+  const int j = ci / a.cpb;
+  const int c = ci - j * a.cpb;
+  const int blk0 = block_start(j, a.L0, a.L);
+  const int blk1 = min(blk0 + (j == 0 ? a.L0 : a.L), a.N);
+  const int c0 = min(blk0 + c * a.Tc, blk1);
+  const int c1 = min(c0 + a.Tc, blk1);
+  const bool rope_on = a.rope.table != nullptr;
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int tl = lane & 15, ch = lane >> 4;
+  const int h0 = 2 * g;
+  const int nh = min(2, a.H - h0);
+  const int ngroups = (c1 - c0 + 15) >> 4;
+  unsigned char* wtile = smem + w * WAVE_BYTES;
+
+  const int RB = a.H * D * ES, RO = a.H * D * EO;
+  const size_t row0 = (size_t)b * a.N + c0;
+  const uint32_t span = (uint32_t)(c1 - c0);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(static_cast<const char*>(a.q) + row0 * RB, span * RB);
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(static_cast<const char*>(a.g) + row0 * RB, span * RB);
+  const __amdgpu_buffer_rsrc_t rdq = make_rsrc(static_cast<char*>(a.dq) + row0 * RO, span * RO);
+  int ioff = (w * 16 + tl) * RB + (h0 * D + 8 * ch) * ES;
+  int ooff = (w * 16) * RO + h0 * D * EO;
+  const int o_one = tl * RO + 8 * ch * EO;
+  const int o_pair = (tl & 7) * RO + ((tl >> 3) * D + 8 * ch) * EO;
+
+  const TabWindow win = stage_table(tab, a.rope, a.pos.t0, c0, c1, a.pos.mag_tpf);
+  RopeLane<P2> rl;
+  TokPos tp;
+  if (rope_on) {
+    rl.init(a.rope, win, ch);
+    tp.init(c0 + w * 16 + tl, a.pos);
+  }
+
+  u32x4 Nh[2][2], Nl[2][2], Th[2][2], Tl[2][2];
+  float Nf[2][2][8], Tf[2][2][8];
+  float zb[2][8];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int hd = min(h, nh - 1);
+    const float* rec = a.prefix + ((size_t)(b * a.H + h0 + hd) * a.nb + j) * REC32;
+    perm_tiles<BF, false>(rec, lane, Nh[h], Nl[h], Nf[h]);
+    perm_tiles<BF, true>(rec, lane, Th[h], Tl[h], Tf[h]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) zb[h][i] = rec[D * D + 8 * ch + i];
+  }
+
+  struct Buf { Raw8<TIn> q[2], g[2]; };
+  auto load_group = [&](Buf& bf) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bf.q[h] = bload8<TIn>(rq, ioff + h * D * ES);
+      bf.g[h] = bload8<TIn>(rg, ioff + h * D * ES);
+    }
+    ioff += 64 * RB;
+  };
+  Buf b0, b1;
+  load_group(b0);
+  load_group(b1);
+  __syncthreads();
+
+  f32x16 gacc[2] = {{}, {}};
+  float zacc[2][8];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) zacc[h][i] = 0.f;
+
+  // Per-wave tile: row tl, columns h*32 + 8ch .. +7; odd groups of 8 rows keep
+  // the two heads swapped (as the block-state tiles) so transposed reads of the
+  // two half-waves hit different banks.
+  const int tcol = (8 * ch) ^ (((tl >> 3) & 1) << 5);
+  auto put_tile = [&](int arr, int h, const float* x, u32x4 hi, u32x4 lo) {
+    if constexpr (BF) {
+      uint16_t* t16 = reinterpret_cast<uint16_t*>(wtile) + arr * 2 * WT;   // arr 0: a, 1: r
+      *reinterpret_cast<u32x4*>(t16 + tl * TCOLS + (tcol ^ (h * D))) = hi;
+      *reinterpret_cast<u32x4*>(t16 + WT + tl * TCOLS + (tcol ^ (h * D))) = lo;
+    } else {
+      float* t32 = reinterpret_cast<float*>(wtile) + arr * WT;
+      f32x4* dst = reinterpret_cast<f32x4*>(t32 + tl * TCOLS + (tcol ^ (h * D)));
+      dst[0] = f32x4{x[0], x[1], x[2], x[3]};
+      dst[1] = f32x4{x[4], x[5], x[6], x[7]};
+    }
+  };
+
+  auto run_group = [&](const Buf& bf) {
+    float2 cs[4];
+    if (rope_on) {
+      rl.fetch(tab, tp, win, cs);
+      tp.advance(a.pos);
+    }
+    u32x4 pk[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float p[8], rr[8], gx[8], num[8], ax[8], sa[8];
+      relu_widen(bf.q[h], p);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) rr[i] = p[i];
+      if (rope_on) rotate8(rr, cs);
+      widen8(bf.g[h], gx);
+      u32x4 rh{}, rlo{}, ah{}, alo{};
+      if constexpr (BF) {
+        split8(rr, rh, rlo);
+        matvec<true>(Nh[h], Nl[h], nullptr, rh, &rlo, nullptr, num);
+      } else {
+        matvec<false>(nullptr, nullptr, Nf[h], u32x4{}, nullptr, rr, num);
+      }
+      float den = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) den += zb[h][i] * p[i];
+      den = sum4_lanes(den) + a.eps;
+      const float inv = 1.0f / den;
+      float go = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ax[i] = gx[i] * inv;
+        go += gx[i] * (num[i] * inv);
+      }
+      const float beta = -sum4_lanes(go) * inv;
+      if constexpr (BF) {
+        split8(ax, ah, alo);
+        matvec<true>(Th[h], Tl[h], nullptr, ah, &alo, nullptr, sa);
+      } else {
+        matvec<false>(nullptr, nullptr, Tf[h], u32x4{}, nullptr, ax, sa);
+      }
+      if (rope_on) unrotate8(sa, cs);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        sa[i] = p[i] > 0.f ? sa[i] + beta * zb[h][i] : 0.f;
+        zacc[h][i] += beta * p[i];
+      }
+      if (h < nh) put8<EO>(sa, h, pk, rdq, ooff + o_one + h * D * EO);
+      put_tile(0, h, ax, ah, alo);
+      put_tile(1, h, rr, rh, rlo);
+    }
+    if constexpr (EO == 2) store_pair(pk, nh, tl, rdq, ooff + o_pair, ooff + o_one, RO);
+    ooff += 64 * RO;
+
+    // G += a r^T over the group's 16 tokens, per head (wave-local tile).
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if constexpr (BF) {
+      const uint16_t* t16 = reinterpret_cast<const uint16_t*>(wtile);
+      const int Gq = lane >> 4, jr = (lane >> 2) & 3, js = lane & 3;
+      const int r0 = 8 * (Gq >> 1) + jr;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int colb = ((h * D) ^ ((Gq >> 1) << 5)) + 16 * (Gq & 1) + 4 * js;
+        const int e0 = r0 * TCOLS + colb, e1 = e0 + 4 * TCOLS;
+        const u32x4 aH = tr_pair(t16, e0, e1), aL = tr_pair(t16 + WT, e0, e1);
+        const u32x4 rH = tr_pair(t16 + 2 * WT, e0, e1), rL = tr_pair(t16 + 3 * WT, e0, e1);
+        gacc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aH), as_bf16x8(rH), gacc[h], 0, 0, 0);
+        gacc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aH), as_bf16x8(rL), gacc[h], 0, 0, 0);
+        gacc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aL), as_bf16x8(rH), gacc[h], 0, 0, 0);
+      }
+    } else {
+      const float* af = reinterpret_cast<const float*>(wtile);
+      const float* rf = af + WT;
+      const int cl = lane & 31, qq = lane >> 5;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const int row = 2 * s + qq;
+          const int i0 = row * TCOLS + ((h * D + cl) ^ (((row >> 3) & 1) << 5));
+          gacc[h] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i0], rf[i0], gacc[h], 0, 0, 0);
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  for (int gi = w; gi < ngroups; gi += 8) {
+    run_group(b0);
+    load_group(b0);
+    run_group(b1);
+    load_group(b1);
+  }
+
+  // Sum the four waves: G through LDS (over the tiles), gz across the 16 lanes
+  // of a row (the chunk's tokens) and then the waves.
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int e = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      red[((w * 2 + h) * D + e) * D + (lane & 31)] = gacc[h][v];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float s = zacc[h][i];
+      s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x121, 0xf, 0xf, false));
+      s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x122, 0xf, 0xf, false));
+      s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x124, 0xf, 0xf, false));
+      s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x128, 0xf, 0xf, false));
+      if (tl == 0) zred[(w * 2 + h) * D + 8 * ch + i] = s;
+    }
+  }
+  __syncthreads();
+  const int nchunk = a.nb * a.cpb;
+  for (int el = threadIdx.x; el < 2 * REC32; el += NT) {
+    const int h = el / REC32, o = el - h * REC32;
+    if (h >= nh) break;
+    float s;
+    if (o < D * D) {
+      s = red[((0 * 2 + h) * D * D) + o] + red[((1 * 2 + h) * D * D) + o] + red[((2 * 2 + h) * D * D) + o] +
+          red[((3 * 2 + h) * D * D) + o];
+    } else {
+      const int f = o - D * D;
+      s = zred[(0 * 2 + h) * D + f] + zred[(1 * 2 + h) * D + f] + zred[(2 * 2 + h) * D + f] + zred[(3 * 2 + h) * D + f];
+    }
+    a.part[((size_t)(b * a.H + h0 + h) * nchunk + ci) * REC32 + o] = s;
+  }
+}
+
 // ---------------------------------------------------------------- helpers
 
 __global__ void k_rope_table(float2* tab, int pt, int ph, int pw, int max_frames, int gh, int gw,
@@ -1034,7 +1546,7 @@ int launch_forward(const Plan& p, const void* q, const void* k, const void* v, v
   PrefixArgs pa;
   pa.part = part; pa.prefix = prefix; pa.S_init = S_init; pa.z_init = z_init;
   pa.S_save = S_save; pa.z_save = z_save; pa.H = p.H; pa.nb = p.nb; pa.cpb = p.cpb;
-  pa.hd = p.D; pa.rec = p.rec;
+  pa.hd = p.D; pa.rec = p.rec; pa.rev = 0;
   const dim3 gp((unsigned)((p.rec + 63) / 64), (unsigned)p.H, (unsigned)p.B);
   hipLaunchKernelGGL(k_prefix, gp, dim3(PFX_NT), 0, s, pa);
   e = hipGetLastError();
@@ -1051,6 +1563,69 @@ int launch_forward(const Plan& p, const void* q, const void* k, const void* v, v
                 : launch_readouts<32>(ra, in_bf16, out_bf16, p2, gr, p.lds_read, s);
   if (e == hipSuccess) e = mark(3);
   return (int)e;
+}
+
+int launch_backward(const Plan& p, const void* q, const void* k, const void* v, const void* dout,
+                    void* dq, void* dk, void* dv, int in_bf16, int grad_bf16, float eps, void* ws,
+                    void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.ws_part);
+  float* prefix = reinterpret_cast<float*>(static_cast<char*>(ws) + p.ws_prefix);
+  float* suffix = reinterpret_cast<float*>(static_cast<char*>(ws) + p.ws_suffix);
+  const PosArgs pa_pos = pos_args(p);
+  const bool p2 = ((p.rope.pt | p.rope.ph | p.rope.pw) & 1) == 0;
+  hipError_t e;
+
+  // Sbar, zbar of every block, as the forward forms them.
+  StateArgs sa;
+  sa.k = k; sa.v = v; sa.part = part;
+  sa.H = p.H; sa.N = p.N; sa.L = p.L; sa.L0 = p.L0; sa.nb = p.nb; sa.cpb = p.cpb; sa.Tc = p.Tc; sa.hg = p.hg;
+  sa.pos = pa_pos;
+  sa.rope = p.rope;
+  const dim3 gs((unsigned)(p.hg * p.nb * p.cpb), (unsigned)p.B);
+  e = launch_state<32>(sa, in_bf16, p2, gs, p.lds_state, s);
+  if (e != hipSuccess) return (int)e;
+  PrefixArgs pa;
+  pa.part = part; pa.prefix = prefix; pa.S_init = nullptr; pa.z_init = nullptr;
+  pa.S_save = nullptr; pa.z_save = nullptr; pa.H = p.H; pa.nb = p.nb; pa.cpb = p.cpb;
+  pa.hd = p.D; pa.rec = p.rec; pa.rev = 0;
+  const dim3 gp((unsigned)((p.rec + 63) / 64), (unsigned)p.H, (unsigned)p.B);
+  hipLaunchKernelGGL(k_prefix, gp, dim3(PFX_NT), 0, s, pa);
+  e = hipGetLastError();
+  if (e != hipSuccess) return (int)e;
+
+  // dq and the chunk partials of (G, gz) (over the forward's partials, which
+  // the prefix kernel has consumed).
+  BwQArgs qa;
+  qa.q = q; qa.g = dout; qa.dq = dq; qa.prefix = prefix; qa.part = part; qa.eps = eps;
+  qa.H = p.H; qa.N = p.N; qa.L = p.L; qa.L0 = p.L0; qa.nb = p.nb; qa.cpb = p.cpb; qa.Tc = p.Tc; qa.hg = p.hg;
+  qa.pos = pa_pos;
+  qa.rope = p.rope;
+  const int lds_q = (4 * 2 * D * D + 4 * 2 * D) * 4 + p.tab_state;
+  if (in_bf16 && grad_bf16) hipLaunchKernelGGL((p2 ? k_bw_q<uint16_t, uint16_t, true> : k_bw_q<uint16_t, uint16_t, false>), gs, dim3(NT), lds_q, s, qa);
+  else if (in_bf16) hipLaunchKernelGGL((p2 ? k_bw_q<uint16_t, float, true> : k_bw_q<uint16_t, float, false>), gs, dim3(NT), lds_q, s, qa);
+  else if (grad_bf16) hipLaunchKernelGGL((p2 ? k_bw_q<float, uint16_t, true> : k_bw_q<float, uint16_t, false>), gs, dim3(NT), lds_q, s, qa);
+  else hipLaunchKernelGGL((p2 ? k_bw_q<float, float, true> : k_bw_q<float, float, false>), gs, dim3(NT), lds_q, s, qa);
+  e = hipGetLastError();
+  if (e != hipSuccess) return (int)e;
+
+  // dS, dz: sums over the blocks at or after each block.
+  pa.prefix = suffix; pa.rev = 1;
+  hipLaunchKernelGGL(k_prefix, gp, dim3(PFX_NT), 0, s, pa);
+  e = hipGetLastError();
+  if (e != hipSuccess) return (int)e;
+
+  BwKVArgs ka;
+  ka.k = k; ka.v = v; ka.dk = dk; ka.dv = dv; ka.suffix = suffix;
+  ka.H = p.H; ka.N = p.N; ka.L = p.L; ka.L0 = p.L0; ka.nb = p.nb; ka.rpb = p.rpb; ka.Tr = p.Tr; ka.hg = p.hg;
+  ka.pos = pa_pos;
+  ka.rope = p.rope;
+  const dim3 gr((unsigned)(p.hg * p.nb * p.rpb), (unsigned)p.B);
+  if (in_bf16 && grad_bf16) hipLaunchKernelGGL((p2 ? k_bw_kv<uint16_t, uint16_t, true> : k_bw_kv<uint16_t, uint16_t, false>), gr, dim3(NT), p.lds_read, s, ka);
+  else if (in_bf16) hipLaunchKernelGGL((p2 ? k_bw_kv<uint16_t, float, true> : k_bw_kv<uint16_t, float, false>), gr, dim3(NT), p.lds_read, s, ka);
+  else if (grad_bf16) hipLaunchKernelGGL((p2 ? k_bw_kv<float, uint16_t, true> : k_bw_kv<float, uint16_t, false>), gr, dim3(NT), p.lds_read, s, ka);
+  else hipLaunchKernelGGL((p2 ? k_bw_kv<float, float, true> : k_bw_kv<float, float, false>), gr, dim3(NT), p.lds_read, s, ka);
+  return (int)hipGetLastError();
 }
 
 }  // namespace lavr

@@ -50,6 +50,9 @@ def _load():
                                                   c_int, c_int, c_int, c_int, c_int, c_int,
                                                   ctypes.POINTER(LaRope), c_float, c_vp, c_size,
                                                   c_vp, ctypes.POINTER(c_vp)]),
+        "la_backward_workspace_bytes": (c_size, [c_int] * 7),
+        "la_block_causal_backward": (c_int, [c_vp] * 7 + [c_int] * 9 + [ctypes.POINTER(LaRope), c_float,
+                                                                         c_vp, c_size, c_vp]),
         "la_state_init": (c_int, [ctypes.POINTER(LaState), c_vp, c_vp, c_int, c_int, c_int, c_vp]),
         "la_stream_block": (c_int, [ctypes.POINTER(LaState), c_vp, c_vp, c_vp, c_vp, c_int, c_int,
                                     c_int, c_int, c_int, c_int, c_int, ctypes.POINTER(LaRope),
@@ -67,7 +70,8 @@ def _load():
 lib = _load()
 
 EXPORTS = ("rope_table_bytes", "rope_table_build", "la_workspace_bytes", "la_block_causal_forward",
-           "la_block_causal_forward_timed", "la_state_init", "la_stream_block", "la_status_string", "la_version")
+           "la_block_causal_forward_timed", "la_backward_workspace_bytes", "la_block_causal_backward",
+           "la_state_init", "la_stream_block", "la_status_string", "la_version")
 
 
 def status_string(code):
@@ -189,6 +193,72 @@ def block_causal_forward(q, k, v, block_frames, tokens_per_frame, rope=None, eps
                                        float(eps), _ptr(ws), ws.numel() * ws.element_size(),
                                        _stream(q.device)), "la_block_causal_forward")
     return out
+
+
+# ------------------------------------------------------------------ backward
+
+def backward_workspace_bytes(B, H, frames, tokens_per_frame, block_frames, head_dim=HEAD_DIM,
+                             first_block_frames=0):
+    n = lib.la_backward_workspace_bytes(int(B), int(H), int(head_dim), int(frames),
+                                        int(tokens_per_frame), int(block_frames),
+                                        int(first_block_frames or 0))
+    if n == 0:
+        raise ValueError("invalid shape for la_backward_workspace_bytes")
+    return n
+
+
+def block_causal_backward(q, k, v, dout, block_frames, tokens_per_frame, rope=None, eps=EPS_DEFAULT,
+                          grad_dtype=None, first_block_frames=None, workspace=None):
+    """Gradients (dq, dk, dv) of sum(dout * block_causal_forward(q, k, v, ...))."""
+    _check_qkv(q, k, v)
+    _check_qkv(q, k, dout)
+    B, N, H, d = q.shape
+    if N % tokens_per_frame:
+        raise ValueError("N must be a multiple of tokens_per_frame")
+    frames = N // tokens_per_frame
+    grad_dtype = q.dtype if grad_dtype is None else grad_dtype
+    dq, dk, dv = (torch.empty((B, N, H, d), dtype=grad_dtype, device=q.device) for _ in range(3))
+    f0 = int(first_block_frames or 0)
+    need = lib.la_backward_workspace_bytes(B, H, d, frames, int(tokens_per_frame), int(block_frames), f0)
+    if need == 0:
+        raise ValueError(f"backward not built for head dim {d} or invalid shape")
+    ws = _workspace(q.device, need) if workspace is None else workspace
+    _check(lib.la_block_causal_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk),
+                                        _ptr(dv), _dtype_code(q.dtype), _dtype_code(grad_dtype), B, H,
+                                        d, frames, int(tokens_per_frame), int(block_frames), f0,
+                                        _rope_ptr(rope), float(eps), _ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream(q.device)),
+           "la_block_causal_backward")
+    return dq, dk, dv
+
+
+class BlockCausalAttention(torch.autograd.Function):
+    """Autograd binding: forward through la_block_causal_forward, backward through
+    la_block_causal_backward (gradients in the input dtype)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, block_frames, tokens_per_frame, rope=None, eps=EPS_DEFAULT,
+                first_block_frames=None):
+        q, k, v = (t.contiguous() for t in (q, k, v))
+        ctx.save_for_backward(q, k, v)
+        ctx.args = (block_frames, tokens_per_frame, rope, eps, first_block_frames)
+        return block_causal_forward(q, k, v, block_frames, tokens_per_frame, rope, eps,
+                                    first_block_frames=first_block_frames)
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v = ctx.saved_tensors
+        bf, tpf, rope, eps, f0 = ctx.args
+        dq, dk, dv = block_causal_backward(q, k, v, dout.contiguous().to(q.dtype), bf, tpf, rope, eps,
+                                           first_block_frames=f0)
+        return dq, dk, dv, None, None, None, None, None
+
+
+def block_causal_attention(q, k, v, block_frames, tokens_per_frame, rope=None, eps=EPS_DEFAULT,
+                           first_block_frames=None):
+    """Differentiable block-causal ReLU linear attention (see BlockCausalAttention)."""
+    return BlockCausalAttention.apply(q, k, v, block_frames, tokens_per_frame, rope, eps,
+                                      first_block_frames)
 
 
 # ----------------------------------------------------------------- streaming

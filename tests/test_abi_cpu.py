@@ -162,3 +162,39 @@ def test_state_init_rejects(lavr):
     assert f(ctypes.byref(st), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 4), 1, 1, 32, None) == 1
     assert f(ctypes.byref(st), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 4096), 1, 1, 48, None) == 2
     assert f(ctypes.byref(st), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 64), 1, 1, 32, None) == 1  # overlap
+
+
+def call_backward(lavr, **kw):
+    args = dict(q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, g=FAKE + 0x3000000,
+                dq=FAKE + 0x4000000, dk=FAKE + 0x5000000, dv=FAKE + 0x6000000,
+                in_dt=lavr.LA_BF16, grad_dt=lavr.LA_BF16, B=1, H=2, d=32, frames=4, tpf=6,
+                bf=2, f0=0, rope=None, eps=1e-8, ws=FAKE + 0x7000000, ws_bytes=1 << 20)
+    args.update(kw)
+    vp = ctypes.c_void_p
+    return lavr.lib.la_block_causal_backward(
+        vp(args["q"]), vp(args["k"]), vp(args["v"]), vp(args["g"]), vp(args["dq"]), vp(args["dk"]),
+        vp(args["dv"]), args["in_dt"], args["grad_dt"], args["B"], args["H"], args["d"],
+        args["frames"], args["tpf"], args["bf"], args["f0"], args["rope"], args["eps"],
+        vp(args["ws"]), args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(g=0), 1),                          # null output gradient
+    (dict(dk=FAKE + 0x5000000 + 4), 1),      # misaligned gradient
+    (dict(dq=FAKE + 0x1000000 + 128), 1),    # dq overlaps k
+    (dict(dv=FAKE + 0x5000000 + 64), 1),     # dv overlaps dk
+    (dict(d=64), 2),                         # the backward builds head dim 32 only
+    (dict(d=48), 2),
+    (dict(grad_dt=5), 1),
+    (dict(eps=-1.0), 1),
+    (dict(ws_bytes=16), 1),
+    (dict(bf=0), 1),
+])
+def test_backward_rejects_bad_arguments(lavr, kw, code):
+    assert call_backward(lavr, **kw) == code
+
+
+def test_backward_workspace_bytes(lavr):
+    n = lavr.backward_workspace_bytes(1, 70, 240, 1560, 8)
+    assert n > lavr.workspace_bytes(1, 70, 240, 1560, 8)     # plus the suffix records
+    assert lavr.lib.la_backward_workspace_bytes(1, 35, 64, 240, 1560, 8, 0) == 0

@@ -1,0 +1,173 @@
+"""GPU parity of the backward (la_block_causal_backward) against the fp64 oracle backward."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import TOL_BF16, TOL_F32, device_inputs, err_bf16_out, to_f64_torch
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+TOL_BF16_IN_F32_GRAD = 1e-3     # bf16 inputs, fp32 gradients (hi/lo operand split inside)
+
+
+@pytest.fixture(scope="module")
+def lavr():
+    import __graft_entry__
+    __graft_entry__.ensure_built()
+    from linear_attention_video_relu_amd import lavr
+    return lavr
+
+
+def W():
+    from linear_attention_video_relu_amd import workloads
+    return workloads
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def small_cfg(**kw):
+    base = dict(index=200, B=2, H=3, head_dim=32, frames=11, tokens_per_frame=60, grid=(6, 10),
+                block_frames=3, dtype="bf16", rope={"split": (8, 12, 12), "base": 10000.0},
+                scale=1.0, outlier_frac=0.05, outlier_scale=8.0, name="bw_small")
+    base.update(kw)
+    return base
+
+
+def rope_for(lavr, cfg):
+    if cfg.get("rope") is None:
+        return None
+    return lavr.RopeTable(cfg["rope"]["split"], cfg["grid"], cfg["frames"], cfg["rope"]["base"], DEV)
+
+
+def draw_dout(cfg, seed=7):
+    """A seeded output gradient with the inputs' shape and dtype."""
+    w = W()
+    shape = (cfg["B"], w.n_tokens(cfg), cfg["H"], cfg["head_dim"])
+    x = np.random.default_rng([seed, cfg["index"]]).standard_normal(shape, dtype=np.float32)
+    arr = w.f32_to_bf16_bits(x) if cfg["dtype"] == "bf16" else x
+    return arr, w.to_torch(cfg, arr, DEV)
+
+
+def oracle_grads(cfg, arrs, garr):
+    w = W()
+    q, k, v = (w.to_f64(cfg, arrs[t]) for t in w.TENSORS)
+    g = w.to_f64(cfg, garr)
+    return oracle.backward(q, k, v, g, cfg["tokens_per_frame"], cfg["block_frames"], w.oracle_rope(cfg),
+                           first_block_frames=cfg.get("first_block_frames"))
+
+
+def run(lavr, cfg, grad_dtype):
+    arrs, (q, k, v) = device_inputs(cfg, DEV)
+    garr, g = draw_dout(cfg)
+    grads = lavr.block_causal_backward(q, k, v, g, cfg["block_frames"], cfg["tokens_per_frame"],
+                                       rope_for(lavr, cfg), grad_dtype=grad_dtype,
+                                       first_block_frames=cfg.get("first_block_frames"))
+    torch.cuda.synchronize()
+    return [to_f64_torch(x) for x in grads], oracle_grads(cfg, arrs, garr)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(),                                              # B=2, H=3 (a half-empty head pair), ragged last block
+    dict(frames=12, block_frames=4, H=2, B=1),
+    dict(frames=40, block_frames=3, H=2, B=1, tokens_per_frame=48, grid=(6, 8)),   # many tiles
+    dict(rope={"split": (6, 14, 12), "base": 10000.0}),  # odd pair counts
+    dict(frames=11, block_frames=3, first_block_frames=4),
+    dict(rope=None),
+])
+@pytest.mark.parametrize("grad", ["f32", "bf16"])
+def test_backward_small_bf16_inputs(lavr, kw, grad):
+    cfg = small_cfg(**kw)
+    say(f"case backward {kw} grads={grad}")
+    got, ref = run(lavr, cfg, torch.float32 if grad == "f32" else torch.bfloat16)
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        if grad == "f32":
+            e = oracle.rel_err(a, b)
+            say(f"  {name} rel err {e:.3e}")
+            assert e <= TOL_BF16_IN_F32_GRAD
+        else:
+            e = err_bf16_out(a, b)
+            say(f"  {name} rel err beyond bf16 rounding {e:.3e}")
+            assert e <= TOL_BF16
+
+
+@pytest.mark.parametrize("split", [(8, 12, 12), (6, 14, 12)])
+def test_backward_f32_inputs(lavr, split):
+    cfg = small_cfg(dtype="f32", rope={"split": split, "base": 10000.0})
+    say(f"case backward f32 split {split}")
+    got, ref = run(lavr, cfg, torch.float32)
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        e = oracle.rel_err(a, b)
+        say(f"  {name} rel err {e:.3e}")
+        assert e <= 10 * TOL_F32
+
+
+def test_backward_zero_queries_and_one_token_blocks(lavr):
+    cfg = small_cfg(dtype="f32", frames=40, tokens_per_frame=1, grid=(1, 1), block_frames=1,
+                    rope={"split": (32, 0, 0), "base": 10000.0}, B=1, H=2)
+    say("case backward one-token blocks, zero queries")
+    arrs, _ = device_inputs(cfg, DEV)
+    arrs["q"][:, 7] = -np.abs(arrs["q"][:, 7])
+    w = W()
+    q, k, v = (w.to_torch(cfg, arrs[t], DEV) for t in w.TENSORS)
+    garr, g = draw_dout(cfg)
+    dq, dk, dv = lavr.block_causal_backward(q, k, v, g, 1, 1, rope_for(lavr, cfg))
+    torch.cuda.synchronize()
+    ref = oracle_grads(cfg, arrs, garr)
+    for name, a, b in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        e = oracle.rel_err(to_f64_torch(a), b)
+        say(f"  {name} rel err {e:.3e}")
+        assert e <= 10 * TOL_F32
+    assert torch.all(dq[:, 7] == 0).item()
+    assert torch.isfinite(dk).all().item() and torch.isfinite(dv).all().item()
+
+
+def test_autograd_binding(lavr):
+    cfg = small_cfg(frames=9)
+    say("case autograd binding")
+    arrs, (q, k, v) = device_inputs(cfg, DEV)
+    garr, g = draw_dout(cfg)
+    q, k, v = (t.clone().requires_grad_(True) for t in (q, k, v))
+    out = lavr.block_causal_attention(q, k, v, cfg["block_frames"], cfg["tokens_per_frame"], rope_for(lavr, cfg))
+    (out.float() * g.float()).sum().backward()
+    torch.cuda.synchronize()
+    ref = oracle_grads(cfg, arrs, garr)
+    for name, t, b in zip(("dq", "dk", "dv"), (q, k, v), ref):
+        e = err_bf16_out(to_f64_torch(t.grad), b)
+        say(f"  {name} rel err beyond bf16 rounding {e:.3e}")
+        assert e <= TOL_BF16
+
+
+def test_backward_deterministic(lavr):
+    cfg = small_cfg(frames=9)
+    _, (q, k, v) = device_inputs(cfg, DEV)
+    _, g = draw_dout(cfg)
+    rope = rope_for(lavr, cfg)
+    a = [x.clone() for x in lavr.block_causal_backward(q, k, v, g, 3, cfg["tokens_per_frame"], rope)]
+    b = lavr.block_causal_backward(q, k, v, g, 3, cfg["tokens_per_frame"], rope)
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("name,heads", [("clip480p_bf16", [(0, 0), (0, 35), (0, 69)])])
+def test_backward_full_size(lavr, name, heads):
+    w = W()
+    cfg = w.workload(name)
+    say(f"case backward full-size {name}")
+    arrs, (q, k, v) = device_inputs(cfg, DEV)
+    garr, g = draw_dout(cfg)
+    dq, dk, dv = lavr.block_causal_backward(q, k, v, g, cfg["block_frames"], cfg["tokens_per_frame"],
+                                            rope_for(lavr, cfg), grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for b_, h in heads:
+        ref = oracle.backward_head(*(w.to_f64(cfg, arrs[t][b_, :, h]) for t in w.TENSORS),
+                                   w.to_f64(cfg, garr[b_, :, h]), cfg["tokens_per_frame"],
+                                   cfg["block_frames"], w.oracle_rope(cfg))
+        for nm, t, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+            e = oracle.rel_err(to_f64_torch(t[b_, :, h]), r)
+            say(f"  b={b_} h={h} {nm} rel err {e:.3e}")
+            assert e <= TOL_BF16_IN_F32_GRAD
