@@ -144,6 +144,8 @@ def main():
     ap.add_argument("--workload", default="minute_bf16", choices=sorted(W.WORKLOADS))
     ap.add_argument("--cpu-heads", type=int, default=30, help="oracle sample size (0 = skip)")
     ap.add_argument("--stream-reps", type=int, default=3, help="timed 40-call streaming runs (0 = skip)")
+    ap.add_argument("--backward-steps", type=int, default=10,
+                    help="timed la_block_causal_backward calls on the same workload (0 = skip)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 1 GiB fill and a 1 GiB device copy, the known-size kernels "
                          "that scale the HBM byte counters")
@@ -266,8 +268,52 @@ def main():
 
     if args.stream_reps > 0:
         result["streaming"] = bench_streaming(lavr, torch, dev, args.stream_reps)
+    if args.backward_steps > 0 and d == 32:
+        del out
+        result["backward"] = bench_backward(lavr, torch, dev, cfg, q, k, v, rope, args.backward_steps)
 
     print(json.dumps(result), flush=True)
+
+
+def bench_backward(lavr, torch, dev, cfg, q, k, v, rope, steps):
+    """Time la_block_causal_backward (dq, dk, dv in the input dtype) on the forward's inputs."""
+    B, H, N, d = cfg["B"], cfg["H"], W.n_tokens(cfg), cfg["head_dim"]
+    tpf, bf = cfg["tokens_per_frame"], cfg["block_frames"]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    g = torch.randn(q.shape, generator=gen, device=dev, dtype=torch.float32).to(q.dtype)
+    grads = [torch.empty_like(q) for _ in range(3)]
+    need = lavr.backward_workspace_bytes(B, H, cfg["frames"], tpf, bf)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    code = lavr._dtype_code(q.dtype)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    ptrs = [ctypes.c_void_p(x.data_ptr()) for x in (q, k, v, g, *grads)]
+
+    def call():
+        rc = lavr.lib.la_block_causal_backward(*ptrs, code, code, B, H, d, cfg["frames"], tpf, bf, 0,
+                                               ctypes.byref(rope.desc), 1e-8,
+                                               ctypes.c_void_p(ws.data_ptr()), need, stream)
+        if rc:
+            raise RuntimeError(lavr.status_string(rc))
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / steps
+    th = B * N * H
+    esz = q.element_size()
+    nb = -(-cfg["frames"] // bf)
+    # q, k, v, dout read; k, v read again for the block states; dq, dk, dv written;
+    # (S, z) records: prefixes and suffixes written and read once each
+    alg = 9 * th * d * esz + 4 * B * H * nb * rec_bytes(d)
+    return {"ms": ms, "tokens_heads_per_s": th / (ms / 1e3), "alg_bytes": alg,
+            "gbs": alg / (ms * 1e6), "frac_of_peak": alg / (ms * 1e6) / HBM_PEAK_GBS, "steps": steps}
 
 
 def bench_streaming(lavr, torch, dev, reps):

@@ -654,7 +654,7 @@ __global__ __launch_bounds__(PFX_NT) void k_prefix(PrefixArgs a) {
 // buffer range check.
 
 template <typename TIn, typename TOut, bool P2, int DH>
-__global__ __launch_bounds__(NT) void k_readout(ReadArgs a) {
+__global__ __launch_bounds__(NT, DH == 32 ? 4 : 2) void k_readout(ReadArgs a) {
   constexpr bool BF = sizeof(TIn) == 2;
   constexpr bool W64 = DH == 64;
   constexpr int RECN = DH * DH + DH;
@@ -1069,7 +1069,7 @@ __device__ __forceinline__ void store_pair(const u32x4* pk, int nh, int tl, __am
 // (R^T dkappa + dz), both products on MFMA with row-permuted A operands.
 
 template <typename TIn, typename TOut, bool P2>
-__global__ __launch_bounds__(NT) void k_bw_kv(BwKVArgs a) {
+__global__ __launch_bounds__(NT, 2) void k_bw_kv(BwKVArgs a) {
   constexpr bool BF = sizeof(TIn) == 2;
   constexpr int ES = (int)sizeof(TIn), EO = (int)sizeof(TOut);
   extern __shared__ __align__(16) unsigned char smem[];
@@ -1198,7 +1198,7 @@ __global__ __launch_bounds__(NT) void k_bw_kv(BwKVArgs a) {
 // written as the chunk's (G, gz) records.
 
 template <typename TIn, typename TOut, bool P2>
-__global__ __launch_bounds__(NT) void k_bw_q(BwQArgs a) {
+__global__ __launch_bounds__(NT, 2) void k_bw_q(BwQArgs a) {
   constexpr bool BF = sizeof(TIn) == 2;
   constexpr int ES = (int)sizeof(TIn), EO = (int)sizeof(TOut);
   constexpr int WT = 16 * TCOLS;                     // elements of one wave tile array
@@ -1206,7 +1206,8 @@ __global__ __launch_bounds__(NT) void k_bw_q(BwQArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   float* red = reinterpret_cast<float*>(smem);                // [4 waves][2 heads][1024] at the end
   float* zred = red + 4 * 2 * D * D;                           // [4 waves][2 heads][32]
-  float2* tab = reinterpret_cast<float2*>(zred + 4 * 2 * D);
+  u32x4* ops = reinterpret_cast<u32x4*>(zred + 4 * 2 * D);     // [16 operands][64 lanes] (see below)
+  float2* tab = reinterpret_cast<float2*>(ops + 16 * 64);
 
   const int g = blockIdx.x % a.hg;
   const int ci = blockIdx.x / a.hg;
@@ -1245,18 +1246,60 @@ __global__ __launch_bounds__(NT) void k_bw_q(BwQArgs a) {
     tp.init(c0 + w * 16 + tl, a.pos);
   }
 
-  u32x4 Nh[2][2], Nl[2][2], Th[2][2], Tl[2][2];
-  float Nf[2][2][8], Tf[2][2][8];
+  // Sbar and Sbar^T operand tiles of both heads are the same for every wave:
+  // wave 0 forms them once and parks them in LDS, one 16-byte slot per lane
+  // (conflict-free reads), so the loop reads them per group instead of holding
+  // 64 registers through it.  Slot op = ((h * 2 + transposed) * 2 + tile) * 2
+  // + part (bf16: hi, lo; fp32: floats 0-3, 4-7 of the tile's 8).
+  if (w == 0) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int hd = min(h, nh - 1);
+      const float* rec = a.prefix + ((size_t)(b * a.H + h0 + hd) * a.nb + j) * REC32;
+      u32x4 th[2], tlo[2];
+      float tf[2][8];
+#pragma unroll
+      for (int tr = 0; tr < 2; ++tr) {
+        if (tr == 0) perm_tiles<BF, false>(rec, lane, th, tlo, tf);
+        else perm_tiles<BF, true>(rec, lane, th, tlo, tf);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int op = ((h * 2 + tr) * 2 + t) * 2;
+          if constexpr (BF) {
+            ops[op * 64 + lane] = th[t];
+            ops[(op + 1) * 64 + lane] = tlo[t];
+          } else {
+            ops[op * 64 + lane] = __builtin_bit_cast(u32x4, f32x4{tf[t][0], tf[t][1], tf[t][2], tf[t][3]});
+            ops[(op + 1) * 64 + lane] = __builtin_bit_cast(u32x4, f32x4{tf[t][4], tf[t][5], tf[t][6], tf[t][7]});
+          }
+        }
+      }
+    }
+  }
   float zb[2][8];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int hd = min(h, nh - 1);
     const float* rec = a.prefix + ((size_t)(b * a.H + h0 + hd) * a.nb + j) * REC32;
-    perm_tiles<BF, false>(rec, lane, Nh[h], Nl[h], Nf[h]);
-    perm_tiles<BF, true>(rec, lane, Th[h], Tl[h], Tf[h]);
 #pragma unroll
     for (int i = 0; i < 8; ++i) zb[h][i] = rec[D * D + 8 * ch + i];
   }
+  // Operand tiles of head h (transposed or not) back from LDS.
+  auto get_ops = [&](int h, int tr, u32x4* hi, u32x4* lo, float (*fs)[8]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int op = ((h * 2 + tr) * 2 + t) * 2;
+      const u32x4 x0 = ops[op * 64 + lane], x1 = ops[(op + 1) * 64 + lane];
+      if constexpr (BF) {
+        hi[t] = x0;
+        lo[t] = x1;
+      } else {
+        const f32x4 f0 = __builtin_bit_cast(f32x4, x0), f1 = __builtin_bit_cast(f32x4, x1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { fs[t][i] = f0[i]; fs[t][4 + i] = f1[i]; }
+      }
+    }
+  };
 
   struct Buf { Raw8<TIn> q[2], g[2]; };
   auto load_group = [&](Buf& bf) {
@@ -1312,29 +1355,33 @@ __global__ __launch_bounds__(NT) void k_bw_q(BwQArgs a) {
       if (rope_on) rotate8(rr, cs);
       widen8(bf.g[h], gx);
       u32x4 rh{}, rlo{}, ah{}, alo{};
+      u32x4 Mh[2], Ml[2];
+      float Mf[2][8];
+      get_ops(h, 0, Mh, Ml, Mf);
       if constexpr (BF) {
         split8(rr, rh, rlo);
-        matvec<true>(Nh[h], Nl[h], nullptr, rh, &rlo, nullptr, num);
+        matvec<true>(Mh, Ml, nullptr, rh, &rlo, nullptr, num);
       } else {
-        matvec<false>(nullptr, nullptr, Nf[h], u32x4{}, nullptr, rr, num);
+        matvec<false>(nullptr, nullptr, Mf, u32x4{}, nullptr, rr, num);
       }
       float den = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) den += zb[h][i] * p[i];
       den = sum4_lanes(den) + a.eps;
-      const float inv = 1.0f / den;
+      const float inv = __builtin_amdgcn_rcpf(den);   // v_rcp_f32, as in the readout
       float go = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         ax[i] = gx[i] * inv;
-        go += gx[i] * (num[i] * inv);
+        go += gx[i] * num[i];
       }
-      const float beta = -sum4_lanes(go) * inv;
+      const float beta = -sum4_lanes(go) * (inv * inv);
+      get_ops(h, 1, Mh, Ml, Mf);
       if constexpr (BF) {
         split8(ax, ah, alo);
-        matvec<true>(Th[h], Tl[h], nullptr, ah, &alo, nullptr, sa);
+        matvec<true>(Mh, Ml, nullptr, ah, &alo, nullptr, sa);
       } else {
-        matvec<false>(nullptr, nullptr, Tf[h], u32x4{}, nullptr, ax, sa);
+        matvec<false>(nullptr, nullptr, Mf, u32x4{}, nullptr, ax, sa);
       }
       if (rope_on) unrotate8(sa, cs);
 #pragma unroll
@@ -1601,7 +1648,7 @@ int launch_backward(const Plan& p, const void* q, const void* k, const void* v, 
   qa.H = p.H; qa.N = p.N; qa.L = p.L; qa.L0 = p.L0; qa.nb = p.nb; qa.cpb = p.cpb; qa.Tc = p.Tc; qa.hg = p.hg;
   qa.pos = pa_pos;
   qa.rope = p.rope;
-  const int lds_q = (4 * 2 * D * D + 4 * 2 * D) * 4 + p.tab_state;
+  const int lds_q = (4 * 2 * D * D + 4 * 2 * D) * 4 + 16 * 64 * 16 + p.tab_state;
   if (in_bf16 && grad_bf16) hipLaunchKernelGGL((p2 ? k_bw_q<uint16_t, uint16_t, true> : k_bw_q<uint16_t, uint16_t, false>), gs, dim3(NT), lds_q, s, qa);
   else if (in_bf16) hipLaunchKernelGGL((p2 ? k_bw_q<uint16_t, float, true> : k_bw_q<uint16_t, float, false>), gs, dim3(NT), lds_q, s, qa);
   else if (grad_bf16) hipLaunchKernelGGL((p2 ? k_bw_q<float, uint16_t, true> : k_bw_q<float, uint16_t, false>), gs, dim3(NT), lds_q, s, qa);
