@@ -317,6 +317,65 @@ def stream_block(state, q, k, v, tokens_per_frame, rope=None, eps=EPS_DEFAULT, s
     return out
 
 
+# ------------------------------------------------------ fused q/k/v prologue
+#
+# The projection of x (B, N, C) to q, k, v gives one (B, N, 3, C) tensor: per
+# token row q (C channels), then k, then v ([ImplBCLA], "The Linear Attention
+# Kernel", step 1: x projects to Q/K/V through learned weights; the (3, C) order
+# inside a row is a reading, the pages do not fix it).  qk_norm ([ImplBCLA],
+# "Direct Instantiation of ChunkCausalAttention", the qk_norm flag) is read as
+# RMSNorm -- the norm class the pages name ([SANA-WM], review thread) -- over
+# the C channels of each token's q and of its k, before the split into heads,
+# with one learned weight per channel.  The pages give no eps for it; it is an
+# argument here.
+
+NORM_EPS_DEFAULT = 1e-6
+
+
+def qk_rms_norm(x, gamma, norm_eps=NORM_EPS_DEFAULT):
+    """RMSNorm over the last axis: x / sqrt(mean(x**2) + norm_eps) * gamma."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + norm_eps) * np.asarray(gamma, dtype=np.float64)
+
+
+def split_qkv(qkv, heads):
+    """(B, N, 3, C) projection output -> q, k, v as (B, N, C) float64 arrays."""
+    qkv = np.asarray(qkv, dtype=np.float64)
+    B, N, three, C = qkv.shape
+    if three != 3 or C % heads:
+        raise ValueError("qkv must be (B, N, 3, heads * head_dim)")
+    return qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+
+
+def _prologue(qkv, heads, q_gamma, k_gamma, norm_eps):
+    q, k, v = split_qkv(qkv, heads)
+    if q_gamma is not None:
+        q = qk_rms_norm(q, q_gamma, norm_eps)
+    if k_gamma is not None:
+        k = qk_rms_norm(k, k_gamma, norm_eps)
+    B, N, C = q.shape
+    d = C // heads
+    return tuple(a.reshape(B, N, heads, d) for a in (q, k, v))
+
+
+def forward_qkv(qkv, heads, tokens_per_frame, block_frames, rope=None, eps=EPS_DEFAULT,
+                q_gamma=None, k_gamma=None, norm_eps=NORM_EPS_DEFAULT, first_block_frames=None):
+    """Block-causal forward from the fused (B, N, 3, C) projection output, with
+    the optional q/k RMSNorm (a None weight leaves that tensor as it is).
+    Returns out (B, N, heads, C // heads) float64."""
+    q, k, v = _prologue(qkv, heads, q_gamma, k_gamma, norm_eps)
+    return forward(q, k, v, tokens_per_frame, block_frames, rope, eps,
+                   first_block_frames=first_block_frames)
+
+
+def stream_block_qkv(state, qkv, heads, tokens_per_frame, rope=None, eps=EPS_DEFAULT,
+                     q_gamma=None, k_gamma=None, norm_eps=NORM_EPS_DEFAULT, save=True):
+    """stream_block from the fused projection output (see forward_qkv)."""
+    q, k, v = _prologue(qkv, heads, q_gamma, k_gamma, norm_eps)
+    return stream_block(state, q, k, v, tokens_per_frame, rope, eps, save)
+
+
 # ------------------------------------------------------------- independent checks
 
 def brute_force(q, k, v, tokens_per_frame, block_frames, rope=None, eps=EPS_DEFAULT,
