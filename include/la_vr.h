@@ -1,6 +1,7 @@
 /*
  * la_vr.h -- C ABI of liblavr: block-causal ReLU linear attention with RoPE
- * (forward, one-shot and streaming) on AMD MI355X (gfx950).
+ * (forward, one-shot and streaming; its backward; a fused q/k/v input with the
+ * q/k RMSNorm prologue) on AMD MI355X (gfx950).
  *
  * What is computed.  For every batch row b and head h, with phi = ReLU applied
  * elementwise to queries and keys ("Implementing Block Causal Linear Attention
@@ -182,6 +183,48 @@ int la_stream_block(la_state* st, const void* q, const void* k, const void* v, v
                     la_dtype in_dt, la_dtype out_dt, int B, int H, int head_dim,
                     int block_frames, int tokens_per_frame, const la_rope* rope, float eps,
                     int save, void* ws, size_t ws_bytes, void* stream);
+
+/* Fused prologue.  The projection of x (B, N, C) to queries, keys and values
+ * ("Implementing Block Causal Linear Attention for Long Video Generation with
+ * Sana", "The Linear Attention Kernel", step 1) hands over one contiguous
+ * (B, N, 3, C) tensor qkv: each token row holds q (C = H * head_dim channels,
+ * heads in order), then k, then v.  The attention module's qk_norm flag (same
+ * page, "Direct Instantiation of ChunkCausalAttention") is taken as RMSNorm of
+ * each token's q and k over its C channels, with one weight per channel:
+ *   x_hat = x / sqrt(mean_C(x^2) + norm_eps) * gamma,
+ * applied before phi (a weight may be negative).  The pages name the flag
+ * only; this reading is the library's.  The kernels read q, k, v in place
+ * from the fused rows, so neither a split copy nor normalised q and k make a
+ * round trip through memory; a small pre-pass forms the per-token 1 / rms
+ * values (8 bytes per token in the workspace). */
+
+/* Workspace bytes of la_block_causal_forward_qkv (for la_stream_block_qkv pass
+ * frames = block_frames and first_block_frames = 0).  0 for invalid sizes. */
+size_t la_qkv_workspace_bytes(int B, int H, int head_dim, int frames, int tokens_per_frame,
+                              int block_frames, int first_block_frames);
+
+/* la_block_causal_forward from the fused input qkv (B, N, 3, H * head_dim) of
+ * dtype in_dt (16-byte aligned).  q_gamma and k_gamma are device arrays of
+ * H * head_dim fp32 weights (16-byte aligned), or NULL to leave that tensor
+ * unnormalised; norm_eps must be finite and > 0 when either is given.  out is
+ * (B, N, H, head_dim) of dtype out_dt and must not overlap qkv or the weights.
+ * ws (256-byte aligned, ws_bytes >= la_qkv_workspace_bytes) is caller-owned
+ * scratch.  Block schedule, RoPE, eps, status codes and stream semantics as
+ * for la_block_causal_forward. */
+int la_block_causal_forward_qkv(const void* qkv, void* out, la_dtype in_dt, la_dtype out_dt,
+                                int B, int H, int head_dim, int frames, int tokens_per_frame,
+                                int block_frames, int first_block_frames, const la_rope* rope,
+                                float eps, const float* q_gamma, const float* k_gamma,
+                                float norm_eps, void* ws, size_t ws_bytes, void* stream);
+
+/* la_stream_block from the fused input: qkv is (B, block_frames *
+ * tokens_per_frame, 3, H * head_dim); weights and norm_eps as for
+ * la_block_causal_forward_qkv; cache semantics as for la_stream_block. */
+int la_stream_block_qkv(la_state* st, const void* qkv, void* out, la_dtype in_dt, la_dtype out_dt,
+                        int B, int H, int head_dim, int block_frames, int tokens_per_frame,
+                        const la_rope* rope, float eps, const float* q_gamma,
+                        const float* k_gamma, float norm_eps, int save, void* ws,
+                        size_t ws_bytes, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* la_status_string(int status);

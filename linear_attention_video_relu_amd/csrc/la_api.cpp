@@ -89,9 +89,11 @@ bool split_block(int L, int max_tokens, long long min_n, int mult, const la_rope
   }
 }
 
-// first_block_frames: frames of the first block (0 = block_frames).
+// first_block_frames: frames of the first block (0 = block_frames).  row_mult:
+// input token rows hold row_mult * H * head_dim elements (3 for fused q|k|v).
 int make_plan(Plan* p, int B, int H, int head_dim, int frames, int tpf, int block_frames,
-              int first_block_frames, const la_rope* rope, long long t0, la_dtype in_dt) {
+              int first_block_frames, const la_rope* rope, long long t0, la_dtype in_dt,
+              int row_mult = 1) {
   if (B < 1 || H < 1 || head_dim < 1 || frames < 1 || tpf < 1 || block_frames < 1 ||
       first_block_frames < 0)
     return LA_ERR_INVALID_ARG;
@@ -111,6 +113,7 @@ int make_plan(Plan* p, int B, int H, int head_dim, int frames, int tpf, int bloc
   p->D = head_dim;
   p->rec = lavr::rec_floats(head_dim);
   p->N = (int)N;
+  p->row_in = row_mult * H * head_dim;
   p->tpf = tpf;
   p->gw_div = gw_div;
   p->L = (int)((long long)(block_frames < frames ? block_frames : frames) * tpf);
@@ -121,7 +124,7 @@ int make_plan(Plan* p, int B, int H, int head_dim, int frames, int tpf, int bloc
   p->t0 = t0;
   p->mag_tpf = (uint64_t)(kTwo42 / tpf) + 1;
   p->mag_gw = (uint64_t)(kTwo42 / gw_div) + 1;
-  const long long row_bytes = (long long)H * head_dim * 4;
+  const long long row_bytes = (long long)p->row_in * 4;
   const long long min_n = cdiv(kMinWg, (long long)B * p->hg * p->nb);
   if (!split_block(Lmax, kStateMax, min_n, kStep, rope, tpf, row_bytes, &p->cpb, &p->Tc))
     return LA_ERR_UNSUPPORTED;
@@ -152,6 +155,8 @@ int make_plan(Plan* p, int B, int H, int head_dim, int frames, int tpf, int bloc
   p->ws_total = p->ws_prefix + align256(prefix);
   p->ws_suffix = p->ws_total;
   p->ws_total_bw = p->ws_suffix + align256(prefix);
+  p->ws_scale = p->ws_total;
+  p->ws_total_qkv = p->ws_scale + 2 * align256((size_t)B * N * sizeof(float));
   return LA_OK;
 }
 
@@ -173,6 +178,35 @@ int check_tensors(const void* q, const void* k, const void* v, void* out, la_dty
 }
 
 int hip_status(int e) { return e == 0 ? LA_OK : LA_ERR_HIP; }
+
+// Fused (B, N, 3, C) input, its output and the optional norm weights; fills
+// the prologue (scales in the workspace) and the q, k, v row pointers.
+int check_fused(const void* qkv, void* out, la_dtype in_dt, la_dtype out_dt, const Plan& p,
+                const float* q_gamma, const float* k_gamma, float norm_eps, void* ws,
+                size_t ws_bytes, lavr::Prologue* pro, const void** q, const void** k,
+                const void** v) {
+  if (!qkv || !out || !aligned(qkv, 16) || !aligned(out, 16)) return LA_ERR_INVALID_ARG;
+  const size_t C = (size_t)p.H * p.D;
+  const size_t nin = (size_t)p.B * p.N * 3 * C * esize(in_dt), nout = (size_t)p.B * p.N * C * esize(out_dt);
+  if (overlaps(out, nout, qkv, nin)) return LA_ERR_INVALID_ARG;
+  for (const float* gm : {q_gamma, k_gamma}) {
+    if (gm == nullptr) continue;
+    if (!aligned(gm, 16) || overlaps(out, nout, gm, C * sizeof(float))) return LA_ERR_INVALID_ARG;
+  }
+  if ((q_gamma || k_gamma) && (!std::isfinite(norm_eps) || !(norm_eps > 0.f))) return LA_ERR_INVALID_ARG;
+  if (!ws || !aligned(ws, 256) || ws_bytes < p.ws_total_qkv) return LA_ERR_INVALID_ARG;
+  float* sc = reinterpret_cast<float*>(static_cast<char*>(ws) + p.ws_scale);
+  pro->q_gamma = q_gamma;
+  pro->k_gamma = k_gamma;
+  pro->q_scale = sc;
+  pro->k_scale = reinterpret_cast<float*>(reinterpret_cast<char*>(sc) + align256((size_t)p.B * p.N * sizeof(float)));
+  pro->norm_eps = norm_eps;
+  const char* base = static_cast<const char*>(qkv);
+  *q = base;
+  *k = base + C * esize(in_dt);
+  *v = base + 2 * C * esize(in_dt);
+  return LA_OK;
+}
 
 }  // namespace
 
@@ -295,6 +329,34 @@ int la_block_causal_backward(const void* q, const void* k, const void* v, const 
                                           grad_dt == LA_BF16, eps, ws, stream));
 }
 
+size_t la_qkv_workspace_bytes(int B, int H, int head_dim, int frames, int tokens_per_frame,
+                              int block_frames, int first_block_frames) {
+  Plan p;
+  if (make_plan(&p, B, H, head_dim, frames, tokens_per_frame, block_frames, first_block_frames,
+                nullptr, 0, LA_BF16, 3) != LA_OK)
+    return 0;
+  return p.ws_total_qkv;
+}
+
+int la_block_causal_forward_qkv(const void* qkv, void* out, la_dtype in_dt, la_dtype out_dt, int B,
+                                int H, int head_dim, int frames, int tokens_per_frame,
+                                int block_frames, int first_block_frames, const la_rope* rope,
+                                float eps, const float* q_gamma, const float* k_gamma,
+                                float norm_eps, void* ws, size_t ws_bytes, void* stream) {
+  if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return LA_ERR_INVALID_ARG;
+  if (!std::isfinite(eps) || eps < 0.f) return LA_ERR_INVALID_ARG;
+  Plan p;
+  int st = make_plan(&p, B, H, head_dim, frames, tokens_per_frame, block_frames, first_block_frames,
+                     rope, 0, in_dt, 3);
+  if (st != LA_OK) return st;
+  lavr::Prologue pro;
+  const void *q, *k, *v;
+  st = check_fused(qkv, out, in_dt, out_dt, p, q_gamma, k_gamma, norm_eps, ws, ws_bytes, &pro, &q, &k, &v);
+  if (st != LA_OK) return st;
+  return hip_status(lavr::launch_forward(p, q, k, v, out, in_dt == LA_BF16, out_dt == LA_BF16, eps,
+                                         ws, nullptr, nullptr, nullptr, nullptr, stream, nullptr, &pro));
+}
+
 int la_state_init(la_state* st, float* S_dev, float* z_dev, int B, int H, int head_dim,
                   void* stream) {
   if (!st || !S_dev || !z_dev || !aligned(S_dev, 16) || !aligned(z_dev, 16)) return LA_ERR_INVALID_ARG;
@@ -339,6 +401,31 @@ int la_stream_block(la_state* st, const void* q, const void* k, const void* v, v
   return LA_OK;
 }
 
+int la_stream_block_qkv(la_state* st, const void* qkv, void* out, la_dtype in_dt, la_dtype out_dt,
+                        int B, int H, int head_dim, int block_frames, int tokens_per_frame,
+                        const la_rope* rope, float eps, const float* q_gamma, const float* k_gamma,
+                        float norm_eps, int save, void* ws, size_t ws_bytes, void* stream) {
+  if (!st || !st->S || !st->z) return LA_ERR_INVALID_ARG;
+  if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return LA_ERR_INVALID_ARG;
+  if (!std::isfinite(eps) || eps < 0.f) return LA_ERR_INVALID_ARG;
+  if (st->frames_done < 0) return LA_ERR_INVALID_ARG;
+  if (B != st->B || H != st->H || head_dim != st->head_dim) return LA_ERR_STATE_MISMATCH;
+  Plan p;
+  int rc = make_plan(&p, B, H, head_dim, block_frames, tokens_per_frame, block_frames, 0, rope,
+                     st->frames_done, in_dt, 3);
+  if (rc != LA_OK) return rc;
+  lavr::Prologue pro;
+  const void *q, *k, *v;
+  rc = check_fused(qkv, out, in_dt, out_dt, p, q_gamma, k_gamma, norm_eps, ws, ws_bytes, &pro, &q, &k, &v);
+  if (rc != LA_OK) return rc;
+  const int e = lavr::launch_forward(p, q, k, v, out, in_dt == LA_BF16, out_dt == LA_BF16, eps, ws,
+                                     st->S, st->z, save ? st->S : nullptr, save ? st->z : nullptr,
+                                     stream, nullptr, &pro);
+  if (e != 0) return LA_ERR_HIP;
+  if (save) st->frames_done += block_frames;
+  return LA_OK;
+}
+
 const char* la_status_string(int status) {
   switch (status) {
     case LA_OK: return "LA_OK";
@@ -350,6 +437,6 @@ const char* la_status_string(int status) {
   }
 }
 
-const char* la_version(void) { return "0.2.0"; }
+const char* la_version(void) { return "0.3.0"; }
 
 }  // extern "C"

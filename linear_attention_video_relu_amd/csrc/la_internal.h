@@ -27,6 +27,7 @@ struct Plan {
   int D;                // head dim (32 or 64)
   int rec;              // floats of one (S, z) record: D * D + D
   int N;                // tokens per sequence in this call
+  int row_in;           // elements from one input token row to the next (H * D, or 3 * H * D fused)
   int tpf;              // tokens per frame
   int gw_div;           // divisor for row/col (grid_w, or 1 without spatial sections)
   int L;                // tokens per block (after the first)
@@ -47,6 +48,18 @@ struct Plan {
   size_t ws_suffix;     // byte offset of the per-block suffix sums (backward only)
   size_t ws_total_bw;   // workspace bytes of the backward
   size_t ws_total;      // workspace bytes
+  size_t ws_scale;      // byte offset of the q/k token scales (fused prologue only)
+  size_t ws_total_qkv;  // workspace bytes of the fused-prologue forward
+};
+
+// q/k RMSNorm prologue of a forward call (null weights: that tensor is not
+// normalised).  The scales live in the workspace.
+struct Prologue {
+  const float* q_gamma;
+  const float* k_gamma;
+  float* q_scale;       // B * N floats
+  float* k_scale;       // B * N floats
+  float norm_eps;
 };
 
 // Launchers; each returns a hipError_t value (0 = success).
@@ -55,7 +68,7 @@ int launch_rope_table(float* table, int pt, int ph, int pw, int max_frames, int 
 int launch_forward(const Plan& p, const void* q, const void* k, const void* v, void* out,
                    int in_bf16, int out_bf16, float eps, void* ws,
                    const float* S_init, const float* z_init, float* S_save, float* z_save,
-                   void* stream, void* const* events = nullptr);
+                   void* stream, void* const* events = nullptr, const Prologue* pro = nullptr);
 int launch_zero(float* p, size_t n, void* stream);
 int launch_backward(const Plan& p, const void* q, const void* k, const void* v, const void* dout,
                     void* dq, void* dk, void* dv, int in_bf16, int grad_bf16, float eps, void* ws,

@@ -34,6 +34,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "la_internal.h"
 
 namespace lavr {
@@ -72,7 +74,10 @@ struct StateArgs {
   const void* k;
   const void* v;
   float* part;
+  const float* scale;        // normalised k: per-token 1 / rms of the token's k row
+  const float* gamma;        // normalised k: per-channel weight (H * head_dim floats)
   int H, N, L, L0, nb, cpb, Tc, hg;   // L0: tokens of the first block
+  int row_in;                // elements from one token row of k (and v) to the next
   PosArgs pos;
   RopeDev rope;
 };
@@ -93,8 +98,11 @@ struct ReadArgs {
   const void* q;
   void* out;
   const float* prefix;
+  const float* scale;        // normalised q: per-token 1 / rms of the token's q row
+  const float* gamma;        // normalised q: per-channel weight (H * head_dim floats)
   float eps;
   int H, N, L, L0, nb, rpb, Tr, hg;   // L0: tokens of the first block
+  int row_in;                // elements from one token row of q to the next
   PosArgs pos;
   RopeDev rope;
 };
@@ -166,6 +174,35 @@ __device__ __forceinline__ void relu_widen(const Raw8<uint16_t>& r, float* x) {
     x[2 * i + 1] = __uint_as_float(w & 0xffff0000u);
   }
 }
+// Normalised input: x = phi(s * gamma * raw) for a token scale s = 1 / rms and
+// the channels' weights; the weight may be negative, so phi comes last.
+__device__ __forceinline__ void norm_relu_widen(const Raw8<uint16_t>& r, const float* gam, float s, float* x) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t ri = r.r[0][i];
+    x[2 * i] = __uint_as_float(ri << 16);
+    x[2 * i + 1] = __uint_as_float(ri & 0xffff0000u);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = fmaxf(x[i] * (s * gam[i]), 0.f);
+}
+__device__ __forceinline__ void norm_relu_widen(const Raw8<float>& r, const float* gam, float s, float* x) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = fmaxf(__uint_as_float(r.r[i >> 2][i & 3]) * (s * gam[i]), 0.f);
+}
+
+// The 8 weights of channels c0 .. c0+7 (zeros for a half that holds no head).
+__device__ __forceinline__ void load_gamma8(const float* gamma, int c0, bool live, float* g) {
+  const float* src = gamma + (live ? c0 : 0);    // a dead half reads channel 0 and drops it
+  const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    g[i] = live ? a[i] : 0.f;
+    g[4 + i] = live ? b[i] : 0.f;
+  }
+}
+
 __device__ __forceinline__ void relu_widen(const Raw8<float>& r, float* x) {
 #pragma unroll
   for (int i = 0; i < 8; ++i)
@@ -351,8 +388,8 @@ struct TabStage {
 // swapped, so the two half-waves read disjoint LDS banks.  Tokens past the
 // chunk read as zeros (buffer range check) and add nothing.
 
-template <typename TIn, bool P2, int DH>
-__global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? ((P2 && DH == 32) ? 4 : 3) : 2) void k_block_state(StateArgs a) {
+template <typename TIn, bool P2, int DH, bool NRM>
+__global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? ((P2 && DH == 32 && !NRM) ? 4 : (NRM && DH == 64) ? 2 : 3) : 2) void k_block_state(StateArgs a) {
   constexpr bool BF = sizeof(TIn) == 2;
   constexpr bool W64 = DH == 64;
   constexpr int RECN = DH * DH + DH;
@@ -385,13 +422,23 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? ((P2 && DH == 32) ? 4 : 3) :
   const bool rope_on = a.rope.table != nullptr;
 
   // K and V of this chunk: rows c0 .. c1-1 of batch b.
-  const int RB = a.H * DH * ES;
+  const int RB = a.row_in * ES;
   const size_t base = ((size_t)b * a.N + c0) * RB;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const char*>(a.k) + base, (uint32_t)(c1 - c0) * RB);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const char*>(a.v) + base, (uint32_t)(c1 - c0) * RB);
   int voff = lrow * RB + (g * 64 + 8 * lc) * ES;
+  // Normalised k: the token scales of the chunk (past it they read 0, and so
+  // does the key) and this thread's 16 channel weights.
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(NRM ? a.scale + (size_t)b * a.N + c0 : nullptr, NRM ? (uint32_t)(c1 - c0) * 4 : 0u);
+  int soff = lrow * 4;
+  float gam[2][8];
+  if constexpr (NRM) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) load_gamma8(a.gamma, g * 64 + h * D + 8 * lc, h < nh, gam[h]);
+  }
 
-  struct Buf { Raw8<TIn> k[2], v[2]; };
+  struct Buf { Raw8<TIn> k[2], v[2]; float s; };
   auto load_step = [&](Buf& bf) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -399,6 +446,10 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? ((P2 && DH == 32) ? 4 : 3) :
       bf.v[h] = bload8<TIn>(rv, voff + h * D * ES);
     }
     voff += STEP * RB;
+    if constexpr (NRM) {
+      bf.s = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, soff, 0, 0));
+      soff += STEP * 4;
+    }
   };
   // Rotary window reads first, then the K/V loads, then the window's LDS
   // writes: the writes wait only for the window reads.
@@ -446,7 +497,8 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? ((P2 && DH == 32) ? 4 : 3) :
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       float x[8];
-      relu_widen(bf.k[h], x);
+      if constexpr (NRM) norm_relu_widen(bf.k[h], gam[h], bf.s, x);
+      else relu_widen(bf.k[h], x);
 #pragma unroll
       for (int i = 0; i < 8; ++i) zacc[h][i] += x[i];
       if (rope_on) rotate8(x, (W64 && h == 1) ? cs1 : cs);
@@ -653,8 +705,8 @@ __global__ __launch_bounds__(PFX_NT) void k_prefix(PrefixArgs a) {
 // Tokens past the tile read as zeros and their stores are dropped by the
 // buffer range check.
 
-template <typename TIn, typename TOut, bool P2, int DH>
-__global__ __launch_bounds__(NT, DH == 32 ? 4 : 2) void k_readout(ReadArgs a) {
+template <typename TIn, typename TOut, bool P2, int DH, bool NRM>
+__global__ __launch_bounds__(NT, (DH == 32 && !NRM) ? 4 : 2) void k_readout(ReadArgs a) {
   constexpr bool BF = sizeof(TIn) == 2;
   constexpr bool W64 = DH == 64;
   constexpr int RECN = DH * DH + DH;
@@ -681,7 +733,7 @@ __global__ __launch_bounds__(NT, DH == 32 ? 4 : 2) void k_readout(ReadArgs a) {
   const int nh = W64 ? 2 : min(2, a.H - h0);   // 32-channel halves that hold data
   const int ngroups = (t1 - t0 + 15) >> 4;
 
-  const int RB = a.H * DH * ES, RO = a.H * DH * EO;
+  const int RB = a.row_in * ES, RO = a.H * DH * EO;
   const __amdgpu_buffer_rsrc_t rq =
       make_rsrc(static_cast<const char*>(a.q) + ((size_t)b * a.N + t0) * RB, (uint32_t)(t1 - t0) * RB);
   const __amdgpu_buffer_rsrc_t ro =
@@ -749,11 +801,29 @@ __global__ __launch_bounds__(NT, DH == 32 ? 4 : 2) void k_readout(ReadArgs a) {
     }
   }
 
-  struct Buf { Raw8<TIn> x[2]; };
+  // Normalised q: token scales of the tile (0 past it) and the lane's weights.
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(NRM ? a.scale + (size_t)b * a.N + t0 : nullptr, NRM ? (uint32_t)(t1 - t0) * 4 : 0u);
+  int soff = (w * 16 + tl) * 4;
+  float gam[2][8];
+  if constexpr (NRM) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) load_gamma8(a.gamma, g * 64 + h * D + 8 * ch, h < nh, gam[h]);
+  }
+
+  struct Buf { Raw8<TIn> x[2]; float s; };
   auto load_group = [&](Buf& bf) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) bf.x[h] = bload8<TIn>(rq, qoff + h * D * ES);
     qoff += 64 * RB;
+    if constexpr (NRM) {
+      bf.s = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, soff, 0, 0));
+      soff += 64 * 4;
+    }
+  };
+  auto widen_q = [&](const Buf& bf, int h, float* x) {
+    if constexpr (NRM) norm_relu_widen(bf.x[h], gam[h], bf.s, x);
+    else relu_widen(bf.x[h], x);
   };
   // Register buffers: loads run RPF groups ahead of the arithmetic.  Every
   // load is issued, also past the tile (those read zeros and touch no memory),
@@ -808,7 +878,7 @@ __global__ __launch_bounds__(NT, DH == 32 ? 4 : 2) void k_readout(ReadArgs a) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         float x[8];
-        relu_widen(bf.x[h], x);
+        widen_q(bf, h, x);
 #pragma unroll
         for (int i = 0; i < 8; ++i) den += zb[h][i] * x[i];
         if (rope_on) rotate8(x, h ? cs1 : cs);
@@ -849,7 +919,7 @@ __global__ __launch_bounds__(NT, DH == 32 ? 4 : 2) void k_readout(ReadArgs a) {
       for (int h = 0; h < 2; ++h) {
         if (h >= nh) break;
         float x[8];
-        relu_widen(bf.x[h], x);
+        widen_q(bf, h, x);
         float den = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) den += zb[h][i] * x[i];
@@ -1503,29 +1573,99 @@ __global__ void k_fill_zero(float* p, size_t n) {
   if (i < n) p[i] = 0.f;
 }
 
-template <typename TIn, typename TOut, int DH>
+// ---------------------------------------------------------------- k_qk_rms
+//
+// Token scales of the q/k RMSNorm: 1 / sqrt(mean(x^2) + norm_eps) of each
+// token's q row and k row over its C channels.  One wave per token, grid-stride
+// over the tokens: lane l reads the 8-channel pieces l, l + 64, ... of both
+// rows, adds their squares in fp32, and the wave adds its lanes.  A tensor that
+// is not normalised gets an empty buffer range (its loads read zeros and touch
+// no memory).  The channel weights are applied where q and k are consumed.
+struct RmsArgs {
+  const void* q;
+  const void* k;
+  float* sq;
+  float* sk;
+  long long ntok;            // token rows (B * N)
+  int row_in;                // elements from one token row to the next
+  int C;                     // channels per row (a multiple of 8)
+  float norm_eps;
+};
+
+template <typename TIn>
+__global__ __launch_bounds__(NT) void k_qk_rms(RmsArgs a) {
+  constexpr int ES = (int)sizeof(TIn);
+  const int lane = threadIdx.x & 63;
+  const long long nwaves = (long long)gridDim.x * (NT / 64);
+  const int pieces = a.C / 8;
+  const uint32_t row_bytes = (uint32_t)a.C * ES;
+  const char* bq = static_cast<const char*>(a.q != nullptr ? a.q : a.k);
+  const char* bk = static_cast<const char*>(a.k != nullptr ? a.k : a.q);
+  const float inv_c = 1.0f / (float)a.C;
+  for (long long tok = ((long long)blockIdx.x * NT + threadIdx.x) >> 6; tok < a.ntok; tok += nwaves) {
+    const size_t off = (size_t)tok * a.row_in * ES;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(bq + off, a.q != nullptr ? row_bytes : 0u);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(bk + off, a.k != nullptr ? row_bytes : 0u);
+    float sq = 0.f, sk = 0.f;
+#pragma unroll 4
+    for (int pc = lane; pc < pieces; pc += 64) {
+      float fq[8], fk[8];
+      widen8(bload8<TIn>(rq, pc * 8 * ES), fq);
+      widen8(bload8<TIn>(rk, pc * 8 * ES), fk);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        sq += fq[i] * fq[i];
+        sk += fk[i] * fk[i];
+      }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      sq += __shfl_xor(sq, m, 64);
+      sk += __shfl_xor(sk, m, 64);
+    }
+    if (lane == 0) {
+      if (a.sq != nullptr) a.sq[tok] = 1.0f / sqrtf(sq * inv_c + a.norm_eps);
+      if (a.sk != nullptr) a.sk[tok] = 1.0f / sqrtf(sk * inv_c + a.norm_eps);
+    }
+  }
+}
+
+template <typename TIn, typename TOut, int DH, bool NRM>
 hipError_t launch_readout(const ReadArgs& ra, bool p2, dim3 grid, int lds, hipStream_t s) {
-  if (p2) hipLaunchKernelGGL((k_readout<TIn, TOut, true, DH>), grid, dim3(NT), lds, s, ra);
-  else hipLaunchKernelGGL((k_readout<TIn, TOut, false, DH>), grid, dim3(NT), lds, s, ra);
+  if (p2) hipLaunchKernelGGL((k_readout<TIn, TOut, true, DH, NRM>), grid, dim3(NT), lds, s, ra);
+  else hipLaunchKernelGGL((k_readout<TIn, TOut, false, DH, NRM>), grid, dim3(NT), lds, s, ra);
+  return hipGetLastError();
+}
+
+template <int DH, bool NRM>
+hipError_t launch_state_n(const StateArgs& sa, bool in_bf16, bool p2, dim3 grid, int lds, hipStream_t s) {
+  if (in_bf16 && p2) hipLaunchKernelGGL((k_block_state<uint16_t, true, DH, NRM>), grid, dim3(NT), lds, s, sa);
+  else if (in_bf16) hipLaunchKernelGGL((k_block_state<uint16_t, false, DH, NRM>), grid, dim3(NT), lds, s, sa);
+  else if (p2) hipLaunchKernelGGL((k_block_state<float, true, DH, NRM>), grid, dim3(NT), lds, s, sa);
+  else hipLaunchKernelGGL((k_block_state<float, false, DH, NRM>), grid, dim3(NT), lds, s, sa);
   return hipGetLastError();
 }
 
 template <int DH>
 hipError_t launch_state(const StateArgs& sa, bool in_bf16, bool p2, dim3 grid, int lds, hipStream_t s) {
-  if (in_bf16 && p2) hipLaunchKernelGGL((k_block_state<uint16_t, true, DH>), grid, dim3(NT), lds, s, sa);
-  else if (in_bf16) hipLaunchKernelGGL((k_block_state<uint16_t, false, DH>), grid, dim3(NT), lds, s, sa);
-  else if (p2) hipLaunchKernelGGL((k_block_state<float, true, DH>), grid, dim3(NT), lds, s, sa);
-  else hipLaunchKernelGGL((k_block_state<float, false, DH>), grid, dim3(NT), lds, s, sa);
-  return hipGetLastError();
+  return sa.scale != nullptr ? launch_state_n<DH, true>(sa, in_bf16, p2, grid, lds, s)
+                             : launch_state_n<DH, false>(sa, in_bf16, p2, grid, lds, s);
+}
+
+template <int DH, bool NRM>
+hipError_t launch_readouts_n(const ReadArgs& ra, bool in_bf16, bool out_bf16, bool p2, dim3 grid, int lds,
+                             hipStream_t s) {
+  if (in_bf16 && out_bf16) return launch_readout<uint16_t, uint16_t, DH, NRM>(ra, p2, grid, lds, s);
+  if (in_bf16) return launch_readout<uint16_t, float, DH, NRM>(ra, p2, grid, lds, s);
+  if (out_bf16) return launch_readout<float, uint16_t, DH, NRM>(ra, p2, grid, lds, s);
+  return launch_readout<float, float, DH, NRM>(ra, p2, grid, lds, s);
 }
 
 template <int DH>
 hipError_t launch_readouts(const ReadArgs& ra, bool in_bf16, bool out_bf16, bool p2, dim3 grid, int lds,
                            hipStream_t s) {
-  if (in_bf16 && out_bf16) return launch_readout<uint16_t, uint16_t, DH>(ra, p2, grid, lds, s);
-  if (in_bf16) return launch_readout<uint16_t, float, DH>(ra, p2, grid, lds, s);
-  if (out_bf16) return launch_readout<float, uint16_t, DH>(ra, p2, grid, lds, s);
-  return launch_readout<float, float, DH>(ra, p2, grid, lds, s);
+  return ra.scale != nullptr ? launch_readouts_n<DH, true>(ra, in_bf16, out_bf16, p2, grid, lds, s)
+                             : launch_readouts_n<DH, false>(ra, in_bf16, out_bf16, p2, grid, lds, s);
 }
 
 PosArgs pos_args(const Plan& p) {
@@ -1567,20 +1707,42 @@ int launch_zero(float* p, size_t n, void* stream) {
 int launch_forward(const Plan& p, const void* q, const void* k, const void* v, void* out,
                    int in_bf16, int out_bf16, float eps, void* ws,
                    const float* S_init, const float* z_init, float* S_save, float* z_save,
-                   void* stream, void* const* events) {
+                   void* stream, void* const* events, const Prologue* pro) {
   hipStream_t s = (hipStream_t)stream;
   auto mark = [&](int i) -> hipError_t {
     return events ? hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), s) : hipSuccess;
   };
   hipError_t e = mark(0);
   if (e != hipSuccess) return (int)e;
+  const bool nq = pro != nullptr && pro->q_gamma != nullptr;
+  const bool nk = pro != nullptr && pro->k_gamma != nullptr;
+  if (nq || nk) {
+    RmsArgs ra;
+    ra.q = nq ? q : nullptr;
+    ra.k = nk ? k : nullptr;
+    ra.sq = nq ? pro->q_scale : nullptr;
+    ra.sk = nk ? pro->k_scale : nullptr;
+    ra.ntok = (long long)p.B * p.N;
+    ra.row_in = p.row_in;
+    ra.C = p.H * p.D;
+    ra.norm_eps = pro->norm_eps;
+    const long long waves = ra.ntok;
+    const unsigned grid = (unsigned)std::min<long long>((waves + 3) / 4, 256LL * 8);
+    if (in_bf16) hipLaunchKernelGGL(k_qk_rms<uint16_t>, dim3(grid), dim3(NT), 0, s, ra);
+    else hipLaunchKernelGGL(k_qk_rms<float>, dim3(grid), dim3(NT), 0, s, ra);
+    e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+  }
   float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.ws_part);
   float* prefix = reinterpret_cast<float*>(static_cast<char*>(ws) + p.ws_prefix);
   const PosArgs pa_pos = pos_args(p);
 
   StateArgs sa;
   sa.k = k; sa.v = v; sa.part = part;
+  sa.scale = nk ? pro->k_scale : nullptr;
+  sa.gamma = nk ? pro->k_gamma : nullptr;
   sa.H = p.H; sa.N = p.N; sa.L = p.L; sa.L0 = p.L0; sa.nb = p.nb; sa.cpb = p.cpb; sa.Tc = p.Tc; sa.hg = p.hg;
+  sa.row_in = p.row_in;
   sa.pos = pa_pos;
   sa.rope = p.rope;
   const dim3 gs((unsigned)(p.hg * p.nb * p.cpb), (unsigned)p.B);
@@ -1602,7 +1764,10 @@ int launch_forward(const Plan& p, const void* q, const void* k, const void* v, v
 
   ReadArgs ra;
   ra.q = q; ra.out = out; ra.prefix = prefix; ra.eps = eps;
+  ra.scale = nq ? pro->q_scale : nullptr;
+  ra.gamma = nq ? pro->q_gamma : nullptr;
   ra.H = p.H; ra.N = p.N; ra.L = p.L; ra.L0 = p.L0; ra.nb = p.nb; ra.rpb = p.rpb; ra.Tr = p.Tr; ra.hg = p.hg;
+  ra.row_in = p.row_in;
   ra.pos = pa_pos;
   ra.rope = p.rope;
   const dim3 gr((unsigned)(p.hg * p.nb * p.rpb), (unsigned)p.B);
@@ -1626,6 +1791,7 @@ int launch_backward(const Plan& p, const void* q, const void* k, const void* v, 
   // Sbar, zbar of every block, as the forward forms them.
   StateArgs sa;
   sa.k = k; sa.v = v; sa.part = part;
+  sa.scale = nullptr; sa.gamma = nullptr; sa.row_in = p.row_in;
   sa.H = p.H; sa.N = p.N; sa.L = p.L; sa.L0 = p.L0; sa.nb = p.nb; sa.cpb = p.cpb; sa.Tc = p.Tc; sa.hg = p.hg;
   sa.pos = pa_pos;
   sa.rope = p.rope;

@@ -19,6 +19,7 @@ LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_STATE_MISMATCH, LA_ERR_HIP
 LA_F32, LA_BF16 = 0, 1
 HEAD_DIM = 32
 EPS_DEFAULT = 1e-8
+NORM_EPS_DEFAULT = 1e-6
 
 
 class LaRope(ctypes.Structure):
@@ -53,6 +54,13 @@ def _load():
         "la_backward_workspace_bytes": (c_size, [c_int] * 7),
         "la_block_causal_backward": (c_int, [c_vp] * 7 + [c_int] * 9 + [ctypes.POINTER(LaRope), c_float,
                                                                          c_vp, c_size, c_vp]),
+        "la_qkv_workspace_bytes": (c_size, [c_int] * 7),
+        "la_block_causal_forward_qkv": (c_int, [c_vp, c_vp, c_int, c_int] + [c_int] * 7 +
+                                        [ctypes.POINTER(LaRope), c_float, c_vp, c_vp, c_float, c_vp,
+                                         c_size, c_vp]),
+        "la_stream_block_qkv": (c_int, [ctypes.POINTER(LaState), c_vp, c_vp, c_int, c_int] + [c_int] * 5 +
+                                [ctypes.POINTER(LaRope), c_float, c_vp, c_vp, c_float, c_int, c_vp,
+                                 c_size, c_vp]),
         "la_state_init": (c_int, [ctypes.POINTER(LaState), c_vp, c_vp, c_int, c_int, c_int, c_vp]),
         "la_stream_block": (c_int, [ctypes.POINTER(LaState), c_vp, c_vp, c_vp, c_vp, c_int, c_int,
                                     c_int, c_int, c_int, c_int, c_int, ctypes.POINTER(LaRope),
@@ -71,6 +79,7 @@ lib = _load()
 
 EXPORTS = ("rope_table_bytes", "rope_table_build", "la_workspace_bytes", "la_block_causal_forward",
            "la_block_causal_forward_timed", "la_backward_workspace_bytes", "la_block_causal_backward",
+           "la_qkv_workspace_bytes", "la_block_causal_forward_qkv", "la_stream_block_qkv",
            "la_state_init", "la_stream_block", "la_status_string", "la_version")
 
 
@@ -195,6 +204,67 @@ def block_causal_forward(q, k, v, block_frames, tokens_per_frame, rope=None, eps
     return out
 
 
+# ------------------------------------------------------------ fused prologue
+
+def qkv_workspace_bytes(B, H, frames, tokens_per_frame, block_frames, head_dim=HEAD_DIM,
+                        first_block_frames=0):
+    n = lib.la_qkv_workspace_bytes(int(B), int(H), int(head_dim), int(frames), int(tokens_per_frame),
+                                   int(block_frames), int(first_block_frames or 0))
+    if n == 0:
+        raise ValueError("invalid shape for la_qkv_workspace_bytes")
+    return n
+
+
+def _check_fused(qkv, heads, q_gamma, k_gamma):
+    if not isinstance(qkv, torch.Tensor) or qkv.device.type != "cuda":
+        raise ValueError("qkv must be a CUDA (HIP) tensor")
+    if qkv.dim() != 4 or qkv.shape[2] != 3 or not qkv.is_contiguous():
+        raise ValueError("qkv must be a contiguous (B, N, 3, C) tensor")
+    C = qkv.shape[3]
+    if C % heads:
+        raise ValueError("C must be a multiple of heads")
+    for g in (q_gamma, k_gamma):
+        if g is None:
+            continue
+        if (not isinstance(g, torch.Tensor) or g.device != qkv.device or g.dtype != torch.float32
+                or g.shape != (C,) or not g.is_contiguous()):
+            raise ValueError("q_gamma / k_gamma must be contiguous float32 (C,) tensors on qkv's device")
+    return C // heads
+
+
+def _gptr(g):
+    return None if g is None else _ptr(g)
+
+
+def block_causal_forward_qkv(qkv, heads, block_frames, tokens_per_frame, rope=None, eps=EPS_DEFAULT,
+                             q_gamma=None, k_gamma=None, norm_eps=NORM_EPS_DEFAULT, out=None,
+                             out_dtype=None, workspace=None, first_block_frames=None):
+    """One-shot forward from the fused projection output qkv (B, N, 3, C): q, k, v
+    rows in place, with q and/or k RMS-normalised over C when a weight is given.
+    Returns out (B, N, heads, C // heads)."""
+    d = _check_fused(qkv, heads, q_gamma, k_gamma)
+    B, N = qkv.shape[0], qkv.shape[1]
+    if N % tokens_per_frame:
+        raise ValueError("N must be a multiple of tokens_per_frame")
+    frames = N // tokens_per_frame
+    out_dtype = qkv.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, N, heads, d), dtype=out_dtype, device=qkv.device)
+    elif (out.shape != (B, N, heads, d) or out.dtype != out_dtype or not out.is_contiguous()
+          or out.device != qkv.device):
+        raise ValueError("out must be a contiguous (B, N, heads, head_dim) tensor of out_dtype")
+    f0 = int(first_block_frames or 0)
+    need = lib.la_qkv_workspace_bytes(B, heads, d, frames, int(tokens_per_frame), int(block_frames), f0)
+    ws = _workspace(qkv.device, need) if workspace is None else workspace
+    _check(lib.la_block_causal_forward_qkv(_ptr(qkv), _ptr(out), _dtype_code(qkv.dtype),
+                                           _dtype_code(out_dtype), B, int(heads), d, frames,
+                                           int(tokens_per_frame), int(block_frames), f0,
+                                           _rope_ptr(rope), float(eps), _gptr(q_gamma), _gptr(k_gamma),
+                                           float(norm_eps), _ptr(ws), ws.numel() * ws.element_size(),
+                                           _stream(qkv.device)), "la_block_causal_forward_qkv")
+    return out
+
+
 # ------------------------------------------------------------------ backward
 
 def backward_workspace_bytes(B, H, frames, tokens_per_frame, block_frames, head_dim=HEAD_DIM,
@@ -308,4 +378,29 @@ class StreamState:
                                    int(tokens_per_frame), _rope_ptr(rope), float(eps), int(bool(save)),
                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(q.device)),
                "la_stream_block")
+        return out
+
+    def step_qkv(self, qkv, tokens_per_frame, rope=None, eps=EPS_DEFAULT, q_gamma=None, k_gamma=None,
+                 norm_eps=NORM_EPS_DEFAULT, save=True, out=None, out_dtype=None, workspace=None):
+        """step() from the fused projection output qkv (B, N, 3, C); see
+        la_stream_block_qkv."""
+        H = int(self.desc.H)
+        d = _check_fused(qkv, H, q_gamma, k_gamma)
+        B, N = qkv.shape[0], qkv.shape[1]
+        if N % tokens_per_frame:
+            raise ValueError("N must be a multiple of tokens_per_frame")
+        frames = N // tokens_per_frame
+        out_dtype = qkv.dtype if out_dtype is None else out_dtype
+        if out is None:
+            out = torch.empty((B, N, H, d), dtype=out_dtype, device=qkv.device)
+        elif out.shape != (B, N, H, d) or out.dtype != out_dtype or not out.is_contiguous():
+            raise ValueError("out must be a contiguous (B, N, H, head_dim) tensor of out_dtype")
+        need = lib.la_qkv_workspace_bytes(B, H, d, frames, int(tokens_per_frame), frames, 0)
+        ws = _workspace(qkv.device, need) if workspace is None else workspace
+        _check(lib.la_stream_block_qkv(ctypes.byref(self.desc), _ptr(qkv), _ptr(out), _dtype_code(qkv.dtype),
+                                       _dtype_code(out_dtype), B, H, d, frames, int(tokens_per_frame),
+                                       _rope_ptr(rope), float(eps), _gptr(q_gamma), _gptr(k_gamma),
+                                       float(norm_eps), int(bool(save)), _ptr(ws),
+                                       ws.numel() * ws.element_size(), _stream(qkv.device)),
+               "la_stream_block_qkv")
         return out

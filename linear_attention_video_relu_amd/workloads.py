@@ -11,7 +11,8 @@ Recipe (the same for every workload):
   * for keys with an outlier fraction p: an independent Bernoulli(p) mask per
     element, masked entries multiplied by the outlier factor after the draw;
   * bf16 workloads round the float32 draws to bf16 (round to nearest, ties to even);
-  * B > 1 (conditional / unconditional) is simply independent draws per batch row.
+  * B > 1 (conditional / unconditional) is simply independent draws per batch row;
+  * the q/k norm weights of the fused prologue are 1 + 0.5 * N(0, 1) per channel.
 """
 
 from concurrent.futures import ThreadPoolExecutor
@@ -147,6 +148,24 @@ def draw(cfg, tensor, token_range=None, threads=None):
         with ThreadPoolExecutor(max_workers=threads) as ex:
             list(ex.map(one, jobs))
     return out
+
+
+# Per-channel weights of the q/k RMSNorm prologue: 1 + 0.5 * N(0, 1) in float32
+# (a few come out negative), one SeedSequence per weight vector.
+NORM_WEIGHTS = ("q_gamma", "k_gamma")
+
+
+def draw_norm_weight(cfg, which):
+    """Seeded (C,) float32 weight vector of the q or k norm (C = H * head_dim)."""
+    ss = np.random.SeedSequence([ROOT_SEED, cfg["index"], len(TENSORS) + NORM_WEIGHTS.index(which)])
+    rng = np.random.default_rng(ss)
+    return (1.0 + 0.5 * rng.standard_normal(cfg["H"] * cfg["head_dim"])).astype(np.float32)
+
+
+def fuse_qkv(q, k, v):
+    """(B, N, H, d) q, k, v arrays -> one (B, N, 3, H * d) array with q | k | v rows."""
+    B, N, H, d = q.shape
+    return np.stack([a.reshape(B, N, H * d) for a in (q, k, v)], axis=2)
 
 
 def to_f64(cfg, arr):

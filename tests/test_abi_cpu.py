@@ -35,7 +35,7 @@ def test_exports_every_declared_function(lavr):
 
 
 def test_version_and_status_strings(lavr):
-    assert lavr.lib.la_version() == b"0.2.0"
+    assert lavr.lib.la_version() == b"0.3.0"
     for code in range(5):
         assert lavr.status_string(code).startswith("LA_")
     assert "unknown" in lavr.status_string(99)
@@ -198,3 +198,55 @@ def test_backward_workspace_bytes(lavr):
     n = lavr.backward_workspace_bytes(1, 70, 240, 1560, 8)
     assert n > lavr.workspace_bytes(1, 70, 240, 1560, 8)     # plus the suffix records
     assert lavr.lib.la_backward_workspace_bytes(1, 35, 64, 240, 1560, 8, 0) == 0
+
+
+def call_forward_qkv(lavr, **kw):
+    args = dict(qkv=FAKE, out=FAKE + 0x3000000, in_dt=lavr.LA_BF16, out_dt=lavr.LA_BF16, B=1, H=2,
+                d=32, frames=4, tpf=6, bf=2, f0=0, rope=None, eps=1e-8, qg=FAKE + 0x5000000,
+                kg=FAKE + 0x5001000, norm_eps=1e-6, ws=FAKE + 0x4000000, ws_bytes=1 << 20)
+    args.update(kw)
+    vp = ctypes.c_void_p
+    return lavr.lib.la_block_causal_forward_qkv(
+        vp(args["qkv"]), vp(args["out"]), args["in_dt"], args["out_dt"], args["B"], args["H"],
+        args["d"], args["frames"], args["tpf"], args["bf"], args["f0"], args["rope"], args["eps"],
+        vp(args["qg"]), vp(args["kg"]), args["norm_eps"], vp(args["ws"]), args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(qkv=0), 1),                        # null input
+    (dict(qkv=FAKE + 4), 1),                 # misaligned input
+    (dict(out=FAKE + 3 * 24 * 64 * 2 - 64), 1),  # out overlaps the fused rows (3 * C per token)
+    (dict(qg=FAKE + 0x5000000 + 4), 1),      # misaligned weight
+    (dict(kg=FAKE + 0x3000000 + 16), 1),     # weight overlaps out
+    (dict(norm_eps=0.0), 1),                 # a norm needs norm_eps > 0
+    (dict(norm_eps=float("nan")), 1),
+    (dict(d=48), 2),
+    (dict(eps=-1.0), 1),
+    (dict(ws_bytes=16), 1),
+    (dict(bf=0), 1),
+])
+def test_forward_qkv_rejects_bad_arguments(lavr, kw, code):
+    assert call_forward_qkv(lavr, **kw) == code
+
+
+def test_qkv_workspace_bytes(lavr):
+    # the forward's workspace plus two per-token scale arrays (q and k)
+    base = lavr.workspace_bytes(1, 70, 240, 1560, 8)
+    n = lavr.qkv_workspace_bytes(1, 70, 240, 1560, 8)
+    assert n >= base + 2 * 374400 * 4
+    assert n < base + 2 * 374400 * 4 + 1024
+    assert lavr.lib.la_qkv_workspace_bytes(1, 70, 48, 240, 1560, 8, 0) == 0
+
+
+def test_stream_block_qkv_state_checks(lavr):
+    st = lavr.LaState()
+    st.S, st.z, st.B, st.H, st.head_dim, st.frames_done = FAKE, FAKE + 0x100000, 2, 4, 32, 0
+    f = lavr.lib.la_stream_block_qkv
+    vp = ctypes.c_void_p
+    qkv, out, ws = vp(FAKE + 0x1000000), vp(FAKE + 0x3000000), vp(FAKE + 0x6000000)
+    g = vp(FAKE + 0x5000000)
+    assert f(ctypes.byref(st), qkv, out, 1, 1, 1, 4, 32, 3, 6, None, 1e-8, g, g, 1e-6, 1, ws, 1 << 24, None) == 3
+    assert f(ctypes.byref(st), qkv, out, 1, 1, 2, 4, 32, 3, 6, None, 1e-8, g, g, 1e-6, 1, ws, 64, None) == 1
+    assert f(ctypes.byref(st), qkv, out, 1, 1, 2, 4, 32, 3, 6, None, 1e-8, g, None, -1.0, 1, ws, 1 << 24,
+             None) == 1
+    assert st.frames_done == 0
