@@ -146,6 +146,8 @@ def main():
     ap.add_argument("--stream-reps", type=int, default=3, help="timed 40-call streaming runs (0 = skip)")
     ap.add_argument("--backward-steps", type=int, default=10,
                     help="timed la_block_causal_backward calls on the same workload (0 = skip)")
+    ap.add_argument("--prologue-steps", type=int, default=10,
+                    help="timed fused q/k/v + q/k RMSNorm forward calls on the same workload (0 = skip)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 1 GiB fill and a 1 GiB device copy, the known-size kernels "
                          "that scale the HBM byte counters")
@@ -268,11 +270,65 @@ def main():
 
     if args.stream_reps > 0:
         result["streaming"] = bench_streaming(lavr, torch, dev, args.stream_reps)
+    if args.prologue_steps > 0:
+        result["prologue"] = bench_prologue(lavr, torch, dev, cfg, q, k, v, rope, args.prologue_steps)
     if args.backward_steps > 0 and d == 32:
         del out
         result["backward"] = bench_backward(lavr, torch, dev, cfg, q, k, v, rope, args.backward_steps)
 
     print(json.dumps(result), flush=True)
+
+
+def bench_prologue(lavr, torch, dev, cfg, q, k, v, rope, steps):
+    """Time la_block_causal_forward_qkv with both norms on the fused (B, N, 3, C)
+    form of the workload, and the unfused sequence it replaces (torch RMSNorm of
+    q and k, a copy of v, then la_block_causal_forward) for comparison."""
+    B, H, N, d = cfg["B"], cfg["H"], W.n_tokens(cfg), cfg["head_dim"]
+    C = H * d
+    tpf, bf = cfg["tokens_per_frame"], cfg["block_frames"]
+    norm_eps = 1e-6
+    qkv = torch.stack([t.reshape(B, N, C) for t in (q, k, v)], dim=2).contiguous()
+    gq, gk = (torch.from_numpy(W.draw_norm_weight(cfg, w)).to(dev) for w in W.NORM_WEIGHTS)
+    out = torch.empty((B, N, H, d), dtype=q.dtype, device=dev)
+    ws = torch.empty(lavr.qkv_workspace_bytes(B, H, cfg["frames"], tpf, bf, d), dtype=torch.uint8, device=dev)
+
+    def fused():
+        lavr.block_causal_forward_qkv(qkv, H, bf, tpf, rope, q_gamma=gq, k_gamma=gk, norm_eps=norm_eps,
+                                      out=out, workspace=ws)
+
+    def unfused():
+        qn = torch.nn.functional.rms_norm(qkv[:, :, 0], (C,), gq.to(q.dtype), norm_eps)
+        kn = torch.nn.functional.rms_norm(qkv[:, :, 1], (C,), gk.to(q.dtype), norm_eps)
+        vc = qkv[:, :, 2].contiguous()
+        lavr.block_causal_forward(qn.view(B, N, H, d), kn.view(B, N, H, d), vc.view(B, N, H, d), bf, tpf,
+                                  rope, out=out)
+
+    def timed(fn, n):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize(dev)
+        return e0.elapsed_time(e1) / n
+
+    ms = timed(fused, steps)
+    ms_unfused = timed(unfused, max(2, steps // 2))
+    th = B * N * H
+    esz = q.element_size()
+    nb = -(-cfg["frames"] // bf)
+    # each input element read once and out written once, plus the block records;
+    # the build reads q and k a second time for the token scales (moved bytes)
+    alg = 4 * th * d * esz + 2 * B * H * nb * rec_bytes(d)
+    moved = alg + 2 * th * d * esz + 2 * 2 * B * N * 4
+    del qkv, out, ws
+    torch.cuda.empty_cache()
+    return {"ms": ms, "tokens_heads_per_s": th / (ms / 1e3), "alg_bytes": alg, "moved_bytes": moved,
+            "gbs_alg": alg / (ms * 1e6), "gbs_moved": moved / (ms * 1e6),
+            "unfused_ms": ms_unfused, "norm_eps": norm_eps, "steps": steps}
 
 
 def bench_backward(lavr, torch, dev, cfg, q, k, v, rope, steps):
