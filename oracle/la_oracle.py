@@ -376,6 +376,83 @@ def stream_block_qkv(state, qkv, heads, tokens_per_frame, rope=None, eps=EPS_DEF
     return stream_block(state, q, k, v, tokens_per_frame, rope, eps, save)
 
 
+# ----------------------------------------------- cached temporal convolution
+#
+# The causal Mix-FFN keeps the previous block's last frame for its temporal
+# convolution ([BCLA] "What SANA-Video Actually Uses"; [LongSANA], the pull
+# request description: causal logic for the Mix-FFN, the conv in the MLP, and
+# its block name CachedGLUMBConvTemp).  Reading: a depthwise (per-channel)
+# convolution along the frame axis at every spatial position, y[t] = sum_i
+# w[i] * x[t + i - 1] over the taps i < kt, with kt = 3 (frames t-1, t, t+1)
+# or kt = 2 (frames t-1, t).  Inside a block the taps see the block's own
+# frames; before the block's first frame they see the previous block's last
+# frame (the cache; zeros before the first block), after its last frame zeros
+# (the next block does not exist yet).  So, like the attention, it is
+# bidirectional inside a block and causal across blocks, and one cached frame
+# is all it needs.  An optional per-channel bias is added.  The 1x1
+# projections and the gate around it are ordinary matrix products and are not
+# part of this oracle.
+
+
+def temporal_conv_block(x, w, cache=None, bias=None):
+    """Temporal conv of one block: x (B, F, P, Ch) frames of P spatial positions,
+    w (kt, Ch), cache (B, P, Ch) = the previous block's last frame (None: zeros).
+    Returns y (B, F, P, Ch) float64."""
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    kt = w.shape[0]
+    if kt not in (2, 3):
+        raise ValueError("kt must be 2 or 3")
+    B, F, P, Ch = x.shape
+    prev = np.zeros((B, 1, P, Ch)) if cache is None else np.asarray(cache, dtype=np.float64)[:, None]
+    padded = np.concatenate([prev, x, np.zeros((B, 1, P, Ch))], axis=1)     # frames -1 .. F
+    y = np.zeros_like(x)
+    for i in range(kt):
+        y += w[i] * padded[:, i:i + F]          # tap i reads frame t + i - 1
+    if bias is not None:
+        y += np.asarray(bias, dtype=np.float64)
+    return y
+
+
+def temporal_conv(x, w, tokens_per_frame, block_frames, bias=None, first_block_frames=None):
+    """One-shot temporal conv over a whole sequence x (B, N, Ch) of frame-major
+    tokens (N = frames * tokens_per_frame), block by block, each block reading
+    the last frame of the one before.  Returns y (B, N, Ch) float64."""
+    x = np.asarray(x, dtype=np.float64)
+    B, N, Ch = x.shape
+    frames = N // tokens_per_frame
+    xf = x.reshape(B, frames, tokens_per_frame, Ch)
+    y = np.empty_like(xf)
+    cache = None
+    for s, e in block_bounds(frames, block_frames, first_block_frames):
+        y[:, s:e] = temporal_conv_block(xf[:, s:e], w, cache, bias)
+        cache = xf[:, e - 1]
+    return y.reshape(B, N, Ch)
+
+
+class ConvCache:
+    """The temporal conv's streaming cache: the last frame of the last committed
+    block, (B, P, Ch), zeros at the start."""
+
+    def __init__(self, B, P, Ch):
+        self.last = np.zeros((B, P, Ch))
+        self.frames_done = 0
+
+
+def temporal_conv_stream_block(cache, x, w, tokens_per_frame, bias=None, save=True):
+    """One streamed block x (B, F * P, Ch) against the cache; with save the cache
+    becomes this block's last frame."""
+    x = np.asarray(x, dtype=np.float64)
+    B, n, Ch = x.shape
+    F = n // tokens_per_frame
+    xf = x.reshape(B, F, tokens_per_frame, Ch)
+    y = temporal_conv_block(xf, w, cache.last, bias)
+    if save:
+        cache.last = xf[:, -1].copy()
+        cache.frames_done += F
+    return y.reshape(B, n, Ch)
+
+
 # ------------------------------------------------------------- independent checks
 
 def brute_force(q, k, v, tokens_per_frame, block_frames, rope=None, eps=EPS_DEFAULT,
