@@ -148,6 +148,8 @@ def main():
                     help="timed la_block_causal_backward calls on the same workload (0 = skip)")
     ap.add_argument("--prologue-steps", type=int, default=10,
                     help="timed fused q/k/v + q/k RMSNorm forward calls on the same workload (0 = skip)")
+    ap.add_argument("--tconv-steps", type=int, default=20,
+                    help="timed cached temporal convolution calls at the workload's token grid (0 = skip)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 1 GiB fill and a 1 GiB device copy, the known-size kernels "
                          "that scale the HBM byte counters")
@@ -270,6 +272,8 @@ def main():
 
     if args.stream_reps > 0:
         result["streaming"] = bench_streaming(lavr, torch, dev, args.stream_reps)
+    if args.tconv_steps > 0:
+        result["tconv"] = bench_tconv(lavr, torch, dev, cfg, args.tconv_steps)
     if args.prologue_steps > 0:
         result["prologue"] = bench_prologue(lavr, torch, dev, cfg, q, k, v, rope, args.prologue_steps)
     if args.backward_steps > 0 and d == 32:
@@ -277,6 +281,34 @@ def main():
         result["backward"] = bench_backward(lavr, torch, dev, cfg, q, k, v, rope, args.backward_steps)
 
     print(json.dumps(result), flush=True)
+
+
+def bench_tconv(lavr, torch, dev, cfg, steps):
+    """Time la_temporal_conv (kernel 3, bias, bf16 in and out) over the workload's
+    token grid with C = H * head_dim channels, blocks of block_frames frames."""
+    B, N, C = cfg["B"], W.n_tokens(cfg), cfg["H"] * cfg["head_dim"]
+    tpf, bf = cfg["tokens_per_frame"], cfg["block_frames"]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    x = torch.randn((B, N, C), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    w = torch.randn((3, C), generator=gen, device=dev, dtype=torch.float32) / 3 ** 0.5
+    bias = 0.1 * torch.randn((C,), generator=gen, device=dev, dtype=torch.float32)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        lavr.temporal_conv(x, w, tpf, bf, bias=bias, out=y)
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        lavr.temporal_conv(x, w, tpf, bf, bias=bias, out=y)
+    e1.record()
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / steps
+    alg = 2 * B * N * C * 2                               # x read once, y written once
+    del x, y
+    torch.cuda.empty_cache()
+    return {"ms": ms, "channels": C, "kt": 3, "alg_bytes": alg, "gbs": alg / (ms * 1e6),
+            "frac_of_peak": alg / (ms * 1e6) / HBM_PEAK_GBS, "steps": steps}
 
 
 def bench_prologue(lavr, torch, dev, cfg, q, k, v, rope, steps):

@@ -1,7 +1,8 @@
 /*
  * la_vr.h -- C ABI of liblavr: block-causal ReLU linear attention with RoPE
  * (forward, one-shot and streaming; its backward; a fused q/k/v input with the
- * q/k RMSNorm prologue) on AMD MI355X (gfx950).
+ * q/k RMSNorm prologue) and the cached temporal convolution of the causal
+ * Mix-FFN, on AMD MI355X (gfx950).
  *
  * What is computed.  For every batch row b and head h, with phi = ReLU applied
  * elementwise to queries and keys ("Implementing Block Causal Linear Attention
@@ -225,6 +226,54 @@ int la_stream_block_qkv(la_state* st, const void* qkv, void* out, la_dtype in_dt
                         const la_rope* rope, float eps, const float* q_gamma,
                         const float* k_gamma, float norm_eps, int save, void* ws,
                         size_t ws_bytes, void* stream);
+
+/* Cached temporal convolution of the causal Mix-FFN.  The pages say that the
+ * causal Mix-FFN keeps the previous block's last frame for its temporal
+ * convolution ("Block Causal Linear Attention", happyin.space, "What SANA-Video
+ * Actually Uses"; "[feat] LongSANA ..." pull request: causal logic for the
+ * Mix-FFN, block CachedGLUMBConvTemp).  The library's reading: a depthwise
+ * convolution along frames at every spatial position,
+ *   y[t] = bias + sum_{i < kt} w[i] * x[t + i - 1],
+ * kt = 3 (frames t-1, t, t+1) or kt = 2 (t-1, t).  Inside a block the taps see
+ * the block's frames; before a block's first frame they see the previous
+ * block's last frame (zeros before the first block of a stream), after its
+ * last frame zeros.  x and y are contiguous (B, frames * tokens_per_frame,
+ * channels), frame-major tokens as for attention; w is (kt, channels) fp32,
+ * bias (channels) fp32 or NULL; channels is a multiple of 8; accumulation is
+ * fp32 and a bf16 y is rounded to nearest even.  All pointers 16-byte aligned;
+ * y must not overlap x, w, bias or the cache.  One batch row of x or y
+ * (plus 16 frames) must stay below 4 GiB, else LA_ERR_UNSUPPORTED. */
+
+/* Streaming cache of the temporal convolution: `last` is the last frame of the
+ * last committed block, (B, tokens_per_frame, channels) in `dtype` (device,
+ * caller-owned); frames_done counts committed frames. */
+typedef struct {
+  void* last;
+  int B, tokens_per_frame, channels;
+  la_dtype dtype;
+  long long frames_done;
+} la_conv_state;
+
+/* One-shot convolution over `frames` frames in blocks (first_block_frames as
+ * for la_block_causal_forward; the first block starts from zeros). */
+int la_temporal_conv(const void* x, void* y, la_dtype in_dt, la_dtype out_dt, int B, int frames,
+                     int tokens_per_frame, int channels, int block_frames, int first_block_frames,
+                     int kt, const float* w, const float* bias, void* stream);
+
+/* Bind and zero the caller's cache buffer last_dev (B * tokens_per_frame *
+ * channels elements of dtype) on `stream`; frames_done = 0. */
+int la_conv_state_init(la_conv_state* st, void* last_dev, la_dtype dtype, int B, int tokens_per_frame,
+                       int channels, void* stream);
+
+/* One streamed block of block_frames frames: x (B, block_frames *
+ * tokens_per_frame, channels) in the cache's dtype.  The block's first frame
+ * reads the cache; with save != 0 the cache becomes the block's last frame and
+ * frames_done advances (on the host, at enqueue time), with save == 0 the cache
+ * is unchanged.  (B, tokens_per_frame, channels) must equal the cache's, else
+ * LA_ERR_STATE_MISMATCH. */
+int la_temporal_conv_stream_block(la_conv_state* st, const void* x, void* y, la_dtype out_dt, int B,
+                                  int block_frames, int tokens_per_frame, int channels, int kt,
+                                  const float* w, const float* bias, int save, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* la_status_string(int status);

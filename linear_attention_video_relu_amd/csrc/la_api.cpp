@@ -208,6 +208,25 @@ int check_fused(const void* qkv, void* out, la_dtype in_dt, la_dtype out_dt, con
   return LA_OK;
 }
 
+// Shared checks of the temporal convolution entry points.
+int check_conv(const void* x, const void* y, la_dtype in_dt, la_dtype out_dt, int B, int frames,
+               int tpf, int ch, int kt, const float* w, const float* bias) {
+  if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return LA_ERR_INVALID_ARG;
+  if (B < 1 || frames < 1 || tpf < 1 || ch < 8 || (ch % 8) != 0) return LA_ERR_INVALID_ARG;
+  if (kt != 2 && kt != 3) return LA_ERR_INVALID_ARG;
+  if (!x || !y || !w || !aligned(x, 16) || !aligned(y, 16) || !aligned(w, 16)) return LA_ERR_INVALID_ARG;
+  if (bias && !aligned(bias, 16)) return LA_ERR_INVALID_ARG;
+  if (B > 65535) return LA_ERR_UNSUPPORTED;
+  const int wide = esize(in_dt) > esize(out_dt) ? esize(in_dt) : esize(out_dt);
+  if ((long long)(frames + 16) * tpf * ch * wide >= (1LL << 32)) return LA_ERR_UNSUPPORTED;
+  if ((long long)tpf * (ch / 8) > 0x7fffffffLL - 256) return LA_ERR_UNSUPPORTED;
+  const size_t n = (size_t)B * frames * tpf * ch;
+  const size_t nx = n * esize(in_dt), ny = n * esize(out_dt);
+  if (overlaps(y, ny, x, nx) || overlaps(y, ny, w, (size_t)kt * ch * 4)) return LA_ERR_INVALID_ARG;
+  if (bias && overlaps(y, ny, bias, (size_t)ch * 4)) return LA_ERR_INVALID_ARG;
+  return LA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -421,6 +440,54 @@ int la_stream_block_qkv(la_state* st, const void* qkv, void* out, la_dtype in_dt
   const int e = lavr::launch_forward(p, q, k, v, out, in_dt == LA_BF16, out_dt == LA_BF16, eps, ws,
                                      st->S, st->z, save ? st->S : nullptr, save ? st->z : nullptr,
                                      stream, nullptr, &pro);
+  if (e != 0) return LA_ERR_HIP;
+  if (save) st->frames_done += block_frames;
+  return LA_OK;
+}
+
+int la_temporal_conv(const void* x, void* y, la_dtype in_dt, la_dtype out_dt, int B, int frames,
+                     int tokens_per_frame, int channels, int block_frames, int first_block_frames,
+                     int kt, const float* w, const float* bias, void* stream) {
+  if (block_frames < 1 || first_block_frames < 0) return LA_ERR_INVALID_ARG;
+  const int st = check_conv(x, y, in_dt, out_dt, B, frames, tokens_per_frame, channels, kt, w, bias);
+  if (st != LA_OK) return st;
+  lavr::ConvPlan c{B, frames, tokens_per_frame, channels,
+                   first_block_frames == 0 ? block_frames : first_block_frames, block_frames, kt};
+  return hip_status(lavr::launch_tconv(c, x, y, in_dt == LA_BF16, out_dt == LA_BF16, w, bias, nullptr,
+                                       nullptr, stream));
+}
+
+int la_conv_state_init(la_conv_state* st, void* last_dev, la_dtype dtype, int B, int tokens_per_frame,
+                       int channels, void* stream) {
+  if (!st || !last_dev || !aligned(last_dev, 16) || !valid_dtype(dtype)) return LA_ERR_INVALID_ARG;
+  if (B < 1 || tokens_per_frame < 1 || channels < 8 || (channels % 8) != 0) return LA_ERR_INVALID_ARG;
+  const size_t bytes = (size_t)B * tokens_per_frame * channels * esize(dtype);
+  if (lavr::launch_zero(static_cast<float*>(last_dev), bytes / 4, stream) != 0) return LA_ERR_HIP;
+  st->last = last_dev;
+  st->B = B;
+  st->tokens_per_frame = tokens_per_frame;
+  st->channels = channels;
+  st->dtype = dtype;
+  st->frames_done = 0;
+  return LA_OK;
+}
+
+int la_temporal_conv_stream_block(la_conv_state* st, const void* x, void* y, la_dtype out_dt, int B,
+                                  int block_frames, int tokens_per_frame, int channels, int kt,
+                                  const float* w, const float* bias, int save, void* stream) {
+  if (!st || !st->last || !aligned(st->last, 16) || st->frames_done < 0) return LA_ERR_INVALID_ARG;
+  if (block_frames < 1) return LA_ERR_INVALID_ARG;
+  if (B != st->B || tokens_per_frame != st->tokens_per_frame || channels != st->channels)
+    return LA_ERR_STATE_MISMATCH;
+  const la_dtype in_dt = st->dtype;
+  const int rc = check_conv(x, y, in_dt, out_dt, B, block_frames, tokens_per_frame, channels, kt, w, bias);
+  if (rc != LA_OK) return rc;
+  const size_t ny = (size_t)B * block_frames * tokens_per_frame * channels * esize(out_dt);
+  const size_t nc = (size_t)B * tokens_per_frame * channels * esize(in_dt);
+  if (overlaps(y, ny, st->last, nc)) return LA_ERR_INVALID_ARG;
+  lavr::ConvPlan c{B, block_frames, tokens_per_frame, channels, block_frames, block_frames, kt};
+  const int e = lavr::launch_tconv(c, x, y, in_dt == LA_BF16, out_dt == LA_BF16, w, bias, st->last,
+                                   save ? st->last : nullptr, stream);
   if (e != 0) return LA_ERR_HIP;
   if (save) st->frames_done += block_frames;
   return LA_OK;

@@ -70,6 +70,14 @@ int launch_forward(const Plan& p, const void* q, const void* k, const void* v, v
                    const float* S_init, const float* z_init, float* S_save, float* z_save,
                    void* stream, void* const* events = nullptr, const Prologue* pro = nullptr);
 int launch_zero(float* p, size_t n, void* stream);
+
+// Cached temporal convolution of one call: F frames of P tokens x Ch channels
+// per batch row, blocks of F0 then BF frames, kt taps.
+struct ConvPlan {
+  int B, F, P, Ch, F0, BF, kt;
+};
+int launch_tconv(const ConvPlan& c, const void* x, void* y, int in_bf16, int out_bf16, const float* w,
+                 const float* bias, const void* cache_in, void* cache_out, void* stream);
 int launch_backward(const Plan& p, const void* q, const void* k, const void* v, const void* dout,
                     void* dq, void* dk, void* dv, int in_bf16, int grad_bf16, float eps, void* ws,
                     void* stream);

@@ -1573,6 +1573,121 @@ __global__ void k_fill_zero(float* p, size_t n) {
   if (i < n) p[i] = 0.f;
 }
 
+// ---------------------------------------------------------------- k_tconv
+//
+// Cached temporal convolution of the causal Mix-FFN: depthwise along frames,
+// y[t] = sum_i w[i] * x[t + i - 1] over the kt taps (kt = 3: frames t-1, t,
+// t+1; kt = 2: t-1, t), plus an optional bias.  Inside a block the taps see the
+// block's frames; before the first frame of the call they see the cache (the
+// previous block's last frame, or zeros), before a later block's first frame
+// the last frame of the block before, and after a block's last frame zeros.
+// Grid: x = 256-thread groups over (spatial position, 8-channel piece), y =
+// batch.  A thread owns one position's 8 channels and walks the call's frames
+// in order with the window (prev, cur, next) in registers and loads running
+// PF frames ahead, so every input element is read from memory once and every
+// output written once; consecutive threads cover consecutive 16-byte pieces of
+// a token row.  The frame after the call reads zero through the buffer range.
+struct ConvArgs {
+  const void* x;
+  void* y;
+  const float* w;            // (kt, Ch) taps, tap 0 = previous frame
+  const float* bias;         // (Ch) or nullptr
+  const void* cache_in;      // (B, P, Ch) in x's dtype, or nullptr (zeros)
+  void* cache_out;           // (B, P, Ch): receives the call's last frame, or nullptr
+  int F, P, Ch;              // frames of the call, tokens per frame, channels
+  int F0, BF;                // frames of the first block and of later blocks
+  int kt;
+  int seg;                   // frames per segment (grid z); a segment re-reads the frame before it
+};
+
+template <typename TIn, typename TOut>
+__global__ __launch_bounds__(NT) void k_tconv(ConvArgs a) {
+  constexpr int ES = (int)sizeof(TIn), EO = (int)sizeof(TOut);
+  constexpr int PF = 4;                                // ring of raw frames f .. f + 3
+  const int pieces = a.Ch / 8;
+  const int gid = blockIdx.x * NT + threadIdx.x;
+  if (gid >= a.P * pieces) return;
+  const int b = blockIdx.y;
+  const int pos = gid / pieces, cp = gid - pos * pieces;
+  const int c0 = 8 * cp;
+  // This thread's frames [fs, fe): segment blockIdx.z of a.seg frames.
+  const int fs = blockIdx.z * a.seg;
+  const int fe = min(a.F, fs + a.seg);
+  const uint32_t frame_in = (uint32_t)a.P * a.Ch * ES, frame_out = (uint32_t)a.P * a.Ch * EO;
+  const uint32_t col_in = (uint32_t)(pos * a.Ch + c0) * ES, col_out = (uint32_t)(pos * a.Ch + c0) * EO;
+  // Loads see frames up to fe (the next tap of the segment's last frame);
+  // stores only the segment's own frames.
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(static_cast<const char*>(a.x) + (size_t)b * a.F * frame_in,
+                                              (uint32_t)min(a.F, fe + 1) * frame_in);
+  const __amdgpu_buffer_rsrc_t ry =
+      make_rsrc(static_cast<char*>(a.y) + (size_t)b * a.F * frame_out, (uint32_t)fe * frame_out);
+
+  float w0[8], w1[8], w2[8], bs[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    w0[i] = a.w[c0 + i];
+    w1[i] = a.w[a.Ch + c0 + i];
+    w2[i] = a.kt == 3 ? a.w[2 * a.Ch + c0 + i] : 0.f;
+    bs[i] = a.bias != nullptr ? a.bias[c0 + i] : 0.f;
+  }
+  // The window stays in its raw input form (widened where used).  The frame
+  // before the segment: the previous frame of the call, else the cache, else 0.
+  Raw8<TIn> prev;
+  if (fs > 0) {
+    prev = bload8<TIn>(rx, (uint32_t)(fs - 1) * frame_in + col_in);
+  } else if (a.cache_in != nullptr) {
+    const TIn* cin = static_cast<const TIn*>(a.cache_in) + ((size_t)b * a.P + pos) * a.Ch + c0;
+#pragma unroll
+    for (int i = 0; i < ES / 2; ++i) prev.r[i] = *reinterpret_cast<const u32x4*>(cin + i * (16 / ES));
+  } else {
+#pragma unroll
+    for (int i = 0; i < ES / 2; ++i) prev.r[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+  Raw8<TIn> ring[PF];
+#pragma unroll
+  for (int k = 0; k < PF; ++k) ring[k] = bload8<TIn>(rx, (uint32_t)(fs + k) * frame_in + col_in);
+  // frames left in the block holding frame fs
+  int rem = fs < a.F0 ? a.F0 - fs : a.BF - (fs - a.F0) % a.BF;
+  // Whole passes of PF frames; frames past the segment compute on what the
+  // load range gives and their stores fall outside the store range (dropped),
+  // so no load is conditional.  Slot k holds frame f when frame f is produced,
+  // slot k + 1 frame f + 1; slot k is then refilled with frame f + PF.
+  for (int f0 = fs; f0 < fe; f0 += PF) {
+#pragma unroll
+    for (int k = 0; k < PF; ++k) {
+      const int f = f0 + k;
+      const bool block_end = rem == 1;
+      float xp[8], xc[8], xn[8], o[8];
+      widen8(prev, xp);
+      widen8(ring[k], xc);
+      widen8(ring[(k + 1) % PF], xn);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = bs[i] + w0[i] * xp[i] + w1[i] * xc[i] + (block_end ? 0.f : w2[i] * xn[i]);
+      if constexpr (EO == 2) {
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]), pack_bf16(o[4], o[5]), pack_bf16(o[6], o[7])},
+            ry, (uint32_t)f * frame_out + col_out, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{o[0], o[1], o[2], o[3]}), ry,
+                                               (uint32_t)f * frame_out + col_out, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{o[4], o[5], o[6], o[7]}), ry,
+                                               (uint32_t)f * frame_out + col_out + 16, 0, 0);
+      }
+      rem = block_end ? a.BF : rem - 1;
+      prev = ring[k];
+      ring[k] = bload8<TIn>(rx, (uint32_t)(f + PF) * frame_in + col_in);   // zeros past the load range
+    }
+  }
+  if (a.cache_out != nullptr && fe == a.F) {
+    // the call's last frame, read again (cache_out may be cache_in: this thread
+    // read its element of the old cache above)
+    const Raw8<TIn> r = bload8<TIn>(rx, (uint32_t)(a.F - 1) * frame_in + col_in);
+    TIn* cout = static_cast<TIn*>(a.cache_out) + ((size_t)b * a.P + pos) * a.Ch + c0;
+#pragma unroll
+    for (int i = 0; i < ES / 2; ++i) *reinterpret_cast<u32x4*>(cout + i * (16 / ES)) = r.r[i];
+  }
+}
+
 // ---------------------------------------------------------------- k_qk_rms
 //
 // Token scales of the q/k RMSNorm: 1 / sqrt(mean(x^2) + norm_eps) of each
@@ -1693,6 +1808,34 @@ int launch_rope_table(float* table, int pt, int ph, int pw, int max_frames, int 
   const long long nblk = (tot + nt - 1) / nt;
   hipLaunchKernelGGL(k_rope_table, dim3((unsigned)nblk), dim3(nt), 0, (hipStream_t)stream,
                      reinterpret_cast<float2*>(table), pt, ph, pw, max_frames, gh, gw, base);
+  return (int)hipGetLastError();
+}
+
+// Threads a long temporal-convolution call aims for (about 5 waves per SIMD;
+// measured on the 240-frame, 436800-column call: 3 segments 0.662 ms, 1 segment
+// 0.678, 8 segments 0.713, 15 segments 0.869).
+#ifndef TCONV_TARGET_THREADS
+#define TCONV_TARGET_THREADS (5LL * 256 * 4 * 256)
+#endif
+int launch_tconv(const ConvPlan& c, const void* x, void* y, int in_bf16, int out_bf16, const float* w,
+                 const float* bias, const void* cache_in, void* cache_out, void* stream) {
+  ConvArgs a;
+  a.x = x; a.y = y; a.w = w; a.bias = bias; a.cache_in = cache_in; a.cache_out = cache_out;
+  a.F = c.F; a.P = c.P; a.Ch = c.Ch; a.F0 = c.F0; a.BF = c.BF; a.kt = c.kt;
+  // Frame segments multiply the threads of a long call; each re-reads one
+  // frame.  A call with a cache runs as one segment: its first segment reads
+  // the cache that its last one may overwrite.
+  const long long threads = (long long)c.P * (c.Ch / 8);
+  long long nseg = (TCONV_TARGET_THREADS + threads * c.B / 2) / (threads * c.B);   // rounded
+  nseg = std::max(1LL, std::min(nseg, (long long)c.F / 16));
+  if (cache_in != nullptr || cache_out != nullptr) nseg = 1;
+  a.seg = (int)((c.F + nseg - 1) / nseg);
+  const dim3 grid((unsigned)((threads + NT - 1) / NT), (unsigned)c.B, (unsigned)((c.F + a.seg - 1) / a.seg));
+  hipStream_t s = (hipStream_t)stream;
+  if (in_bf16 && out_bf16) hipLaunchKernelGGL((k_tconv<uint16_t, uint16_t>), grid, dim3(NT), 0, s, a);
+  else if (in_bf16) hipLaunchKernelGGL((k_tconv<uint16_t, float>), grid, dim3(NT), 0, s, a);
+  else if (out_bf16) hipLaunchKernelGGL((k_tconv<float, uint16_t>), grid, dim3(NT), 0, s, a);
+  else hipLaunchKernelGGL((k_tconv<float, float>), grid, dim3(NT), 0, s, a);
   return (int)hipGetLastError();
 }
 

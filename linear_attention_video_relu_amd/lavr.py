@@ -33,6 +33,11 @@ class LaState(ctypes.Structure):
                 ("H", ctypes.c_int), ("head_dim", ctypes.c_int), ("frames_done", ctypes.c_longlong)]
 
 
+class LaConvState(ctypes.Structure):
+    _fields_ = [("last", ctypes.c_void_p), ("B", ctypes.c_int), ("tokens_per_frame", ctypes.c_int),
+                ("channels", ctypes.c_int), ("dtype", ctypes.c_int), ("frames_done", ctypes.c_longlong)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
@@ -61,6 +66,10 @@ def _load():
         "la_stream_block_qkv": (c_int, [ctypes.POINTER(LaState), c_vp, c_vp, c_int, c_int] + [c_int] * 5 +
                                 [ctypes.POINTER(LaRope), c_float, c_vp, c_vp, c_float, c_int, c_vp,
                                  c_size, c_vp]),
+        "la_temporal_conv": (c_int, [c_vp, c_vp] + [c_int] * 9 + [c_vp, c_vp, c_vp]),
+        "la_conv_state_init": (c_int, [ctypes.POINTER(LaConvState), c_vp] + [c_int] * 4 + [c_vp]),
+        "la_temporal_conv_stream_block": (c_int, [ctypes.POINTER(LaConvState), c_vp, c_vp] + [c_int] * 6 +
+                                          [c_vp, c_vp, c_int, c_vp]),
         "la_state_init": (c_int, [ctypes.POINTER(LaState), c_vp, c_vp, c_int, c_int, c_int, c_vp]),
         "la_stream_block": (c_int, [ctypes.POINTER(LaState), c_vp, c_vp, c_vp, c_vp, c_int, c_int,
                                     c_int, c_int, c_int, c_int, c_int, ctypes.POINTER(LaRope),
@@ -80,6 +89,7 @@ lib = _load()
 EXPORTS = ("rope_table_bytes", "rope_table_build", "la_workspace_bytes", "la_block_causal_forward",
            "la_block_causal_forward_timed", "la_backward_workspace_bytes", "la_block_causal_backward",
            "la_qkv_workspace_bytes", "la_block_causal_forward_qkv", "la_stream_block_qkv",
+           "la_temporal_conv", "la_conv_state_init", "la_temporal_conv_stream_block",
            "la_state_init", "la_stream_block", "la_status_string", "la_version")
 
 
@@ -263,6 +273,72 @@ def block_causal_forward_qkv(qkv, heads, block_frames, tokens_per_frame, rope=No
                                            float(norm_eps), _ptr(ws), ws.numel() * ws.element_size(),
                                            _stream(qkv.device)), "la_block_causal_forward_qkv")
     return out
+
+
+# ------------------------------------------------- cached temporal convolution
+
+def _check_conv_args(x, w, bias):
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda" or x.dim() != 3 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous CUDA (B, N, channels) tensor")
+    Ch = x.shape[2]
+    if (not isinstance(w, torch.Tensor) or w.dtype != torch.float32 or w.dim() != 2 or w.shape[1] != Ch
+            or w.shape[0] not in (2, 3) or not w.is_contiguous() or w.device != x.device):
+        raise ValueError("w must be a contiguous float32 (kt, channels) tensor on x's device, kt 2 or 3")
+    if bias is not None and (not isinstance(bias, torch.Tensor) or bias.dtype != torch.float32
+                             or bias.shape != (Ch,) or not bias.is_contiguous() or bias.device != x.device):
+        raise ValueError("bias must be a contiguous float32 (channels,) tensor on x's device")
+    return Ch, w.shape[0]
+
+
+def temporal_conv(x, w, tokens_per_frame, block_frames, bias=None, first_block_frames=None, out=None,
+                  out_dtype=None):
+    """One-shot cached temporal convolution of x (B, N, channels); see la_temporal_conv."""
+    Ch, kt = _check_conv_args(x, w, bias)
+    B, N = x.shape[0], x.shape[1]
+    if N % tokens_per_frame:
+        raise ValueError("N must be a multiple of tokens_per_frame")
+    out_dtype = x.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, N, Ch), dtype=out_dtype, device=x.device)
+    elif out.shape != x.shape or out.dtype != out_dtype or not out.is_contiguous() or out.device != x.device:
+        raise ValueError("out must be a contiguous tensor of x's shape and out_dtype")
+    _check(lib.la_temporal_conv(_ptr(x), _ptr(out), _dtype_code(x.dtype), _dtype_code(out_dtype), B,
+                                N // tokens_per_frame, int(tokens_per_frame), Ch, int(block_frames),
+                                int(first_block_frames or 0), kt, _ptr(w), _gptr(bias), _stream(x.device)),
+           "la_temporal_conv")
+    return out
+
+
+class ConvState:
+    """Streaming cache of the temporal convolution (the last committed frame)."""
+
+    def __init__(self, B, tokens_per_frame, channels, dtype=torch.bfloat16, device="cuda"):
+        self.device = torch.device(device)
+        self.last = torch.empty((B, tokens_per_frame, channels), dtype=dtype, device=self.device)
+        self.desc = LaConvState()
+        _check(lib.la_conv_state_init(ctypes.byref(self.desc), _ptr(self.last), _dtype_code(dtype), int(B),
+                                      int(tokens_per_frame), int(channels), _stream(self.device)),
+               "la_conv_state_init")
+
+    @property
+    def frames_done(self):
+        return int(self.desc.frames_done)
+
+    def step(self, x, w, bias=None, save=True, out=None, out_dtype=None):
+        """One block (all of x's frames) against the cache; see la_temporal_conv_stream_block."""
+        Ch, kt = _check_conv_args(x, w, bias)
+        B, N = x.shape[0], x.shape[1]
+        tpf = int(self.desc.tokens_per_frame)
+        if N % tpf:
+            raise ValueError("N must be a multiple of the cache's tokens_per_frame")
+        out_dtype = x.dtype if out_dtype is None else out_dtype
+        if out is None:
+            out = torch.empty((B, N, Ch), dtype=out_dtype, device=x.device)
+        _check(lib.la_temporal_conv_stream_block(ctypes.byref(self.desc), _ptr(x), _ptr(out),
+                                                 _dtype_code(out_dtype), B, N // tpf, tpf, Ch, kt, _ptr(w),
+                                                 _gptr(bias), int(bool(save)), _stream(x.device)),
+               "la_temporal_conv_stream_block")
+        return out
 
 
 # ------------------------------------------------------------------ backward

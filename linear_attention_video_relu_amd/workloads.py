@@ -162,6 +162,16 @@ def draw_norm_weight(cfg, which):
     return (1.0 + 0.5 * rng.standard_normal(cfg["H"] * cfg["head_dim"])).astype(np.float32)
 
 
+def draw_conv(seed, B, N, Ch, kt):
+    """Seeded inputs of the temporal convolution: x (B, N, Ch) standard normal
+    float32, taps w (kt, Ch) and bias (Ch) as N(0, 1) / sqrt(kt) and 0.1 * N(0, 1)."""
+    rng = np.random.default_rng(np.random.SeedSequence([ROOT_SEED, 1000 + seed]))
+    x = rng.standard_normal((B, N, Ch), dtype=np.float32)
+    w = (rng.standard_normal((kt, Ch)) / np.sqrt(kt)).astype(np.float32)
+    b = (0.1 * rng.standard_normal(Ch)).astype(np.float32)
+    return x, w, b
+
+
 def fuse_qkv(q, k, v):
     """(B, N, H, d) q, k, v arrays -> one (B, N, 3, H * d) array with q | k | v rows."""
     B, N, H, d = q.shape

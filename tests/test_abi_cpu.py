@@ -250,3 +250,45 @@ def test_stream_block_qkv_state_checks(lavr):
     assert f(ctypes.byref(st), qkv, out, 1, 1, 2, 4, 32, 3, 6, None, 1e-8, g, None, -1.0, 1, ws, 1 << 24,
              None) == 1
     assert st.frames_done == 0
+
+
+def call_tconv(lavr, **kw):
+    args = dict(x=FAKE, y=FAKE + 0x1000000, in_dt=lavr.LA_BF16, out_dt=lavr.LA_BF16, B=1, frames=8,
+                tpf=6, ch=64, bf=2, f0=0, kt=3, w=FAKE + 0x2000000, bias=FAKE + 0x2001000)
+    args.update(kw)
+    vp = ctypes.c_void_p
+    return lavr.lib.la_temporal_conv(vp(args["x"]), vp(args["y"]), args["in_dt"], args["out_dt"], args["B"],
+                                     args["frames"], args["tpf"], args["ch"], args["bf"], args["f0"],
+                                     args["kt"], vp(args["w"]), vp(args["bias"]), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=0), 1),
+    (dict(w=0), 1),                          # weights are required, bias is not
+    (dict(y=FAKE + 8), 1),                   # misaligned
+    (dict(ch=60), 1),                        # channels not a multiple of 8
+    (dict(kt=4), 1),
+    (dict(kt=1), 1),
+    (dict(bf=0), 1),
+    (dict(f0=-1), 1),
+    (dict(frames=0), 1),
+    (dict(y=FAKE + 512), 1),                 # y overlaps x
+    (dict(w=FAKE + 0x1000000 + 32), 1),      # w overlaps y
+    (dict(frames=1 << 20, tpf=1024, ch=2048), 2),   # a batch row past 4 GiB
+])
+def test_tconv_rejects_bad_arguments(lavr, kw, code):
+    assert call_tconv(lavr, **kw) == code
+
+
+def test_tconv_stream_state_checks(lavr):
+    st = lavr.LaConvState()
+    st.last, st.B, st.tokens_per_frame, st.channels, st.dtype, st.frames_done = FAKE, 2, 6, 64, 1, 0
+    f = lavr.lib.la_temporal_conv_stream_block
+    vp = ctypes.c_void_p
+    x, y, w = vp(FAKE + 0x1000000), vp(FAKE + 0x2000000), vp(FAKE + 0x3000000)
+    assert f(ctypes.byref(st), x, y, 1, 1, 3, 6, 64, 3, w, None, 1, None) == 3       # B differs
+    assert f(ctypes.byref(st), x, y, 1, 2, 3, 6, 72, 3, w, None, 1, None) == 3       # channels differ
+    assert f(ctypes.byref(st), x, vp(FAKE + 64), 1, 2, 3, 6, 64, 3, w, None, 1, None) == 1   # y over the cache
+    assert f(ctypes.byref(st), x, y, 1, 2, 0, 6, 64, 3, w, None, 1, None) == 1       # no frames
+    assert st.frames_done == 0
+    assert lavr.lib.la_conv_state_init(ctypes.byref(st), vp(FAKE + 4), 1, 2, 6, 64, None) == 1
