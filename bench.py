@@ -276,7 +276,7 @@ def main():
         result["tconv"] = bench_tconv(lavr, torch, dev, cfg, args.tconv_steps)
     if args.prologue_steps > 0:
         result["prologue"] = bench_prologue(lavr, torch, dev, cfg, q, k, v, rope, args.prologue_steps)
-    if args.backward_steps > 0 and d == 32:
+    if args.backward_steps > 0:
         del out
         result["backward"] = bench_backward(lavr, torch, dev, cfg, q, k, v, rope, args.backward_steps)
 
@@ -371,7 +371,7 @@ def bench_backward(lavr, torch, dev, cfg, q, k, v, rope, steps):
     gen.manual_seed(7)
     g = torch.randn(q.shape, generator=gen, device=dev, dtype=torch.float32).to(q.dtype)
     grads = [torch.empty_like(q) for _ in range(3)]
-    need = lavr.backward_workspace_bytes(B, H, cfg["frames"], tpf, bf)
+    need = lavr.backward_workspace_bytes(B, H, cfg["frames"], tpf, bf, head_dim=d)
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     code = lavr._dtype_code(q.dtype)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)

@@ -143,7 +143,7 @@ int la_block_causal_forward_timed(const void* q, const void* k, const void* v, v
                                   void* const* events);
 
 /* Workspace bytes needed by la_block_causal_backward for this shape (0 for
- * invalid sizes and for head dims the backward does not build). */
+ * invalid sizes). */
 size_t la_backward_workspace_bytes(int B, int H, int head_dim, int frames, int tokens_per_frame,
                                    int block_frames, int first_block_frames);
 
@@ -154,8 +154,8 @@ size_t la_backward_workspace_bytes(int B, int H, int head_dim, int frames, int t
  * Causality"); this is its exact derivative (ReLU's derivative taken as 0 at
  * 0), for training.  q, k, v and dout have dtype in_dt and layout (B, N, H,
  * head_dim); dq, dk, dv have dtype grad_dt and the same layout, and must not
- * overlap the inputs or each other.  Only head_dim 32 is built (other valid
- * head dims return LA_ERR_UNSUPPORTED).  The block states are formed again from
+ * overlap the inputs or each other.  Head dims 32 and 64 are built, as for the
+ * forward.  The block states are formed again from
  * k and v.  ws (256-byte aligned, ws_bytes >= la_backward_workspace_bytes) is
  * caller-owned scratch.  Same status codes and stream semantics as the forward. */
 int la_block_causal_backward(const void* q, const void* k, const void* v, const void* dout,

@@ -309,7 +309,6 @@ int la_block_causal_forward_timed(const void* q, const void* k, const void* v, v
 size_t la_backward_workspace_bytes(int B, int H, int head_dim, int frames, int tokens_per_frame,
                                    int block_frames, int first_block_frames) {
   Plan p;
-  if (head_dim != 32) return 0;
   if (make_plan(&p, B, H, head_dim, frames, tokens_per_frame, block_frames, first_block_frames,
                 nullptr, 0, LA_BF16) != LA_OK)
     return 0;
@@ -327,7 +326,6 @@ int la_block_causal_backward(const void* q, const void* k, const void* v, const 
   int st = make_plan(&p, B, H, head_dim, frames, tokens_per_frame, block_frames, first_block_frames,
                      rope, 0, in_dt);
   if (st != LA_OK) return st;
-  if (head_dim != 32) return LA_ERR_UNSUPPORTED;
   // inputs q, k, v, dout; gradient outputs dq, dk, dv: each output checked
   // against the inputs (as the forward checks out) and against the others.
   const void* ins[4] = {q, k, v, dout};

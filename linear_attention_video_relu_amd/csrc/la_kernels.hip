@@ -991,7 +991,6 @@ __global__ __launch_bounds__(NT, (DH == 32 && !NRM) ? 4 : 2) void k_readout(Read
 
 // =================================================================== backward
 
-constexpr int REC32 = D * D + D;   // floats of a head-dim-32 record
 //
 // The exact derivative of the forward for an output gradient g, per (batch,
 // head); for token n of block j (p = phi(q_n), r = R p, den = zbar_j . p + eps,
@@ -1056,44 +1055,87 @@ __device__ __forceinline__ void widen8(const Raw8<float>& r, float* x) {
 // 8ch + 4t .. +3: with both tiles, exactly the channels its inputs hold.
 __device__ __forceinline__ int perm_row(int t, int i) { return 8 * (i >> 2) + 4 * t + (i & 3); }
 
-// A operands of a 32 x 32 fp32 matrix m (row-major) or of its transpose, for
-// both tiles: bf16 hi/lo pairs, or 8 floats per tile for the fp32 MFMA.
+// Operand tiles of one 32 x 32 block of an fp32 matrix m with row stride ld
+// (element [r][c] = m[r * ld + c]), or of the block's transpose (TR: [r][c] =
+// m[c * ld + r]), for both 16-row tiles, parked in LDS: slot (tile * 2 + part)
+// of `op` holds, per lane, the bf16 hi (part 0) and lo (part 1) of the lane's 8
+// values, or for fp32 values 0-3 (part 0) and 4-7 (part 1).  16-byte slots
+// per lane keep the reads conflict-free.
 template <bool BF, bool TR>
-__device__ __forceinline__ void perm_tiles(const float* m, int lane, u32x4* hi, u32x4* lo, float (*fs)[8]) {
+__device__ __forceinline__ void put_block_ops(const float* m, int ld, int lane, u32x4* op) {
   const int i = lane & 15, kc = lane >> 4;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int row = perm_row(t, i);
     float sv[8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) sv[s] = TR ? m[(8 * kc + s) * D + row] : m[row * D + 8 * kc + s];
+    for (int s = 0; s < 8; ++s) sv[s] = TR ? m[(8 * kc + s) * ld + row] : m[row * ld + 8 * kc + s];
     if constexpr (BF) {
-      split8(sv, hi[t], lo[t]);
+      u32x4 hi, lo;
+      split8(sv, hi, lo);
+      op[(t * 2) * 64 + lane] = hi;
+      op[(t * 2 + 1) * 64 + lane] = lo;
     } else {
+      op[(t * 2) * 64 + lane] = __builtin_bit_cast(u32x4, f32x4{sv[0], sv[1], sv[2], sv[3]});
+      op[(t * 2 + 1) * 64 + lane] = __builtin_bit_cast(u32x4, f32x4{sv[4], sv[5], sv[6], sv[7]});
+    }
+  }
+}
+constexpr int OPS_BLOCK = 4 * 64;                   // u32x4 slots of one block's operand tiles
+
+// c[t] += (block, tile t) x for the lane's token; x as bf16 hi/lo (xl may be
+// null: x exact in bf16) or 8 floats.  Output tile t, lane row ch holds the
+// block's output channels 8ch + 4t .. +3 (row-permuted operands).
+template <bool BF>
+__device__ __forceinline__ void mv_acc(const u32x4* op, int lane, u32x4 xh, const u32x4* xl, const float* xf,
+                                       f32x4* c) {
 #pragma unroll
-      for (int s = 0; s < 8; ++s) fs[t][s] = sv[s];
+  for (int t = 0; t < 2; ++t) {
+    const u32x4 p0 = op[(t * 2) * 64 + lane], p1 = op[(t * 2 + 1) * 64 + lane];
+    if constexpr (BF) {
+      c[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(p0), as_bf16x8(xh), c[t], 0, 0, 0);
+      if (xl != nullptr) c[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(p0), as_bf16x8(*xl), c[t], 0, 0, 0);
+      c[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(p1), as_bf16x8(xh), c[t], 0, 0, 0);
+    } else {
+      const f32x4 f0 = __builtin_bit_cast(f32x4, p0), f1 = __builtin_bit_cast(f32x4, p1);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) c[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(f0[s], xf[s], c[t], 0, 0, 0);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) c[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(f1[s], xf[4 + s], c[t], 0, 0, 0);
     }
   }
 }
 
-// y = M x for the lane's token: x as bf16 hi/lo (xl may be null: x exact in
-// bf16) or as 8 floats; y in the lane's 8 channels.
-template <bool BF>
-__device__ __forceinline__ void matvec(const u32x4* Mh, const u32x4* Ml, const float (*Mf)[8],
-                                       u32x4 xh, const u32x4* xl, const float* xf, float* y) {
+__device__ __forceinline__ void take8(const f32x4* c, float* y) {
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    f32x4 c = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (BF) {
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Mh[t]), as_bf16x8(xh), c, 0, 0, 0);
-      if (xl != nullptr) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Mh[t]), as_bf16x8(*xl), c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Ml[t]), as_bf16x8(xh), c, 0, 0, 0);
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) y[4 * t + v] = c[t][v];
+}
+
+// Operand blocks of a matrix per workgroup: at head dim 32 one 32 x 32 block
+// per head of the pair, at 64 the four quadrants (a, b) of the head's 64 x 64
+// matrix (block 2a + b maps input half b to output half a).  Blocks 0 .. NB-1
+// hold the matrix, NB .. 2NB-1 its transpose; the four waves form them.
+template <bool BF, bool W64>
+__device__ __forceinline__ void form_ops(u32x4* ops, const float* rec0, const float* rec1, int w, int lane) {
+  constexpr int NB = W64 ? 4 : 2;
+#pragma unroll
+  for (int k = 0; k < 2 * NB / 4; ++k) {
+    const int bo = w + 4 * k;
+    const int tr = bo / NB, blk = bo - tr * NB;
+    u32x4* op = ops + bo * OPS_BLOCK;
+    if constexpr (W64) {
+      const int qa = blk >> 1, qb = blk & 1;
+      // block (qa, qb) of M: rows 32qa.., columns 32qb..; of M^T: the
+      // transpose of M's block (qb, qa)
+      if (tr == 0) put_block_ops<BF, false>(rec0 + (32 * qa) * 64 + 32 * qb, 64, lane, op);
+      else put_block_ops<BF, true>(rec0 + (32 * qb) * 64 + 32 * qa, 64, lane, op);
     } else {
-#pragma unroll
-      for (int s = 0; s < 8; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(Mf[t][s], xf[s], c, 0, 0, 0);
+      const float* m = blk == 0 ? rec0 : rec1;
+      if (tr == 0) put_block_ops<BF, false>(m, 32, lane, op);
+      else put_block_ops<BF, true>(m, 32, lane, op);
     }
-#pragma unroll
-    for (int v = 0; v < 4; ++v) y[4 * t + v] = c[v];
   }
 }
 
@@ -1134,16 +1176,22 @@ __device__ __forceinline__ void store_pair(const u32x4* pk, int nh, int tl, __am
 
 // ------------------------------------------------------------------ k_bw_kv
 //
-// Grid and token layout as k_readout (tiles of one block, head pairs).  Per
-// token: kappa = R phi(k), dv = dS kappa, dkappa = dS^T v, dk = [k > 0]
-// (R^T dkappa + dz), both products on MFMA with row-permuted A operands.
+// Grid and token layout as k_readout (tiles of one block; a head pair at head
+// dim 32, one head at 64).  Per token: kappa = R phi(k), dv = dS kappa,
+// dkappa = dS^T v, dk = [k > 0] (R^T dkappa + dz), both products on MFMA with
+// row-permuted operand blocks of dS and dS^T read from LDS (at head dim 64 each
+// output half sums the products of both input halves).
 
-template <typename TIn, typename TOut, bool P2>
+template <typename TIn, typename TOut, bool P2, int DH>
 __global__ __launch_bounds__(NT, 2) void k_bw_kv(BwKVArgs a) {
   constexpr bool BF = sizeof(TIn) == 2;
+  constexpr bool W64 = DH == 64;
+  constexpr int NB = W64 ? 4 : 2;
+  constexpr int RECN = DH * DH + DH;
   constexpr int ES = (int)sizeof(TIn), EO = (int)sizeof(TOut);
   extern __shared__ __align__(16) unsigned char smem[];
-  float2* tab = reinterpret_cast<float2*>(smem);
+  u32x4* ops = reinterpret_cast<u32x4*>(smem);                      // [2 NB blocks][4 slots][64 lanes]
+  float2* tab = reinterpret_cast<float2*>(ops + 2 * NB * OPS_BLOCK);
 
   const int g = blockIdx.x % a.hg;
   const int ti = blockIdx.x / a.hg;
@@ -1159,41 +1207,40 @@ __global__ __launch_bounds__(NT, 2) void k_bw_kv(BwKVArgs a) {
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int tl = lane & 15, ch = lane >> 4;
-  const int h0 = 2 * g;
-  const int nh = min(2, a.H - h0);
+  const int h0 = W64 ? g : 2 * g;
+  const int nh = W64 ? 2 : min(2, a.H - h0);      // 32-channel halves that hold data
   const int ngroups = (t1 - t0 + 15) >> 4;
 
-  const int RB = a.H * D * ES, RO = a.H * D * EO;
+  const int RB = a.H * DH * ES, RO = a.H * DH * EO;
   const size_t row0 = (size_t)b * a.N + t0;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const char*>(a.k) + row0 * RB, (uint32_t)(t1 - t0) * RB);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const char*>(a.v) + row0 * RB, (uint32_t)(t1 - t0) * RB);
   const __amdgpu_buffer_rsrc_t rdk = make_rsrc(static_cast<char*>(a.dk) + row0 * RO, (uint32_t)(t1 - t0) * RO);
   const __amdgpu_buffer_rsrc_t rdv = make_rsrc(static_cast<char*>(a.dv) + row0 * RO, (uint32_t)(t1 - t0) * RO);
-  int ioff = (w * 16 + tl) * RB + (h0 * D + 8 * ch) * ES;
-  int ooff = (w * 16) * RO + h0 * D * EO;
+  int ioff = (w * 16 + tl) * RB + (g * 64 + 8 * ch) * ES;
+  int ooff = (w * 16) * RO + g * 64 * EO;
   const int o_one = tl * RO + 8 * ch * EO;
   const int o_pair = (tl & 7) * RO + ((tl >> 3) * D + 8 * ch) * EO;
 
   const TabWindow win = stage_table(tab, a.rope, a.pos.t0, t0, t1, a.pos.mag_tpf);
-  RopeLane<P2> rl;
+  RopeLane<P2> rl, rl1;                  // rl1: the second half at head dim 64
   TokPos tp;
   if (rope_on) {
     rl.init(a.rope, win, ch);
+    if constexpr (W64) rl1.init(a.rope, win, ch + 4);
     tp.init(t0 + w * 16 + tl, a.pos);
   }
 
-  // dS (for dv) and dS^T (for dkappa) of block j, per head; dz slices.
-  u32x4 Nh[2][2], Nl[2][2], Th[2][2], Tl[2][2];
-  float Nf[2][2][8], Tf[2][2][8];
+  // dS and dS^T operand blocks of block j in LDS; dz slices per half.
+  const float* rec0 = a.suffix + ((size_t)(b * a.H + h0) * a.nb + j) * RECN;
+  const float* rec1 = a.suffix + ((size_t)(b * a.H + h0 + (nh - 1)) * a.nb + j) * RECN;
+  form_ops<BF, W64>(ops, rec0, rec1, w, lane);
   float dzb[2][8];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int hd = min(h, nh - 1);
-    const float* rec = a.suffix + ((size_t)(b * a.H + h0 + hd) * a.nb + j) * REC32;
-    perm_tiles<BF, false>(rec, lane, Nh[h], Nl[h], Nf[h]);
-    perm_tiles<BF, true>(rec, lane, Th[h], Tl[h], Tf[h]);
+    const float* zp = W64 ? rec0 + DH * DH + h * D : (h == 0 ? rec0 : rec1) + D * D;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dzb[h][i] = rec[D * D + 8 * ch + i];
+    for (int i = 0; i < 8; ++i) dzb[h][i] = zp[8 * ch + i];
   }
 
   struct Buf { Raw8<TIn> k[2], v[2]; };
@@ -1211,33 +1258,50 @@ __global__ __launch_bounds__(NT, 2) void k_bw_kv(BwKVArgs a) {
   __syncthreads();
 
   auto run_group = [&](const Buf& bf) {
-    float2 cs[4];
+    // At head dim 64 the operand blocks (32 tiles) are read from LDS where they
+    // are used; an empty asm with a memory clobber keeps the compiler from
+    // hoisting those reads out of the loop into 128 registers.
+    if constexpr (W64) __asm__ volatile("" ::: "memory");
+    float2 cs[4], cs1[4];
     if (rope_on) {
       rl.fetch(tab, tp, win, cs);
+      if constexpr (W64) rl1.fetch(tab, tp, win, cs1);
       tp.advance(a.pos);
+    }
+    float kx[2][8], kap[2][8], vx[2][8];
+    u32x4 kh[2], kl[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      relu_widen(bf.k[h], kx[h]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) kap[h][i] = kx[h][i];
+      if (rope_on) rotate8(kap[h], (W64 && h == 1) ? cs1 : cs);
+      if constexpr (BF) split8(kap[h], kh[h], kl[h]);
+      else widen8(bf.v[h], vx[h]);
     }
     u32x4 pkk[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}}, pkv[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < 2; ++h) {                   // output half
       if (h >= nh) break;
-      float kx[8], kap[8], vx[8], dv[8], dka[8];
-      relu_widen(bf.k[h], kx);
+      f32x4 cv[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, ck[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) kap[i] = kx[i];
-      if (rope_on) rotate8(kap, cs);
-      widen8(bf.v[h], vx);
-      if constexpr (BF) {
-        u32x4 kh, klo;
-        split8(kap, kh, klo);
-        matvec<true>(Nh[h], Nl[h], nullptr, kh, &klo, nullptr, dv);
-        matvec<true>(Th[h], Tl[h], nullptr, bf.v[h].r[0], nullptr, nullptr, dka);   // v is exact in bf16
-      } else {
-        matvec<false>(nullptr, nullptr, Nf[h], u32x4{}, nullptr, kap, dv);
-        matvec<false>(nullptr, nullptr, Tf[h], u32x4{}, nullptr, vx, dka);
+      for (int x = 0; x < (W64 ? 2 : 1); ++x) {     // input half
+        const int xi = W64 ? x : h;
+        const int blk = W64 ? 2 * h + x : h;
+        if constexpr (BF) {
+          mv_acc<true>(ops + blk * OPS_BLOCK, lane, kh[xi], &kl[xi], nullptr, cv);
+          mv_acc<true>(ops + (NB + blk) * OPS_BLOCK, lane, bf.v[xi].r[0], nullptr, nullptr, ck);   // v exact in bf16
+        } else {
+          mv_acc<false>(ops + blk * OPS_BLOCK, lane, u32x4{}, nullptr, kap[xi], cv);
+          mv_acc<false>(ops + (NB + blk) * OPS_BLOCK, lane, u32x4{}, nullptr, vx[xi], ck);
+        }
       }
-      if (rope_on) unrotate8(dka, cs);
+      float dv[8], dka[8];
+      take8(cv, dv);
+      take8(ck, dka);
+      if (rope_on) unrotate8(dka, (W64 && h == 1) ? cs1 : cs);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) dka[i] = kx[i] > 0.f ? dka[i] + dzb[h][i] : 0.f;
+      for (int i = 0; i < 8; ++i) dka[i] = kx[h][i] > 0.f ? dka[i] + dzb[h][i] : 0.f;
       put8<EO>(dka, h, pkk, rdk, ooff + o_one + h * D * EO);
       put8<EO>(dv, h, pkv, rdv, ooff + o_one + h * D * EO);
     }
@@ -1258,26 +1322,33 @@ __global__ __launch_bounds__(NT, 2) void k_bw_kv(BwKVArgs a) {
 
 // ------------------------------------------------------------------- k_bw_q
 //
-// Grid as k_block_state (chunks of one block, head pairs); token layout as
-// k_readout, wave w taking the chunk's 16-token groups w, w+4, ...  Per token:
-// num = Sbar r, den, out, a, beta, Sbar^T a (MFMA, row-permuted operands) and
-// dq.  The chunk's G = sum a r^T goes through a per-wave LDS tile [16 tokens]
-// [2 heads x 32] holding a and r (bf16 hi and lo, or fp32), read back
-// transposed into 32x32 MFMAs over the group's tokens; gz = sum beta p stays in
-// registers.  At the end the four waves' partials are added through LDS and
-// written as the chunk's (G, gz) records.
+// Grid as k_block_state (chunks of one block; a head pair at head dim 32, one
+// head at 64); token layout as k_readout, wave w taking the chunk's 16-token
+// groups w, w+4, ...  Per token: num = Sbar r, den, a, beta, Sbar^T a (MFMA,
+// row-permuted operand blocks read from LDS) and dq.  The chunk's G = sum a r^T
+// goes through a per-wave LDS tile [16 tokens][2 halves x 32] holding a and r
+// (bf16 hi and lo, or fp32), read back transposed into 32x32 MFMAs over the
+// group's tokens: one 32 x 32 block per head at head dim 32, the four quadrants
+// of the 64 x 64 G at 64.  gz = sum beta p stays in registers.  At the end the
+// four waves' partials are added through LDS (over the tiles and operand
+// blocks, no longer needed) and written as the chunk's (G, gz) records.
 
-template <typename TIn, typename TOut, bool P2>
+template <typename TIn, typename TOut, bool P2, int DH>
 __global__ __launch_bounds__(NT, 2) void k_bw_q(BwQArgs a) {
   constexpr bool BF = sizeof(TIn) == 2;
+  constexpr bool W64 = DH == 64;
+  constexpr int NB = W64 ? 4 : 2;                    // operand blocks per matrix, G accumulators
+  constexpr int RECN = DH * DH + DH;
   constexpr int ES = (int)sizeof(TIn), EO = (int)sizeof(TOut);
   constexpr int WT = 16 * TCOLS;                     // elements of one wave tile array
   constexpr int WAVE_BYTES = BF ? 4 * WT * 2 : 2 * WT * 4;   // a hi/lo, r hi/lo (bf16) or a, r (fp32)
+  static_assert(4 * WAVE_BYTES + 2 * NB * OPS_BLOCK * 16 >= 4 * NB * 1024 * 4, "reduction space");
   extern __shared__ __align__(16) unsigned char smem[];
-  float* red = reinterpret_cast<float*>(smem);                // [4 waves][2 heads][1024] at the end
-  float* zred = red + 4 * 2 * D * D;                           // [4 waves][2 heads][32]
-  u32x4* ops = reinterpret_cast<u32x4*>(zred + 4 * 2 * D);     // [16 operands][64 lanes] (see below)
-  float2* tab = reinterpret_cast<float2*>(ops + 16 * 64);
+  u32x4* ops = reinterpret_cast<u32x4*>(smem + 4 * WAVE_BYTES);   // [2 NB blocks][4 slots][64 lanes]
+  float* zred = reinterpret_cast<float*>(ops + 2 * NB * OPS_BLOCK);   // [4 waves][2 halves][32]
+  float* zl = zred + 4 * 2 * D;                                          // zbar of the block (64)
+  float2* tab = reinterpret_cast<float2*>(zl + 2 * D);
+  float* red = reinterpret_cast<float*>(smem);       // after the loop: [4 waves][NB][1024] over tiles + ops
 
   const int g = blockIdx.x % a.hg;
   const int ci = blockIdx.x / a.hg;
@@ -1292,84 +1363,49 @@ __global__ __launch_bounds__(NT, 2) void k_bw_q(BwQArgs a) {
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int tl = lane & 15, ch = lane >> 4;
-  const int h0 = 2 * g;
-  const int nh = min(2, a.H - h0);
+  const int h0 = W64 ? g : 2 * g;
+  const int nh = W64 ? 2 : min(2, a.H - h0);      // 32-channel halves that hold data
   const int ngroups = (c1 - c0 + 15) >> 4;
   unsigned char* wtile = smem + w * WAVE_BYTES;
 
-  const int RB = a.H * D * ES, RO = a.H * D * EO;
+  const int RB = a.H * DH * ES, RO = a.H * DH * EO;
   const size_t row0 = (size_t)b * a.N + c0;
   const uint32_t span = (uint32_t)(c1 - c0);
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(static_cast<const char*>(a.q) + row0 * RB, span * RB);
   const __amdgpu_buffer_rsrc_t rg = make_rsrc(static_cast<const char*>(a.g) + row0 * RB, span * RB);
   const __amdgpu_buffer_rsrc_t rdq = make_rsrc(static_cast<char*>(a.dq) + row0 * RO, span * RO);
-  int ioff = (w * 16 + tl) * RB + (h0 * D + 8 * ch) * ES;
-  int ooff = (w * 16) * RO + h0 * D * EO;
+  int ioff = (w * 16 + tl) * RB + (g * 64 + 8 * ch) * ES;
+  int ooff = (w * 16) * RO + g * 64 * EO;
   const int o_one = tl * RO + 8 * ch * EO;
   const int o_pair = (tl & 7) * RO + ((tl >> 3) * D + 8 * ch) * EO;
 
   const TabWindow win = stage_table(tab, a.rope, a.pos.t0, c0, c1, a.pos.mag_tpf);
-  RopeLane<P2> rl;
+  RopeLane<P2> rl, rl1;                  // rl1: the second half at head dim 64
   TokPos tp;
   if (rope_on) {
     rl.init(a.rope, win, ch);
+    if constexpr (W64) rl1.init(a.rope, win, ch + 4);
     tp.init(c0 + w * 16 + tl, a.pos);
   }
 
-  // Sbar and Sbar^T operand tiles of both heads are the same for every wave:
-  // wave 0 forms them once and parks them in LDS, one 16-byte slot per lane
-  // (conflict-free reads), so the loop reads them per group instead of holding
-  // 64 registers through it.  Slot op = ((h * 2 + transposed) * 2 + tile) * 2
-  // + part (bf16: hi, lo; fp32: floats 0-3, 4-7 of the tile's 8).
-  if (w == 0) {
+  // Sbar and Sbar^T operand blocks of block j in LDS (the same for every
+  // wave); zbar slices per half.
+  const float* rec0 = a.prefix + ((size_t)(b * a.H + h0) * a.nb + j) * RECN;
+  const float* rec1 = a.prefix + ((size_t)(b * a.H + h0 + (nh - 1)) * a.nb + j) * RECN;
+  form_ops<BF, W64>(ops, rec0, rec1, w, lane);
+  // zbar slices per half: in registers at 32; at 64 in LDS, read per group
+  // (registers are the limit there).
+  float zb[2][8];
+  if constexpr (W64) {
+    if (threadIdx.x < DH) zl[threadIdx.x] = rec0[DH * DH + threadIdx.x];
+  } else {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int hd = min(h, nh - 1);
-      const float* rec = a.prefix + ((size_t)(b * a.H + h0 + hd) * a.nb + j) * REC32;
-      u32x4 th[2], tlo[2];
-      float tf[2][8];
+      const float* zp = (h == 0 ? rec0 : rec1) + D * D;
 #pragma unroll
-      for (int tr = 0; tr < 2; ++tr) {
-        if (tr == 0) perm_tiles<BF, false>(rec, lane, th, tlo, tf);
-        else perm_tiles<BF, true>(rec, lane, th, tlo, tf);
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int op = ((h * 2 + tr) * 2 + t) * 2;
-          if constexpr (BF) {
-            ops[op * 64 + lane] = th[t];
-            ops[(op + 1) * 64 + lane] = tlo[t];
-          } else {
-            ops[op * 64 + lane] = __builtin_bit_cast(u32x4, f32x4{tf[t][0], tf[t][1], tf[t][2], tf[t][3]});
-            ops[(op + 1) * 64 + lane] = __builtin_bit_cast(u32x4, f32x4{tf[t][4], tf[t][5], tf[t][6], tf[t][7]});
-          }
-        }
-      }
+      for (int i = 0; i < 8; ++i) zb[h][i] = zp[8 * ch + i];
     }
   }
-  float zb[2][8];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int hd = min(h, nh - 1);
-    const float* rec = a.prefix + ((size_t)(b * a.H + h0 + hd) * a.nb + j) * REC32;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) zb[h][i] = rec[D * D + 8 * ch + i];
-  }
-  // Operand tiles of head h (transposed or not) back from LDS.
-  auto get_ops = [&](int h, int tr, u32x4* hi, u32x4* lo, float (*fs)[8]) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int op = ((h * 2 + tr) * 2 + t) * 2;
-      const u32x4 x0 = ops[op * 64 + lane], x1 = ops[(op + 1) * 64 + lane];
-      if constexpr (BF) {
-        hi[t] = x0;
-        lo[t] = x1;
-      } else {
-        const f32x4 f0 = __builtin_bit_cast(f32x4, x0), f1 = __builtin_bit_cast(f32x4, x1);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { fs[t][i] = f0[i]; fs[t][4 + i] = f1[i]; }
-      }
-    }
-  };
 
   struct Buf { Raw8<TIn> q[2], g[2]; };
   auto load_group = [&](Buf& bf) {
@@ -1380,12 +1416,22 @@ __global__ __launch_bounds__(NT, 2) void k_bw_q(BwQArgs a) {
     }
     ioff += 64 * RB;
   };
+  // The lane's token within the chunk, for the group being processed: tokens
+  // past the chunk read zeros and must add nothing to G (1/den is taken as 0
+  // there, which also keeps eps = 0 from turning them into NaN).
+  int tok = w * 16 + tl;
   Buf b0, b1;
   load_group(b0);
   load_group(b1);
   __syncthreads();
 
-  f32x16 gacc[2] = {{}, {}};
+  // G accumulators: at 32 each wave adds both heads' blocks over its own
+  // tokens; at 64 wave w adds quadrant w (a's half w >> 1 against r's half
+  // w & 1) over the tokens of all four waves' tiles.
+  constexpr int NACC = W64 ? 1 : NB;
+  f32x16 gacc[NACC];
+#pragma unroll
+  for (int q = 0; q < NACC; ++q) gacc[q] = f32x16{};
   float zacc[2][8];
 #pragma unroll
   for (int h = 0; h < 2; ++h)
@@ -1393,8 +1439,8 @@ __global__ __launch_bounds__(NT, 2) void k_bw_q(BwQArgs a) {
     for (int i = 0; i < 8; ++i) zacc[h][i] = 0.f;
 
   // Per-wave tile: row tl, columns h*32 + 8ch .. +7; odd groups of 8 rows keep
-  // the two heads swapped (as the block-state tiles) so transposed reads of the
-  // two half-waves hit different banks.
+  // the two halves swapped (as the block-state tiles) so transposed reads of
+  // the two half-waves hit different banks.
   const int tcol = (8 * ch) ^ (((tl >> 3) & 1) << 5);
   auto put_tile = [&](int arr, int h, const float* x, u32x4 hi, u32x4 lo) {
     if constexpr (BF) {
@@ -1410,115 +1456,187 @@ __global__ __launch_bounds__(NT, 2) void k_bw_q(BwQArgs a) {
   };
 
   auto run_group = [&](const Buf& bf) {
-    float2 cs[4];
+    if constexpr (W64) {
+      __asm__ volatile("" ::: "memory");   // operand and zbar reads stay in the loop
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const f32x4 z0 = *reinterpret_cast<const f32x4*>(zl + h * D + 8 * ch);
+        const f32x4 z1 = *reinterpret_cast<const f32x4*>(zl + h * D + 8 * ch + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { zb[h][i] = z0[i]; zb[h][4 + i] = z1[i]; }
+      }
+    }
+    float2 cs[4], cs1[4];
     if (rope_on) {
       rl.fetch(tab, tp, win, cs);
+      if constexpr (W64) rl1.fetch(tab, tp, win, cs1);
       tp.advance(a.pos);
+    }
+    float p[2][8], rr[2][8], gx[2][8];
+    u32x4 rh[2] = {}, rlo[2] = {};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      relu_widen(bf.q[h], p[h]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) rr[h][i] = p[h][i];
+      if (rope_on) rotate8(rr[h], (W64 && h == 1) ? cs1 : cs);
+      widen8(bf.g[h], gx[h]);
+      if constexpr (BF) split8(rr[h], rh[h], rlo[h]);
+    }
+    // g . num and z . phi(q) per output half (num = Sbar r; at 64 both input
+    // halves contribute); num itself is needed only in g . num.
+    float go_h[2], den_h[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      f32x4 cc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int x = 0; x < (W64 ? 2 : 1); ++x) {
+        const int xi = W64 ? x : h, blk = W64 ? 2 * h + x : h;
+        mv_acc<BF>(ops + blk * OPS_BLOCK, lane, rh[xi], &rlo[xi], rr[xi], cc);
+      }
+      float num[8];
+      take8(cc, num);
+      go_h[h] = 0.f;
+      den_h[h] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        go_h[h] += gx[h][i] * num[i];
+        den_h[h] += zb[h][i] * p[h][i];
+      }
+    }
+    // 1/den and beta: per head at 32, over both halves at 64 (v_rcp_f32, as in the readout)
+    const bool live = tok < (int)span;
+    tok += 64;
+    float inv[2], beta[2];
+    if constexpr (W64) {
+      const float dsum = sum4_lanes(den_h[0] + den_h[1]), gsum = sum4_lanes(go_h[0] + go_h[1]);
+      const float iv = live ? __builtin_amdgcn_rcpf(dsum + a.eps) : 0.f;
+      const float be = -gsum * (iv * iv);
+      inv[0] = inv[1] = iv;
+      beta[0] = beta[1] = be;
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float dsum = sum4_lanes(den_h[h]), gsum = sum4_lanes(go_h[h]);
+        inv[h] = live ? __builtin_amdgcn_rcpf(dsum + a.eps) : 0.f;
+        beta[h] = -gsum * (inv[h] * inv[h]);
+      }
+    }
+    float ax[2][8];
+    u32x4 ah[2] = {}, al[2] = {};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ax[h][i] = gx[h][i] * inv[h];
+      if constexpr (BF) split8(ax[h], ah[h], al[h]);
     }
     u32x4 pk[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      float p[8], rr[8], gx[8], num[8], ax[8], sa[8];
-      relu_widen(bf.q[h], p);
+      f32x4 cc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) rr[i] = p[i];
-      if (rope_on) rotate8(rr, cs);
-      widen8(bf.g[h], gx);
-      u32x4 rh{}, rlo{}, ah{}, alo{};
-      u32x4 Mh[2], Ml[2];
-      float Mf[2][8];
-      get_ops(h, 0, Mh, Ml, Mf);
-      if constexpr (BF) {
-        split8(rr, rh, rlo);
-        matvec<true>(Mh, Ml, nullptr, rh, &rlo, nullptr, num);
-      } else {
-        matvec<false>(nullptr, nullptr, Mf, u32x4{}, nullptr, rr, num);
+      for (int x = 0; x < (W64 ? 2 : 1); ++x) {
+        const int xi = W64 ? x : h, blk = W64 ? 2 * h + x : h;
+        mv_acc<BF>(ops + (NB + blk) * OPS_BLOCK, lane, ah[xi], &al[xi], ax[xi], cc);
       }
-      float den = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) den += zb[h][i] * p[i];
-      den = sum4_lanes(den) + a.eps;
-      const float inv = __builtin_amdgcn_rcpf(den);   // v_rcp_f32, as in the readout
-      float go = 0.f;
+      float sa[8];
+      take8(cc, sa);
+      if (rope_on) unrotate8(sa, (W64 && h == 1) ? cs1 : cs);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        ax[i] = gx[i] * inv;
-        go += gx[i] * num[i];
-      }
-      const float beta = -sum4_lanes(go) * (inv * inv);
-      get_ops(h, 1, Mh, Ml, Mf);
-      if constexpr (BF) {
-        split8(ax, ah, alo);
-        matvec<true>(Mh, Ml, nullptr, ah, &alo, nullptr, sa);
-      } else {
-        matvec<false>(nullptr, nullptr, Mf, u32x4{}, nullptr, ax, sa);
-      }
-      if (rope_on) unrotate8(sa, cs);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        sa[i] = p[i] > 0.f ? sa[i] + beta * zb[h][i] : 0.f;
-        zacc[h][i] += beta * p[i];
+        sa[i] = p[h][i] > 0.f ? sa[i] + beta[h] * zb[h][i] : 0.f;
+        zacc[h][i] += beta[h] * p[h][i];
       }
       if (h < nh) put8<EO>(sa, h, pk, rdq, ooff + o_one + h * D * EO);
-      put_tile(0, h, ax, ah, alo);
-      put_tile(1, h, rr, rh, rlo);
     }
     if constexpr (EO == 2) store_pair(pk, nh, tl, rdq, ooff + o_pair, ooff + o_one, RO);
     ooff += 64 * RO;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      put_tile(0, h, ax[h], ah[h], al[h]);
+      put_tile(1, h, rr[h], rh[h], rlo[h]);
+    }
 
-    // G += a r^T over the group's 16 tokens, per head (wave-local tile).
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  // G += a r^T over 16 tokens of tile `src` (a wave's tile): block (qa, qb)
+  // takes a's half qa against r's half qb into accumulator q.
+  auto g_block = [&](const unsigned char* src, int q, int qa, int qb) {
     if constexpr (BF) {
-      const uint16_t* t16 = reinterpret_cast<const uint16_t*>(wtile);
+      const uint16_t* t16 = reinterpret_cast<const uint16_t*>(src);
       const int Gq = lane >> 4, jr = (lane >> 2) & 3, js = lane & 3;
       const int r0 = 8 * (Gq >> 1) + jr;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int colb = ((h * D) ^ ((Gq >> 1) << 5)) + 16 * (Gq & 1) + 4 * js;
-        const int e0 = r0 * TCOLS + colb, e1 = e0 + 4 * TCOLS;
-        const u32x4 aH = tr_pair(t16, e0, e1), aL = tr_pair(t16 + WT, e0, e1);
-        const u32x4 rH = tr_pair(t16 + 2 * WT, e0, e1), rL = tr_pair(t16 + 3 * WT, e0, e1);
-        gacc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aH), as_bf16x8(rH), gacc[h], 0, 0, 0);
-        gacc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aH), as_bf16x8(rL), gacc[h], 0, 0, 0);
-        gacc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aL), as_bf16x8(rH), gacc[h], 0, 0, 0);
-      }
+      const int ca = ((qa * D) ^ ((Gq >> 1) << 5)) + 16 * (Gq & 1) + 4 * js;
+      const int cb = ((qb * D) ^ ((Gq >> 1) << 5)) + 16 * (Gq & 1) + 4 * js;
+      const int a0 = r0 * TCOLS + ca, b0_ = r0 * TCOLS + cb;
+      const u32x4 aH = tr_pair(t16, a0, a0 + 4 * TCOLS), aL = tr_pair(t16 + WT, a0, a0 + 4 * TCOLS);
+      const u32x4 rH = tr_pair(t16 + 2 * WT, b0_, b0_ + 4 * TCOLS), rL = tr_pair(t16 + 3 * WT, b0_, b0_ + 4 * TCOLS);
+      gacc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aH), as_bf16x8(rH), gacc[q], 0, 0, 0);
+      gacc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aH), as_bf16x8(rL), gacc[q], 0, 0, 0);
+      gacc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aL), as_bf16x8(rH), gacc[q], 0, 0, 0);
     } else {
-      const float* af = reinterpret_cast<const float*>(wtile);
+      const float* af = reinterpret_cast<const float*>(src);
       const float* rf = af + WT;
       const int cl = lane & 31, qq = lane >> 5;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const int row = 2 * s + qq;
-          const int i0 = row * TCOLS + ((h * D + cl) ^ (((row >> 3) & 1) << 5));
-          gacc[h] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i0], rf[i0], gacc[h], 0, 0, 0);
-        }
+      for (int s = 0; s < 8; ++s) {
+        const int row = 2 * s + qq;
+        const int sw = ((row >> 3) & 1) << 5;
+        gacc[q] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[row * TCOLS + ((qa * D + cl) ^ sw)],
+                                                       rf[row * TCOLS + ((qb * D + cl) ^ sw)], gacc[q], 0, 0, 0);
+      }
     }
+  };
+  auto wave_sync = [&]() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
+  // After a group's tiles are written: at 32 the wave's own two head blocks; at
+  // 64 quadrant w over the four waves' tiles, between workgroup barriers (so
+  // every wave runs the same number of groups; groups past the chunk are zeros).
+  auto g_step = [&]() {
+    if constexpr (W64) {
+      __syncthreads();
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) g_block(smem + tt * WAVE_BYTES, 0, w >> 1, w & 1);
+      __syncthreads();
+    } else {
+      wave_sync();
+#pragma unroll
+      for (int q = 0; q < NB; ++q) g_block(wtile, q, q, q);
+      wave_sync();
+    }
+  };
 
-  for (int gi = w; gi < ngroups; gi += 8) {
+  const int iters = W64 ? (ngroups + 7) / 8 : (ngroups - w + 7) / 8;   // uniform at 64
+  for (int it = 0; it < iters; ++it) {
     run_group(b0);
+    g_step();
     load_group(b0);
     run_group(b1);
+    g_step();
     load_group(b1);
   }
 
-  // Sum the four waves: G through LDS (over the tiles), gz across the 16 lanes
-  // of a row (the chunk's tokens) and then the waves.
+  // Sum the four waves: G through LDS (over the tiles and operand blocks), gz
+  // across the 16 lanes of a row (the chunk's tokens) and then the waves.
+  // red holds each wave's G as [32 NB / 2 rows][...]: at 32 two 32 x 32 heads,
+  // at 64 the 64 x 64 matrix.
   __syncthreads();
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int q = 0; q < NACC; ++q) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int e = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      red[((w * 2 + h) * D + e) * D + (lane & 31)] = gacc[h][v];
+      // at 64: wave w's quadrant straight into the one 64 x 64 G (the four
+      // waves hold the four quadrants, already summed over every token)
+      if constexpr (W64) red[(32 * (w >> 1) + e) * DH + 32 * (w & 1) + (lane & 31)] = gacc[q][v];
+      else red[((w * 2 + q) * D + e) * D + (lane & 31)] = gacc[q][v];
     }
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float s = zacc[h][i];
@@ -1531,18 +1649,33 @@ __global__ __launch_bounds__(NT, 2) void k_bw_q(BwQArgs a) {
   }
   __syncthreads();
   const int nchunk = a.nb * a.cpb;
-  for (int el = threadIdx.x; el < 2 * REC32; el += NT) {
-    const int h = el / REC32, o = el - h * REC32;
-    if (h >= nh) break;
-    float s;
-    if (o < D * D) {
-      s = red[((0 * 2 + h) * D * D) + o] + red[((1 * 2 + h) * D * D) + o] + red[((2 * 2 + h) * D * D) + o] +
-          red[((3 * 2 + h) * D * D) + o];
-    } else {
-      const int f = o - D * D;
-      s = zred[(0 * 2 + h) * D + f] + zred[(1 * 2 + h) * D + f] + zred[(2 * 2 + h) * D + f] + zred[(3 * 2 + h) * D + f];
+  if constexpr (W64) {
+    // one record: G (64 x 64) then gz (64)
+    for (int o = threadIdx.x; o < RECN; o += NT) {
+      float s;
+      if (o < DH * DH) {
+        s = red[o];
+      } else {
+        const int f = o - DH * DH;
+        s = zred[f] + zred[2 * D + f] + zred[4 * D + f] + zred[6 * D + f];
+      }
+      a.part[((size_t)(b * a.H + h0) * nchunk + ci) * RECN + o] = s;
     }
-    a.part[((size_t)(b * a.H + h0 + h) * nchunk + ci) * REC32 + o] = s;
+  } else {
+    for (int el = threadIdx.x; el < 2 * RECN; el += NT) {
+      const int h = el / RECN, o = el - h * RECN;
+      if (h >= nh) break;
+      float s;
+      if (o < D * D) {
+        s = red[((0 * 2 + h) * D * D) + o] + red[((1 * 2 + h) * D * D) + o] + red[((2 * 2 + h) * D * D) + o] +
+            red[((3 * 2 + h) * D * D) + o];
+      } else {
+        const int f = o - D * D;
+        s = zred[(0 * 2 + h) * D + f] + zred[(1 * 2 + h) * D + f] + zred[(2 * 2 + h) * D + f] +
+            zred[(3 * 2 + h) * D + f];
+      }
+      a.part[((size_t)(b * a.H + h0 + h) * nchunk + ci) * RECN + o] = s;
+    }
   }
 }
 
@@ -1920,6 +2053,24 @@ int launch_forward(const Plan& p, const void* q, const void* k, const void* v, v
   return (int)e;
 }
 
+template <int DH>
+hipError_t launch_bw_q(const BwQArgs& qa, bool in_bf16, bool grad_bf16, bool p2, dim3 grid, int lds, hipStream_t s) {
+  if (in_bf16 && grad_bf16) hipLaunchKernelGGL((p2 ? k_bw_q<uint16_t, uint16_t, true, DH> : k_bw_q<uint16_t, uint16_t, false, DH>), grid, dim3(NT), lds, s, qa);
+  else if (in_bf16) hipLaunchKernelGGL((p2 ? k_bw_q<uint16_t, float, true, DH> : k_bw_q<uint16_t, float, false, DH>), grid, dim3(NT), lds, s, qa);
+  else if (grad_bf16) hipLaunchKernelGGL((p2 ? k_bw_q<float, uint16_t, true, DH> : k_bw_q<float, uint16_t, false, DH>), grid, dim3(NT), lds, s, qa);
+  else hipLaunchKernelGGL((p2 ? k_bw_q<float, float, true, DH> : k_bw_q<float, float, false, DH>), grid, dim3(NT), lds, s, qa);
+  return hipGetLastError();
+}
+
+template <int DH>
+hipError_t launch_bw_kv(const BwKVArgs& ka, bool in_bf16, bool grad_bf16, bool p2, dim3 grid, int lds, hipStream_t s) {
+  if (in_bf16 && grad_bf16) hipLaunchKernelGGL((p2 ? k_bw_kv<uint16_t, uint16_t, true, DH> : k_bw_kv<uint16_t, uint16_t, false, DH>), grid, dim3(NT), lds, s, ka);
+  else if (in_bf16) hipLaunchKernelGGL((p2 ? k_bw_kv<uint16_t, float, true, DH> : k_bw_kv<uint16_t, float, false, DH>), grid, dim3(NT), lds, s, ka);
+  else if (grad_bf16) hipLaunchKernelGGL((p2 ? k_bw_kv<float, uint16_t, true, DH> : k_bw_kv<float, uint16_t, false, DH>), grid, dim3(NT), lds, s, ka);
+  else hipLaunchKernelGGL((p2 ? k_bw_kv<float, float, true, DH> : k_bw_kv<float, float, false, DH>), grid, dim3(NT), lds, s, ka);
+  return hipGetLastError();
+}
+
 int launch_backward(const Plan& p, const void* q, const void* k, const void* v, const void* dout,
                     void* dq, void* dk, void* dv, int in_bf16, int grad_bf16, float eps, void* ws,
                     void* stream) {
@@ -1939,7 +2090,8 @@ int launch_backward(const Plan& p, const void* q, const void* k, const void* v, 
   sa.pos = pa_pos;
   sa.rope = p.rope;
   const dim3 gs((unsigned)(p.hg * p.nb * p.cpb), (unsigned)p.B);
-  e = launch_state<32>(sa, in_bf16, p2, gs, p.lds_state, s);
+  e = p.D == 64 ? launch_state<64>(sa, in_bf16, p2, gs, p.lds_state, s)
+                : launch_state<32>(sa, in_bf16, p2, gs, p.lds_state, s);
   if (e != hipSuccess) return (int)e;
   PrefixArgs pa;
   pa.part = part; pa.prefix = prefix; pa.S_init = nullptr; pa.z_init = nullptr;
@@ -1957,12 +2109,11 @@ int launch_backward(const Plan& p, const void* q, const void* k, const void* v, 
   qa.H = p.H; qa.N = p.N; qa.L = p.L; qa.L0 = p.L0; qa.nb = p.nb; qa.cpb = p.cpb; qa.Tc = p.Tc; qa.hg = p.hg;
   qa.pos = pa_pos;
   qa.rope = p.rope;
-  const int lds_q = (4 * 2 * D * D + 4 * 2 * D) * 4 + 16 * 64 * 16 + p.tab_state;
-  if (in_bf16 && grad_bf16) hipLaunchKernelGGL((p2 ? k_bw_q<uint16_t, uint16_t, true> : k_bw_q<uint16_t, uint16_t, false>), gs, dim3(NT), lds_q, s, qa);
-  else if (in_bf16) hipLaunchKernelGGL((p2 ? k_bw_q<uint16_t, float, true> : k_bw_q<uint16_t, float, false>), gs, dim3(NT), lds_q, s, qa);
-  else if (grad_bf16) hipLaunchKernelGGL((p2 ? k_bw_q<float, uint16_t, true> : k_bw_q<float, uint16_t, false>), gs, dim3(NT), lds_q, s, qa);
-  else hipLaunchKernelGGL((p2 ? k_bw_q<float, float, true> : k_bw_q<float, float, false>), gs, dim3(NT), lds_q, s, qa);
-  e = hipGetLastError();
+  const int nbk = p.D == 64 ? 4 : 2;                  // operand blocks per matrix
+  const int lds_ops = 2 * nbk * OPS_BLOCK * 16;
+  const int lds_q = 4 * 8192 + lds_ops + (4 * 2 * D + 2 * D) * 4 + p.tab_state;   // tiles, operands, gz, zbar, table
+  e = p.D == 64 ? launch_bw_q<64>(qa, in_bf16, grad_bf16, p2, gs, lds_q, s)
+                : launch_bw_q<32>(qa, in_bf16, grad_bf16, p2, gs, lds_q, s);
   if (e != hipSuccess) return (int)e;
 
   // dS, dz: sums over the blocks at or after each block.
@@ -1977,11 +2128,9 @@ int launch_backward(const Plan& p, const void* q, const void* k, const void* v, 
   ka.pos = pa_pos;
   ka.rope = p.rope;
   const dim3 gr((unsigned)(p.hg * p.nb * p.rpb), (unsigned)p.B);
-  if (in_bf16 && grad_bf16) hipLaunchKernelGGL((p2 ? k_bw_kv<uint16_t, uint16_t, true> : k_bw_kv<uint16_t, uint16_t, false>), gr, dim3(NT), p.lds_read, s, ka);
-  else if (in_bf16) hipLaunchKernelGGL((p2 ? k_bw_kv<uint16_t, float, true> : k_bw_kv<uint16_t, float, false>), gr, dim3(NT), p.lds_read, s, ka);
-  else if (grad_bf16) hipLaunchKernelGGL((p2 ? k_bw_kv<float, uint16_t, true> : k_bw_kv<float, uint16_t, false>), gr, dim3(NT), p.lds_read, s, ka);
-  else hipLaunchKernelGGL((p2 ? k_bw_kv<float, float, true> : k_bw_kv<float, float, false>), gr, dim3(NT), p.lds_read, s, ka);
-  return (int)hipGetLastError();
+  const int lds_kv = lds_ops + p.lds_read;
+  return (int)(p.D == 64 ? launch_bw_kv<64>(ka, in_bf16, grad_bf16, p2, gr, lds_kv, s)
+                         : launch_bw_kv<32>(ka, in_bf16, grad_bf16, p2, gr, lds_kv, s));
 }
 
 }  // namespace lavr

@@ -78,6 +78,10 @@ def run(lavr, cfg, grad_dtype):
     dict(rope={"split": (6, 14, 12), "base": 10000.0}),  # odd pair counts
     dict(frames=11, block_frames=3, first_block_frames=4),
     dict(rope=None),
+    dict(head_dim=64, H=2, rope={"split": (16, 24, 24), "base": 10000.0}),          # one head per workgroup
+    dict(head_dim=64, H=1, B=1, frames=40, block_frames=3, tokens_per_frame=48, grid=(6, 8),
+         rope={"split": (14, 26, 24), "base": 10000.0}),                             # many groups, odd pairs
+    dict(head_dim=64, H=2, rope=None, frames=7, block_frames=2, first_block_frames=3),
 ])
 @pytest.mark.parametrize("grad", ["f32", "bf16"])
 def test_backward_small_bf16_inputs(lavr, kw, grad):
@@ -95,9 +99,10 @@ def test_backward_small_bf16_inputs(lavr, kw, grad):
             assert e <= TOL_BF16
 
 
-@pytest.mark.parametrize("split", [(8, 12, 12), (6, 14, 12)])
+@pytest.mark.parametrize("split", [(8, 12, 12), (6, 14, 12), (16, 24, 24), (14, 26, 24)])
 def test_backward_f32_inputs(lavr, split):
-    cfg = small_cfg(dtype="f32", rope={"split": split, "base": 10000.0})
+    d = sum(split)
+    cfg = small_cfg(dtype="f32", rope={"split": split, "base": 10000.0}, head_dim=d, H=3 if d == 32 else 2)
     say(f"case backward f32 split {split}")
     got, ref = run(lavr, cfg, torch.float32)
     for name, a, b in zip(("dq", "dk", "dv"), got, ref):
@@ -106,10 +111,11 @@ def test_backward_f32_inputs(lavr, split):
         assert e <= 10 * TOL_F32
 
 
-def test_backward_zero_queries_and_one_token_blocks(lavr):
+@pytest.mark.parametrize("d", [32, 64])
+def test_backward_zero_queries_and_one_token_blocks(lavr, d):
     cfg = small_cfg(dtype="f32", frames=40, tokens_per_frame=1, grid=(1, 1), block_frames=1,
-                    rope={"split": (32, 0, 0), "base": 10000.0}, B=1, H=2)
-    say("case backward one-token blocks, zero queries")
+                    rope={"split": (d, 0, 0), "base": 10000.0}, B=1, H=2, head_dim=d)
+    say(f"case backward one-token blocks, zero queries, d={d}")
     arrs, _ = device_inputs(cfg, DEV)
     arrs["q"][:, 7] = -np.abs(arrs["q"][:, 7])
     w = W()
@@ -153,7 +159,30 @@ def test_backward_deterministic(lavr):
     assert all(torch.equal(x, y) for x, y in zip(a, b))
 
 
-@pytest.mark.parametrize("name,heads", [("clip480p_bf16", [(0, 0), (0, 35), (0, 69)])])
+@pytest.mark.parametrize("d", [32, 64])
+def test_backward_eps_zero_with_padded_groups(lavr, d):
+    """eps = 0 with every query positive (den > 0 for every real token): groups
+    past a chunk's end must add nothing to G, not 0 * inf."""
+    cfg = small_cfg(frames=7, head_dim=d, H=2, rope=None, dtype="f32")
+    say(f"case backward eps=0, d={d}")
+    arrs, _ = device_inputs(cfg, DEV)
+    arrs["q"] = np.abs(arrs["q"]) + 0.01
+    w = W()
+    q, k, v = (w.to_torch(cfg, arrs[t], DEV) for t in w.TENSORS)
+    garr, g = draw_dout(cfg)
+    grads = lavr.block_causal_backward(q, k, v, g, cfg["block_frames"], cfg["tokens_per_frame"], None, eps=0.0)
+    torch.cuda.synchronize()
+    assert all(torch.isfinite(t).all().item() for t in grads)
+    ref = oracle.backward(*(w.to_f64(cfg, arrs[t]) for t in w.TENSORS), garr, cfg["tokens_per_frame"],
+                          cfg["block_frames"], None, eps=0.0)
+    for name, a, b in zip(("dq", "dk", "dv"), grads, ref):
+        e = oracle.rel_err(to_f64_torch(a), b)
+        say(f"  {name} rel err {e:.3e}")
+        assert e <= 10 * TOL_F32
+
+
+@pytest.mark.parametrize("name,heads", [("clip480p_bf16", [(0, 0), (0, 35), (0, 69)]),
+                                        ("clip480p_d64_bf16", [(0, 0), (0, 17), (0, 34)])])
 def test_backward_full_size(lavr, name, heads):
     w = W()
     cfg = w.workload(name)
