@@ -1115,15 +1115,18 @@ __device__ __forceinline__ void take8(const f32x4* c, float* y) {
 
 // Operand blocks of a matrix per workgroup: at head dim 32 one 32 x 32 block
 // per head of the pair, at 64 the four quadrants (a, b) of the head's 64 x 64
-// matrix (block 2a + b maps input half b to output half a).  Blocks 0 .. NB-1
-// hold the matrix, NB .. 2NB-1 its transpose; the four waves form them.
-template <bool BF, bool W64>
+// matrix (block 2a + b maps input half b to output half a).  NMAT = 2: blocks
+// 0 .. NB-1 hold the matrix, NB .. 2NB-1 its transpose; NMAT = 1: blocks 0 ..
+// NB-1 hold the transpose only.  The four waves form them.
+template <bool BF, bool W64, int NMAT>
 __device__ __forceinline__ void form_ops(u32x4* ops, const float* rec0, const float* rec1, int w, int lane) {
   constexpr int NB = W64 ? 4 : 2;
+  constexpr int TOT = NMAT * NB;
 #pragma unroll
-  for (int k = 0; k < 2 * NB / 4; ++k) {
+  for (int k = 0; k < (TOT + 3) / 4; ++k) {
     const int bo = w + 4 * k;
-    const int tr = bo / NB, blk = bo - tr * NB;
+    if (bo >= TOT) break;
+    const int tr = NMAT == 2 ? bo / NB : 1, blk = bo % NB;
     u32x4* op = ops + bo * OPS_BLOCK;
     if constexpr (W64) {
       const int qa = blk >> 1, qb = blk & 1;
@@ -1234,7 +1237,7 @@ __global__ __launch_bounds__(NT, 2) void k_bw_kv(BwKVArgs a) {
   // dS and dS^T operand blocks of block j in LDS; dz slices per half.
   const float* rec0 = a.suffix + ((size_t)(b * a.H + h0) * a.nb + j) * RECN;
   const float* rec1 = a.suffix + ((size_t)(b * a.H + h0 + (nh - 1)) * a.nb + j) * RECN;
-  form_ops<BF, W64>(ops, rec0, rec1, w, lane);
+  form_ops<BF, W64, 2>(ops, rec0, rec1, w, lane);
   float dzb[2][8];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -1324,31 +1327,35 @@ __global__ __launch_bounds__(NT, 2) void k_bw_kv(BwKVArgs a) {
 //
 // Grid as k_block_state (chunks of one block; a head pair at head dim 32, one
 // head at 64); token layout as k_readout, wave w taking the chunk's 16-token
-// groups w, w+4, ...  Per token: num = Sbar r, den, a, beta, Sbar^T a (MFMA,
-// row-permuted operand blocks read from LDS) and dq.  The chunk's G = sum a r^T
-// goes through a per-wave LDS tile [16 tokens][2 halves x 32] holding a and r
-// (bf16 hi and lo, or fp32), read back transposed into 32x32 MFMAs over the
-// group's tokens: one 32 x 32 block per head at head dim 32, the four quadrants
-// of the 64 x 64 G at 64.  gz = sum beta p stays in registers.  At the end the
-// four waves' partials are added through LDS (over the tiles and operand
-// blocks, no longer needed) and written as the chunk's (G, gz) records.
+// groups w, w+4, ...  One matrix-vector product per token does both jobs of
+// Sbar: u = Sbar^T g (MFMA, row-permuted operand blocks of Sbar^T from LDS)
+// gives g . num = u . r (num = Sbar r) and Sbar^T a = u / den, so
+//   beta = -(u . r) / den^2,  dq = [q > 0] (R^T u / den + beta zbar).
+// G = sum a r^T = sum g (r / den)^T goes through a per-wave LDS tile [16
+// tokens][2 halves x 32] holding g (exact in bf16, or fp32) and r / den (bf16
+// hi and lo, or fp32), read back transposed into 32x32 MFMAs over the group's
+// tokens: one 32 x 32 block per head at head dim 32; at 64 wave w takes
+// quadrant w of the 64 x 64 G over the four waves' tiles.  gz = sum beta p
+// stays in registers.  At the end the waves' partials are added through LDS
+// (over the tiles, no longer needed) and written as the chunk's (G, gz) records.
 
 template <typename TIn, typename TOut, bool P2, int DH>
 __global__ __launch_bounds__(NT, 2) void k_bw_q(BwQArgs a) {
   constexpr bool BF = sizeof(TIn) == 2;
   constexpr bool W64 = DH == 64;
-  constexpr int NB = W64 ? 4 : 2;                    // operand blocks per matrix, G accumulators
+  constexpr int NB = W64 ? 4 : 2;                    // operand blocks of Sbar^T
   constexpr int RECN = DH * DH + DH;
   constexpr int ES = (int)sizeof(TIn), EO = (int)sizeof(TOut);
   constexpr int WT = 16 * TCOLS;                     // elements of one wave tile array
-  constexpr int WAVE_BYTES = BF ? 4 * WT * 2 : 2 * WT * 4;   // a hi/lo, r hi/lo (bf16) or a, r (fp32)
-  static_assert(4 * WAVE_BYTES + 2 * NB * OPS_BLOCK * 16 >= 4 * NB * 1024 * 4, "reduction space");
+  constexpr int WAVE_BYTES = BF ? 3 * WT * 2 : 2 * WT * 4;   // g, r/den hi, lo (bf16) or g, r/den (fp32)
+  constexpr int RED_FLOATS = W64 ? DH * DH : 4 * 2 * D * D;  // waves' G partials at the end
+  static_assert(4 * WAVE_BYTES + NB * OPS_BLOCK * 16 >= RED_FLOATS * 4, "reduction space");
   extern __shared__ __align__(16) unsigned char smem[];
-  u32x4* ops = reinterpret_cast<u32x4*>(smem + 4 * WAVE_BYTES);   // [2 NB blocks][4 slots][64 lanes]
-  float* zred = reinterpret_cast<float*>(ops + 2 * NB * OPS_BLOCK);   // [4 waves][2 halves][32]
-  float* zl = zred + 4 * 2 * D;                                          // zbar of the block (64)
+  u32x4* ops = reinterpret_cast<u32x4*>(smem + 4 * WAVE_BYTES);   // [NB blocks][4 slots][64 lanes]
+  float* zred = reinterpret_cast<float*>(ops + NB * OPS_BLOCK);    // [4 waves][2 halves][32]
+  float* zl = zred + 4 * 2 * D;                                     // zbar of the block (head dim 64)
   float2* tab = reinterpret_cast<float2*>(zl + 2 * D);
-  float* red = reinterpret_cast<float*>(smem);       // after the loop: [4 waves][NB][1024] over tiles + ops
+  float* red = reinterpret_cast<float*>(smem);       // after the loop, over tiles + operands
 
   const int g = blockIdx.x % a.hg;
   const int ci = blockIdx.x / a.hg;
@@ -1388,13 +1395,12 @@ __global__ __launch_bounds__(NT, 2) void k_bw_q(BwQArgs a) {
     tp.init(c0 + w * 16 + tl, a.pos);
   }
 
-  // Sbar and Sbar^T operand blocks of block j in LDS (the same for every
-  // wave); zbar slices per half.
+  // Sbar^T operand blocks of block j in LDS (the same for every wave); zbar
+  // slices per half: in registers at 32, at 64 in LDS, read per group
+  // (registers are the limit there).
   const float* rec0 = a.prefix + ((size_t)(b * a.H + h0) * a.nb + j) * RECN;
   const float* rec1 = a.prefix + ((size_t)(b * a.H + h0 + (nh - 1)) * a.nb + j) * RECN;
-  form_ops<BF, W64>(ops, rec0, rec1, w, lane);
-  // zbar slices per half: in registers at 32; at 64 in LDS, read per group
-  // (registers are the limit there).
+  form_ops<BF, W64, 1>(ops, rec0, rec1, w, lane);
   float zb[2][8];
   if constexpr (W64) {
     if (threadIdx.x < DH) zl[threadIdx.x] = rec0[DH * DH + threadIdx.x];
@@ -1426,8 +1432,8 @@ __global__ __launch_bounds__(NT, 2) void k_bw_q(BwQArgs a) {
   __syncthreads();
 
   // G accumulators: at 32 each wave adds both heads' blocks over its own
-  // tokens; at 64 wave w adds quadrant w (a's half w >> 1 against r's half
-  // w & 1) over the tokens of all four waves' tiles.
+  // tokens; at 64 wave w adds quadrant w (g's half w >> 1 against (r/den)'s
+  // half w & 1) over the tokens of all four waves' tiles.
   constexpr int NACC = W64 ? 1 : NB;
   f32x16 gacc[NACC];
 #pragma unroll
@@ -1440,19 +1446,18 @@ __global__ __launch_bounds__(NT, 2) void k_bw_q(BwQArgs a) {
 
   // Per-wave tile: row tl, columns h*32 + 8ch .. +7; odd groups of 8 rows keep
   // the two halves swapped (as the block-state tiles) so transposed reads of
-  // the two half-waves hit different banks.
+  // the two half-waves hit different banks.  Arrays: 0 = g, 1 = r/den (hi), 2
+  // = r/den (lo) in bf16; 0 = g, 1 = r/den in fp32.
   const int tcol = (8 * ch) ^ (((tl >> 3) & 1) << 5);
-  auto put_tile = [&](int arr, int h, const float* x, u32x4 hi, u32x4 lo) {
-    if constexpr (BF) {
-      uint16_t* t16 = reinterpret_cast<uint16_t*>(wtile) + arr * 2 * WT;   // arr 0: a, 1: r
-      *reinterpret_cast<u32x4*>(t16 + tl * TCOLS + (tcol ^ (h * D))) = hi;
-      *reinterpret_cast<u32x4*>(t16 + WT + tl * TCOLS + (tcol ^ (h * D))) = lo;
-    } else {
-      float* t32 = reinterpret_cast<float*>(wtile) + arr * WT;
-      f32x4* dst = reinterpret_cast<f32x4*>(t32 + tl * TCOLS + (tcol ^ (h * D)));
-      dst[0] = f32x4{x[0], x[1], x[2], x[3]};
-      dst[1] = f32x4{x[4], x[5], x[6], x[7]};
-    }
+  auto tile_put16 = [&](int arr, int h, u32x4 x) {      // bf16 arrays
+    uint16_t* t16 = reinterpret_cast<uint16_t*>(wtile) + arr * WT;
+    *reinterpret_cast<u32x4*>(t16 + tl * TCOLS + (tcol ^ (h * D))) = x;
+  };
+  auto tile_put32 = [&](int arr, int h, const float* x) {   // fp32 arrays
+    float* t32 = reinterpret_cast<float*>(wtile) + arr * WT;
+    f32x4* dst = reinterpret_cast<f32x4*>(t32 + tl * TCOLS + (tcol ^ (h * D)));
+    dst[0] = f32x4{x[0], x[1], x[2], x[3]};
+    dst[1] = f32x4{x[4], x[5], x[6], x[7]};
   };
 
   auto run_group = [&](const Buf& bf) {
@@ -1473,34 +1478,35 @@ __global__ __launch_bounds__(NT, 2) void k_bw_q(BwQArgs a) {
       tp.advance(a.pos);
     }
     float p[2][8], rr[2][8], gx[2][8];
-    u32x4 rh[2] = {}, rlo[2] = {};
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       relu_widen(bf.q[h], p[h]);
 #pragma unroll
       for (int i = 0; i < 8; ++i) rr[h][i] = p[h][i];
       if (rope_on) rotate8(rr[h], (W64 && h == 1) ? cs1 : cs);
-      widen8(bf.g[h], gx[h]);
-      if constexpr (BF) split8(rr[h], rh[h], rlo[h]);
+      if constexpr (BF) tile_put16(0, h, bf.g[h].r[0]);        // g, exact in bf16
+      else {
+        widen8(bf.g[h], gx[h]);
+        tile_put32(0, h, gx[h]);
+      }
     }
-    // g . num and z . phi(q) per output half (num = Sbar r; at 64 both input
-    // halves contribute); num itself is needed only in g . num.
-    float go_h[2], den_h[2];
+    // u = Sbar^T g per output half (at 64 both input halves contribute), then
+    // u . r and z . phi(q)
+    float u[2][8], ur[2], den_h[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       f32x4 cc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int x = 0; x < (W64 ? 2 : 1); ++x) {
         const int xi = W64 ? x : h, blk = W64 ? 2 * h + x : h;
-        mv_acc<BF>(ops + blk * OPS_BLOCK, lane, rh[xi], &rlo[xi], rr[xi], cc);
+        mv_acc<BF>(ops + blk * OPS_BLOCK, lane, bf.g[xi].r[0], nullptr, gx[xi], cc);
       }
-      float num[8];
-      take8(cc, num);
-      go_h[h] = 0.f;
+      take8(cc, u[h]);
+      ur[h] = 0.f;
       den_h[h] = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        go_h[h] += gx[h][i] * num[i];
+        ur[h] += u[h][i] * rr[h][i];
         den_h[h] += zb[h][i] * p[h][i];
       }
     }
@@ -1509,38 +1515,37 @@ __global__ __launch_bounds__(NT, 2) void k_bw_q(BwQArgs a) {
     tok += 64;
     float inv[2], beta[2];
     if constexpr (W64) {
-      const float dsum = sum4_lanes(den_h[0] + den_h[1]), gsum = sum4_lanes(go_h[0] + go_h[1]);
+      const float dsum = sum4_lanes(den_h[0] + den_h[1]), usum = sum4_lanes(ur[0] + ur[1]);
       const float iv = live ? __builtin_amdgcn_rcpf(dsum + a.eps) : 0.f;
-      const float be = -gsum * (iv * iv);
       inv[0] = inv[1] = iv;
-      beta[0] = beta[1] = be;
+      beta[0] = beta[1] = -usum * (iv * iv);
     } else {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const float dsum = sum4_lanes(den_h[h]), gsum = sum4_lanes(go_h[h]);
+        const float dsum = sum4_lanes(den_h[h]), usum = sum4_lanes(ur[h]);
         inv[h] = live ? __builtin_amdgcn_rcpf(dsum + a.eps) : 0.f;
-        beta[h] = -gsum * (inv[h] * inv[h]);
+        beta[h] = -usum * (inv[h] * inv[h]);
       }
-    }
-    float ax[2][8];
-    u32x4 ah[2] = {}, al[2] = {};
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) ax[h][i] = gx[h][i] * inv[h];
-      if constexpr (BF) split8(ax[h], ah[h], al[h]);
     }
     u32x4 pk[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      f32x4 cc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      // r / den into the tile for G
+      float rs[8];
 #pragma unroll
-      for (int x = 0; x < (W64 ? 2 : 1); ++x) {
-        const int xi = W64 ? x : h, blk = W64 ? 2 * h + x : h;
-        mv_acc<BF>(ops + (NB + blk) * OPS_BLOCK, lane, ah[xi], &al[xi], ax[xi], cc);
+      for (int i = 0; i < 8; ++i) rs[i] = rr[h][i] * inv[h];
+      if constexpr (BF) {
+        u32x4 hi, lo;
+        split8(rs, hi, lo);
+        tile_put16(1, h, hi);
+        tile_put16(2, h, lo);
+      } else {
+        tile_put32(1, h, rs);
       }
+      // dq = [q > 0] (R^T u / den + beta zbar); gz += beta phi(q)
       float sa[8];
-      take8(cc, sa);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sa[i] = u[h][i] * inv[h];
       if (rope_on) unrotate8(sa, (W64 && h == 1) ? cs1 : cs);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -1551,16 +1556,10 @@ __global__ __launch_bounds__(NT, 2) void k_bw_q(BwQArgs a) {
     }
     if constexpr (EO == 2) store_pair(pk, nh, tl, rdq, ooff + o_pair, ooff + o_one, RO);
     ooff += 64 * RO;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      put_tile(0, h, ax[h], ah[h], al[h]);
-      put_tile(1, h, rr[h], rh[h], rlo[h]);
-    }
-
   };
 
-  // G += a r^T over 16 tokens of tile `src` (a wave's tile): block (qa, qb)
-  // takes a's half qa against r's half qb into accumulator q.
+  // G += g (r/den)^T over 16 tokens of tile `src` (a wave's tile): block (qa,
+  // qb) takes g's half qa against (r/den)'s half qb into accumulator q.
   auto g_block = [&](const unsigned char* src, int q, int qa, int qb) {
     if constexpr (BF) {
       const uint16_t* t16 = reinterpret_cast<const uint16_t*>(src);
@@ -1568,12 +1567,11 @@ __global__ __launch_bounds__(NT, 2) void k_bw_q(BwQArgs a) {
       const int r0 = 8 * (Gq >> 1) + jr;
       const int ca = ((qa * D) ^ ((Gq >> 1) << 5)) + 16 * (Gq & 1) + 4 * js;
       const int cb = ((qb * D) ^ ((Gq >> 1) << 5)) + 16 * (Gq & 1) + 4 * js;
-      const int a0 = r0 * TCOLS + ca, b0_ = r0 * TCOLS + cb;
-      const u32x4 aH = tr_pair(t16, a0, a0 + 4 * TCOLS), aL = tr_pair(t16 + WT, a0, a0 + 4 * TCOLS);
-      const u32x4 rH = tr_pair(t16 + 2 * WT, b0_, b0_ + 4 * TCOLS), rL = tr_pair(t16 + 3 * WT, b0_, b0_ + 4 * TCOLS);
-      gacc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aH), as_bf16x8(rH), gacc[q], 0, 0, 0);
-      gacc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aH), as_bf16x8(rL), gacc[q], 0, 0, 0);
-      gacc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aL), as_bf16x8(rH), gacc[q], 0, 0, 0);
+      const int ea = r0 * TCOLS + ca, eb = r0 * TCOLS + cb;
+      const u32x4 gA = tr_pair(t16, ea, ea + 4 * TCOLS);
+      const u32x4 rH = tr_pair(t16 + WT, eb, eb + 4 * TCOLS), rL = tr_pair(t16 + 2 * WT, eb, eb + 4 * TCOLS);
+      gacc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(gA), as_bf16x8(rH), gacc[q], 0, 0, 0);
+      gacc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(gA), as_bf16x8(rL), gacc[q], 0, 0, 0);
     } else {
       const float* af = reinterpret_cast<const float*>(src);
       const float* rf = af + WT;
@@ -2111,7 +2109,8 @@ int launch_backward(const Plan& p, const void* q, const void* k, const void* v, 
   qa.rope = p.rope;
   const int nbk = p.D == 64 ? 4 : 2;                  // operand blocks per matrix
   const int lds_ops = 2 * nbk * OPS_BLOCK * 16;
-  const int lds_q = 4 * 8192 + lds_ops + (4 * 2 * D + 2 * D) * 4 + p.tab_state;   // tiles, operands, gz, zbar, table
+  const int wave_tile = in_bf16 ? 3 * 16 * TCOLS * 2 : 2 * 16 * TCOLS * 4;
+  const int lds_q = 4 * wave_tile + nbk * OPS_BLOCK * 16 + (4 * 2 * D + 2 * D) * 4 + p.tab_state;   // tiles, Sbar^T, gz, zbar, table
   e = p.D == 64 ? launch_bw_q<64>(qa, in_bf16, grad_bf16, p2, gs, lds_q, s)
                 : launch_bw_q<32>(qa, in_bf16, grad_bf16, p2, gs, lds_q, s);
   if (e != hipSuccess) return (int)e;
