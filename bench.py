@@ -394,14 +394,40 @@ def bench_backward(lavr, torch, dev, cfg, q, k, v, rope, steps):
     e1.record()
     torch.cuda.synchronize(dev)
     ms = e0.elapsed_time(e1) / steps
+
+    # training path: the forward's block prefixes reused (la_block_causal_backward_from_forward)
+    lavr.lib.la_block_causal_forward(ptrs[0], ptrs[1], ptrs[2], ptrs[4], code, code, B, H, d, cfg["frames"],
+                                     tpf, bf, 0, ctypes.byref(rope.desc), 1e-8,
+                                     ctypes.c_void_p(ws.data_ptr()), need, stream)
+
+    def call_ff():
+        rc = lavr.lib.la_block_causal_backward_from_forward(*ptrs, code, code, B, H, d, cfg["frames"], tpf, bf,
+                                                            0, ctypes.byref(rope.desc), 1e-8,
+                                                            ctypes.c_void_p(ws.data_ptr()), need, stream)
+        if rc:
+            raise RuntimeError(lavr.status_string(rc))
+
+    for _ in range(3):
+        call_ff()
+    torch.cuda.synchronize(dev)
+    e0.record()
+    for _ in range(steps):
+        call_ff()
+    e1.record()
+    torch.cuda.synchronize(dev)
+    ms_ff = e0.elapsed_time(e1) / steps
     th = B * N * H
     esz = q.element_size()
     nb = -(-cfg["frames"] // bf)
     # q, k, v, dout read; k, v read again for the block states; dq, dk, dv written;
     # (S, z) records: prefixes and suffixes written and read once each
     alg = 9 * th * d * esz + 4 * B * H * nb * rec_bytes(d)
+    # from the forward: the block-state pass over k and v and its records drop out
+    alg_ff = 7 * th * d * esz + 2 * B * H * nb * rec_bytes(d)
     return {"ms": ms, "tokens_heads_per_s": th / (ms / 1e3), "alg_bytes": alg,
-            "gbs": alg / (ms * 1e6), "frac_of_peak": alg / (ms * 1e6) / HBM_PEAK_GBS, "steps": steps}
+            "gbs": alg / (ms * 1e6), "frac_of_peak": alg / (ms * 1e6) / HBM_PEAK_GBS, "steps": steps,
+            "from_forward": {"ms": ms_ff, "tokens_heads_per_s": th / (ms_ff / 1e3), "alg_bytes": alg_ff,
+                             "gbs": alg_ff / (ms_ff * 1e6), "frac_of_peak": alg_ff / (ms_ff * 1e6) / HBM_PEAK_GBS}}
 
 
 def bench_streaming(lavr, torch, dev, reps):

@@ -164,6 +164,21 @@ int la_block_causal_backward(const void* q, const void* k, const void* v, const 
                              int block_frames, int first_block_frames, const la_rope* rope,
                              float eps, void* ws, size_t ws_bytes, void* stream);
 
+/* la_block_causal_backward for training, where the forward has just run: ws
+ * (ws_bytes >= la_backward_workspace_bytes) must be the workspace that a
+ * la_block_causal_forward call with the same q, k, v and arguments (out dtype
+ * aside) wrote, left untouched since; the block prefixes it holds are used as
+ * they are instead of being formed again from k and v.  The result is the one
+ * la_block_causal_backward gives, bit for bit.  Passing any other workspace
+ * gives wrong gradients; the library cannot detect it. */
+int la_block_causal_backward_from_forward(const void* q, const void* k, const void* v,
+                                          const void* dout, void* dq, void* dk, void* dv,
+                                          la_dtype in_dt, la_dtype grad_dt, int B, int H,
+                                          int head_dim, int frames, int tokens_per_frame,
+                                          int block_frames, int first_block_frames,
+                                          const la_rope* rope, float eps, void* ws, size_t ws_bytes,
+                                          void* stream);
+
 /* Bind the caller's device buffers S_dev ([B][H][d][d] fp32) and z_dev
  * ([B][H][d] fp32), both 16-byte aligned, to *st, zero them on `stream`, and set
  * frames_done = 0. */

@@ -227,6 +227,37 @@ int check_conv(const void* x, const void* y, la_dtype in_dt, la_dtype out_dt, in
   return LA_OK;
 }
 
+
+int backward_common(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
+                    void* dv, la_dtype in_dt, la_dtype grad_dt, int B, int H, int head_dim, int frames,
+                    int tokens_per_frame, int block_frames, int first_block_frames, const la_rope* rope,
+                    float eps, void* ws, size_t ws_bytes, void* stream, bool have_prefix) {
+  if (!valid_dtype(in_dt) || !valid_dtype(grad_dt)) return LA_ERR_INVALID_ARG;
+  if (!std::isfinite(eps) || eps < 0.f) return LA_ERR_INVALID_ARG;
+  Plan p;
+  int st = make_plan(&p, B, H, head_dim, frames, tokens_per_frame, block_frames, first_block_frames,
+                     rope, 0, in_dt);
+  if (st != LA_OK) return st;
+  // inputs q, k, v, dout; gradient outputs dq, dk, dv: each output checked
+  // against the inputs (as the forward checks out) and against the others.
+  const void* ins[4] = {q, k, v, dout};
+  void* outs[3] = {dq, dk, dv};
+  const size_t elems = (size_t)p.B * p.N * p.H * p.D;
+  const size_t nin = elems * esize(in_dt), nout = elems * esize(grad_dt);
+  for (const void* x : ins)
+    if (!x || !aligned(x, 16)) return LA_ERR_INVALID_ARG;
+  for (int i = 0; i < 3; ++i) {
+    if (!outs[i] || !aligned(outs[i], 16)) return LA_ERR_INVALID_ARG;
+    for (const void* x : ins)
+      if (overlaps(outs[i], nout, x, nin)) return LA_ERR_INVALID_ARG;
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], nout, outs[j], nout)) return LA_ERR_INVALID_ARG;
+    if (ws && overlaps(outs[i], nout, ws, ws_bytes)) return LA_ERR_INVALID_ARG;
+  }
+  if (!ws || !aligned(ws, 256) || ws_bytes < p.ws_total_bw) return LA_ERR_INVALID_ARG;
+  return hip_status(lavr::launch_backward(p, q, k, v, dout, dq, dk, dv, in_dt == LA_BF16,
+                                          grad_dt == LA_BF16, eps, ws, stream, have_prefix));
+}
 }  // namespace
 
 extern "C" {
@@ -320,30 +351,21 @@ int la_block_causal_backward(const void* q, const void* k, const void* v, const 
                              int B, int H, int head_dim, int frames, int tokens_per_frame,
                              int block_frames, int first_block_frames, const la_rope* rope,
                              float eps, void* ws, size_t ws_bytes, void* stream) {
-  if (!valid_dtype(in_dt) || !valid_dtype(grad_dt)) return LA_ERR_INVALID_ARG;
-  if (!std::isfinite(eps) || eps < 0.f) return LA_ERR_INVALID_ARG;
-  Plan p;
-  int st = make_plan(&p, B, H, head_dim, frames, tokens_per_frame, block_frames, first_block_frames,
-                     rope, 0, in_dt);
-  if (st != LA_OK) return st;
-  // inputs q, k, v, dout; gradient outputs dq, dk, dv: each output checked
-  // against the inputs (as the forward checks out) and against the others.
-  const void* ins[4] = {q, k, v, dout};
-  void* outs[3] = {dq, dk, dv};
-  const size_t elems = (size_t)p.B * p.N * p.H * p.D;
-  const size_t nin = elems * esize(in_dt), nout = elems * esize(grad_dt);
-  for (const void* x : ins)
-    if (!x || !aligned(x, 16)) return LA_ERR_INVALID_ARG;
-  for (int i = 0; i < 3; ++i) {
-    if (!outs[i] || !aligned(outs[i], 16)) return LA_ERR_INVALID_ARG;
-    for (const void* x : ins)
-      if (overlaps(outs[i], nout, x, nin)) return LA_ERR_INVALID_ARG;
-    for (int j = 0; j < i; ++j)
-      if (overlaps(outs[i], nout, outs[j], nout)) return LA_ERR_INVALID_ARG;
-  }
-  if (!ws || !aligned(ws, 256) || ws_bytes < p.ws_total_bw) return LA_ERR_INVALID_ARG;
-  return hip_status(lavr::launch_backward(p, q, k, v, dout, dq, dk, dv, in_dt == LA_BF16,
-                                          grad_dt == LA_BF16, eps, ws, stream));
+  return backward_common(q, k, v, dout, dq, dk, dv, in_dt, grad_dt, B, H, head_dim, frames,
+                         tokens_per_frame, block_frames, first_block_frames, rope, eps, ws, ws_bytes,
+                         stream, false);
+}
+
+int la_block_causal_backward_from_forward(const void* q, const void* k, const void* v,
+                                          const void* dout, void* dq, void* dk, void* dv,
+                                          la_dtype in_dt, la_dtype grad_dt, int B, int H,
+                                          int head_dim, int frames, int tokens_per_frame,
+                                          int block_frames, int first_block_frames,
+                                          const la_rope* rope, float eps, void* ws, size_t ws_bytes,
+                                          void* stream) {
+  return backward_common(q, k, v, dout, dq, dk, dv, in_dt, grad_dt, B, H, head_dim, frames,
+                         tokens_per_frame, block_frames, first_block_frames, rope, eps, ws, ws_bytes,
+                         stream, true);
 }
 
 size_t la_qkv_workspace_bytes(int B, int H, int head_dim, int frames, int tokens_per_frame,

@@ -78,8 +78,10 @@ struct ConvPlan {
 };
 int launch_tconv(const ConvPlan& c, const void* x, void* y, int in_bf16, int out_bf16, const float* w,
                  const float* bias, const void* cache_in, void* cache_out, void* stream);
+// have_prefix: ws already holds the block prefixes the forward wrote (the
+// block-state and prefix kernels are skipped).
 int launch_backward(const Plan& p, const void* q, const void* k, const void* v, const void* dout,
                     void* dq, void* dk, void* dv, int in_bf16, int grad_bf16, float eps, void* ws,
-                    void* stream);
+                    void* stream, bool have_prefix = false);
 
 }  // namespace lavr

@@ -2071,7 +2071,7 @@ hipError_t launch_bw_kv(const BwKVArgs& ka, bool in_bf16, bool grad_bf16, bool p
 
 int launch_backward(const Plan& p, const void* q, const void* k, const void* v, const void* dout,
                     void* dq, void* dk, void* dv, int in_bf16, int grad_bf16, float eps, void* ws,
-                    void* stream) {
+                    void* stream, bool have_prefix) {
   hipStream_t s = (hipStream_t)stream;
   float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + p.ws_part);
   float* prefix = reinterpret_cast<float*>(static_cast<char*>(ws) + p.ws_prefix);
@@ -2080,7 +2080,8 @@ int launch_backward(const Plan& p, const void* q, const void* k, const void* v, 
   const bool p2 = ((p.rope.pt | p.rope.ph | p.rope.pw) & 1) == 0;
   hipError_t e;
 
-  // Sbar, zbar of every block, as the forward forms them.
+  // Sbar, zbar of every block, as the forward forms them (unless the forward's
+  // are still in the workspace).
   StateArgs sa;
   sa.k = k; sa.v = v; sa.part = part;
   sa.scale = nullptr; sa.gamma = nullptr; sa.row_in = p.row_in;
@@ -2088,17 +2089,19 @@ int launch_backward(const Plan& p, const void* q, const void* k, const void* v, 
   sa.pos = pa_pos;
   sa.rope = p.rope;
   const dim3 gs((unsigned)(p.hg * p.nb * p.cpb), (unsigned)p.B);
-  e = p.D == 64 ? launch_state<64>(sa, in_bf16, p2, gs, p.lds_state, s)
-                : launch_state<32>(sa, in_bf16, p2, gs, p.lds_state, s);
-  if (e != hipSuccess) return (int)e;
   PrefixArgs pa;
   pa.part = part; pa.prefix = prefix; pa.S_init = nullptr; pa.z_init = nullptr;
   pa.S_save = nullptr; pa.z_save = nullptr; pa.H = p.H; pa.nb = p.nb; pa.cpb = p.cpb;
   pa.hd = p.D; pa.rec = p.rec; pa.rev = 0;
   const dim3 gp((unsigned)((p.rec + 63) / 64), (unsigned)p.H, (unsigned)p.B);
-  hipLaunchKernelGGL(k_prefix, gp, dim3(PFX_NT), 0, s, pa);
-  e = hipGetLastError();
-  if (e != hipSuccess) return (int)e;
+  if (!have_prefix) {
+    e = p.D == 64 ? launch_state<64>(sa, in_bf16, p2, gs, p.lds_state, s)
+                  : launch_state<32>(sa, in_bf16, p2, gs, p.lds_state, s);
+    if (e != hipSuccess) return (int)e;
+    hipLaunchKernelGGL(k_prefix, gp, dim3(PFX_NT), 0, s, pa);
+    e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+  }
 
   // dq and the chunk partials of (G, gz) (over the forward's partials, which
   // the prefix kernel has consumed).

@@ -59,6 +59,8 @@ def _load():
         "la_backward_workspace_bytes": (c_size, [c_int] * 7),
         "la_block_causal_backward": (c_int, [c_vp] * 7 + [c_int] * 9 + [ctypes.POINTER(LaRope), c_float,
                                                                          c_vp, c_size, c_vp]),
+        "la_block_causal_backward_from_forward": (c_int, [c_vp] * 7 + [c_int] * 9 +
+                                                  [ctypes.POINTER(LaRope), c_float, c_vp, c_size, c_vp]),
         "la_qkv_workspace_bytes": (c_size, [c_int] * 7),
         "la_block_causal_forward_qkv": (c_int, [c_vp, c_vp, c_int, c_int] + [c_int] * 7 +
                                         [ctypes.POINTER(LaRope), c_float, c_vp, c_vp, c_float, c_vp,
@@ -88,6 +90,7 @@ lib = _load()
 
 EXPORTS = ("rope_table_bytes", "rope_table_build", "la_workspace_bytes", "la_block_causal_forward",
            "la_block_causal_forward_timed", "la_backward_workspace_bytes", "la_block_causal_backward",
+           "la_block_causal_backward_from_forward",
            "la_qkv_workspace_bytes", "la_block_causal_forward_qkv", "la_stream_block_qkv",
            "la_temporal_conv", "la_conv_state_init", "la_temporal_conv_stream_block",
            "la_state_init", "la_stream_block", "la_status_string", "la_version")
@@ -354,8 +357,12 @@ def backward_workspace_bytes(B, H, frames, tokens_per_frame, block_frames, head_
 
 
 def block_causal_backward(q, k, v, dout, block_frames, tokens_per_frame, rope=None, eps=EPS_DEFAULT,
-                          grad_dtype=None, first_block_frames=None, workspace=None):
-    """Gradients (dq, dk, dv) of sum(dout * block_causal_forward(q, k, v, ...))."""
+                          grad_dtype=None, first_block_frames=None, workspace=None, from_forward=False):
+    """Gradients (dq, dk, dv) of sum(dout * block_causal_forward(q, k, v, ...)).
+
+    from_forward=True: `workspace` is the one a block_causal_forward call with the
+    same arguments filled (sized by backward_workspace_bytes) and the block
+    states are not formed again (la_block_causal_backward_from_forward)."""
     _check_qkv(q, k, v)
     _check_qkv(q, k, dout)
     B, N, H, d = q.shape
@@ -368,35 +375,42 @@ def block_causal_backward(q, k, v, dout, block_frames, tokens_per_frame, rope=No
     need = lib.la_backward_workspace_bytes(B, H, d, frames, int(tokens_per_frame), int(block_frames), f0)
     if need == 0:
         raise ValueError(f"backward not built for head dim {d} or invalid shape")
+    if from_forward and workspace is None:
+        raise ValueError("from_forward needs the forward's workspace")
     ws = _workspace(q.device, need) if workspace is None else workspace
-    _check(lib.la_block_causal_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk),
-                                        _ptr(dv), _dtype_code(q.dtype), _dtype_code(grad_dtype), B, H,
-                                        d, frames, int(tokens_per_frame), int(block_frames), f0,
-                                        _rope_ptr(rope), float(eps), _ptr(ws),
-                                        ws.numel() * ws.element_size(), _stream(q.device)),
+    fn = lib.la_block_causal_backward_from_forward if from_forward else lib.la_block_causal_backward
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _dtype_code(q.dtype),
+              _dtype_code(grad_dtype), B, H, d, frames, int(tokens_per_frame), int(block_frames), f0,
+              _rope_ptr(rope), float(eps), _ptr(ws), ws.numel() * ws.element_size(), _stream(q.device)),
            "la_block_causal_backward")
     return dq, dk, dv
 
 
 class BlockCausalAttention(torch.autograd.Function):
-    """Autograd binding: forward through la_block_causal_forward, backward through
-    la_block_causal_backward (gradients in the input dtype)."""
+    """Autograd binding: forward through la_block_causal_forward into a workspace
+    kept for the backward, backward through la_block_causal_backward_from_forward
+    (the forward's block states reused; gradients in the input dtype)."""
 
     @staticmethod
     def forward(ctx, q, k, v, block_frames, tokens_per_frame, rope=None, eps=EPS_DEFAULT,
                 first_block_frames=None):
         q, k, v = (t.contiguous() for t in (q, k, v))
-        ctx.save_for_backward(q, k, v)
+        B, N, H, d = q.shape
+        need = backward_workspace_bytes(B, H, N // tokens_per_frame, tokens_per_frame, block_frames,
+                                        head_dim=d, first_block_frames=first_block_frames)
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+        out = block_causal_forward(q, k, v, block_frames, tokens_per_frame, rope, eps, workspace=ws,
+                                   first_block_frames=first_block_frames)
+        ctx.save_for_backward(q, k, v, ws)
         ctx.args = (block_frames, tokens_per_frame, rope, eps, first_block_frames)
-        return block_causal_forward(q, k, v, block_frames, tokens_per_frame, rope, eps,
-                                    first_block_frames=first_block_frames)
+        return out
 
     @staticmethod
     def backward(ctx, dout):
-        q, k, v = ctx.saved_tensors
+        q, k, v, ws = ctx.saved_tensors
         bf, tpf, rope, eps, f0 = ctx.args
         dq, dk, dv = block_causal_backward(q, k, v, dout.contiguous().to(q.dtype), bf, tpf, rope, eps,
-                                           first_block_frames=f0)
+                                           first_block_frames=f0, workspace=ws, from_forward=True)
         return dq, dk, dv, None, None, None, None, None
 
 

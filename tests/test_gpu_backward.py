@@ -148,6 +148,29 @@ def test_autograd_binding(lavr):
         assert e <= TOL_BF16
 
 
+@pytest.mark.parametrize("d", [32, 64])
+def test_backward_from_forward_matches(lavr, d):
+    """Reusing the forward's block prefixes gives the recomputing backward's
+    gradients bit for bit."""
+    cfg = small_cfg(frames=10, head_dim=d, H=3 if d == 32 else 2,
+                    rope={"split": (8, 12, 12) if d == 32 else (16, 24, 24), "base": 10000.0},
+                    first_block_frames=4)
+    say(f"case backward from forward d={d}")
+    _, (q, k, v) = device_inputs(cfg, DEV)
+    _, g = draw_dout(cfg)
+    rope = rope_for(lavr, cfg)
+    tpf, bf, f0 = cfg["tokens_per_frame"], cfg["block_frames"], cfg["first_block_frames"]
+    need = lavr.backward_workspace_bytes(cfg["B"], cfg["H"], cfg["frames"], tpf, bf, head_dim=d,
+                                         first_block_frames=f0)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    lavr.block_causal_forward(q, k, v, bf, tpf, rope, workspace=ws, first_block_frames=f0)
+    a = lavr.block_causal_backward(q, k, v, g, bf, tpf, rope, first_block_frames=f0, workspace=ws,
+                                   from_forward=True)
+    b = lavr.block_causal_backward(q, k, v, g, bf, tpf, rope, first_block_frames=f0)
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
 def test_backward_deterministic(lavr):
     cfg = small_cfg(frames=9)
     _, (q, k, v) = device_inputs(cfg, DEV)
@@ -189,9 +212,18 @@ def test_backward_full_size(lavr, name, heads):
     say(f"case backward full-size {name}")
     arrs, (q, k, v) = device_inputs(cfg, DEV)
     garr, g = draw_dout(cfg)
+    rope = rope_for(lavr, cfg)
     dq, dk, dv = lavr.block_causal_backward(q, k, v, g, cfg["block_frames"], cfg["tokens_per_frame"],
-                                            rope_for(lavr, cfg), grad_dtype=torch.float32)
+                                            rope, grad_dtype=torch.float32)
+    # the training path (the forward's block prefixes reused) gives the same bits
+    ws = torch.empty(lavr.backward_workspace_bytes(cfg["B"], cfg["H"], cfg["frames"], cfg["tokens_per_frame"],
+                                                   cfg["block_frames"], head_dim=cfg["head_dim"]),
+                     dtype=torch.uint8, device=DEV)
+    lavr.block_causal_forward(q, k, v, cfg["block_frames"], cfg["tokens_per_frame"], rope, workspace=ws)
+    again = lavr.block_causal_backward(q, k, v, g, cfg["block_frames"], cfg["tokens_per_frame"], rope,
+                                       grad_dtype=torch.float32, workspace=ws, from_forward=True)
     torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip((dq, dk, dv), again))
     for b_, h in heads:
         ref = oracle.backward_head(*(w.to_f64(cfg, arrs[t][b_, :, h]) for t in w.TENSORS),
                                    w.to_f64(cfg, garr[b_, :, h]), cfg["tokens_per_frame"],
