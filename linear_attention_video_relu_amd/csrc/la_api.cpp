@@ -16,7 +16,10 @@ namespace {
 // Work split.  A block-state chunk or readout tile holds at most kStateMax /
 // kReadMax tokens (long chunks keep the partial-state traffic and the prefix
 // kernel small), and the launch is split finer until it has at least kMinWg
-// workgroups (a single streamed block must still fill 256 CUs).
+// workgroups, so that a single streamed block still fills 256 CUs.  kMinWg is
+// about one resident round of the block-state kernel (3 workgroups per CU);
+// measured on a streamed 3-frame block (B = 2, 70 heads): 1024 -> 56-57 us,
+// 700 -> 54 us, 1536 -> 59 us per call.
 #ifndef LAVR_STATE_MAX
 #define LAVR_STATE_MAX 3200
 #endif
@@ -24,7 +27,7 @@ namespace {
 #define LAVR_READ_MAX 1024
 #endif
 #ifndef LAVR_MIN_WG
-#define LAVR_MIN_WG 1024
+#define LAVR_MIN_WG 700
 #endif
 constexpr int kStateMax = LAVR_STATE_MAX;
 constexpr int kReadMax = LAVR_READ_MAX;
@@ -144,7 +147,7 @@ int make_plan(Plan* p, int B, int H, int head_dim, int frames, int tpf, int bloc
   }
   const int tiles = (in_dt == LA_BF16 ? 3 : 2) * kStep * 64 * esize(in_dt);   // 64 channels per row
   p->tab_state = (int)(tab_pairs(rope, tpf, p->Tc) * 8);
-  p->lds_state = tiles + p->tab_state;
+  p->lds_state = lavr::kStateTileSets * tiles + p->tab_state;
   p->lds_read = (int)(tab_pairs(rope, tpf, p->Tr) * 8);
 
   const size_t rec = (size_t)p->rec * sizeof(float);

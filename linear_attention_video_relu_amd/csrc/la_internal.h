@@ -13,6 +13,13 @@ namespace lavr {
 constexpr bool head_dim_built(int d) { return d == 32 || d == 64; }
 constexpr int rec_floats(int d) { return d * d + d; }   // floats of one (S, z) record
 
+// Block-state LDS tiles: 1 = one set (two barriers per step), 2 = double
+// buffered (one barrier per step).
+#ifndef LAVR_STATE_DB
+#define LAVR_STATE_DB 2
+#endif
+constexpr int kStateTileSets = LAVR_STATE_DB == 2 ? 2 : 1;
+
 // Rotary table as the kernels see it.
 struct RopeDev {
   const float* table;   // (cos, sin) pairs; nullptr = RoPE off

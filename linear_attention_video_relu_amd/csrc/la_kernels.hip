@@ -401,10 +401,11 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? ((P2 && DH == 32 && !NRM) ? 
   constexpr int PF = (BF && P2 && !W64) ? LAVR_STATE_PF : 2;   // steps of loads in flight
 
   extern __shared__ __align__(16) unsigned char smem[];
+  // Tile set in use (two sets alternate per step when double buffered).
   TIn* tV = reinterpret_cast<TIn*>(smem);
   TIn* tK = tV + TILE_ELEMS;
   TIn* tKl = tK + TILE_ELEMS;            // bf16 only
-  float2* tab = reinterpret_cast<float2*>(smem + TILE_BYTES);
+  float2* tab = reinterpret_cast<float2*>(smem + kStateTileSets * TILE_BYTES);
 
   const int g = blockIdx.x % a.hg;
   const int ci = blockIdx.x / a.hg;
@@ -556,18 +557,29 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? ((P2 && DH == 32 && !NRM) ? 
   };
 
   // Whole rounds of PF steps; steps past the chunk hold zeros and add nothing.
+  // With two tile sets, the barrier after step s+1's tile writes also orders
+  // every wave's step-s MFMA reads before step s+2 rewrites that set.
   auto one_step = [&](Buf& bf) {
     run_step(bf);
     __syncthreads();
     load_step(bf);
     mfma_step();
-    __syncthreads();
+    if constexpr (kStateTileSets == 2) {
+      const int off = (tV == reinterpret_cast<TIn*>(smem)) ? TILE_BYTES : 0;
+      tV = reinterpret_cast<TIn*>(smem + off);
+      tK = tV + TILE_ELEMS;
+      tKl = tK + TILE_ELEMS;
+    } else {
+      __syncthreads();
+    }
   };
   for (int s0 = c0; s0 < c1; s0 += PF * STEP) {
     one_step(b0);
     one_step(b1);
     if constexpr (PF > 2) one_step(b2);
   }
+
+  if constexpr (kStateTileSets == 2) __syncthreads();   // last MFMA reads before red reuses the tiles
 
   // Head dim 32: combine the two waves of each head through LDS.  Key sums:
   // first across the 16 lanes of a wave that hold the same channel chunk
