@@ -389,7 +389,7 @@ struct TabStage {
 // chunk read as zeros (buffer range check) and add nothing.
 
 template <typename TIn, bool P2, int DH, bool NRM>
-__global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? ((P2 && DH == 32 && !NRM) ? 4 : (NRM && DH == 64) ? 2 : 3) : 2) void k_block_state(StateArgs a) {
+__global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? ((P2 && DH == 32 && !NRM && kStateTileSets == 1) ? 4 : (NRM && DH == 64) ? 2 : 3) : 2) void k_block_state(StateArgs a) {
   constexpr bool BF = sizeof(TIn) == 2;
   constexpr bool W64 = DH == 64;
   constexpr int RECN = DH * DH + DH;
@@ -398,7 +398,8 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? ((P2 && DH == 32 && !NRM) ? 
   constexpr int TILE_ELEMS = STEP * TCOLS;
   constexpr int TILE_BYTES = NTILE * TILE_ELEMS * ES;
   constexpr int W16 = 16 / ES;           // elements per 16 bytes
-  constexpr int PF = (BF && P2 && !W64) ? LAVR_STATE_PF : 2;   // steps of loads in flight
+  constexpr int PF = (BF && P2 && !W64 && !NRM) ? LAVR_STATE_PF : 2;   // steps of loads in flight
+  static_assert(PF == 2 || PF == 3, "block-state prefetch depth: two or three register buffers");
 
   extern __shared__ __align__(16) unsigned char smem[];
   // Tile set in use (two sets alternate per step when double buffered).
