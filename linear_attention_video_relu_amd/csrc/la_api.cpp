@@ -21,7 +21,7 @@ namespace {
 // measured on a streamed 3-frame block (B = 2, 70 heads): 1024 -> 56-57 us,
 // 700 -> 54 us, 1536 -> 59 us per call.
 #ifndef LAVR_STATE_MAX
-#define LAVR_STATE_MAX 3200
+#define LAVR_STATE_MAX 4200
 #endif
 #ifndef LAVR_READ_MAX
 #define LAVR_READ_MAX 1024
