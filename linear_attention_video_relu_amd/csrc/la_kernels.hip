@@ -46,6 +46,18 @@ constexpr int NT = 256;              // threads of the state and readout workgro
 constexpr int STEP = 64;             // tokens per step of the state kernel
 constexpr int TCOLS = 2 * D;         // an LDS tile row holds two heads
 constexpr int RSRC_WORD3 = 0x00020000;  // gfx9 raw buffer: 32-bit data, range checked
+// Cache policy of the streaming q/k/v loads and of the large output stores
+// (out, dq, dk, dv, the convolution's y): 0 = default, 2 = non-temporal.
+// Non-temporal output stores keep a call's written tensors from sitting dirty
+// in L2/MALL, where their write-back competed with the next kernel's loads
+// (block-state kernel after a readout: 0.636 -> 0.599 ms); non-temporal loads
+// were slower (0.676 ms).
+#ifndef LAVR_LOAD_CPOL
+#define LAVR_LOAD_CPOL 0
+#endif
+#ifndef LAVR_STORE_CPOL
+#define LAVR_STORE_CPOL 2
+#endif
 #ifndef LAVR_STATE_PF
 #define LAVR_STATE_PF 2   // block-state: 64-token steps of K/V loads in flight
 #endif
@@ -156,7 +168,7 @@ template <typename T>
 __device__ __forceinline__ Raw8<T> bload8(__amdgpu_buffer_rsrc_t rs, int off) {
   Raw8<T> o;
 #pragma unroll
-  for (int i = 0; i < (int)(sizeof(T) / 2); ++i) o.r[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16 * i, 0, 0);
+  for (int i = 0; i < (int)(sizeof(T) / 2); ++i) o.r[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16 * i, 0, LAVR_LOAD_CPOL);
   return o;
 }
 
@@ -870,7 +882,7 @@ __global__ __launch_bounds__(NT, (DH == 32 && !NRM) ? 4 : 2) void k_readout(Read
       for (int hf = 0; hf < 2; ++hf) {
         const f32x4 ov = o[hf] * inv;
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ov), ro,
-                                               ooff + o_one + (h * D + 16 * hf) * EO, 0, 0);
+                                               ooff + o_one + (h * D + 16 * hf) * EO, 0, LAVR_STORE_CPOL);
       }
     }
   };
@@ -978,11 +990,11 @@ __global__ __launch_bounds__(NT, (DH == 32 && !NRM) ? 4 : 2) void k_readout(Read
           second[i] = lo ? rcv : p1;
         }
         __builtin_amdgcn_raw_buffer_store_b128(u32x4{first[0], first[1], first[2], first[3]}, ro,
-                                               ooff + o_pair, 0, 0);
+                                               ooff + o_pair, 0, LAVR_STORE_CPOL);
         __builtin_amdgcn_raw_buffer_store_b128(u32x4{second[0], second[1], second[2], second[3]}, ro,
-                                               ooff + o_pair + 8 * RO, 0, 0);
+                                               ooff + o_pair + 8 * RO, 0, LAVR_STORE_CPOL);
       } else {
-        __builtin_amdgcn_raw_buffer_store_b128(pk[0], ro, ooff + o_one, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(pk[0], ro, ooff + o_one, 0, LAVR_STORE_CPOL);
       }
     }
     ooff += 64 * RO;
@@ -1162,8 +1174,10 @@ __device__ __forceinline__ void put8(const float* y, int h, u32x4* pk, __amdgpu_
   if constexpr (EO == 2) {
     pk[h] = u32x4{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7])};
   } else {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{y[0], y[1], y[2], y[3]}), rs, off, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{y[4], y[5], y[6], y[7]}), rs, off + 16, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{y[0], y[1], y[2], y[3]}), rs, off, 0,
+                                           LAVR_STORE_CPOL);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{y[4], y[5], y[6], y[7]}), rs, off + 16, 0,
+                                           LAVR_STORE_CPOL);
   }
 }
 
@@ -1182,11 +1196,12 @@ __device__ __forceinline__ void store_pair(const u32x4* pk, int nh, int tl, __am
       first[i] = lo ? p0 : rcv;
       second[i] = lo ? rcv : p1;
     }
-    __builtin_amdgcn_raw_buffer_store_b128(u32x4{first[0], first[1], first[2], first[3]}, rs, off_pair, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{first[0], first[1], first[2], first[3]}, rs, off_pair, 0,
+                                           LAVR_STORE_CPOL);
     __builtin_amdgcn_raw_buffer_store_b128(u32x4{second[0], second[1], second[2], second[3]}, rs,
-                                           off_pair + 8 * RO, 0, 0);
+                                           off_pair + 8 * RO, 0, LAVR_STORE_CPOL);
   } else {
-    __builtin_amdgcn_raw_buffer_store_b128(pk[0], rs, off_one, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(pk[0], rs, off_one, 0, LAVR_STORE_CPOL);
   }
 }
 
@@ -1810,12 +1825,12 @@ __global__ __launch_bounds__(NT) void k_tconv(ConvArgs a) {
       if constexpr (EO == 2) {
         __builtin_amdgcn_raw_buffer_store_b128(
             u32x4{pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]), pack_bf16(o[4], o[5]), pack_bf16(o[6], o[7])},
-            ry, (uint32_t)f * frame_out + col_out, 0, 0);
+            ry, (uint32_t)f * frame_out + col_out, 0, LAVR_STORE_CPOL);
       } else {
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{o[0], o[1], o[2], o[3]}), ry,
-                                               (uint32_t)f * frame_out + col_out, 0, 0);
+                                               (uint32_t)f * frame_out + col_out, 0, LAVR_STORE_CPOL);
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{o[4], o[5], o[6], o[7]}), ry,
-                                               (uint32_t)f * frame_out + col_out + 16, 0, 0);
+                                               (uint32_t)f * frame_out + col_out + 16, 0, LAVR_STORE_CPOL);
       }
       rem = block_end ? a.BF : rem - 1;
       prev = ring[k];
