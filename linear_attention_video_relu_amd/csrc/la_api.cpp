@@ -19,12 +19,14 @@ namespace {
 // workgroups, so that a single streamed block still fills 256 CUs.  kMinWg is
 // about one resident round of the block-state kernel (3 workgroups per CU);
 // measured on a streamed 3-frame block (B = 2, 70 heads): 1024 -> 56-57 us,
-// 700 -> 54 us, 1536 -> 59 us per call.
+// 700 -> 54 us, 1536 -> 59 us per call.  Readout tiles of at most 640 tokens
+// (20 per 8-frame block of the minute-long clip): 0.636 ms against 0.641 ms
+// at 1024 (13 tiles), 0.656 at 2048 and 0.725 at 320.
 #ifndef LAVR_STATE_MAX
 #define LAVR_STATE_MAX 4200
 #endif
 #ifndef LAVR_READ_MAX
-#define LAVR_READ_MAX 1024
+#define LAVR_READ_MAX 640
 #endif
 #ifndef LAVR_MIN_WG
 #define LAVR_MIN_WG 700

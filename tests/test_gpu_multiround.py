@@ -1,0 +1,142 @@
+"""GPU parity of launches of many resident rounds, every element.
+
+4 batch rows x 16 head groups x 32 blocks of 256 tokens make 2048 block-state
+workgroups and 2048 readout workgroups, a few rounds of the chip's resident
+slots, with a ragged last block (127 frames in blocks of 4) and a first block
+of another length; head dims 32 and 64, bf16 and fp32 inputs, the backward,
+and blocks streamed one at a time on top of the cache.  Every output element
+is compared with the oracle (the full-size workloads compare sampled heads).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import TOL_BF16, TOL_F32, device_inputs, err_bf16_out, to_f64_torch
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+TOL_BF16_IN_F32_GRAD = 1e-3     # bf16 inputs, fp32 gradients (hi/lo operand split inside)
+
+
+@pytest.fixture(scope="module")
+def lavr():
+    import __graft_entry__
+    __graft_entry__.ensure_built()
+    from linear_attention_video_relu_amd import lavr
+    return lavr
+
+
+def W():
+    from linear_attention_video_relu_amd import workloads
+    return workloads
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def rounds_cfg(**kw):
+    base = dict(index=300, B=4, H=32, head_dim=32, frames=127, tokens_per_frame=64, grid=(8, 8),
+                block_frames=4, dtype="bf16", rope={"split": (8, 12, 12), "base": 10000.0},
+                scale=1.0, outlier_frac=0.05, outlier_scale=8.0, name="rounds")
+    base.update(kw)
+    return base
+
+
+def rope_for(lavr, cfg):
+    return lavr.RopeTable(cfg["rope"]["split"], cfg["grid"], cfg["frames"], cfg["rope"]["base"], DEV)
+
+
+def oracle_fwd(cfg, arrs):
+    w = W()
+    return oracle.forward(*(w.to_f64(cfg, arrs[t]) for t in w.TENSORS), cfg["tokens_per_frame"],
+                          cfg["block_frames"], w.oracle_rope(cfg),
+                          first_block_frames=cfg.get("first_block_frames"))
+
+
+@pytest.mark.parametrize("kw", [
+    dict(),
+    dict(first_block_frames=6),
+    dict(head_dim=64, rope={"split": (16, 24, 24), "base": 10000.0}),
+    dict(dtype="f32"),
+])
+def test_forward_many_rounds(lavr, kw):
+    cfg = rounds_cfg(**kw)
+    say(f"case many-round forward {kw}")
+    arrs, (q, k, v) = device_inputs(cfg, DEV)
+    ref = oracle_fwd(cfg, arrs)
+    rope = rope_for(lavr, cfg)
+    fb = cfg.get("first_block_frames")
+    if cfg["dtype"] == "bf16":
+        out32 = lavr.block_causal_forward(q, k, v, cfg["block_frames"], cfg["tokens_per_frame"], rope,
+                                          first_block_frames=fb, out_dtype=torch.float32)
+        out16 = lavr.block_causal_forward(q, k, v, cfg["block_frames"], cfg["tokens_per_frame"], rope,
+                                          first_block_frames=fb)
+        torch.cuda.synchronize()
+        e32 = oracle.rel_err(to_f64_torch(out32), ref)
+        e16 = err_bf16_out(to_f64_torch(out16), ref)
+        say(f"  f32 out err {e32:.3e}, bf16 out err beyond rounding {e16:.3e}")
+        assert e32 <= TOL_BF16 and e16 <= TOL_BF16
+        # the bf16 output is the rounding of the fp32 one
+        assert torch.equal(out16, out32.to(torch.bfloat16))
+    else:
+        out = lavr.block_causal_forward(q, k, v, cfg["block_frames"], cfg["tokens_per_frame"], rope,
+                                        first_block_frames=fb)
+        torch.cuda.synchronize()
+        e = oracle.rel_err(to_f64_torch(out), ref)
+        say(f"  f32 err {e:.3e}")
+        assert e <= TOL_F32
+
+
+def test_streaming_matches_many_round_launch(lavr):
+    """Blocks streamed one at a time on top of the cache agree with the one-shot
+    launch.  fp32 outputs: a streamed block is cut into more, shorter chunks
+    (so that one block still fills the chip), so the two sum a block's state
+    in other pieces and differ by rounding only; each is within ~1e-4 of the
+    oracle (bf16 inputs, states and queries carried as hi + lo bf16 pairs), so
+    they agree to 5e-4."""
+    cfg = rounds_cfg(frames=128)
+    say("case many-round one-shot vs streamed")
+    arrs, (q, k, v) = device_inputs(cfg, DEV)
+    rope = rope_for(lavr, cfg)
+    bf, tpf = cfg["block_frames"], cfg["tokens_per_frame"]
+    one = lavr.block_causal_forward(q, k, v, bf, tpf, rope, out_dtype=torch.float32)
+    st = lavr.StreamState(cfg["B"], cfg["H"], device=DEV)
+    parts = []
+    L = bf * tpf
+    for i in range(0, q.shape[1], L):
+        parts.append(st.step(q[:, i:i + L].contiguous(), k[:, i:i + L].contiguous(),
+                             v[:, i:i + L].contiguous(), tpf, rope, out_dtype=torch.float32))
+    torch.cuda.synchronize()
+    streamed = to_f64_torch(torch.cat(parts, dim=1))
+    e = oracle.rel_err(streamed, to_f64_torch(one))
+    say(f"  streamed vs one-shot rel err {e:.3e}")
+    ref = oracle_fwd(cfg, arrs)
+    e_s, e_o = oracle.rel_err(streamed, ref), oracle.rel_err(to_f64_torch(one), ref)
+    say(f"  vs oracle: streamed {e_s:.3e}, one-shot {e_o:.3e}")
+    assert e <= 5e-4
+    assert e_s <= TOL_BF16 and e_o <= TOL_BF16
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(head_dim=64, rope={"split": (16, 24, 24), "base": 10000.0})])
+def test_backward_many_rounds(lavr, kw):
+    cfg = rounds_cfg(**kw)
+    say(f"case many-round backward {kw}")
+    w = W()
+    arrs, (q, k, v) = device_inputs(cfg, DEV)
+    shape = (cfg["B"], w.n_tokens(cfg), cfg["H"], cfg["head_dim"])
+    garr = w.f32_to_bf16_bits(np.random.default_rng([7, cfg["index"]]).standard_normal(shape, dtype=np.float32))
+    g = w.to_torch(cfg, garr, DEV)
+    rope = rope_for(lavr, cfg)
+    grads = lavr.block_causal_backward(q, k, v, g, cfg["block_frames"], cfg["tokens_per_frame"], rope,
+                                       grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.backward(*(w.to_f64(cfg, arrs[t]) for t in w.TENSORS), w.to_f64(cfg, garr),
+                          cfg["tokens_per_frame"], cfg["block_frames"], w.oracle_rope(cfg))
+    for name, a, b in zip(("dq", "dk", "dv"), grads, ref):
+        e = oracle.rel_err(to_f64_torch(a), b)
+        say(f"  {name} rel err {e:.3e}")
+        assert e <= TOL_BF16_IN_F32_GRAD
