@@ -715,6 +715,39 @@ __global__ __launch_bounds__(PFX_NT) void k_prefix(PrefixArgs a) {
   }
 }
 
+// Single-block calls (a streamed block, or a one-shot call of one block): no
+// scan over blocks, so every thread takes one element of one record, sums the
+// block's chunk partials in chunk order (sixteen loads in flight) and adds the
+// carried state, in the same order as k_prefix.  Grid: x = element group of
+// 256, y = head, z = batch.
+__global__ __launch_bounds__(256) void k_prefix1(PrefixArgs a) {
+  const int el = blockIdx.x * 256 + threadIdx.x;
+  const int REC = a.rec;
+  if (el >= REC) return;
+  const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
+  const float* part = a.part + bh * a.cpb * REC + el;
+  constexpr int BATCH = 16;
+  float s = 0.f;
+  for (int c0 = 0; c0 < a.cpb; c0 += BATCH) {
+    float v[BATCH];
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) v[i] = part[(size_t)min(c0 + i, a.cpb - 1) * REC];
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i)
+      if (c0 + i < a.cpb) s += v[i];
+  }
+  const bool inS = el < a.hd * a.hd;
+  const size_t si = bh * a.hd * a.hd + el, zi = bh * a.hd + el - a.hd * a.hd;
+  float acc = 0.f;
+  if (a.S_init != nullptr) acc = inS ? a.S_init[si] : a.z_init[zi];
+  acc += s;
+  a.prefix[bh * REC + el] = acc;
+  if (a.S_save != nullptr) {
+    if (inS) a.S_save[si] = acc;
+    else a.z_save[zi] = acc;
+  }
+}
+
 // ------------------------------------------------------------- k_readout
 //
 // Grid: x = tile * hg + head group, y = batch.  256 threads; a workgroup owns
@@ -2006,6 +2039,19 @@ int launch_zero(float* p, size_t n, void* stream) {
   return (int)hipGetLastError();
 }
 
+// Prefix (or, reversed, suffix) sums of the block states: one element per
+// thread for a single block, the run-wise scan otherwise.
+hipError_t launch_prefix(const PrefixArgs& pa, const Plan& p, hipStream_t s) {
+  if (p.nb == 1) {
+    const dim3 g((unsigned)((p.rec + 255) / 256), (unsigned)p.H, (unsigned)p.B);
+    hipLaunchKernelGGL(k_prefix1, g, dim3(256), 0, s, pa);
+  } else {
+    const dim3 g((unsigned)((p.rec + 63) / 64), (unsigned)p.H, (unsigned)p.B);
+    hipLaunchKernelGGL(k_prefix, g, dim3(PFX_NT), 0, s, pa);
+  }
+  return hipGetLastError();
+}
+
 int launch_forward(const Plan& p, const void* q, const void* k, const void* v, void* out,
                    int in_bf16, int out_bf16, float eps, void* ws,
                    const float* S_init, const float* z_init, float* S_save, float* z_save,
@@ -2058,9 +2104,7 @@ int launch_forward(const Plan& p, const void* q, const void* k, const void* v, v
   pa.part = part; pa.prefix = prefix; pa.S_init = S_init; pa.z_init = z_init;
   pa.S_save = S_save; pa.z_save = z_save; pa.H = p.H; pa.nb = p.nb; pa.cpb = p.cpb;
   pa.hd = p.D; pa.rec = p.rec; pa.rev = 0;
-  const dim3 gp((unsigned)((p.rec + 63) / 64), (unsigned)p.H, (unsigned)p.B);
-  hipLaunchKernelGGL(k_prefix, gp, dim3(PFX_NT), 0, s, pa);
-  e = hipGetLastError();
+  e = launch_prefix(pa, p, s);
   if (e == hipSuccess) e = mark(2);
   if (e != hipSuccess) return (int)e;
 
@@ -2121,13 +2165,11 @@ int launch_backward(const Plan& p, const void* q, const void* k, const void* v, 
   pa.part = part; pa.prefix = prefix; pa.S_init = nullptr; pa.z_init = nullptr;
   pa.S_save = nullptr; pa.z_save = nullptr; pa.H = p.H; pa.nb = p.nb; pa.cpb = p.cpb;
   pa.hd = p.D; pa.rec = p.rec; pa.rev = 0;
-  const dim3 gp((unsigned)((p.rec + 63) / 64), (unsigned)p.H, (unsigned)p.B);
   if (!have_prefix) {
     e = p.D == 64 ? launch_state<64>(sa, in_bf16, p2, gs, p.lds_state, s)
                   : launch_state<32>(sa, in_bf16, p2, gs, p.lds_state, s);
     if (e != hipSuccess) return (int)e;
-    hipLaunchKernelGGL(k_prefix, gp, dim3(PFX_NT), 0, s, pa);
-    e = hipGetLastError();
+    e = launch_prefix(pa, p, s);
     if (e != hipSuccess) return (int)e;
   }
 
@@ -2148,8 +2190,7 @@ int launch_backward(const Plan& p, const void* q, const void* k, const void* v, 
 
   // dS, dz: sums over the blocks at or after each block.
   pa.prefix = suffix; pa.rev = 1;
-  hipLaunchKernelGGL(k_prefix, gp, dim3(PFX_NT), 0, s, pa);
-  e = hipGetLastError();
+  e = launch_prefix(pa, p, s);
   if (e != hipSuccess) return (int)e;
 
   BwKVArgs ka;
