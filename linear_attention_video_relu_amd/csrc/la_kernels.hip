@@ -43,6 +43,7 @@ namespace {
 
 constexpr int D = 32;                // channels of one lane chunk's half (a head at head dim 32)
 constexpr int NT = 256;              // threads of the state and readout workgroups
+constexpr int kReadAlBytes = 2 * 8 * 64 * 16;   // head dim 64, bf16: Sbar hi and lo tiles of a readout workgroup
 constexpr int STEP = 64;             // tokens per step of the state kernel
 constexpr int TCOLS = 2 * D;         // an LDS tile row holds two heads
 constexpr int RSRC_WORD3 = 0x00020000;  // gfx9 raw buffer: 32-bit data, range checked
@@ -764,14 +765,19 @@ __global__ __launch_bounds__(256) void k_prefix1(PrefixArgs a) {
 // buffer range check.
 
 template <typename TIn, typename TOut, bool P2, int DH, bool NRM>
-__global__ __launch_bounds__(NT, (DH == 32 && !NRM) ? 4 : 2) void k_readout(ReadArgs a) {
+__global__ __launch_bounds__(NT, (!NRM && (DH == 32 || sizeof(TIn) == 2)) ? 4 : 2) void k_readout(ReadArgs a) {
   constexpr bool BF = sizeof(TIn) == 2;
   constexpr bool W64 = DH == 64;
   constexpr int RECN = DH * DH + DH;
   constexpr int ES = (int)sizeof(TIn), EO = (int)sizeof(TOut);
   constexpr int NA = W64 ? 8 : 4;        // Sbar tiles of 16 rows x 32 channels a lane holds
   extern __shared__ __align__(16) unsigned char smem[];
-  float2* tab = reinterpret_cast<float2*>(smem);
+  // bf16 at head dim 64: the hi and lo parts of the Sbar tiles live in LDS
+  // (one copy per workgroup, lane-major: slot (2 i + part) * 64 + lane), which
+  // keeps the kernel within 128 registers.
+  constexpr bool A_LDS = BF && W64;
+  u32x4* lds_a = reinterpret_cast<u32x4*>(smem);
+  float2* tab = reinterpret_cast<float2*>(smem + (A_LDS ? kReadAlBytes : 0));
 
   const int g = blockIdx.x % a.hg;
   const int ti = blockIdx.x / a.hg;
@@ -830,7 +836,14 @@ __global__ __launch_bounds__(NT, (DH == 32 && !NRM) ? 4 : 2) void k_readout(Read
     float sv[8];
 #pragma unroll
     for (int k = 0; k < 4; ++k) { sv[k] = s0[k]; sv[4 + k] = s1[k]; }
-    if constexpr (BF) {
+    if constexpr (A_LDS) {
+      u32x4 hi, lo;
+      split8(sv, hi, lo);
+      if (w == 0) {
+        lds_a[(2 * i) * 64 + lane] = hi;
+        lds_a[(2 * i + 1) * 64 + lane] = lo;
+      }
+    } else if constexpr (BF) {
       split8(sv, Ah[i], Al[i]);
     } else {
 #pragma unroll
@@ -931,6 +944,10 @@ __global__ __launch_bounds__(NT, (DH == 32 && !NRM) ? 4 : 2) void k_readout(Read
     if constexpr (W64) {
       // one head: den over both halves, every output tile from both halves
       float den = 0.f;
+      // The Sbar operands are read from LDS in every group: an opaque copy of
+      // the lane index keeps the compiler from hoisting them into registers.
+      int aslot = lane;
+      if constexpr (A_LDS) asm volatile("" : "+v"(aslot));
       u32x4 bh[2], bl[2];
       float xs[2][8];
 #pragma unroll
@@ -959,9 +976,11 @@ __global__ __launch_bounds__(NT, (DH == 32 && !NRM) ? 4 : 2) void k_readout(Read
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt) {
             if constexpr (BF) {
-              cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Ah[et * 2 + kt]), as_bf16x8(bh[kt]), cc, 0, 0, 0);
-              cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Ah[et * 2 + kt]), as_bf16x8(bl[kt]), cc, 0, 0, 0);
-              cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(Al[et * 2 + kt]), as_bf16x8(bh[kt]), cc, 0, 0, 0);
+              const u32x4 ah = lds_a[(2 * (et * 2 + kt)) * 64 + aslot];
+              const u32x4 al = lds_a[(2 * (et * 2 + kt) + 1) * 64 + aslot];
+              cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah), as_bf16x8(bh[kt]), cc, 0, 0, 0);
+              cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah), as_bf16x8(bl[kt]), cc, 0, 0, 0);
+              cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al), as_bf16x8(bh[kt]), cc, 0, 0, 0);
             } else {
 #pragma unroll
               for (int s = 0; s < 8; ++s)
@@ -2117,7 +2136,7 @@ int launch_forward(const Plan& p, const void* q, const void* k, const void* v, v
   ra.pos = pa_pos;
   ra.rope = p.rope;
   const dim3 gr((unsigned)(p.hg * p.nb * p.rpb), (unsigned)p.B);
-  e = p.D == 64 ? launch_readouts<64>(ra, in_bf16, out_bf16, p2, gr, p.lds_read, s)
+  e = p.D == 64 ? launch_readouts<64>(ra, in_bf16, out_bf16, p2, gr, p.lds_read + (in_bf16 ? kReadAlBytes : 0), s)
                 : launch_readouts<32>(ra, in_bf16, out_bf16, p2, gr, p.lds_read, s);
   if (e == hipSuccess) e = mark(3);
   return (int)e;
