@@ -34,6 +34,7 @@ namespace {
 constexpr int kStateMax = LAVR_STATE_MAX;
 constexpr int kReadMax = LAVR_READ_MAX;
 constexpr int kMinWg = LAVR_MIN_WG;
+constexpr long long kReadSlots = 4 * 256;   // readout workgroups resident at once (4 per CU)
 constexpr int kTabLdsMax = 32768;      // LDS bytes for a staged rotary window
 constexpr int kStep = 64;              // block-state kernel step (tokens)
 constexpr long long kTwo42 = 1LL << 42;
@@ -94,6 +95,23 @@ bool split_block(int L, int max_tokens, long long min_n, int mult, const la_rope
   }
 }
 
+// Small launches run a few resident rounds of workgroups, and a last round that
+// has barely begun costs almost a whole round.  If fewer, longer pieces (at most
+// twice max_tokens) drop that round, take them.  `rows` workgroups share each
+// piece index; `slots` is one resident round.
+void fit_rounds(int L, int max_tokens, long long rows, long long slots, int mult, const la_rope* r, int tpf,
+                long long row_bytes, int* n, int* T) {
+  const long long R = cdiv(rows * *n, slots);
+  if (R <= 1 || R > 4) return;
+  const long long n2 = (R - 1) * slots / rows;
+  if (n2 < 1) return;
+  const long long T2 = round_up(cdiv(L, n2), mult);
+  if (T2 > 2LL * max_tokens || tab_pairs(r, tpf, (int)T2) * 8 > kTabLdsMax || (T2 + 256) * row_bytes >= (1LL << 31))
+    return;
+  *n = (int)cdiv(L, T2);
+  *T = (int)T2;
+}
+
 // first_block_frames: frames of the first block (0 = block_frames).  row_mult:
 // input token rows hold row_mult * H * head_dim elements (3 for fused q|k|v).
 int make_plan(Plan* p, int B, int H, int head_dim, int frames, int tpf, int block_frames,
@@ -135,6 +153,7 @@ int make_plan(Plan* p, int B, int H, int head_dim, int frames, int tpf, int bloc
     return LA_ERR_UNSUPPORTED;
   if (!split_block(Lmax, kReadMax, min_n, 64, rope, tpf, row_bytes, &p->rpb, &p->Tr))
     return LA_ERR_UNSUPPORTED;
+  fit_rounds(Lmax, kReadMax, (long long)B * p->hg * p->nb, kReadSlots, 64, rope, tpf, row_bytes, &p->rpb, &p->Tr);
   if ((long long)p->hg * p->nb * p->cpb > 0x7fffffffLL || (long long)p->hg * p->nb * p->rpb > 0x7fffffffLL)
     return LA_ERR_UNSUPPORTED;
 
