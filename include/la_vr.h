@@ -122,7 +122,9 @@ size_t la_workspace_bytes(int B, int H, int head_dim, int frames, int tokens_per
  * nearest even from the fp32 result).  All accumulation is fp32.  eps >= 0 is
  * added to the normaliser (1e-8 in SANA).  ws (256-byte aligned, ws_bytes >=
  * la_workspace_bytes) is scratch owned by the caller and must not be touched
- * by other work until the call's kernels finish.  out must not overlap q, k, v.
+ * by other work until the call's kernels finish.  out must not overlap q, k, v;
+ * the used part of ws must not overlap q, k, v, out or the rotary table, nor
+ * out the table (LA_ERR_INVALID_ARG).
  * If rope->table is non-NULL, frames <= rope->max_frames and, when d_h + d_w >
  * 0, grid_h * grid_w == tokens_per_frame.  rope may be NULL (RoPE off). */
 int la_block_causal_forward(const void* q, const void* k, const void* v, void* out,
@@ -157,7 +159,9 @@ size_t la_backward_workspace_bytes(int B, int H, int head_dim, int frames, int t
  * overlap the inputs or each other.  Head dims 32 and 64 are built, as for the
  * forward.  The block states are formed again from
  * k and v.  ws (256-byte aligned, ws_bytes >= la_backward_workspace_bytes) is
- * caller-owned scratch.  Same status codes and stream semantics as the forward. */
+ * caller-owned scratch; its used part must not overlap the inputs, the
+ * gradients or the rotary table, nor the gradients the table.  Same status
+ * codes and stream semantics as the forward. */
 int la_block_causal_backward(const void* q, const void* k, const void* v, const void* dout,
                              void* dq, void* dk, void* dv, la_dtype in_dt, la_dtype grad_dt,
                              int B, int H, int head_dim, int frames, int tokens_per_frame,
@@ -194,7 +198,8 @@ int la_state_init(la_state* st, float* S_dev, float* z_dev, int B, int H, int he
  * with save == 0 the cache is left unchanged (several denoising steps of one
  * block may reuse it, [feat] LongSANA pull request: timesteps per chunk).
  * The result is the one-shot result of the concatenated blocks.  Workspace as
- * for la_block_causal_forward with frames = block_frames. */
+ * for la_block_causal_forward with frames = block_frames; the state's S and z
+ * must not overlap q, k, v, out, the workspace or the rotary table. */
 int la_stream_block(la_state* st, const void* q, const void* k, const void* v, void* out,
                     la_dtype in_dt, la_dtype out_dt, int B, int H, int head_dim,
                     int block_frames, int tokens_per_frame, const la_rope* rope, float eps,
@@ -225,7 +230,8 @@ size_t la_qkv_workspace_bytes(int B, int H, int head_dim, int frames, int tokens
  * unnormalised; norm_eps must be finite and > 0 when either is given.  out is
  * (B, N, H, head_dim) of dtype out_dt and must not overlap qkv or the weights.
  * ws (256-byte aligned, ws_bytes >= la_qkv_workspace_bytes) is caller-owned
- * scratch.  Block schedule, RoPE, eps, status codes and stream semantics as
+ * scratch; its used part must not overlap qkv, out, the weights or the
+ * rotary table.  Block schedule, RoPE, eps, status codes and stream semantics as
  * for la_block_causal_forward. */
 int la_block_causal_forward_qkv(const void* qkv, void* out, la_dtype in_dt, la_dtype out_dt,
                                 int B, int H, int head_dim, int frames, int tokens_per_frame,

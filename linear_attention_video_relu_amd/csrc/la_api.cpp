@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <initializer_list>
 
 #include "la_internal.h"
 #include "la_vr.h"
@@ -203,6 +204,50 @@ int check_tensors(const void* q, const void* k, const void* v, void* out, la_dty
 
 int hip_status(int e) { return e == 0 ? LA_OK : LA_ERR_HIP; }
 
+// Bytes of one (B, N, H, head_dim) tensor of dtype dt (rows * row_mult for
+// the fused q|k|v input).
+size_t tensor_bytes(const Plan& p, la_dtype dt, int row_mult = 1) {
+  return (size_t)p.B * p.N * row_mult * p.H * p.D * esize(dt);
+}
+
+// A byte range a call touches.
+struct Span {
+  const void* p;
+  size_t n;
+};
+
+// True if the range w, which the call writes, shares bytes with any of the
+// others (null or empty ranges are skipped).
+bool clashes(Span w, std::initializer_list<Span> others) {
+  if (!w.p || !w.n) return false;
+  for (const Span& o : others)
+    if (o.p && o.n && overlaps(w.p, w.n, o.p, o.n)) return true;
+  return false;
+}
+
+Span rope_span(const la_rope* r) {
+  if (!rope_on(r)) return {nullptr, 0};
+  return {r->table, 8 * ((size_t)r->max_frames * (r->d_t / 2) + (size_t)r->grid_h * (r->d_h / 2) +
+                         (size_t)r->grid_w * (r->d_w / 2))};
+}
+
+// The workspace (the part the call uses) against the call's tensors and the
+// rotary table, the output against the rotary table, and a carried state
+// (written when `save` is set) against all of them.
+int check_scratch(const Plan& p, void* ws, size_t used, Span out, std::initializer_list<Span> tensors,
+                  const la_rope* rope, const la_state* st = nullptr) {
+  const Span r = rope_span(rope);
+  if (clashes({ws, used}, tensors) || clashes({ws, used}, {out, r}) || clashes(out, {r}))
+    return LA_ERR_INVALID_ARG;
+  if (st) {
+    const Span S{st->S, (size_t)p.B * p.H * p.D * p.D * 4}, z{st->z, (size_t)p.B * p.H * p.D * 4};
+    if (clashes({ws, used}, {S, z}) || clashes(S, tensors) || clashes(z, tensors) || clashes(S, {out, r}) ||
+        clashes(z, {out, r}))
+      return LA_ERR_INVALID_ARG;
+  }
+  return LA_OK;
+}
+
 // Fused (B, N, 3, C) input, its output and the optional norm weights; fills
 // the prologue (scales in the workspace) and the q, k, v row pointers.
 int check_fused(const void* qkv, void* out, la_dtype in_dt, la_dtype out_dt, const Plan& p,
@@ -279,6 +324,11 @@ int backward_common(const void* q, const void* k, const void* v, const void* dou
     if (ws && overlaps(outs[i], nout, ws, ws_bytes)) return LA_ERR_INVALID_ARG;
   }
   if (!ws || !aligned(ws, 256) || ws_bytes < p.ws_total_bw) return LA_ERR_INVALID_ARG;
+  st = check_scratch(p, ws, p.ws_total_bw, {nullptr, 0}, {{q, nin}, {k, nin}, {v, nin}, {dout, nin}}, rope);
+  if (st != LA_OK) return st;
+  for (int i = 0; i < 3; ++i)
+    if (clashes({outs[i], nout}, {rope_span(rope)})) return LA_ERR_INVALID_ARG;
+  if (st != LA_OK) return st;
   return hip_status(lavr::launch_backward(p, q, k, v, dout, dq, dk, dv, in_dt == LA_BF16,
                                           grad_dt == LA_BF16, eps, ws, stream, have_prefix));
 }
@@ -338,6 +388,9 @@ int la_block_causal_forward(const void* q, const void* k, const void* v, void* o
   st = check_tensors(q, k, v, out, in_dt, out_dt, p);
   if (st != LA_OK) return st;
   if (!ws || !aligned(ws, 256) || ws_bytes < p.ws_total) return LA_ERR_INVALID_ARG;
+  const size_t nin = tensor_bytes(p, in_dt), nout = tensor_bytes(p, out_dt);
+  st = check_scratch(p, ws, p.ws_total, {out, nout}, {{q, nin}, {k, nin}, {v, nin}}, rope);
+  if (st != LA_OK) return st;
   return hip_status(lavr::launch_forward(p, q, k, v, out, in_dt == LA_BF16, out_dt == LA_BF16, eps,
                                          ws, nullptr, nullptr, nullptr, nullptr, stream));
 }
@@ -357,6 +410,9 @@ int la_block_causal_forward_timed(const void* q, const void* k, const void* v, v
   st = check_tensors(q, k, v, out, in_dt, out_dt, p);
   if (st != LA_OK) return st;
   if (!ws || !aligned(ws, 256) || ws_bytes < p.ws_total) return LA_ERR_INVALID_ARG;
+  const size_t nin = tensor_bytes(p, in_dt), nout = tensor_bytes(p, out_dt);
+  st = check_scratch(p, ws, p.ws_total, {out, nout}, {{q, nin}, {k, nin}, {v, nin}}, rope);
+  if (st != LA_OK) return st;
   return hip_status(lavr::launch_forward(p, q, k, v, out, in_dt == LA_BF16, out_dt == LA_BF16, eps,
                                          ws, nullptr, nullptr, nullptr, nullptr, stream, events));
 }
@@ -416,6 +472,10 @@ int la_block_causal_forward_qkv(const void* qkv, void* out, la_dtype in_dt, la_d
   const void *q, *k, *v;
   st = check_fused(qkv, out, in_dt, out_dt, p, q_gamma, k_gamma, norm_eps, ws, ws_bytes, &pro, &q, &k, &v);
   if (st != LA_OK) return st;
+  const size_t C4 = (size_t)p.H * p.D * 4;
+  st = check_scratch(p, ws, p.ws_total_qkv, {out, tensor_bytes(p, out_dt)},
+                     {{qkv, tensor_bytes(p, in_dt, 3)}, {q_gamma, C4}, {k_gamma, C4}}, rope);
+  if (st != LA_OK) return st;
   return hip_status(lavr::launch_forward(p, q, k, v, out, in_dt == LA_BF16, out_dt == LA_BF16, eps,
                                          ws, nullptr, nullptr, nullptr, nullptr, stream, nullptr, &pro));
 }
@@ -456,6 +516,9 @@ int la_stream_block(la_state* st, const void* q, const void* k, const void* v, v
   rc = check_tensors(q, k, v, out, in_dt, out_dt, p);
   if (rc != LA_OK) return rc;
   if (!ws || !aligned(ws, 256) || ws_bytes < p.ws_total) return LA_ERR_INVALID_ARG;
+  const size_t nin = tensor_bytes(p, in_dt), nout = tensor_bytes(p, out_dt);
+  rc = check_scratch(p, ws, p.ws_total, {out, nout}, {{q, nin}, {k, nin}, {v, nin}}, rope, st);
+  if (rc != LA_OK) return rc;
   const int e = lavr::launch_forward(p, q, k, v, out, in_dt == LA_BF16, out_dt == LA_BF16, eps, ws,
                                      st->S, st->z, save ? st->S : nullptr, save ? st->z : nullptr,
                                      stream);
@@ -480,6 +543,10 @@ int la_stream_block_qkv(la_state* st, const void* qkv, void* out, la_dtype in_dt
   lavr::Prologue pro;
   const void *q, *k, *v;
   rc = check_fused(qkv, out, in_dt, out_dt, p, q_gamma, k_gamma, norm_eps, ws, ws_bytes, &pro, &q, &k, &v);
+  if (rc != LA_OK) return rc;
+  const size_t C4 = (size_t)p.H * p.D * 4;
+  rc = check_scratch(p, ws, p.ws_total_qkv, {out, tensor_bytes(p, out_dt)},
+                     {{qkv, tensor_bytes(p, in_dt, 3)}, {q_gamma, C4}, {k_gamma, C4}}, rope, st);
   if (rc != LA_OK) return rc;
   const int e = lavr::launch_forward(p, q, k, v, out, in_dt == LA_BF16, out_dt == LA_BF16, eps, ws,
                                      st->S, st->z, save ? st->S : nullptr, save ? st->z : nullptr,

@@ -122,6 +122,44 @@ def test_forward_rejects_bad_rope(lavr, kw):
     assert call_forward(lavr, rope=ctypes.byref(r)) == lavr.LA_ERR_INVALID_ARG
 
 
+def test_forward_rejects_shared_memory(lavr):
+    """The workspace may not share bytes with the tensors or the rotary table,
+    nor the output with the table (checked before anything is launched)."""
+    r = rope_desc(lavr)                  # table at FAKE + 0x5000000
+    rp = ctypes.byref(r)
+    assert call_forward(lavr, ws=FAKE, rope=rp) == 1                      # workspace over q
+    assert call_forward(lavr, ws=FAKE + 0x3000000, rope=rp) == 1          # workspace over out
+    assert call_forward(lavr, ws=FAKE + 0x5000000 - 256, rope=rp) == 1    # workspace over the table
+    assert call_forward(lavr, out=FAKE + 0x5000000 - 64, rope=rp) == 1    # out over the table
+
+
+def test_stream_block_rejects_shared_memory(lavr):
+    st = lavr.LaState()
+    st.S, st.z, st.B, st.H, st.head_dim, st.frames_done = FAKE, FAKE + 0x100000, 2, 4, 32, 0
+    f = lavr.lib.la_stream_block
+    vp = ctypes.c_void_p
+    q, k, v, out = (FAKE + i * 0x1000000 for i in range(1, 5))
+    ws = FAKE + 0x6000000
+
+    def call(**kw):
+        a = dict(q=q, k=k, v=v, out=out, ws=ws)
+        a.update(kw)
+        return f(ctypes.byref(st), vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["out"]), 1, 1, 2, 4, 32, 3, 6,
+                 None, 1e-8, 1, vp(a["ws"]), 1 << 24, None)
+
+    assert call(out=FAKE) == 1                   # out over the carried S
+    assert call(ws=FAKE + 0x100000) == 1         # workspace over the carried z
+    assert call(q=FAKE + 0x100000 - 64) == 1     # q over the carried S and z
+    assert st.frames_done == 0
+
+
+def test_backward_and_qkv_reject_shared_memory(lavr):
+    assert call_backward(lavr, ws=FAKE + 0x3000000) == 1      # workspace over dout
+    assert call_backward(lavr, ws=FAKE + 0x1000000) == 1      # workspace over k
+    assert call_forward_qkv(lavr, ws=FAKE) == 1               # workspace over the fused rows
+    assert call_forward_qkv(lavr, ws=FAKE + 0x5000000) == 1   # workspace over the q weights
+
+
 def test_rope_table_build_rejects(lavr):
     r = lavr.LaRope()
     f = lavr.lib.rope_table_build
