@@ -113,7 +113,13 @@ def test_bf16_output_is_rne_of_f32_output(lavr):
     assert torch.equal(o16, o32.to(torch.bfloat16))
 
 
-@pytest.mark.parametrize("split", [(8, 12, 12), (6, 14, 12)])
+@pytest.mark.parametrize("split", [
+    (8, 12, 12), (6, 14, 12),
+    (0, 16, 16),                         # no temporal section
+    (32, 0, 0),                          # frames only (the grid is not used)
+    (8, 24, 0), (0, 32, 0),              # an empty spatial section
+    (2, 30, 0),                          # odd pair count next to an empty section
+])
 def test_f32_small_3d(lavr, split):
     cfg = small_cfg(dtype="f32", rope={"split": split, "base": 10000.0})
     say("case small f32 3-D RoPE")
