@@ -122,6 +122,13 @@ struct ReadArgs {
 
 // ------------------------------------------------------------------ helpers
 
+// Chunk partial records are stored chunk-major: record (chunk ci, batch row *
+// H + head bh) at ci * BH + bh, BH = batch rows * H.  The workgroups that
+// finish together (the head groups of one chunk index) then write one
+// contiguous range; a head-major layout scattered those writes across the
+// workspace, and the write bursts slowed the K/V read stream around them.
+__device__ __forceinline__ size_t part_rec(size_t bh, int ci, size_t BH) { return (size_t)ci * BH + bh; }
+
 __device__ __forceinline__ uint32_t fast_div(uint32_t n, uint64_t mag) {
   // floor(n / d) with mag = floor(2^42 / d) + 1; exact while n * d < 2^42.
   return (uint32_t)(((uint64_t)n * mag) >> 42);
@@ -614,16 +621,15 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? ((P2 && DH == 32 && !NRM && 
   __syncthreads();
 
   // Records: S (DH x DH, row e, column f) then z (DH).
-  const int nchunk = a.nb * a.cpb;
   if constexpr (W64) {
-    float* dst = a.part + ((size_t)(b * a.H + h0) * nchunk + ci) * RECN;
+    float* dst = a.part + part_rec((size_t)(b * a.H + h0), ci, (size_t)gridDim.y * a.H) * RECN;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int e = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
       dst[(ha * D + e) * DH + hb * D + (lane & 31)] = acc[v];
     }
   } else if (w < 2 && w < nh) {
-    float* dst = a.part + ((size_t)(b * a.H + h0 + w) * nchunk + ci) * RECN;
+    float* dst = a.part + part_rec((size_t)(b * a.H + h0 + w), ci, (size_t)gridDim.y * a.H) * RECN;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int e = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
@@ -636,8 +642,8 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? ((P2 && DH == 32 && !NRM && 
     float s = 0.f;
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) s += zred[(ww * 4 + lc2) * 16 + hd * 8 + el];
-    const size_t zi = W64 ? ((size_t)(b * a.H + h0) * nchunk + ci) * RECN + DH * DH + hd * D + ch
-                          : ((size_t)(b * a.H + h0 + hd) * nchunk + ci) * RECN + D * D + ch;
+    const size_t zi = W64 ? part_rec((size_t)(b * a.H + h0), ci, (size_t)gridDim.y * a.H) * RECN + DH * DH + hd * D + ch
+                          : part_rec((size_t)(b * a.H + h0 + hd), ci, (size_t)gridDim.y * a.H) * RECN + D * D + ch;
     a.part[zi] = s;
   }
 }
@@ -664,7 +670,8 @@ __global__ __launch_bounds__(PFX_NT) void k_prefix(PrefixArgs a) {
   const bool ok = el < REC;
   const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
   // (lanes past the record read its last element and discard it)
-  const float* part = a.part + bh * a.nb * a.cpb * REC + min(el, REC - 1);
+  const size_t cstride = (size_t)gridDim.z * a.H * REC;   // from one chunk's record to the next
+  const float* part = a.part + bh * REC + min(el, REC - 1);
   float* o = a.prefix + bh * a.nb * REC + el;
   float acc = 0.f;
   if (w == 0 && ok && a.S_init != nullptr)
@@ -685,7 +692,7 @@ __global__ __launch_bounds__(PFX_NT) void k_prefix(PrefixArgs a) {
 #pragma unroll
       for (int i = 0; i < BATCH; ++i) {
         const int jb = a.rev ? a.nb - 1 - (r0 + w + 4 * lb) : r0 + w + 4 * lb;
-        v[i] = part[((size_t)jb * a.cpb + lcn) * REC];
+        v[i] = part[((size_t)jb * a.cpb + lcn) * cstride];
         if (q0 + i + 1 < items && ++lcn == a.cpb) { lcn = 0; ++lb; }
       }
 #pragma unroll
@@ -726,13 +733,14 @@ __global__ __launch_bounds__(256) void k_prefix1(PrefixArgs a) {
   const int REC = a.rec;
   if (el >= REC) return;
   const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
-  const float* part = a.part + bh * a.cpb * REC + el;
+  const size_t cstride = (size_t)gridDim.z * a.H * REC;   // from one chunk's record to the next
+  const float* part = a.part + bh * REC + el;
   constexpr int BATCH = 16;
   float s = 0.f;
   for (int c0 = 0; c0 < a.cpb; c0 += BATCH) {
     float v[BATCH];
 #pragma unroll
-    for (int i = 0; i < BATCH; ++i) v[i] = part[(size_t)min(c0 + i, a.cpb - 1) * REC];
+    for (int i = 0; i < BATCH; ++i) v[i] = part[(size_t)min(c0 + i, a.cpb - 1) * cstride];
 #pragma unroll
     for (int i = 0; i < BATCH; ++i)
       if (c0 + i < a.cpb) s += v[i];
@@ -1726,7 +1734,6 @@ __global__ __launch_bounds__(NT, 2) void k_bw_q(BwQArgs a) {
     }
   }
   __syncthreads();
-  const int nchunk = a.nb * a.cpb;
   if constexpr (W64) {
     // one record: G (64 x 64) then gz (64)
     for (int o = threadIdx.x; o < RECN; o += NT) {
@@ -1737,7 +1744,7 @@ __global__ __launch_bounds__(NT, 2) void k_bw_q(BwQArgs a) {
         const int f = o - DH * DH;
         s = zred[f] + zred[2 * D + f] + zred[4 * D + f] + zred[6 * D + f];
       }
-      a.part[((size_t)(b * a.H + h0) * nchunk + ci) * RECN + o] = s;
+      a.part[part_rec((size_t)(b * a.H + h0), ci, (size_t)gridDim.y * a.H) * RECN + o] = s;
     }
   } else {
     for (int el = threadIdx.x; el < 2 * RECN; el += NT) {
@@ -1752,7 +1759,7 @@ __global__ __launch_bounds__(NT, 2) void k_bw_q(BwQArgs a) {
         s = zred[(0 * 2 + h) * D + f] + zred[(1 * 2 + h) * D + f] + zred[(2 * 2 + h) * D + f] +
             zred[(3 * 2 + h) * D + f];
       }
-      a.part[((size_t)(b * a.H + h0 + h) * nchunk + ci) * RECN + o] = s;
+      a.part[part_rec((size_t)(b * a.H + h0 + h), ci, (size_t)gridDim.y * a.H) * RECN + o] = s;
     }
   }
 }
