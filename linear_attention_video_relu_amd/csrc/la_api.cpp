@@ -615,6 +615,6 @@ const char* la_status_string(int status) {
   }
 }
 
-const char* la_version(void) { return "0.3.0"; }
+const char* la_version(void) { return "0.4.0"; }
 
 }  // extern "C"

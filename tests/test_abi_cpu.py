@@ -35,7 +35,7 @@ def test_exports_every_declared_function(lavr):
 
 
 def test_version_and_status_strings(lavr):
-    assert lavr.lib.la_version() == b"0.3.0"
+    assert lavr.lib.la_version() == b"0.4.0"
     for code in range(5):
         assert lavr.status_string(code).startswith("LA_")
     assert "unknown" in lavr.status_string(99)
