@@ -82,6 +82,7 @@ def run(lavr, cfg, grad_dtype):
     dict(head_dim=64, H=1, B=1, frames=40, block_frames=3, tokens_per_frame=48, grid=(6, 8),
          rope={"split": (14, 26, 24), "base": 10000.0}),                             # many groups, odd pairs
     dict(head_dim=64, H=2, rope=None, frames=7, block_frames=2, first_block_frames=3),
+    dict(B=6, H=2, frames=7, block_frames=2),                                        # many batch rows
 ])
 @pytest.mark.parametrize("grad", ["f32", "bf16"])
 def test_backward_small_bf16_inputs(lavr, kw, grad):

@@ -78,6 +78,7 @@ def test_tiny_f32_matches_oracle(lavr):
     dict(frames=5, block_frames=8),                   # one block shorter than block_frames
     dict(frames=40, block_frames=3, H=2, B=1, tokens_per_frame=48, grid=(6, 8)),  # many tiles
     dict(rope={"split": (6, 14, 12), "base": 10000.0}),   # odd pair counts: per-pair table reads
+    dict(B=6, H=2, frames=7, block_frames=2),         # many batch rows, one head group: tiny chunks
 ])
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 def test_small_bf16_matches_oracle(lavr, kw, out_dtype):
