@@ -33,6 +33,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 def rec_bytes(d):
     """Bytes of one fp32 (S, z) record at head dim d."""
     return (d * d + d) * 4
+
+
 KERNEL_SOURCES = ("la_kernels.hip", "la_internal.h", "la_api.cpp")
 
 
