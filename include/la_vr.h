@@ -32,6 +32,12 @@
  * head_dim.  head_dim 32 and 64 are built (the per-head widths the walkthrough
  * names, "Integration into Sana's Video Backbone").
  *
+ * Size limits.  A call takes at most 2^30 tokens per batch row (N = frames *
+ * tokens_per_frame), B <= 65535 and B * H <= 2^24, and N * tokens_per_frame must
+ * stay below 2^42 (exact integer division of token indices); past them a call
+ * returns LA_ERR_UNSUPPORTED and the workspace-size queries return 0.  A batch
+ * row may hold more than 4 GiB.
+ *
  * RoPE.  head_dim is split into consecutive sections of d_t, d_h and d_w
  * channels that follow the token's frame index t, row and column.  Pair i
  * (channels 2i, 2i+1 of a section of width d_s) turns by the angle

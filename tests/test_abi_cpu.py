@@ -101,6 +101,20 @@ def test_forward_rejects_bad_arguments(lavr, kw, code):
     assert call_forward(lavr, **kw) == code
 
 
+def test_size_limits(lavr):
+    """The documented maxima: 2^30 tokens per batch row, B <= 65535, B * H <= 2^24."""
+    assert lavr.lib.la_workspace_bytes(1, 2, 32, 1 << 20, 1024, 2, 0) > 0          # N = 2^30 plans
+    assert lavr.lib.la_workspace_bytes(1, 2, 32, (1 << 20) + 1, 1024, 2, 0) == 0   # one frame more does not
+    assert call_forward(lavr, frames=(1 << 20) + 1, tpf=1024) == lavr.LA_ERR_UNSUPPORTED
+    # at the maximum the plan is fine and the call fails only on the small workspace
+    assert call_forward(lavr, frames=1 << 20, tpf=1024) == lavr.LA_ERR_INVALID_ARG
+    assert call_forward(lavr, B=65536) == lavr.LA_ERR_UNSUPPORTED
+    assert call_forward(lavr, B=4096, H=4097) == lavr.LA_ERR_UNSUPPORTED
+    # N * tokens_per_frame reaches 2^42 (N = 2^27 tokens in frames of 2^15)
+    assert lavr.lib.la_workspace_bytes(1, 2, 32, (1 << 12) - 1, 1 << 15, 2, 0) > 0
+    assert lavr.lib.la_workspace_bytes(1, 2, 32, 1 << 12, 1 << 15, 2, 0) == 0
+
+
 def rope_desc(lavr, **kw):
     r = lavr.LaRope()
     d = dict(table=FAKE + 0x5000000, d_t=8, d_h=12, d_w=12, max_frames=4, grid_h=2, grid_w=3)
