@@ -59,6 +59,16 @@ constexpr int RSRC_WORD3 = 0x00020000;  // gfx9 raw buffer: 32-bit data, range c
 #ifndef LAVR_STORE_CPOL
 #define LAVR_STORE_CPOL 2
 #endif
+// k_bw_q with bf16 inputs: 16-token groups of q/g loads in flight per wave, at
+// head dim 32 and 64.  A third group took the minute backward (d 32) from 2.91
+// to 2.89 ms and measured the same at 64; fp32 inputs keep two (a third spills
+// at 2 waves per SIMD).
+#ifndef LAVR_BWQ_PF
+#define LAVR_BWQ_PF 3
+#endif
+#ifndef LAVR_BWQ_PF64
+#define LAVR_BWQ_PF64 2
+#endif
 #ifndef LAVR_STATE_PF
 #define LAVR_STATE_PF 2   // block-state: 64-token steps of K/V loads in flight
 #endif
@@ -1437,6 +1447,8 @@ __global__ __launch_bounds__(NT, 2) void k_bw_q(BwQArgs a) {
   constexpr int WT = 16 * TCOLS;                     // elements of one wave tile array
   constexpr int WAVE_BYTES = BF ? 3 * WT * 2 : 2 * WT * 4;   // g, r/den hi, lo (bf16) or g, r/den (fp32)
   constexpr int RED_FLOATS = W64 ? DH * DH : 4 * 2 * D * D;  // waves' G partials at the end
+  constexpr int PFQ = !BF ? 2 : W64 ? LAVR_BWQ_PF64 : LAVR_BWQ_PF;   // 16-token groups of loads in flight per wave
+  static_assert(PFQ == 2 || PFQ == 3, "k_bw_q prefetch depth: two or three register buffers");
   static_assert(4 * WAVE_BYTES + NB * OPS_BLOCK * 16 >= RED_FLOATS * 4, "reduction space");
   extern __shared__ __align__(16) unsigned char smem[];
   u32x4* ops = reinterpret_cast<u32x4*>(smem + 4 * WAVE_BYTES);   // [NB blocks][4 slots][64 lanes]
@@ -1514,9 +1526,10 @@ __global__ __launch_bounds__(NT, 2) void k_bw_q(BwQArgs a) {
   // past the chunk read zeros and must add nothing to G (1/den is taken as 0
   // there, which also keeps eps = 0 from turning them into NaN).
   int tok = w * 16 + tl;
-  Buf b0, b1;
+  Buf b0, b1, b2;
   load_group(b0);
   load_group(b1);
+  if constexpr (PFQ > 2) load_group(b2);
   __syncthreads();
 
   // G accumulators: at 32 each wave adds both heads' blocks over its own
@@ -1695,7 +1708,8 @@ __global__ __launch_bounds__(NT, 2) void k_bw_q(BwQArgs a) {
     }
   };
 
-  const int iters = W64 ? (ngroups + 7) / 8 : (ngroups - w + 7) / 8;   // uniform at 64
+  // PFQ groups per wave per iteration (4 PFQ per workgroup); uniform at 64
+  const int iters = W64 ? (ngroups + 4 * PFQ - 1) / (4 * PFQ) : (ngroups - w + 4 * PFQ - 1) / (4 * PFQ);
   for (int it = 0; it < iters; ++it) {
     run_group(b0);
     g_step();
@@ -1703,6 +1717,11 @@ __global__ __launch_bounds__(NT, 2) void k_bw_q(BwQArgs a) {
     run_group(b1);
     g_step();
     load_group(b1);
+    if constexpr (PFQ > 2) {
+      run_group(b2);
+      g_step();
+      load_group(b2);
+    }
   }
 
   // Sum the four waves: G through LDS (over the tiles and operand blocks), gz
