@@ -206,7 +206,8 @@ def test_backward_eps_zero_with_padded_groups(lavr, d):
 
 
 @pytest.mark.parametrize("name,heads", [("clip480p_bf16", [(0, 0), (0, 35), (0, 69)]),
-                                        ("clip480p_d64_bf16", [(0, 0), (0, 17), (0, 34)])])
+                                        ("clip480p_d64_bf16", [(0, 0), (0, 17), (0, 34)]),
+                                        ("minute_bf16", [(0, 0), (0, 41)])])   # the timed backward's shape
 def test_backward_full_size(lavr, name, heads):
     w = W()
     cfg = w.workload(name)
@@ -233,3 +234,5 @@ def test_backward_full_size(lavr, name, heads):
             e = oracle.rel_err(to_f64_torch(t[b_, :, h]), r)
             say(f"  b={b_} h={h} {nm} rel err {e:.3e}")
             assert e <= TOL_BF16_IN_F32_GRAD
+    del dq, dk, dv, again, q, k, v, g, ws
+    torch.cuda.empty_cache()
