@@ -52,7 +52,12 @@
  * checks its arguments on the host first and returns an error code without
  * touching the GPU if they are wrong; otherwise it enqueues its kernels on
  * `stream` (a hipStream_t, NULL = default stream) and returns at once.  The
- * library never aborts and never prints.
+ * library never aborts and never prints.  A call enqueues kernels only (no
+ * allocation, memset, copy or synchronisation), so calls on different streams
+ * with their own workspaces run side by side, and one-shot forward and backward
+ * calls can be captured into a HIP graph and replayed.  A streamed call reads
+ * and advances la_state.frames_done on the host, so a captured one would replay
+ * with the rotary frame offset it was captured with.
  */
 #ifndef LA_VR_H
 #define LA_VR_H
