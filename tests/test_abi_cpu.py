@@ -34,6 +34,24 @@ def test_exports_every_declared_function(lavr):
         assert hasattr(raw, n), n
 
 
+def test_calls_only_enqueue_kernels():
+    """The header promises that a call enqueues kernels only (so it can run under
+    HIP graph capture): the library sources make no allocation, memset, copy or
+    synchronisation call.  Only the timed forward records events."""
+    src_dir = os.path.join(ROOT, "linear_attention_video_relu_amd", "csrc")
+    banned = re.compile(r"\b(hipMalloc\w*|hipFree\w*|hipHostMalloc|hipMemset\w*|hipMemcpy\w*|"
+                        r"hipDeviceSynchronize|hipStreamSynchronize|hipEventSynchronize|hipStreamCreate\w*)\s*\(")
+    events = 0
+    for name in sorted(os.listdir(src_dir)):
+        if not name.endswith((".hip", ".cpp", ".h")):
+            continue
+        with open(os.path.join(src_dir, name)) as f:
+            code = re.sub(r"//[^\n]*|/\*.*?\*/", "", f.read(), flags=re.S)
+        assert not banned.search(code), (name, banned.search(code).group(0))
+        events += len(re.findall(r"\bhipEventRecord\s*\(", code))
+    assert events == 1
+
+
 def test_version_and_status_strings(lavr):
     assert lavr.lib.la_version() == b"0.4.0"
     for code in range(5):
