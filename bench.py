@@ -89,13 +89,32 @@ def _oracle_task(h):
     return time.perf_counter() - t
 
 
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None if unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+# Worker processes of the oracle leg.  A one-GPU box grants this process a
+# share of 16 host cores whatever the affinity mask shows, and more workers
+# than that oversubscribe the share.
+MAX_CPU_WORKERS = 16
+
+
 def cpu_baseline(cfg, arrs, n_heads):
     """Time the fp64 oracle on heads 0 .. n_heads-1 of batch row 0, one process per head.
 
     Runs before anything touches the GPU, so the forked workers inherit the drawn
     inputs without copying them."""
     _CPU_JOB.update(cfg=cfg, arrs=arrs)
-    workers = max(1, min(n_heads, len(os.sched_getaffinity(0)), 16))
+    host_cores = len(os.sched_getaffinity(0))
+    workers = max(1, min(n_heads, host_cores, MAX_CPU_WORKERS))
     ctxm = mp.get_context("fork")
     t = time.perf_counter()
     with ctxm.Pool(workers) as pool:
@@ -104,6 +123,7 @@ def cpu_baseline(cfg, arrs, n_heads):
     _CPU_JOB.clear()
     N = W.n_tokens(cfg)
     return {"value": n_heads * N / wall, "unit": "tokens·heads/s", "cores": workers,
+            "workers": workers, "host_cores": host_cores, "cpu_model": cpu_model(),
             "kind": "oracle",
             "sample": f"{n_heads} of {cfg['B'] * cfg['H']} (batch, head) streams of {cfg['name']}, "
                       f"full length {N} tokens, fp64 numpy oracle (inputs widened from bf16 inside "
@@ -269,6 +289,11 @@ def main():
         "step_frac_of_peak": bytes_step / (ms_step * 1e6) / HBM_PEAK_GBS,
         "event_ms_per_step": float(ev_step.mean()),
         "kernels": kernels,
+        # per timed step, HIP-event ms of each kernel: the shader clock dips
+        # when the heavy load starts and recovers over ~40 ms, and the trend
+        # shows how much of the timed region falls in that ramp
+        "step_trend": {name: [round(float(x), 4) for x in ph[:, i]]
+                       for i, name in enumerate(("k_block_state", "k_prefix", "k_readout"))},
         "cpu_baseline": cpu,
     }
 

@@ -36,7 +36,9 @@ constexpr int kStateMax = LAVR_STATE_MAX;
 constexpr int kReadMax = LAVR_READ_MAX;
 constexpr int kMinWg = LAVR_MIN_WG;
 constexpr long long kReadSlots = 4 * 256;   // readout workgroups resident at once (4 per CU)
-constexpr int kTabLdsMax = 32768;      // LDS bytes for a staged rotary window
+constexpr int kTabLdsMax = 32768;      // LDS bytes for a staged rotary window ((cos, sin) pairs)
+constexpr int kTabLdsMax16 = 49152;    // the same for a readout tile's rope_words (with the 16 KB Sbar
+                                       // copy at head dim 64, at most 64 KB per workgroup)
 constexpr int kStep = 64;              // block-state kernel step (tokens)
 constexpr long long kTwo42 = 1LL << 42;
 constexpr long long kMaxTokens = 1LL << 30;
@@ -81,12 +83,12 @@ long long tab_pairs(const la_rope* r, int tpf, int tokens) {
 // ahead) stays within the 32-bit buffer offsets the kernels use; row_bytes is
 // the widest token row (fp32).  Returns false if no split fits.
 bool split_block(int L, int max_tokens, long long min_n, int mult, const la_rope* r, int tpf,
-                 long long row_bytes, int* n_out, int* T_out) {
+                 long long row_bytes, int entry_bytes, int tab_cap, int* n_out, int* T_out) {
   long long n = cdiv(L, max_tokens);
   if (n < min_n) n = min_n;
   for (;;) {
     const long long T = round_up(cdiv(L, n), mult);
-    if (tab_pairs(r, tpf, (int)T) * 8 <= kTabLdsMax && (T + 256) * row_bytes < (1LL << 31)) {
+    if (tab_pairs(r, tpf, (int)T) * entry_bytes <= tab_cap && (T + 256) * row_bytes < (1LL << 31)) {
       *n_out = (int)cdiv(L, T);
       *T_out = (int)T;
       return true;
@@ -101,13 +103,14 @@ bool split_block(int L, int max_tokens, long long min_n, int mult, const la_rope
 // twice max_tokens) drop that round, take them.  `rows` workgroups share each
 // piece index; `slots` is one resident round.
 void fit_rounds(int L, int max_tokens, long long rows, long long slots, int mult, const la_rope* r, int tpf,
-                long long row_bytes, int* n, int* T) {
+                long long row_bytes, int entry_bytes, int tab_cap, int* n, int* T) {
   const long long R = cdiv(rows * *n, slots);
   if (R <= 1 || R > 4) return;
   const long long n2 = (R - 1) * slots / rows;
   if (n2 < 1) return;
   const long long T2 = round_up(cdiv(L, n2), mult);
-  if (T2 > 2LL * max_tokens || tab_pairs(r, tpf, (int)T2) * 8 > kTabLdsMax || (T2 + 256) * row_bytes >= (1LL << 31))
+  if (T2 > 2LL * max_tokens || tab_pairs(r, tpf, (int)T2) * entry_bytes > tab_cap ||
+      (T2 + 256) * row_bytes >= (1LL << 31))
     return;
   *n = (int)cdiv(L, T2);
   *T = (int)T2;
@@ -150,11 +153,14 @@ int make_plan(Plan* p, int B, int H, int head_dim, int frames, int tpf, int bloc
   p->mag_gw = (uint64_t)(kTwo42 / gw_div) + 1;
   const long long row_bytes = (long long)p->row_in * 4;
   const long long min_n = cdiv(kMinWg, (long long)B * p->hg * p->nb);
-  if (!split_block(Lmax, kStateMax, min_n, kStep, rope, tpf, row_bytes, &p->cpb, &p->Tc))
+  // Block-state chunks stage (cos, sin) pairs (8 bytes); readout tiles may
+  // stage them as rope_words (16 bytes).
+  if (!split_block(Lmax, kStateMax, min_n, kStep, rope, tpf, row_bytes, 8, kTabLdsMax, &p->cpb, &p->Tc))
     return LA_ERR_UNSUPPORTED;
-  if (!split_block(Lmax, kReadMax, min_n, 64, rope, tpf, row_bytes, &p->rpb, &p->Tr))
+  if (!split_block(Lmax, kReadMax, min_n, 64, rope, tpf, row_bytes, 16, kTabLdsMax16, &p->rpb, &p->Tr))
     return LA_ERR_UNSUPPORTED;
-  fit_rounds(Lmax, kReadMax, (long long)B * p->hg * p->nb, kReadSlots, 64, rope, tpf, row_bytes, &p->rpb, &p->Tr);
+  fit_rounds(Lmax, kReadMax, (long long)B * p->hg * p->nb, kReadSlots, 64, rope, tpf, row_bytes, 16, kTabLdsMax16,
+             &p->rpb, &p->Tr);
   if ((long long)p->hg * p->nb * p->cpb > 0x7fffffffLL || (long long)p->hg * p->nb * p->rpb > 0x7fffffffLL)
     return LA_ERR_UNSUPPORTED;
 
@@ -171,6 +177,7 @@ int make_plan(Plan* p, int B, int H, int head_dim, int frames, int tpf, int bloc
   p->tab_state = (int)(tab_pairs(rope, tpf, p->Tc) * 8);
   p->lds_state = lavr::kStateTileSets * tiles + p->tab_state;
   p->lds_read = (int)(tab_pairs(rope, tpf, p->Tr) * 8);
+  p->lds_read16 = 2 * p->lds_read;
 
   const size_t rec = (size_t)p->rec * sizeof(float);
   const size_t part = (size_t)B * H * p->nb * p->cpb * rec;

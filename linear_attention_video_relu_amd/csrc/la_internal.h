@@ -49,7 +49,8 @@ struct Plan {
   RopeDev rope;
   int lds_state;        // dynamic LDS bytes of the block-state kernel
   int tab_state;        // of which the rotary window of a chunk
-  int lds_read;         // dynamic LDS bytes of the readout kernel
+  int lds_read;         // dynamic LDS bytes of the readout kernel's rotary window ((cos, sin) pairs)
+  int lds_read16;       // the same window as rope_words (16 bytes per pair)
   size_t ws_part;       // byte offset of the per-chunk partial states
   size_t ws_prefix;     // byte offset of the per-block prefix states
   size_t ws_suffix;     // byte offset of the per-block suffix sums (backward only)

@@ -35,6 +35,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "la_internal.h"
 
@@ -44,6 +45,7 @@ namespace {
 constexpr int D = 32;                // channels of one lane chunk's half (a head at head dim 32)
 constexpr int NT = 256;              // threads of the state and readout workgroups
 constexpr int kReadAlBytes = 2 * 8 * 64 * 16;   // head dim 64, bf16: Sbar hi and lo tiles of a readout workgroup
+constexpr int kReadZBytes = 2 * 2 * 4 * 16;     // head dim 32, packed path: zbar hi and lo slices of a readout workgroup
 constexpr int STEP = 64;             // tokens per step of the state kernel
 constexpr int TCOLS = 2 * D;         // an LDS tile row holds two heads
 constexpr int RSRC_WORD3 = 0x00020000;  // gfx9 raw buffer: 32-bit data, range checked
@@ -164,6 +166,20 @@ __device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
   }
 }
 
+// split8 with h << 16 formed by a byte permute: written as a shift, the
+// compiler forms it with a second conversion of x[2i] (one more instruction
+// per pair).  Used where the instruction count matters (the readout's packed
+// path); elsewhere the shift form needs fewer registers.
+__device__ __forceinline__ void split8p(const float* x, u32x4& hi, u32x4& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t h = pack_bf16(x[2 * i], x[2 * i + 1]);
+    hi[i] = h;
+    const uint32_t h0 = __builtin_amdgcn_perm(h, h, 0x01000c0cu);
+    lo[i] = pack_bf16(x[2 * i] - __uint_as_float(h0), x[2 * i + 1] - __uint_as_float(h & 0xffff0000u));
+  }
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 
 // First token of block j when the first block holds L0 tokens and every later
@@ -278,6 +294,36 @@ __device__ __forceinline__ TabWindow stage_table(float2* lds, const RopeDev& r, 
   return w;
 }
 
+// Rotary entry for rotating a packed bf16 pair (a, b) = (x_2i, x_2i+1) with
+// v_dot2_f32_bf16 (exact bf16 products, fp32 sum).  cos and sin are split into
+// bf16 parts c = ch + cl, s = sh + sl (ch, sh rounded to nearest, cl, sl the
+// rounded remainders, together ~2^-17 relative), and
+//   a c - b s = dot(a b, ch -sh) + dot(a b, cl -sl),
+//   a s + b c = dot(a b, sh  ch) + dot(a b, sl  cl).
+__device__ __forceinline__ float bf16_round(float x) { return (float)(__bf16)x; }
+
+__device__ __forceinline__ u32x4 rope_words(float2 cs) {
+  const float ch = bf16_round(cs.x), sh = bf16_round(cs.y);
+  const float cl = cs.x - ch, sl = cs.y - sh;
+  return u32x4{pack_bf16(ch, -sh), pack_bf16(cl, -sl), pack_bf16(sh, ch), pack_bf16(sl, cl)};
+}
+
+// stage_table with every (cos, sin) pair stored as its four rope_words.
+__device__ __forceinline__ TabWindow stage_table16(u32x4* lds, const RopeDev& r, long long t0,
+                                                   int n0, int n1, uint64_t mag_tpf) {
+  TabWindow w{0, 0};
+  if (r.table == nullptr || n1 <= n0) return w;
+  w.f_lo = (int)fast_div((uint32_t)n0, mag_tpf);
+  w.nf = (int)fast_div((uint32_t)(n1 - 1), mag_tpf) - w.f_lo + 1;
+  const float2* tab = reinterpret_cast<const float2*>(r.table);
+  const float2* tsrc = tab + (size_t)(t0 + w.f_lo) * r.pt;
+  const float2* hwsrc = tab + (size_t)r.max_frames * r.pt;
+  const int nt = w.nf * r.pt;
+  const int tot = nt + r.gh * r.ph + r.gw * r.pw;
+  for (int i = threadIdx.x; i < tot; i += blockDim.x) lds[i] = rope_words(i < nt ? tsrc[i] : hwsrc[i - nt]);
+  return w;
+}
+
 // (frame, row, col) of a lane's token, advanced 64 tokens at a time without
 // divisions: the carries are at most one row and one frame per step.
 struct TokPos {
@@ -337,7 +383,58 @@ struct RopeLane {
       }
     }
   }
+
+  // The same lookups in a table staged by stage_table16: T[p] holds the
+  // rope_words of the lane's pair p.
+  __device__ void fetch16(const u32x4* lds, const TokPos& tp, const TabWindow& w, u32x4* T) const {
+    const int fl = min(tp.f - w.f_lo, w.nf - 1);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int idx = base[i] + __umul24(fl, sf[i]) + __umul24(tp.row, sr[i]) + __umul24(tp.col, sc[i]);
+      if constexpr (P2) {
+        T[2 * i] = lds[idx];
+        T[2 * i + 1] = lds[idx + 1];
+      } else {
+        T[i] = lds[idx];
+      }
+    }
+  }
 };
+
+// phi = ReLU of 8 packed bf16 values, kept packed (integer max with 0 clears
+// every value whose sign bit is set).
+__device__ __forceinline__ u32x4 relu_pk(u32x4 r) {
+  const s16x2 z = {0, 0};
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t ri = r[i];
+    o[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(s16x2, ri), z));
+  }
+  return o;
+}
+
+// Rotate the 8 packed values of p (pairs p[i]) with their rope_words T[i]
+// into fp32 x.
+// dot(a, b) of two packed bf16 pairs with a zero addend.  The builtin would
+// become the accumulating v_dot2c_f32_bf16 after a register cleared to zero;
+// the three-operand form takes the zero as an inline constant.
+__device__ __forceinline__ float dot2_bf16_z(uint32_t a, uint32_t b) {
+  float r;
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+__device__ __forceinline__ void rotate_pk(const u32x4& p, const u32x4* T, float* x) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t pi = p[i];
+    const bf16x2 ab = __builtin_bit_cast(bf16x2, pi);
+    const uint32_t w0 = T[i][0], w1 = T[i][1], w2 = T[i][2], w3 = T[i][3];
+    x[2 * i] = __builtin_amdgcn_fdot2_f32_bf16(ab, __builtin_bit_cast(bf16x2, w1), dot2_bf16_z(pi, w0), false);
+    x[2 * i + 1] = __builtin_amdgcn_fdot2_f32_bf16(ab, __builtin_bit_cast(bf16x2, w3), dot2_bf16_z(pi, w2), false);
+  }
+}
 
 __device__ __forceinline__ void rotate8(float* x, const float2* cs) {
 #pragma unroll
@@ -777,25 +874,45 @@ __global__ __launch_bounds__(256) void k_prefix1(PrefixArgs a) {
 // each 32-channel half of token (l & 15), one 16-byte load of bf16 q per half.
 // At head dim 32 each half is a head; at 64 every 16-row tile of the output
 // sums the products of both halves.  The output lane holds channels
-// 4(l>>4) .. +3 of each 16-row tile for token (l & 15), so the normaliser of
-// that token, summed over the four lanes that share it, is already in place.
-// Tokens past the tile read as zeros and their stores are dropped by the
-// buffer range check.
+// 4(l>>4) .. +3 of each 16-row tile for token (l & 15).  Tokens past the tile
+// read as zeros and their stores are dropped by the buffer range check.
+//
+// bf16 inputs that are not normalised take the packed path: phi(q) stays
+// packed bf16 (exact) and feeds two MFMAs whose A operands repeat zbar's hi and
+// lo bf16 parts in every row, so each output lane receives its own token's
+// normaliser zbar . phi(q) with no cross-lane sum; the rotation is
+// v_dot2_f32_bf16 on the packed pairs against the rope_words table, so phi(q)
+// is never widened.  This path spends about a third fewer VALU instructions
+// per token than widening to fp32, which matters because the kernel's time
+// grows as the shader clock drops (the clock dips under a sudden heavy load).
+// Other inputs widen phi(q) to fp32, form the normaliser with fp32 FMAs summed
+// over the four lanes of a token, and rotate in fp32.
+//
+// RO: RoPE on, a compile-time switch so the loop carries no branch on it.
 
-template <typename TIn, typename TOut, bool P2, int DH, bool NRM>
-__global__ __launch_bounds__(NT, (!NRM && (DH == 32 || sizeof(TIn) == 2)) ? 4 : 2) void k_readout(ReadArgs a) {
+template <typename TIn, typename TOut, bool P2, int DH, bool NRM, bool RO>
+__global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH == 32 && P2) ? 3 : 2) void k_readout(
+    ReadArgs a) {
   constexpr bool BF = sizeof(TIn) == 2;
   constexpr bool W64 = DH == 64;
+  constexpr bool FAST = BF && !NRM;      // packed bf16 phi(q)
   constexpr int RECN = DH * DH + DH;
   constexpr int ES = (int)sizeof(TIn), EO = (int)sizeof(TOut);
   constexpr int NA = W64 ? 8 : 4;        // Sbar tiles of 16 rows x 32 channels a lane holds
   extern __shared__ __align__(16) unsigned char smem[];
-  // bf16 at head dim 64: the hi and lo parts of the Sbar tiles live in LDS
-  // (one copy per workgroup, lane-major: slot (2 i + part) * 64 + lane), which
-  // keeps the kernel within 128 registers.
-  constexpr bool A_LDS = BF && W64;
+  // bf16 at head dim 64, and the packed path: the hi and lo parts of the Sbar
+  // tiles live in LDS (one copy per workgroup, lane-major: slot (2 i + part) *
+  // 64 + lane), and on the packed path at head dim 32 zbar's bf16 parts too
+  // ([head][part][lane row] slices), which keeps the kernel within 128
+  // registers without spills.
+  constexpr bool A_LDS = BF && (W64 || FAST);
+  constexpr bool Z_LDS = FAST && !W64;
+  constexpr int A_BYTES = A_LDS ? 2 * NA * 64 * 16 : 0;
+  constexpr int PRE = A_BYTES + (Z_LDS ? kReadZBytes : 0);
   u32x4* lds_a = reinterpret_cast<u32x4*>(smem);
-  float2* tab = reinterpret_cast<float2*>(smem + (A_LDS ? kReadAlBytes : 0));
+  u32x4* lds_z = reinterpret_cast<u32x4*>(smem + A_BYTES);
+  float2* tab = reinterpret_cast<float2*>(smem + PRE);
+  u32x4* tab16 = reinterpret_cast<u32x4*>(smem + PRE);
 
   const int g = blockIdx.x % a.hg;
   const int ti = blockIdx.x / a.hg;
@@ -807,7 +924,6 @@ __global__ __launch_bounds__(NT, (!NRM && (DH == 32 || sizeof(TIn) == 2)) ? 4 : 
   const int t0 = min(blk0 + r * a.Tr, blk1);
   const int t1 = min(t0 + a.Tr, blk1);
   if (t0 >= t1) return;
-  const bool rope_on = a.rope.table != nullptr;
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int tl = lane & 15, ch = lane >> 4;
@@ -815,37 +931,49 @@ __global__ __launch_bounds__(NT, (!NRM && (DH == 32 || sizeof(TIn) == 2)) ? 4 : 
   const int nh = W64 ? 2 : min(2, a.H - h0);   // 32-channel halves that hold data
   const int ngroups = (t1 - t0 + 15) >> 4;
 
-  const int RB = a.row_in * ES, RO = a.H * DH * EO;
+  const int RB = a.row_in * ES, RO_ = a.H * DH * EO;
   const __amdgpu_buffer_rsrc_t rq =
       make_rsrc(static_cast<const char*>(a.q) + ((size_t)b * a.N + t0) * RB, (uint32_t)(t1 - t0) * RB);
   const __amdgpu_buffer_rsrc_t ro =
-      make_rsrc(static_cast<char*>(a.out) + ((size_t)b * a.N + t0) * RO, (uint32_t)(t1 - t0) * RO);
+      make_rsrc(static_cast<char*>(a.out) + ((size_t)b * a.N + t0) * RO_, (uint32_t)(t1 - t0) * RO_);
   int qoff = (w * 16 + tl) * RB + (g * 64 + 8 * ch) * ES;
-  int ooff = (w * 16) * RO + g * 64 * EO;
+  int ooff = (w * 16) * RO_ + g * 64 * EO;
   // Output offsets of this lane.  fp32: channels 4ch..+3 of each 16-channel
-  // tile of token tl.  bf16 (after the exchange in run_group): a 16-byte piece
+  // tile of token tl.  bf16 (after the exchange in store_pk): a 16-byte piece
   // of channels co..co+7; with both halves present, tokens tl & 7 (first store)
   // and 8 + (tl & 7) (second store) of half tl >> 3, so each store instruction
   // writes whole 128-byte lines (8 tokens x the group's 64 channels).
   const int co = 4 * ch + ((ch & 1) ? 12 : 0);
-  const int o_one = tl * RO + (EO == 2 ? co : 4 * ch) * EO;
-  const int o_pair = (tl & 7) * RO + ((tl >> 3) * D + co) * EO;
+  const int o_one = tl * RO_ + (EO == 2 ? co : 4 * ch) * EO;
+  // The last group of an odd head count (head dim 32) holds one head: its
+  // second half is computed on whatever the loads return, and every store of
+  // that half is sent past the buffer range, where the hardware drops it (an
+  // offset of 2^31 + x, x < 2^31, exceeds any range a call plans).  One loop
+  // then serves every group.
+  const bool two = W64 || nh == 2;
+  constexpr int kDrop = (int)0x80000000u;
+  const int o_pair = (two || tl < 8) ? (tl & 7) * RO_ + ((tl >> 3) * D + co) * EO : kDrop;
+  const int o_half1 = two ? D * EO : kDrop;   // fp32 stores: offset of half 1
 
   // Prologue order: rotary window, then the prefix state, then the first Q
   // loads, so that no wait before the loop drains the Q prefetch.
-  const TabWindow win = stage_table(tab, a.rope, a.pos.t0, t0, t1, a.pos.mag_tpf);
+  TabWindow win{0, 0};
   RopeLane<P2> rl, rl1;                  // rl1: the second half at head dim 64
   TokPos tp;
-  if (rope_on) {
+  if constexpr (RO) {
+    if constexpr (FAST) win = stage_table16(tab16, a.rope, a.pos.t0, t0, t1, a.pos.mag_tpf);
+    else win = stage_table(tab, a.rope, a.pos.t0, t0, t1, a.pos.mag_tpf);
     rl.init(a.rope, win, ch);
     if constexpr (W64) rl1.init(a.rope, win, ch + 4);
     tp.init(t0 + w * 16 + tl, a.pos);
   }
 
-  // Key-sum slices zb[h] (channels 32h + 8ch .. +7 of the half's z) and Sbar
-  // tiles.  Head dim 32: tile 2h + hf = rows 16hf + tl, channels 8ch .. +7 of
-  // head h.  Head dim 64: tile 2et + kt = rows 16et + tl, channels 32kt + 8ch .. +7.
+  // Key-sum slices zb[h] (channels 32h + 8ch .. +7 of the half's z; packed
+  // path: their bf16 parts zh, zl) and Sbar tiles.  Head dim 32: tile 2h + hf
+  // = rows 16hf + tl, channels 8ch .. +7 of head h.  Head dim 64: tile
+  // 2et + kt = rows 16et + tl, channels 32kt + 8ch .. +7.
   float zb[2][8];
+  u32x4 zh[2], zl[2];
   u32x4 Ah[NA], Al[NA];
   float As[NA][8];
   auto take_tile = [&](int i, const float* srow) {
@@ -877,6 +1005,15 @@ __global__ __launch_bounds__(NT, (!NRM && (DH == 32 || sizeof(TIn) == 2)) ? 4 : 
     const f32x4 z1 = *reinterpret_cast<const f32x4*>(zp + 4);
 #pragma unroll
     for (int i = 0; i < 4; ++i) { zb[h][i] = z0[i]; zb[h][4 + i] = z1[i]; }
+    if constexpr (FAST) {
+      split8(zb[h], zh[h], zl[h]);
+      if constexpr (Z_LDS) {
+        if (w == 0 && tl == 0) {
+          lds_z[(2 * h) * 4 + ch] = zh[h];
+          lds_z[(2 * h + 1) * 4 + ch] = zl[h];
+        }
+      }
+    }
     if constexpr (W64) {
       // this h: output rows 32h .. 32h+31 = tiles et = 2h, 2h+1
 #pragma unroll
@@ -946,14 +1083,135 @@ __global__ __launch_bounds__(NT, (!NRM && (DH == 32 || sizeof(TIn) == 2)) ? 4 : 
       for (int hf = 0; hf < 2; ++hf) {
         const f32x4 ov = o[hf] * inv;
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ov), ro,
-                                               ooff + o_one + (h * D + 16 * hf) * EO, 0, LAVR_STORE_CPOL);
+                                               ooff + o_one + (h ? o_half1 : 0) + 16 * hf * EO, 0,
+                                               LAVR_STORE_CPOL);
       }
     }
   };
 
-  auto run_group = [&](const Buf& bf) {
+  // bf16 stores of a group, then the next group's offset.  Lanes tl and
+  // tl ^ 8 (DPP row rotate by 8 inside each 16-lane row) trade one piece: the
+  // low lane keeps half 0 of tokens tl and tl + 8, the high lane half 1 of
+  // tokens tl - 8 and tl.
+  auto store_pk = [&](const u32x4* pk) {
+    if constexpr (EO == 2) {
+      const bool lo = tl < 8;
+      uint32_t first[4], second[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t p0 = pk[0][i], p1 = pk[1][i];
+        const uint32_t snd = lo ? p1 : p0;
+        const uint32_t rcv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)snd, 0x128, 0xf, 0xf, false);
+        first[i] = lo ? p0 : rcv;
+        second[i] = lo ? rcv : p1;
+      }
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{first[0], first[1], first[2], first[3]}, ro,
+                                             ooff + o_pair, 0, LAVR_STORE_CPOL);
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{second[0], second[1], second[2], second[3]}, ro,
+                                             ooff + o_pair + 8 * RO_, 0, LAVR_STORE_CPOL);
+    }
+    ooff += 64 * RO_;
+  };
+
+  // One 16-token group, packed bf16 path.
+  auto run_fast = [&](const Buf& bf) {
+    u32x4 T[4], T1[4];
+    if constexpr (RO) {
+      rl.fetch16(tab16, tp, win, T);
+      if constexpr (W64) rl1.fetch16(tab16, tp, win, T1);
+      tp.advance(a.pos);
+    }
+    u32x4 pk[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+    if constexpr (W64) {
+      // one head: den over both halves, every output tile from both halves
+      u32x4 qp[2], bh[2], bl[2];
+      f32x4 dd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        qp[h] = relu_pk(bf.x[h].r[0]);
+        dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(zh[h]), as_bf16x8(qp[h]), dd, 0, 0, 0);
+        dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(zl[h]), as_bf16x8(qp[h]), dd, 0, 0, 0);
+        if constexpr (RO) {
+          float x[8];
+          rotate_pk(qp[h], h ? T1 : T, x);
+          split8p(x, bh[h], bl[h]);
+        } else {
+          bh[h] = qp[h];
+        }
+      }
+      const float inv = __builtin_amdgcn_rcpf(dd[0] + a.eps);
+      // The Sbar operands are read from LDS in every group: an opaque copy of
+      // the lane index keeps the compiler from hoisting them into registers.
+      int aslot = lane;
+      asm volatile("" : "+v"(aslot));
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        f32x4 o[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int et = 2 * h + hf;
+          f32x4 cc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            const u32x4 ah = lds_a[(2 * (et * 2 + kt)) * 64 + aslot];
+            const u32x4 al = lds_a[(2 * (et * 2 + kt) + 1) * 64 + aslot];
+            cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah), as_bf16x8(bh[kt]), cc, 0, 0, 0);
+            if constexpr (RO) cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah), as_bf16x8(bl[kt]), cc, 0, 0, 0);
+            cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al), as_bf16x8(bh[kt]), cc, 0, 0, 0);
+          }
+          o[hf] = cc;
+        }
+        emit(h, o, inv, pk);
+      }
+    } else {
+      // Sbar and zbar operands from LDS in every group: opaque copies of the
+      // lane index and row keep the compiler from hoisting them into registers.
+      int zrow = ch, aslot = lane;
+      asm volatile("" : "+v"(zrow), "+v"(aslot));
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const u32x4 qp = relu_pk(bf.x[h].r[0]);
+        const u32x4 zhh = lds_z[(2 * h) * 4 + zrow], zlh = lds_z[(2 * h + 1) * 4 + zrow];
+        f32x4 dd = {0.f, 0.f, 0.f, 0.f};
+        dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(zhh), as_bf16x8(qp), dd, 0, 0, 0);
+        dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(zlh), as_bf16x8(qp), dd, 0, 0, 0);
+        f32x4 o[2];
+        if constexpr (RO) {
+          float x[8];
+          rotate_pk(qp, T, x);
+          u32x4 bh, bl;
+          split8p(x, bh, bl);
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const u32x4 ah = lds_a[(2 * (2 * h + hf)) * 64 + aslot];
+            const u32x4 al = lds_a[(2 * (2 * h + hf) + 1) * 64 + aslot];
+            f32x4 cc = {0.f, 0.f, 0.f, 0.f};
+            cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah), as_bf16x8(bh), cc, 0, 0, 0);
+            cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah), as_bf16x8(bl), cc, 0, 0, 0);
+            cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al), as_bf16x8(bh), cc, 0, 0, 0);
+            o[hf] = cc;
+          }
+        } else {
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const u32x4 ah = lds_a[(2 * (2 * h + hf)) * 64 + aslot];
+            const u32x4 al = lds_a[(2 * (2 * h + hf) + 1) * 64 + aslot];
+            f32x4 cc = {0.f, 0.f, 0.f, 0.f};
+            cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah), as_bf16x8(qp), cc, 0, 0, 0);
+            cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al), as_bf16x8(qp), cc, 0, 0, 0);
+            o[hf] = cc;
+          }
+        }
+        emit(h, o, __builtin_amdgcn_rcpf(dd[0] + a.eps), pk);
+      }
+    }
+    store_pk(pk);
+  };
+
+  // One 16-token group, fp32 path (fp32 or normalised inputs).
+  auto run_wide = [&](const Buf& bf) {
     float2 cs[4], cs1[4];
-    if (rope_on) {
+    if constexpr (RO) {
       rl.fetch(tab, tp, win, cs);
       if constexpr (W64) rl1.fetch(tab, tp, win, cs1);
       tp.advance(a.pos);
@@ -962,8 +1220,6 @@ __global__ __launch_bounds__(NT, (!NRM && (DH == 32 || sizeof(TIn) == 2)) ? 4 : 
     if constexpr (W64) {
       // one head: den over both halves, every output tile from both halves
       float den = 0.f;
-      // The Sbar operands are read from LDS in every group: an opaque copy of
-      // the lane index keeps the compiler from hoisting them into registers.
       int aslot = lane;
       if constexpr (A_LDS) asm volatile("" : "+v"(aslot));
       u32x4 bh[2], bl[2];
@@ -974,7 +1230,7 @@ __global__ __launch_bounds__(NT, (!NRM && (DH == 32 || sizeof(TIn) == 2)) ? 4 : 
         widen_q(bf, h, x);
 #pragma unroll
         for (int i = 0; i < 8; ++i) den += zb[h][i] * x[i];
-        if (rope_on) rotate8(x, h ? cs1 : cs);
+        if constexpr (RO) rotate8(x, h ? cs1 : cs);
         if constexpr (BF) {
           split8(x, bh[h], bl[h]);
         } else {
@@ -1012,13 +1268,12 @@ __global__ __launch_bounds__(NT, (!NRM && (DH == 32 || sizeof(TIn) == 2)) ? 4 : 
     } else {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        if (h >= nh) break;
         float x[8];
         widen_q(bf, h, x);
         float den = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) den += zb[h][i] * x[i];
-        if (rope_on) rotate8(x, cs);
+        if constexpr (RO) rotate8(x, cs);
         f32x4 o[2];
         if constexpr (BF) {
           u32x4 bh, bl;
@@ -1044,30 +1299,12 @@ __global__ __launch_bounds__(NT, (!NRM && (DH == 32 || sizeof(TIn) == 2)) ? 4 : 
         emit(h, o, __builtin_amdgcn_rcpf(den + a.eps), pk);
       }
     }
-    if constexpr (EO == 2) {
-      if (nh == 2) {
-        // Lanes tl and tl ^ 8 (DPP row rotate by 8 inside each 16-lane row) trade
-        // one piece: the low lane keeps half 0 of tokens tl and tl + 8, the high
-        // lane half 1 of tokens tl - 8 and tl.
-        const bool lo = tl < 8;
-        uint32_t first[4], second[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t p0 = pk[0][i], p1 = pk[1][i];
-          const uint32_t snd = lo ? p1 : p0;
-          const uint32_t rcv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)snd, 0x128, 0xf, 0xf, false);
-          first[i] = lo ? p0 : rcv;
-          second[i] = lo ? rcv : p1;
-        }
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{first[0], first[1], first[2], first[3]}, ro,
-                                               ooff + o_pair, 0, LAVR_STORE_CPOL);
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{second[0], second[1], second[2], second[3]}, ro,
-                                               ooff + o_pair + 8 * RO, 0, LAVR_STORE_CPOL);
-      } else {
-        __builtin_amdgcn_raw_buffer_store_b128(pk[0], ro, ooff + o_one, 0, LAVR_STORE_CPOL);
-      }
-    }
-    ooff += 64 * RO;
+    store_pk(pk);
+  };
+
+  auto run_group = [&](const Buf& bf) {
+    if constexpr (FAST) run_fast(bf);
+    else run_wide(bf);
   };
 
   // Whole rounds of RPF groups; groups past the tile read zeros and their
@@ -1984,8 +2221,9 @@ __global__ __launch_bounds__(NT) void k_qk_rms(RmsArgs a) {
 
 template <typename TIn, typename TOut, int DH, bool NRM>
 hipError_t launch_readout(const ReadArgs& ra, bool p2, dim3 grid, int lds, hipStream_t s) {
-  if (p2) hipLaunchKernelGGL((k_readout<TIn, TOut, true, DH, NRM>), grid, dim3(NT), lds, s, ra);
-  else hipLaunchKernelGGL((k_readout<TIn, TOut, false, DH, NRM>), grid, dim3(NT), lds, s, ra);
+  if (ra.rope.table == nullptr) hipLaunchKernelGGL((k_readout<TIn, TOut, true, DH, NRM, false>), grid, dim3(NT), lds, s, ra);
+  else if (p2) hipLaunchKernelGGL((k_readout<TIn, TOut, true, DH, NRM, true>), grid, dim3(NT), lds, s, ra);
+  else hipLaunchKernelGGL((k_readout<TIn, TOut, false, DH, NRM, true>), grid, dim3(NT), lds, s, ra);
   return hipGetLastError();
 }
 
@@ -2162,8 +2400,13 @@ int launch_forward(const Plan& p, const void* q, const void* k, const void* v, v
   ra.pos = pa_pos;
   ra.rope = p.rope;
   const dim3 gr((unsigned)(p.hg * p.nb * p.rpb), (unsigned)p.B);
-  e = p.D == 64 ? launch_readouts<64>(ra, in_bf16, out_bf16, p2, gr, p.lds_read + (in_bf16 ? kReadAlBytes : 0), s)
-                : launch_readouts<32>(ra, in_bf16, out_bf16, p2, gr, p.lds_read, s);
+  // bf16 inputs without a q norm stage the rotary window as rope_words (16
+  // bytes per pair instead of 8)
+  const bool packed = in_bf16 && !nq;
+  const int lds_tab = packed ? p.lds_read16 : p.lds_read;
+  e = p.D == 64 ? launch_readouts<64>(ra, in_bf16, out_bf16, p2, gr, lds_tab + (in_bf16 ? kReadAlBytes : 0), s)
+                : launch_readouts<32>(ra, in_bf16, out_bf16, p2, gr,
+                                      lds_tab + (packed ? kReadAlBytes / 2 + kReadZBytes : 0), s);
   if (e == hipSuccess) e = mark(3);
   return (int)e;
 }
