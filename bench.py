@@ -205,8 +205,8 @@ def main():
     dt = q.dtype
     rope = lavr.RopeTable(cfg["rope"]["split"], cfg["grid"], cfg["frames"], cfg["rope"]["base"], dev)
     out = torch.empty_like(q)
-    need = lavr.workspace_bytes(B, H, cfg["frames"], tpf, bf, head_dim=d)
-    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    need = lavr.workspace_bytes(B, H, cfg["frames"], tpf, bf, head_dim=d, rope=rope)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     code = lavr._dtype_code(dt)
     ptrs = [ctypes.c_void_p(x.data_ptr()) for x in (q, k, v, out)]
@@ -349,7 +349,7 @@ def bench_prologue(lavr, torch, dev, cfg, q, k, v, rope, steps):
     qkv = torch.stack([t.reshape(B, N, C) for t in (q, k, v)], dim=2).contiguous()
     gq, gk = (torch.from_numpy(W.draw_norm_weight(cfg, w)).to(dev) for w in W.NORM_WEIGHTS)
     out = torch.empty((B, N, H, d), dtype=q.dtype, device=dev)
-    ws = torch.empty(lavr.qkv_workspace_bytes(B, H, cfg["frames"], tpf, bf, d), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(lavr.qkv_workspace_bytes(B, H, cfg["frames"], tpf, bf, d, rope=rope), dtype=torch.uint8, device=dev)
 
     def fused():
         lavr.block_causal_forward_qkv(qkv, H, bf, tpf, rope, q_gamma=gq, k_gamma=gk, norm_eps=norm_eps,
@@ -398,8 +398,8 @@ def bench_backward(lavr, torch, dev, cfg, q, k, v, rope, steps):
     gen.manual_seed(7)
     g = torch.randn(q.shape, generator=gen, device=dev, dtype=torch.float32).to(q.dtype)
     grads = [torch.empty_like(q) for _ in range(3)]
-    need = lavr.backward_workspace_bytes(B, H, cfg["frames"], tpf, bf, head_dim=d)
-    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    need = lavr.backward_workspace_bytes(B, H, cfg["frames"], tpf, bf, head_dim=d, rope=rope)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
     code = lavr._dtype_code(q.dtype)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     ptrs = [ctypes.c_void_p(x.data_ptr()) for x in (q, k, v, g, *grads)]
@@ -471,8 +471,8 @@ def bench_streaming(lavr, torch, dev, reps):
     del q, k, v
     outs = [torch.empty_like(blocks[0][0]) for _ in range(nblk)]
     rope = lavr.RopeTable(cfg["rope"]["split"], cfg["grid"], cfg["frames"], cfg["rope"]["base"], dev)
-    need = lavr.workspace_bytes(cfg["B"], cfg["H"], bf, tpf, bf)
-    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    need = lavr.workspace_bytes(cfg["B"], cfg["H"], bf, tpf, bf, rope=rope)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
     times = []
     for rep in range(reps + 1):
         st = lavr.StreamState(cfg["B"], cfg["H"], device=dev)

@@ -115,11 +115,15 @@ int rope_table_build(la_rope* out, float* table_dev, size_t bytes, int head_dim,
                      int d_t, int d_h, int d_w, int max_frames, int grid_h, int grid_w,
                      double base, void* stream);
 
-/* Workspace bytes needed by la_block_causal_forward for this shape and block
- * schedule (for la_stream_block pass frames = block_frames and
- * first_block_frames = 0).  0 for invalid sizes. */
+/* Workspace bytes needed by la_block_causal_forward for this shape, block
+ * schedule and rotary description (for la_stream_block pass frames =
+ * block_frames and first_block_frames = 0).  rope is the description the call
+ * will take (NULL or a NULL table = RoPE off): a block's work is split so that
+ * each piece's rotary window fits on chip, and with short frames that can need
+ * more pieces, and so more workspace, than without RoPE.  Only rope's fields
+ * are read, not its table.  0 for invalid sizes or descriptions. */
 size_t la_workspace_bytes(int B, int H, int head_dim, int frames, int tokens_per_frame,
-                          int block_frames, int first_block_frames);
+                          int block_frames, int first_block_frames, const la_rope* rope);
 
 /* One-shot block-causal forward over `frames` frames, starting from an empty
  * cache.  Blocks: the first holds first_block_frames frames (0 means
@@ -155,10 +159,12 @@ int la_block_causal_forward_timed(const void* q, const void* k, const void* v, v
                                   float eps, void* ws, size_t ws_bytes, void* stream,
                                   void* const* events);
 
-/* Workspace bytes needed by la_block_causal_backward for this shape (0 for
+/* Workspace bytes needed by la_block_causal_backward (and by a forward whose
+ * workspace la_block_causal_backward_from_forward will reuse) for this shape,
+ * schedule and rotary description (rope as for la_workspace_bytes; 0 for
  * invalid sizes). */
 size_t la_backward_workspace_bytes(int B, int H, int head_dim, int frames, int tokens_per_frame,
-                                   int block_frames, int first_block_frames);
+                                   int block_frames, int first_block_frames, const la_rope* rope);
 
 /* Gradients of sum(dout * out) with respect to q, k and v, where out is what
  * la_block_causal_forward returns for the same arguments.  The pages state the
@@ -184,8 +190,14 @@ int la_block_causal_backward(const void* q, const void* k, const void* v, const 
  * la_block_causal_forward call with the same q, k, v and arguments (out dtype
  * aside) wrote, left untouched since; the block prefixes it holds are used as
  * they are instead of being formed again from k and v.  The result is the one
- * la_block_causal_backward gives, bit for bit.  Passing any other workspace
- * gives wrong gradients; the library cannot detect it. */
+ * la_block_causal_backward gives, bit for bit.  The forward stores a 128-bit
+ * fingerprint of what its prefixes were formed from (shape, block schedule,
+ * rotary table and offset, the k and v pointers, the input dtype and any k
+ * norm) in the workspace; if the fingerprint does not match this call's
+ * arguments (another shape or schedule, another k or v, a fused-input forward,
+ * a workspace no forward wrote), the call still returns LA_OK but fills dq, dk
+ * and dv with NaN.  Contents of k or v changed in place since the forward are
+ * not detected. */
 int la_block_causal_backward_from_forward(const void* q, const void* k, const void* v,
                                           const void* dout, void* dq, void* dk, void* dv,
                                           la_dtype in_dt, la_dtype grad_dt, int B, int H,
@@ -231,9 +243,10 @@ int la_stream_block(la_state* st, const void* q, const void* k, const void* v, v
  * values (8 bytes per token in the workspace). */
 
 /* Workspace bytes of la_block_causal_forward_qkv (for la_stream_block_qkv pass
- * frames = block_frames and first_block_frames = 0).  0 for invalid sizes. */
+ * frames = block_frames and first_block_frames = 0; rope as for
+ * la_workspace_bytes).  0 for invalid sizes. */
 size_t la_qkv_workspace_bytes(int B, int H, int head_dim, int frames, int tokens_per_frame,
-                              int block_frames, int first_block_frames);
+                              int block_frames, int first_block_frames, const la_rope* rope);
 
 /* la_block_causal_forward from the fused input qkv (B, N, 3, H * head_dim) of
  * dtype in_dt (16-byte aligned).  q_gamma and k_gamma are device arrays of

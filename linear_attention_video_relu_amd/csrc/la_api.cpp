@@ -182,8 +182,11 @@ int make_plan(Plan* p, int B, int H, int head_dim, int frames, int tpf, int bloc
   const size_t rec = (size_t)p->rec * sizeof(float);
   const size_t part = (size_t)B * H * p->nb * p->cpb * rec;
   const size_t prefix = (size_t)B * H * p->nb * rec;
-  p->ws_part = 0;
-  p->ws_prefix = align256(part);
+  // Header: the fingerprint of the block prefixes (what a backward reusing
+  // them checks), then the chunk records and the prefixes.
+  p->ws_fp = 0;
+  p->ws_part = lavr::kWsHeader;
+  p->ws_prefix = p->ws_part + align256(part);
   p->ws_total = p->ws_prefix + align256(prefix);
   p->ws_suffix = p->ws_total;
   p->ws_total_bw = p->ws_suffix + align256(prefix);
@@ -373,10 +376,10 @@ int rope_table_build(la_rope* out, float* table_dev, size_t bytes, int head_dim,
 }
 
 size_t la_workspace_bytes(int B, int H, int head_dim, int frames, int tokens_per_frame,
-                          int block_frames, int first_block_frames) {
+                          int block_frames, int first_block_frames, const la_rope* rope) {
   Plan p;
   if (make_plan(&p, B, H, head_dim, frames, tokens_per_frame, block_frames, first_block_frames,
-                nullptr, 0, LA_BF16) != LA_OK)
+                rope, 0, LA_BF16) != LA_OK)
     return 0;
   return p.ws_total;
 }
@@ -425,10 +428,10 @@ int la_block_causal_forward_timed(const void* q, const void* k, const void* v, v
 }
 
 size_t la_backward_workspace_bytes(int B, int H, int head_dim, int frames, int tokens_per_frame,
-                                   int block_frames, int first_block_frames) {
+                                   int block_frames, int first_block_frames, const la_rope* rope) {
   Plan p;
   if (make_plan(&p, B, H, head_dim, frames, tokens_per_frame, block_frames, first_block_frames,
-                nullptr, 0, LA_BF16) != LA_OK)
+                rope, 0, LA_BF16) != LA_OK)
     return 0;
   return p.ws_total_bw;
 }
@@ -456,10 +459,10 @@ int la_block_causal_backward_from_forward(const void* q, const void* k, const vo
 }
 
 size_t la_qkv_workspace_bytes(int B, int H, int head_dim, int frames, int tokens_per_frame,
-                              int block_frames, int first_block_frames) {
+                              int block_frames, int first_block_frames, const la_rope* rope) {
   Plan p;
   if (make_plan(&p, B, H, head_dim, frames, tokens_per_frame, block_frames, first_block_frames,
-                nullptr, 0, LA_BF16, 3) != LA_OK)
+                rope, 0, LA_BF16, 3) != LA_OK)
     return 0;
   return p.ws_total_qkv;
 }

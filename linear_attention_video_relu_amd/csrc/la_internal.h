@@ -13,6 +13,10 @@ namespace lavr {
 constexpr bool head_dim_built(int d) { return d == 32 || d == 64; }
 constexpr int rec_floats(int d) { return d * d + d; }   // floats of one (S, z) record
 
+// Workspace header: 256 bytes holding the 16-byte fingerprint of the block
+// prefixes; the data follows.
+constexpr size_t kWsHeader = 256;
+
 // Block-state LDS tiles: 1 = one set (two barriers per step), 2 = double
 // buffered (one barrier per step).
 #ifndef LAVR_STATE_DB
@@ -51,6 +55,7 @@ struct Plan {
   int tab_state;        // of which the rotary window of a chunk
   int lds_read;         // dynamic LDS bytes of the readout kernel's rotary window ((cos, sin) pairs)
   int lds_read16;       // the same window as rope_words (16 bytes per pair)
+  size_t ws_fp;         // byte offset of the 16-byte fingerprint of the block prefixes (in the header)
   size_t ws_part;       // byte offset of the per-chunk partial states
   size_t ws_prefix;     // byte offset of the per-block prefix states
   size_t ws_suffix;     // byte offset of the per-block suffix sums (backward only)

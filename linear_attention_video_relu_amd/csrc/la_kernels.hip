@@ -105,6 +105,10 @@ struct StateArgs {
   int row_in;                // elements from one token row of k (and v) to the next
   PosArgs pos;
   RopeDev rope;
+  // Fingerprint of what the block prefixes are formed from, stored in the
+  // workspace header for the backward that reuses them.
+  uint64_t* fp_dst;
+  uint64_t fp0, fp1;
 };
 
 struct PrefixArgs {
@@ -753,6 +757,10 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? ((P2 && DH == 32 && !NRM && 
                           : part_rec((size_t)(b * a.H + h0 + hd), ci, (size_t)gridDim.y * a.H) * RECN + D * D + ch;
     a.part[zi] = s;
   }
+  if (a.fp_dst != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && t == 0) {
+    a.fp_dst[0] = a.fp0;
+    a.fp_dst[1] = a.fp1;
+  }
 }
 
 // -------------------------------------------------------------- k_prefix
@@ -1092,18 +1100,17 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH ==
   // bf16 stores of a group, then the next group's offset.  Lanes tl and
   // tl ^ 8 (DPP row rotate by 8 inside each 16-lane row) trade one piece: the
   // low lane keeps half 0 of tokens tl and tl + 8, the high lane half 1 of
-  // tokens tl - 8 and tl.
+  // tokens tl - 8 and tl.  The bank masks limit each rotated move to the lanes
+  // that take the partner's piece (banks 2-3 = lanes 8-15 of a row, banks 0-1
+  // = lanes 0-7); the other lanes keep their own.
   auto store_pk = [&](const u32x4* pk) {
     if constexpr (EO == 2) {
-      const bool lo = tl < 8;
       uint32_t first[4], second[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t p0 = pk[0][i], p1 = pk[1][i];
-        const uint32_t snd = lo ? p1 : p0;
-        const uint32_t rcv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)snd, 0x128, 0xf, 0xf, false);
-        first[i] = lo ? p0 : rcv;
-        second[i] = lo ? rcv : p1;
+        first[i] = (uint32_t)__builtin_amdgcn_update_dpp((int)p0, (int)p1, 0x128, 0xf, 0xc, false);
+        second[i] = (uint32_t)__builtin_amdgcn_update_dpp((int)p1, (int)p0, 0x128, 0xf, 0x3, false);
       }
       __builtin_amdgcn_raw_buffer_store_b128(u32x4{first[0], first[1], first[2], first[3]}, ro,
                                              ooff + o_pair, 0, LAVR_STORE_CPOL);
@@ -2335,6 +2342,35 @@ hipError_t launch_prefix(const PrefixArgs& pa, const Plan& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// 128-bit fingerprint (two FNV-1a hashes) of everything the block prefixes of
+// a call depend on: shape, block schedule, rotary table and offset, the k and v
+// tensors and their normalisation.
+struct Fnv {
+  uint64_t h;
+  void add(const void* x, size_t n) {
+    const unsigned char* c = static_cast<const unsigned char*>(x);
+    for (size_t i = 0; i < n; ++i) h = (h ^ c[i]) * 0x100000001b3ULL;
+  }
+  template <typename T> void val(T v) { add(&v, sizeof(v)); }
+};
+
+void prefix_fingerprint(const Plan& p, const void* k, const void* v, int in_bf16, const Prologue* pro,
+                        uint64_t* f0, uint64_t* f1) {
+  Fnv a{0xcbf29ce484222325ULL}, b{0x84222325cbf29ce4ULL};
+  for (Fnv* f : {&a, &b}) {
+    f->val(p.B); f->val(p.H); f->val(p.D); f->val(p.N); f->val(p.row_in); f->val(p.tpf); f->val(p.gw_div);
+    f->val(p.L); f->val(p.L0); f->val(p.nb); f->val(p.cpb); f->val(p.Tc); f->val(p.t0);
+    f->val(p.rope.table); f->val(p.rope.pt); f->val(p.rope.ph); f->val(p.rope.pw);
+    f->val(p.rope.max_frames); f->val(p.rope.gh); f->val(p.rope.gw);
+    f->val(k); f->val(v); f->val(in_bf16);
+    const float* kg = pro != nullptr ? pro->k_gamma : nullptr;
+    f->val(kg);
+    f->val(kg != nullptr ? pro->norm_eps : 0.f);
+  }
+  *f0 = a.h;
+  *f1 = b.h;
+}
+
 int launch_forward(const Plan& p, const void* q, const void* k, const void* v, void* out,
                    int in_bf16, int out_bf16, float eps, void* ws,
                    const float* S_init, const float* z_init, float* S_save, float* z_save,
@@ -2376,6 +2412,8 @@ int launch_forward(const Plan& p, const void* q, const void* k, const void* v, v
   sa.row_in = p.row_in;
   sa.pos = pa_pos;
   sa.rope = p.rope;
+  sa.fp_dst = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + p.ws_fp);
+  prefix_fingerprint(p, k, v, in_bf16, nk ? pro : nullptr, &sa.fp0, &sa.fp1);
   const dim3 gs((unsigned)(p.hg * p.nb * p.cpb), (unsigned)p.B);
   const bool p2 = ((p.rope.pt | p.rope.ph | p.rope.pw) & 1) == 0;
   e = p.D == 64 ? launch_state<64>(sa, in_bf16, p2, gs, p.lds_state, s)
@@ -2409,6 +2447,22 @@ int launch_forward(const Plan& p, const void* q, const void* k, const void* v, v
                                       lds_tab + (packed ? kReadAlBytes / 2 + kReadZBytes : 0), s);
   if (e == hipSuccess) e = mark(3);
   return (int)e;
+}
+
+// Guard of the training-path backward: the block prefixes it reused are the
+// ones a matching forward formed only if the workspace's fingerprint equals
+// the one of this call's arguments; otherwise dq, dk and dv (n16 16-byte
+// pieces each) are overwritten with NaN, so a foreign workspace cannot give
+// plausible wrong gradients.  On a match every thread leaves at once.
+__global__ __launch_bounds__(256) void k_fp_guard(const uint64_t* fp, uint64_t f0, uint64_t f1, u32x4* dq,
+                                                  u32x4* dk, u32x4* dv, size_t n16, uint32_t nan_word) {
+  if (fp[0] == f0 && fp[1] == f1) return;
+  const u32x4 nn = {nan_word, nan_word, nan_word, nan_word};
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x) {
+    dq[i] = nn;
+    dk[i] = nn;
+    dv[i] = nn;
+  }
 }
 
 template <int DH>
@@ -2448,6 +2502,8 @@ int launch_backward(const Plan& p, const void* q, const void* k, const void* v, 
   sa.H = p.H; sa.N = p.N; sa.L = p.L; sa.L0 = p.L0; sa.nb = p.nb; sa.cpb = p.cpb; sa.Tc = p.Tc; sa.hg = p.hg;
   sa.pos = pa_pos;
   sa.rope = p.rope;
+  sa.fp_dst = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + p.ws_fp);
+  prefix_fingerprint(p, k, v, in_bf16, nullptr, &sa.fp0, &sa.fp1);
   const dim3 gs((unsigned)(p.hg * p.nb * p.cpb), (unsigned)p.B);
   PrefixArgs pa;
   pa.part = part; pa.prefix = prefix; pa.S_init = nullptr; pa.z_init = nullptr;
@@ -2456,8 +2512,7 @@ int launch_backward(const Plan& p, const void* q, const void* k, const void* v, 
   if (!have_prefix) {
     e = p.D == 64 ? launch_state<64>(sa, in_bf16, p2, gs, p.lds_state, s)
                   : launch_state<32>(sa, in_bf16, p2, gs, p.lds_state, s);
-    if (e != hipSuccess) return (int)e;
-    e = launch_prefix(pa, p, s);
+    if (e == hipSuccess) e = launch_prefix(pa, p, s);
     if (e != hipSuccess) return (int)e;
   }
 
@@ -2488,8 +2543,20 @@ int launch_backward(const Plan& p, const void* q, const void* k, const void* v, 
   ka.rope = p.rope;
   const dim3 gr((unsigned)(p.hg * p.nb * p.rpb), (unsigned)p.B);
   const int lds_kv = lds_ops + p.lds_read;
-  return (int)(p.D == 64 ? launch_bw_kv<64>(ka, in_bf16, grad_bf16, p2, gr, lds_kv, s)
-                         : launch_bw_kv<32>(ka, in_bf16, grad_bf16, p2, gr, lds_kv, s));
+  e = p.D == 64 ? launch_bw_kv<64>(ka, in_bf16, grad_bf16, p2, gr, lds_kv, s)
+                : launch_bw_kv<32>(ka, in_bf16, grad_bf16, p2, gr, lds_kv, s);
+  if (e != hipSuccess || !have_prefix) return (int)e;
+
+  // reused prefixes: check that a matching forward formed them
+  uint64_t f0, f1;
+  prefix_fingerprint(p, k, v, in_bf16, nullptr, &f0, &f1);
+  const size_t n16 = (size_t)p.B * p.N * p.H * p.D * (grad_bf16 ? 2 : 4) / 16;
+  const unsigned blocks = (unsigned)std::min<size_t>((n16 + 255) / 256, 1024);
+  hipLaunchKernelGGL(k_fp_guard, dim3(blocks), dim3(256), 0, s,
+                     reinterpret_cast<const uint64_t*>(static_cast<char*>(ws) + p.ws_fp), f0, f1,
+                     static_cast<u32x4*>(dq), static_cast<u32x4*>(dk), static_cast<u32x4*>(dv), n16,
+                     grad_bf16 ? 0x7fc07fc0u : 0x7fc00000u);
+  return (int)hipGetLastError();
 }
 
 }  // namespace lavr

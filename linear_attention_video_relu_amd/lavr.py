@@ -48,7 +48,7 @@ def _load():
         "rope_table_bytes": (c_size, [c_int] * 6),
         "rope_table_build": (c_int, [ctypes.POINTER(LaRope), c_vp, c_size, c_int, c_int, c_int,
                                      c_int, c_int, c_int, c_int, c_double, c_vp]),
-        "la_workspace_bytes": (c_size, [c_int] * 7),
+        "la_workspace_bytes": (c_size, [c_int] * 7 + [ctypes.POINTER(LaRope)]),
         "la_block_causal_forward": (c_int, [c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int,
                                             c_int, c_int, c_int, c_int, c_int,
                                             ctypes.POINTER(LaRope), c_float, c_vp, c_size, c_vp]),
@@ -56,12 +56,12 @@ def _load():
                                                   c_int, c_int, c_int, c_int, c_int, c_int,
                                                   ctypes.POINTER(LaRope), c_float, c_vp, c_size,
                                                   c_vp, ctypes.POINTER(c_vp)]),
-        "la_backward_workspace_bytes": (c_size, [c_int] * 7),
+        "la_backward_workspace_bytes": (c_size, [c_int] * 7 + [ctypes.POINTER(LaRope)]),
         "la_block_causal_backward": (c_int, [c_vp] * 7 + [c_int] * 9 + [ctypes.POINTER(LaRope), c_float,
                                                                          c_vp, c_size, c_vp]),
         "la_block_causal_backward_from_forward": (c_int, [c_vp] * 7 + [c_int] * 9 +
                                                   [ctypes.POINTER(LaRope), c_float, c_vp, c_size, c_vp]),
-        "la_qkv_workspace_bytes": (c_size, [c_int] * 7),
+        "la_qkv_workspace_bytes": (c_size, [c_int] * 7 + [ctypes.POINTER(LaRope)]),
         "la_block_causal_forward_qkv": (c_int, [c_vp, c_vp, c_int, c_int] + [c_int] * 7 +
                                         [ctypes.POINTER(LaRope), c_float, c_vp, c_vp, c_float, c_vp,
                                          c_size, c_vp]),
@@ -157,13 +157,20 @@ def _rope_ptr(rope):
 # ------------------------------------------------------------------ one-shot
 
 def workspace_bytes(B, H, frames, tokens_per_frame, block_frames, head_dim=HEAD_DIM,
-                    first_block_frames=0):
-    """Workspace bytes of a forward call (first_block_frames 0 = uniform blocks)."""
+                    first_block_frames=0, rope=None):
+    """Workspace bytes of a forward call (first_block_frames 0 = uniform blocks;
+    rope: the RopeTable the call will use, or None)."""
     n = lib.la_workspace_bytes(int(B), int(H), int(head_dim), int(frames), int(tokens_per_frame),
-                               int(block_frames), int(first_block_frames or 0))
+                               int(block_frames), int(first_block_frames or 0), _rope_ptr(rope))
     if n == 0:
         raise ValueError("invalid shape for la_workspace_bytes")
     return n
+
+
+def new_workspace(nbytes, device):
+    """A workspace buffer of nbytes for the library's calls (no initial
+    contents are needed)."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
 _ws_cache = {}
@@ -173,7 +180,7 @@ def _workspace(device, nbytes):
     key = (device, torch.cuda.current_stream(device).cuda_stream)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        buf = new_workspace(nbytes, device)
         _ws_cache[key] = buf
     return buf
 
@@ -207,7 +214,7 @@ def block_causal_forward(q, k, v, block_frames, tokens_per_frame, rope=None, eps
     elif out.shape != q.shape or out.dtype != out_dtype or not out.is_contiguous() or out.device != q.device:
         raise ValueError("out must be a contiguous tensor of q's shape and out_dtype on q's device")
     f0 = int(first_block_frames or 0)
-    need = lib.la_workspace_bytes(B, H, d, frames, int(tokens_per_frame), int(block_frames), f0)
+    need = lib.la_workspace_bytes(B, H, d, frames, int(tokens_per_frame), int(block_frames), f0, _rope_ptr(rope))
     ws = _workspace(q.device, need) if workspace is None else workspace
     _check(lib.la_block_causal_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(q.dtype),
                                        _dtype_code(out_dtype), B, H, d, frames,
@@ -220,9 +227,9 @@ def block_causal_forward(q, k, v, block_frames, tokens_per_frame, rope=None, eps
 # ------------------------------------------------------------ fused prologue
 
 def qkv_workspace_bytes(B, H, frames, tokens_per_frame, block_frames, head_dim=HEAD_DIM,
-                        first_block_frames=0):
+                        first_block_frames=0, rope=None):
     n = lib.la_qkv_workspace_bytes(int(B), int(H), int(head_dim), int(frames), int(tokens_per_frame),
-                                   int(block_frames), int(first_block_frames or 0))
+                                   int(block_frames), int(first_block_frames or 0), _rope_ptr(rope))
     if n == 0:
         raise ValueError("invalid shape for la_qkv_workspace_bytes")
     return n
@@ -267,7 +274,8 @@ def block_causal_forward_qkv(qkv, heads, block_frames, tokens_per_frame, rope=No
           or out.device != qkv.device):
         raise ValueError("out must be a contiguous (B, N, heads, head_dim) tensor of out_dtype")
     f0 = int(first_block_frames or 0)
-    need = lib.la_qkv_workspace_bytes(B, heads, d, frames, int(tokens_per_frame), int(block_frames), f0)
+    need = lib.la_qkv_workspace_bytes(B, heads, d, frames, int(tokens_per_frame), int(block_frames), f0,
+                                      _rope_ptr(rope))
     ws = _workspace(qkv.device, need) if workspace is None else workspace
     _check(lib.la_block_causal_forward_qkv(_ptr(qkv), _ptr(out), _dtype_code(qkv.dtype),
                                            _dtype_code(out_dtype), B, int(heads), d, frames,
@@ -347,10 +355,10 @@ class ConvState:
 # ------------------------------------------------------------------ backward
 
 def backward_workspace_bytes(B, H, frames, tokens_per_frame, block_frames, head_dim=HEAD_DIM,
-                             first_block_frames=0):
+                             first_block_frames=0, rope=None):
     n = lib.la_backward_workspace_bytes(int(B), int(H), int(head_dim), int(frames),
                                         int(tokens_per_frame), int(block_frames),
-                                        int(first_block_frames or 0))
+                                        int(first_block_frames or 0), _rope_ptr(rope))
     if n == 0:
         raise ValueError("invalid shape for la_backward_workspace_bytes")
     return n
@@ -372,7 +380,8 @@ def block_causal_backward(q, k, v, dout, block_frames, tokens_per_frame, rope=No
     grad_dtype = q.dtype if grad_dtype is None else grad_dtype
     dq, dk, dv = (torch.empty((B, N, H, d), dtype=grad_dtype, device=q.device) for _ in range(3))
     f0 = int(first_block_frames or 0)
-    need = lib.la_backward_workspace_bytes(B, H, d, frames, int(tokens_per_frame), int(block_frames), f0)
+    need = lib.la_backward_workspace_bytes(B, H, d, frames, int(tokens_per_frame), int(block_frames), f0,
+                                           _rope_ptr(rope))
     if need == 0:
         raise ValueError(f"backward not built for head dim {d} or invalid shape")
     if from_forward and workspace is None:
@@ -393,14 +402,14 @@ class BlockCausalAttention(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, q, k, v, block_frames, tokens_per_frame, rope=None, eps=EPS_DEFAULT,
-                first_block_frames=None):
+                first_block_frames=None, out_dtype=None):
         q, k, v = (t.contiguous() for t in (q, k, v))
         B, N, H, d = q.shape
         need = backward_workspace_bytes(B, H, N // tokens_per_frame, tokens_per_frame, block_frames,
-                                        head_dim=d, first_block_frames=first_block_frames)
-        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+                                        head_dim=d, first_block_frames=first_block_frames, rope=rope)
+        ws = new_workspace(need, q.device)
         out = block_causal_forward(q, k, v, block_frames, tokens_per_frame, rope, eps, workspace=ws,
-                                   first_block_frames=first_block_frames)
+                                   first_block_frames=first_block_frames, out_dtype=out_dtype)
         ctx.save_for_backward(q, k, v, ws)
         ctx.args = (block_frames, tokens_per_frame, rope, eps, first_block_frames)
         return out
@@ -409,16 +418,27 @@ class BlockCausalAttention(torch.autograd.Function):
     def backward(ctx, dout):
         q, k, v, ws = ctx.saved_tensors
         bf, tpf, rope, eps, f0 = ctx.args
-        dq, dk, dv = block_causal_backward(q, k, v, dout.contiguous().to(q.dtype), bf, tpf, rope, eps,
-                                           first_block_frames=f0, workspace=ws, from_forward=True)
-        return dq, dk, dv, None, None, None, None, None
+        dout = dout.contiguous()
+        if dout.dtype == q.dtype:
+            dq, dk, dv = block_causal_backward(q, k, v, dout, bf, tpf, rope, eps, first_block_frames=f0,
+                                               workspace=ws, from_forward=True)
+        else:
+            # An upstream gradient wider than the inputs (fp32 for bf16 q, k, v)
+            # is not rounded: the inputs are widened exactly and the gradients
+            # are formed from fp32 operands, then returned in the inputs' dtype.
+            w = [t.to(torch.float32) for t in (q, k, v)]
+            dq, dk, dv = block_causal_backward(*w, dout.to(torch.float32), bf, tpf, rope, eps,
+                                               grad_dtype=q.dtype, first_block_frames=f0)
+        return dq, dk, dv, None, None, None, None, None, None
 
 
 def block_causal_attention(q, k, v, block_frames, tokens_per_frame, rope=None, eps=EPS_DEFAULT,
-                           first_block_frames=None):
-    """Differentiable block-causal ReLU linear attention (see BlockCausalAttention)."""
+                           first_block_frames=None, out_dtype=None):
+    """Differentiable block-causal ReLU linear attention (see BlockCausalAttention).
+    out_dtype: dtype of the output (default: the inputs'); an fp32 output of bf16
+    inputs receives an fp32 upstream gradient, which the backward keeps in fp32."""
     return BlockCausalAttention.apply(q, k, v, block_frames, tokens_per_frame, rope, eps,
-                                      first_block_frames)
+                                      first_block_frames, out_dtype)
 
 
 # ----------------------------------------------------------------- streaming
@@ -461,7 +481,7 @@ class StreamState:
             out = torch.empty((B, N, H, d), dtype=out_dtype, device=q.device)
         elif out.shape != q.shape or out.dtype != out_dtype or not out.is_contiguous():
             raise ValueError("out must be a contiguous tensor of q's shape and out_dtype")
-        need = lib.la_workspace_bytes(B, H, d, frames, int(tokens_per_frame), frames, 0)
+        need = lib.la_workspace_bytes(B, H, d, frames, int(tokens_per_frame), frames, 0, _rope_ptr(rope))
         ws = _workspace(q.device, need) if workspace is None else workspace
         _check(lib.la_stream_block(ctypes.byref(self.desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                    _dtype_code(q.dtype), _dtype_code(out_dtype), B, H, d, frames,
@@ -485,7 +505,7 @@ class StreamState:
             out = torch.empty((B, N, H, d), dtype=out_dtype, device=qkv.device)
         elif out.shape != (B, N, H, d) or out.dtype != out_dtype or not out.is_contiguous():
             raise ValueError("out must be a contiguous (B, N, H, head_dim) tensor of out_dtype")
-        need = lib.la_qkv_workspace_bytes(B, H, d, frames, int(tokens_per_frame), frames, 0)
+        need = lib.la_qkv_workspace_bytes(B, H, d, frames, int(tokens_per_frame), frames, 0, _rope_ptr(rope))
         ws = _workspace(qkv.device, need) if workspace is None else workspace
         _check(lib.la_stream_block_qkv(ctypes.byref(self.desc), _ptr(qkv), _ptr(out), _dtype_code(qkv.dtype),
                                        _dtype_code(out_dtype), B, H, d, frames, int(tokens_per_frame),

@@ -72,12 +72,12 @@ def test_workspace_bytes(lavr):
     rec = (32 * 32 + 32) * 4
     assert n >= 70 * 30 * rec            # at least the per-block prefix states
     assert n < 0.05 * 1 * 374400 * 70 * 32 * 2 * 4   # small next to q, k, v, out
-    assert lavr.lib.la_workspace_bytes(1, 70, 48, 240, 1560, 8, 0) == 0   # head_dim 48 not built
+    assert lavr.lib.la_workspace_bytes(1, 70, 48, 240, 1560, 8, 0, None) == 0   # head_dim 48 not built
     # the same channels as 35 heads of 64: records of 64 x 64 + 64 floats
-    n64 = lavr.lib.la_workspace_bytes(1, 35, 64, 240, 1560, 8, 0)
+    n64 = lavr.lib.la_workspace_bytes(1, 35, 64, 240, 1560, 8, 0, None)
     assert n64 >= 35 * 30 * (64 * 64 + 64) * 4
-    assert lavr.lib.la_workspace_bytes(0, 70, 32, 240, 1560, 8, 0) == 0
-    assert lavr.lib.la_workspace_bytes(1, 70, 32, 240, 1560, 8, -1) == 0  # bad first block
+    assert lavr.lib.la_workspace_bytes(0, 70, 32, 240, 1560, 8, 0, None) == 0
+    assert lavr.lib.la_workspace_bytes(1, 70, 32, 240, 1560, 8, -1, None) == 0  # bad first block
     # a first block of 9 frames: 1 + ceil(231 / 8) = 30 blocks, workspace at least as large
     assert lavr.workspace_bytes(1, 70, 240, 1560, 8, first_block_frames=9) >= 70 * 30 * rec
     assert lavr.workspace_bytes(1, 70, 240, 1560, 8, first_block_frames=8) == n
@@ -121,16 +121,16 @@ def test_forward_rejects_bad_arguments(lavr, kw, code):
 
 def test_size_limits(lavr):
     """The documented maxima: 2^30 tokens per batch row, B <= 65535, B * H <= 2^24."""
-    assert lavr.lib.la_workspace_bytes(1, 2, 32, 1 << 20, 1024, 2, 0) > 0          # N = 2^30 plans
-    assert lavr.lib.la_workspace_bytes(1, 2, 32, (1 << 20) + 1, 1024, 2, 0) == 0   # one frame more does not
+    assert lavr.lib.la_workspace_bytes(1, 2, 32, 1 << 20, 1024, 2, 0, None) > 0          # N = 2^30 plans
+    assert lavr.lib.la_workspace_bytes(1, 2, 32, (1 << 20) + 1, 1024, 2, 0, None) == 0   # one frame more does not
     assert call_forward(lavr, frames=(1 << 20) + 1, tpf=1024) == lavr.LA_ERR_UNSUPPORTED
     # at the maximum the plan is fine and the call fails only on the small workspace
     assert call_forward(lavr, frames=1 << 20, tpf=1024) == lavr.LA_ERR_INVALID_ARG
     assert call_forward(lavr, B=65536) == lavr.LA_ERR_UNSUPPORTED
     assert call_forward(lavr, B=4096, H=4097) == lavr.LA_ERR_UNSUPPORTED
     # N * tokens_per_frame reaches 2^42 (N = 2^27 tokens in frames of 2^15)
-    assert lavr.lib.la_workspace_bytes(1, 2, 32, (1 << 12) - 1, 1 << 15, 2, 0) > 0
-    assert lavr.lib.la_workspace_bytes(1, 2, 32, 1 << 12, 1 << 15, 2, 0) == 0
+    assert lavr.lib.la_workspace_bytes(1, 2, 32, (1 << 12) - 1, 1 << 15, 2, 0, None) > 0
+    assert lavr.lib.la_workspace_bytes(1, 2, 32, 1 << 12, 1 << 15, 2, 0, None) == 0
 
 
 def rope_desc(lavr, **kw):
@@ -266,8 +266,8 @@ def test_backward_rejects_bad_arguments(lavr, kw, code):
 def test_backward_workspace_bytes(lavr):
     n = lavr.backward_workspace_bytes(1, 70, 240, 1560, 8)
     assert n > lavr.workspace_bytes(1, 70, 240, 1560, 8)     # plus the suffix records
-    assert lavr.lib.la_backward_workspace_bytes(1, 35, 64, 240, 1560, 8, 0) > 0    # head dim 64 built
-    assert lavr.lib.la_backward_workspace_bytes(1, 35, 48, 240, 1560, 8, 0) == 0
+    assert lavr.lib.la_backward_workspace_bytes(1, 35, 64, 240, 1560, 8, 0, None) > 0    # head dim 64 built
+    assert lavr.lib.la_backward_workspace_bytes(1, 35, 48, 240, 1560, 8, 0, None) == 0
 
 
 def call_forward_qkv(lavr, **kw):
@@ -305,7 +305,7 @@ def test_qkv_workspace_bytes(lavr):
     n = lavr.qkv_workspace_bytes(1, 70, 240, 1560, 8)
     assert n >= base + 2 * 374400 * 4
     assert n < base + 2 * 374400 * 4 + 1024
-    assert lavr.lib.la_qkv_workspace_bytes(1, 70, 48, 240, 1560, 8, 0) == 0
+    assert lavr.lib.la_qkv_workspace_bytes(1, 70, 48, 240, 1560, 8, 0, None) == 0
 
 
 def test_stream_block_qkv_state_checks(lavr):
@@ -362,3 +362,30 @@ def test_tconv_stream_state_checks(lavr):
     assert f(ctypes.byref(st), x, y, 1, 2, 0, 6, 64, 3, w, None, 1, None) == 1       # no frames
     assert st.frames_done == 0
     assert lavr.lib.la_conv_state_init(ctypes.byref(st), vp(FAKE + 4), 1, 2, 6, 64, None) == 1
+
+
+def test_workspace_query_plans_with_the_rotary_window(lavr):
+    """A block's work is cut into pieces whose rotary window fits on chip; with
+    one token per frame and long blocks (1-D RoPE over the token index) that
+    takes more pieces than without RoPE, so the workspace queries take the
+    rotary description.  Queried with it, the size is the one the call checks:
+    a byte less is rejected, and the RoPE-off size is too small.  Placeholder
+    device addresses: every call here returns before any HIP call."""
+    B, H, d, frames, tpf, bf = 1, 70, 32, 16384, 1, 4096
+    rope = lavr.LaRope(16, 32, 0, 0, frames, 1, 1)           # table address only read as a range
+    with_rope = lavr.lib.la_workspace_bytes(B, H, d, frames, tpf, bf, 0, ctypes.byref(rope))
+    without = lavr.lib.la_workspace_bytes(B, H, d, frames, tpf, bf, 0, None)
+    assert with_rope > without > 0
+    q, k, v, out, ws = (ctypes.c_void_p(i << 40) for i in range(1, 6))
+
+    def fwd(nbytes):
+        return lavr.lib.la_block_causal_forward(q, k, v, out, lavr.LA_BF16, lavr.LA_BF16, B, H, d, frames, tpf,
+                                                bf, 0, ctypes.byref(rope), 1e-8, ws, nbytes, None)
+
+    assert fwd(without) == lavr.LA_ERR_INVALID_ARG
+    assert fwd(with_rope - 1) == lavr.LA_ERR_INVALID_ARG
+    for query in (lavr.lib.la_backward_workspace_bytes, lavr.lib.la_qkv_workspace_bytes):
+        assert query(B, H, d, frames, tpf, bf, 0, ctypes.byref(rope)) > query(B, H, d, frames, tpf, bf, 0, None)
+    # a description the call would reject sizes to 0
+    bad = lavr.LaRope(16, 30, 0, 0, frames, 1, 1)             # sections do not sum to head_dim
+    assert lavr.lib.la_workspace_bytes(B, H, d, frames, tpf, bf, 0, ctypes.byref(bad)) == 0

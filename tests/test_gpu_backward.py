@@ -149,6 +149,31 @@ def test_autograd_binding(lavr):
         assert e <= TOL_BF16
 
 
+def test_autograd_fp32_upstream_gradient(lavr):
+    """fp32 output from bf16 inputs: autograd hands the backward an fp32 upstream
+    gradient, which is not rounded to bf16; the gradients (returned in bf16, the
+    inputs' dtype) match the oracle's with an fp32 dout."""
+    cfg = small_cfg(frames=9)
+    say("case autograd, fp32 output and upstream gradient")
+    arrs, (q, k, v) = device_inputs(cfg, DEV)
+    shape = (cfg["B"], W().n_tokens(cfg), cfg["H"], cfg["head_dim"])
+    g32 = np.random.default_rng([9, cfg["index"]]).standard_normal(shape).astype(np.float32)
+    q, k, v = (t.clone().requires_grad_(True) for t in (q, k, v))
+    out = lavr.block_causal_attention(q, k, v, cfg["block_frames"], cfg["tokens_per_frame"], rope_for(lavr, cfg),
+                                      out_dtype=torch.float32)
+    assert out.dtype == torch.float32
+    (out * torch.from_numpy(g32).to(DEV)).sum().backward()
+    torch.cuda.synchronize()
+    w = W()
+    ref = oracle.backward(*(w.to_f64(cfg, arrs[t]) for t in w.TENSORS), g32.astype(np.float64),
+                          cfg["tokens_per_frame"], cfg["block_frames"], w.oracle_rope(cfg))
+    for name, t, b in zip(("dq", "dk", "dv"), (q, k, v), ref):
+        assert t.grad.dtype == torch.bfloat16
+        e = err_bf16_out(to_f64_torch(t.grad), b)
+        say(f"  {name} rel err beyond bf16 rounding {e:.3e}")
+        assert e <= TOL_BF16
+
+
 @pytest.mark.parametrize("d", [32, 64])
 def test_backward_from_forward_matches(lavr, d):
     """Reusing the forward's block prefixes gives the recomputing backward's
@@ -162,14 +187,66 @@ def test_backward_from_forward_matches(lavr, d):
     rope = rope_for(lavr, cfg)
     tpf, bf, f0 = cfg["tokens_per_frame"], cfg["block_frames"], cfg["first_block_frames"]
     need = lavr.backward_workspace_bytes(cfg["B"], cfg["H"], cfg["frames"], tpf, bf, head_dim=d,
-                                         first_block_frames=f0)
-    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+                                         first_block_frames=f0, rope=rope)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
     lavr.block_causal_forward(q, k, v, bf, tpf, rope, workspace=ws, first_block_frames=f0)
     a = lavr.block_causal_backward(q, k, v, g, bf, tpf, rope, first_block_frames=f0, workspace=ws,
                                    from_forward=True)
     b = lavr.block_causal_backward(q, k, v, g, bf, tpf, rope, first_block_frames=f0)
     torch.cuda.synchronize()
     assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("grad_dtype", [torch.float32, torch.bfloat16])
+def test_backward_from_forward_foreign_workspace(lavr, grad_dtype):
+    """The training path checks that its workspace holds the block prefixes of a
+    matching forward: a workspace that a forward of another block schedule, of
+    other k and v tensors or of the fused (B, N, 3, C) input wrote, or that no
+    forward wrote, gives gradients that are NaN everywhere (a value check, the
+    call itself succeeds); the matching workspace gives the recomputing
+    backward's gradients bit for bit."""
+    cfg = small_cfg(frames=9)
+    say(f"case backward from forward, foreign workspaces, {grad_dtype}")
+    _, (q, k, v) = device_inputs(cfg, DEV)
+    _, g = draw_dout(cfg)
+    rope = rope_for(lavr, cfg)
+    tpf, bf = cfg["tokens_per_frame"], cfg["block_frames"]
+    B, H, d = cfg["B"], cfg["H"], cfg["head_dim"]
+    need = max(lavr.backward_workspace_bytes(B, H, cfg["frames"], tpf, bf, head_dim=d, rope=rope),
+               lavr.backward_workspace_bytes(B, H, cfg["frames"], tpf, 1, head_dim=d, rope=rope),
+               lavr.qkv_workspace_bytes(B, H, cfg["frames"], tpf, bf, d, rope=rope))
+
+    def train(ws):
+        out = lavr.block_causal_backward(q, k, v, g, bf, tpf, rope, grad_dtype=grad_dtype, workspace=ws,
+                                         from_forward=True)
+        torch.cuda.synchronize()
+        return out
+
+    ref = lavr.block_causal_backward(q, k, v, g, bf, tpf, rope, grad_dtype=grad_dtype)
+    ws = lavr.new_workspace(need, DEV)
+    lavr.block_causal_forward(q, k, v, bf, tpf, rope, workspace=ws)
+    assert all(torch.equal(x, y) for x, y in zip(train(ws), ref))
+
+    foreign = {}
+    w1 = torch.zeros(need, dtype=torch.uint8, device=DEV)          # no forward wrote it
+    foreign["unwritten"] = w1
+    w2 = lavr.new_workspace(need, DEV)                              # another block schedule
+    lavr.block_causal_forward(q, k, v, 1, tpf, rope, workspace=w2)
+    foreign["other schedule"] = w2
+    w3 = lavr.new_workspace(need, DEV)                              # other k and v tensors, same values
+    lavr.block_causal_forward(q, k.clone(), v.clone(), bf, tpf, rope, workspace=w3)
+    foreign["other tensors"] = w3
+    w4 = lavr.new_workspace(need, DEV)                              # the fused-input forward
+    qkv = torch.stack([t.reshape(B, -1, H * d) for t in (q, k, v)], dim=2).contiguous()
+    lavr.block_causal_forward_qkv(qkv, H, bf, tpf, rope, workspace=w4)
+    foreign["fused input"] = w4
+    for name, wsx in foreign.items():
+        grads = train(wsx)
+        say(f"  {name}: all NaN {[bool(torch.isnan(x).all()) for x in grads]}")
+        assert all(bool(torch.isnan(x).all()) for x in grads), name
+    # the matching workspace still works after the failed calls
+    lavr.block_causal_forward(q, k, v, bf, tpf, rope, workspace=ws)
+    assert all(torch.equal(x, y) for x, y in zip(train(ws), ref))
 
 
 def test_backward_deterministic(lavr):
@@ -218,9 +295,9 @@ def test_backward_full_size(lavr, name, heads):
     dq, dk, dv = lavr.block_causal_backward(q, k, v, g, cfg["block_frames"], cfg["tokens_per_frame"],
                                             rope, grad_dtype=torch.float32)
     # the training path (the forward's block prefixes reused) gives the same bits
-    ws = torch.empty(lavr.backward_workspace_bytes(cfg["B"], cfg["H"], cfg["frames"], cfg["tokens_per_frame"],
-                                                   cfg["block_frames"], head_dim=cfg["head_dim"]),
-                     dtype=torch.uint8, device=DEV)
+    ws = lavr.new_workspace(lavr.backward_workspace_bytes(cfg["B"], cfg["H"], cfg["frames"], cfg["tokens_per_frame"],
+                                                          cfg["block_frames"], head_dim=cfg["head_dim"],
+                                                          rope=rope), DEV)
     lavr.block_causal_forward(q, k, v, cfg["block_frames"], cfg["tokens_per_frame"], rope, workspace=ws)
     again = lavr.block_causal_backward(q, k, v, g, cfg["block_frames"], cfg["tokens_per_frame"], rope,
                                        grad_dtype=torch.float32, workspace=ws, from_forward=True)

@@ -140,3 +140,63 @@ def test_backward_many_rounds(lavr, kw):
         e = oracle.rel_err(to_f64_torch(a), b)
         say(f"  {name} rel err {e:.3e}")
         assert e <= TOL_BF16_IN_F32_GRAD
+
+
+def test_workspace_shared_across_shapes(lavr):
+    """One workspace serves calls of different shapes in turn: a streamed block
+    (one block, many short chunks), then a many-block forward and backward, then
+    the streamed block again.  Every result equals the one from a fresh
+    workspace bit for bit: no call depends on what an earlier call of another
+    shape left in the workspace."""
+    cfg = rounds_cfg(frames=32)
+    say("case workspace shared across shapes")
+    _, (q, k, v) = device_inputs(cfg, DEV)
+    rope = rope_for(lavr, cfg)
+    bf, tpf = cfg["block_frames"], cfg["tokens_per_frame"]
+    B, H = cfg["B"], cfg["H"]
+    g = torch.randn(q.shape, generator=torch.Generator(device=DEV).manual_seed(3), device=DEV).to(q.dtype)
+    L = bf * tpf
+    blk = tuple(x[:, :L].contiguous() for x in (q, k, v))
+
+    def streamed(ws):
+        st = lavr.StreamState(B, H, device=DEV)
+        return st.step(*blk, tpf, rope, out_dtype=torch.float32, workspace=ws)
+
+    def one_shot(ws):
+        out = lavr.block_causal_forward(q, k, v, bf, tpf, rope, out_dtype=torch.float32, workspace=ws)
+        grads = lavr.block_causal_backward(q, k, v, g, bf, tpf, rope, grad_dtype=torch.float32, workspace=ws)
+        return (out, *grads)
+
+    need = max(lavr.backward_workspace_bytes(B, H, cfg["frames"], tpf, bf, rope=rope),
+               lavr.workspace_bytes(B, H, bf, tpf, bf, rope=rope))
+    ref_s = streamed(lavr.new_workspace(need, DEV))
+    ref_o = one_shot(lavr.new_workspace(need, DEV))
+    shared = lavr.new_workspace(need, DEV)
+    got_s1 = streamed(shared)
+    got_o = one_shot(shared)
+    got_s2 = streamed(shared)
+    torch.cuda.synchronize()
+    assert torch.equal(got_s1, ref_s) and torch.equal(got_s2, ref_s)
+    assert all(torch.equal(a, b) for a, b in zip(got_o, ref_o))
+
+
+def test_rope_window_sized_workspace(lavr):
+    """One token per frame, 1-D RoPE and blocks of 4096 frames: each block's
+    pieces are cut short so that their rotary windows fit on chip.  A workspace
+    of exactly the queried size (queried with the rotary description) runs, and
+    the result matches the oracle."""
+    cfg = dict(index=310, B=1, H=32, head_dim=32, frames=16384, tokens_per_frame=1, grid=(1, 1),
+               block_frames=4096, dtype="bf16", rope={"split": (32, 0, 0), "base": 10000.0},
+               scale=1.0, outlier_frac=0.0, outlier_scale=1.0, name="rope_window")
+    say("case workspace sized with the rotary window (1-D RoPE, 4096-frame blocks)")
+    arrs, (q, k, v) = device_inputs(cfg, DEV)
+    rope = rope_for(lavr, cfg)
+    bf, tpf = cfg["block_frames"], cfg["tokens_per_frame"]
+    need = lavr.workspace_bytes(cfg["B"], cfg["H"], cfg["frames"], tpf, bf, rope=rope)
+    assert need > lavr.workspace_bytes(cfg["B"], cfg["H"], cfg["frames"], tpf, bf)
+    ws = lavr.new_workspace(need, DEV)[:need]
+    out = lavr.block_causal_forward(q, k, v, bf, tpf, rope, out_dtype=torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    e = oracle.rel_err(to_f64_torch(out), oracle_fwd(cfg, arrs))
+    say(f"  f32 out err {e:.3e}")
+    assert e <= TOL_BF16

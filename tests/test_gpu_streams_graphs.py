@@ -34,7 +34,7 @@ def inputs(seed, n=3):
 
 def workspace(lavr, backward=False):
     f = lavr.backward_workspace_bytes if backward else lavr.workspace_bytes
-    return torch.empty(f(B, H, FRAMES, TPF, BF, head_dim=D), dtype=torch.uint8, device=DEV)
+    return torch.zeros(f(B, H, FRAMES, TPF, BF, head_dim=D), dtype=torch.uint8, device=DEV)
 
 
 def test_two_streams_at_once(lavr):
