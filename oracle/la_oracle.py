@@ -509,12 +509,14 @@ def token_causal_cumsum(q, k, v, tokens_per_frame, rope=None, eps=EPS_DEFAULT):
 
 
 def lite_la_single_block(q, k, v, tokens_per_frame, rope=None, eps=EPS_DEFAULT):
-    """Non-causal ReLU linear attention over the whole sequence, in (B, h, d, N) layout.
+    """Non-causal ReLU linear attention over the whole sequence: the normalised
+    readout of [ImplBCLA, "The Linear Attention Kernel"] with one block that
+    holds every token, so every query reads the state formed by all keys:
 
-    Follows the normalised readout as [ImplBCLA, "The Linear Attention Kernel"] states
-    it for one block: z = 1 / (sum_n k^T . q + eps), vk = v . k_rot^T, out = vk . q_rot,
-    output = out * z, with k, q already through phi.  A block that spans the whole
-    sequence must give this.
+        out_n = sum_m v_m <R phi(k_m), R phi(q_n)> / (<sum_m phi(k_m), phi(q_n)> + eps)
+
+    (rotated vectors in the numerator, un-rotated ones in the normaliser).  A
+    block spanning the whole sequence must give this.
     """
     q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
     B, N, H, d = q.shape
@@ -522,13 +524,11 @@ def lite_la_single_block(q, k, v, tokens_per_frame, rope=None, eps=EPS_DEFAULT):
     for b in range(B):
         for h in range(H):
             fq, fk = _relu(q[b, :, h]), _relu(k[b, :, h])
-            rq = _rotate_tokens(fq, rope, tokens_per_frame, 0).T   # (d, N)
-            rk = _rotate_tokens(fk, rope, tokens_per_frame, 0).T
-            qd, kd, vd = fq.T, fk.T, v[b, :, h].T                 # (d, N)
-            zz = 1.0 / (kd.sum(axis=-1, keepdims=True).T @ qd + eps)   # (1, N)
-            vk = vd @ rk.T                                         # (d, d)
-            o = (vk @ rq) * zz                                     # (d, N)
-            out[b, :, h] = o.T
+            rq = _rotate_tokens(fq, rope, tokens_per_frame, 0)
+            rk = _rotate_tokens(fk, rope, tokens_per_frame, 0)
+            num = np.einsum("me,mf,nf->ne", v[b, :, h], rk, rq, optimize=True)
+            den = np.einsum("mf,nf->n", fk, fq, optimize=True) + eps
+            out[b, :, h] = num / den[:, None]
     return out
 
 

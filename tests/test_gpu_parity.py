@@ -13,6 +13,11 @@ import torch
 import oracle
 from helpers import (TOL_BF16, TOL_F32, device_inputs, err_bf16_out, oracle_head, to_f64_torch)
 
+# fp32 outputs of bf16 inputs at full size, plain metric: the rotated operands
+# and prefix states carried as bf16 hi + lo pairs (~17 bits each) keep the
+# arithmetic near 1e-4 even over a minute of tokens
+TOL_F32_OUT_FULL = 1e-3
+
 pytestmark = pytest.mark.gpu
 
 DEV = torch.device("cuda:0")
@@ -421,17 +426,27 @@ def check_heads(cfg, arrs, out, heads, label):
     ("minute_d64_bf16", [(0, 0), (0, 20)]),
 ])
 def test_full_size_one_shot(lavr, name, heads):
+    """Full-size workloads on sampled heads.  bf16 outputs are scored with the
+    bf16 output's own rounding allowed (err_bf16_out); the arithmetic itself is
+    held to the plain metric without that allowance through fp32 outputs of the
+    same call (2e-2, and TOL_F32_OUT_FULL for what the hi/lo operand split
+    gives), and the bf16 output must be the round-to-nearest-even of the fp32
+    output over the whole tensor."""
     w = W()
     cfg = w.workload(name)
     say(f"case full-size {name}")
     arrs, (q, k, v) = device_inputs(cfg, DEV)
     rope = rope_for(lavr, cfg)
-    out = lavr.block_causal_forward(q, k, v, cfg["block_frames"], cfg["tokens_per_frame"], rope)
+    bf, tpf = cfg["block_frames"], cfg["tokens_per_frame"]
+    out = lavr.block_causal_forward(q, k, v, bf, tpf, rope)
+    out32 = lavr.block_causal_forward(q, k, v, bf, tpf, rope, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert check_heads(cfg, arrs, out, heads, name) <= TOL_BF16
-    # the whole output is finite and a sampled token of every head agrees too
-    assert torch.isfinite(out).all().item()
-    del out, q, k, v
+    e32 = check_heads(cfg, arrs, out32, heads, name + " fp32 out")
+    assert e32 <= TOL_BF16 and e32 <= TOL_F32_OUT_FULL
+    assert torch.equal(out, out32.to(torch.bfloat16))
+    assert torch.isfinite(out32).all().item()
+    del out, out32, q, k, v
     torch.cuda.empty_cache()
 
 
@@ -483,7 +498,9 @@ def test_full_size_streaming_save_off_reuse(lavr):
 
 
 def test_full_size_streaming(lavr):
-    """40 streamed 3-frame blocks (B=2, 70 heads) match one-shot over 120 frames to one bf16 step."""
+    """40 streamed 3-frame blocks (B=2, 70 heads) match one-shot over 120 frames to
+    one bf16 step; streamed fp32 outputs meet the plain metric without the bf16
+    rounding allowance, and the streamed bf16 outputs are their rounding."""
     w = W()
     cfg = w.workload("stream_bf16")
     say("case full-size streaming 40 x 3 frames")
@@ -494,10 +511,16 @@ def test_full_size_streaming(lavr):
     one = lavr.block_causal_forward(q, k, v, 3, tpf, rope)
     st = lavr.StreamState(cfg["B"], cfg["H"], device=DEV)
     got = stream_run(lavr, st, q, k, v, cfg, rope, 40, L)
+    st32 = lavr.StreamState(cfg["B"], cfg["H"], device=DEV)
+    got32 = stream_run(lavr, st32, q, k, v, cfg, rope, 40, L, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert st.frames_done == 120
     # One-shot and streamed launches may split a block into different chunks, so
     # the fp32 sums differ in rounding order: at most one bf16 step apart.
     diff = (got.float() - one.float()).abs()
     assert torch.all(diff <= 2.0 ** -7 * one.float().abs() + 1e-6).item()
-    assert check_heads(cfg, arrs, got, [(0, 5), (1, 60)], "stream") <= TOL_BF16
+    heads = [(0, 5), (1, 60)]
+    assert check_heads(cfg, arrs, got, heads, "stream") <= TOL_BF16
+    e32 = check_heads(cfg, arrs, got32, heads, "stream fp32 out")
+    assert e32 <= TOL_BF16 and e32 <= TOL_F32_OUT_FULL
+    assert torch.equal(got, got32.to(torch.bfloat16))
