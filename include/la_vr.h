@@ -48,7 +48,8 @@
  *
  * Calling convention.  Every pointer argument named *_dev, q, k, v, out, ws,
  * S, z or table is device memory owned by the caller; the library never
- * allocates or frees device memory and keeps no global state.  Every call
+ * allocates or frees device memory and keeps no global state (apart from the
+ * fixed workspace of la_block_causal_forward_noalloc).  Every call
  * checks its arguments on the host first and returns an error code without
  * touching the GPU if they are wrong; otherwise it enqueues its kernels on
  * `stream` (a hipStream_t, NULL = default stream) and returns at once.  The
@@ -158,6 +159,25 @@ int la_block_causal_forward_timed(const void* q, const void* k, const void* v, v
                                   int block_frames, int first_block_frames, const la_rope* rope,
                                   float eps, void* ws, size_t ws_bytes, void* stream,
                                   void* const* events);
+
+/* la_block_causal_forward for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, and harnesses that forbid
+ * hipMalloc.  The caller passes inputs and outputs only; the workspace is a
+ * fixed device array inside the library, 64 MiB on each GPU the library runs
+ * on (enough for a 240-frame 480p clip at 70 heads), set up on the first call
+ * on a device and held until the process ends.  The call allocates nothing and
+ * makes no allocating library call.  Every call on one GPU shares that GPU's
+ * array, so calls whose kernels overlap on one GPU (concurrent streams, or
+ * other threads) race and give wrong results: serialise them.  stream must
+ * belong to the current device (else LA_ERR_INVALID_ARG).  A shape whose
+ * workspace (la_workspace_bytes) exceeds 64 MiB returns LA_ERR_UNSUPPORTED
+ * before any HIP call.  Arguments, results and other status codes as for
+ * la_block_causal_forward. */
+int la_block_causal_forward_noalloc(const void* q, const void* k, const void* v, void* out,
+                                    la_dtype in_dt, la_dtype out_dt,
+                                    int B, int H, int head_dim, int frames, int tokens_per_frame,
+                                    int block_frames, int first_block_frames, const la_rope* rope,
+                                    float eps, void* stream);
 
 /* Workspace bytes needed by la_block_causal_backward (and by a forward whose
  * workspace la_block_causal_backward_from_forward will reuse) for this shape,

@@ -427,6 +427,34 @@ int la_block_causal_forward_timed(const void* q, const void* k, const void* v, v
                                          ws, nullptr, nullptr, nullptr, nullptr, stream, events));
 }
 
+int la_block_causal_forward_noalloc(const void* q, const void* k, const void* v, void* out,
+                                    la_dtype in_dt, la_dtype out_dt, int B, int H, int head_dim,
+                                    int frames, int tokens_per_frame, int block_frames,
+                                    int first_block_frames, const la_rope* rope, float eps,
+                                    void* stream) {
+  if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return LA_ERR_INVALID_ARG;
+  if (!std::isfinite(eps) || eps < 0.f) return LA_ERR_INVALID_ARG;
+  Plan p;
+  int st = make_plan(&p, B, H, head_dim, frames, tokens_per_frame, block_frames, first_block_frames,
+                     rope, 0, in_dt);
+  if (st != LA_OK) return st;
+  st = check_tensors(q, k, v, out, in_dt, out_dt, p);
+  if (st != LA_OK) return st;
+  if (p.ws_total > lavr::kScratchBytes) return LA_ERR_UNSUPPORTED;   // beyond the fixed workspace
+  void* ws = nullptr;
+  switch (lavr::noalloc_workspace(stream, &ws)) {
+    case 0: break;
+    case lavr::LAVR_NOALLOC_WRONG_DEVICE: return LA_ERR_INVALID_ARG;
+    case lavr::LAVR_NOALLOC_UNSUPPORTED: return LA_ERR_UNSUPPORTED;
+    default: return LA_ERR_HIP;
+  }
+  const size_t nin = tensor_bytes(p, in_dt), nout = tensor_bytes(p, out_dt);
+  st = check_scratch(p, ws, p.ws_total, {out, nout}, {{q, nin}, {k, nin}, {v, nin}}, rope);
+  if (st != LA_OK) return st;
+  return hip_status(lavr::launch_forward(p, q, k, v, out, in_dt == LA_BF16, out_dt == LA_BF16, eps,
+                                         ws, nullptr, nullptr, nullptr, nullptr, stream));
+}
+
 size_t la_backward_workspace_bytes(int B, int H, int head_dim, int frames, int tokens_per_frame,
                                    int block_frames, int first_block_frames, const la_rope* rope) {
   Plan p;

@@ -84,6 +84,15 @@ int launch_forward(const Plan& p, const void* q, const void* k, const void* v, v
                    void* stream, void* const* events = nullptr, const Prologue* pro = nullptr);
 int launch_zero(float* p, size_t n, void* stream);
 
+// Allocation-free forward: the workspace is a device array of kScratchBytes,
+// one per GPU (la_kernels.hip).  noalloc_workspace() returns its address on
+// the current device (0), or one of the codes below.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int LAVR_NOALLOC_HIP = 1;            // a HIP query failed
+constexpr int LAVR_NOALLOC_UNSUPPORTED = 2;    // device index beyond the library's table
+constexpr int LAVR_NOALLOC_WRONG_DEVICE = 3;   // the stream belongs to another device
+int noalloc_workspace(void* stream, void** ws);
+
 // Cached temporal convolution of one call: F frames of P tokens x Ch channels
 // per batch row, blocks of F0 then BF frames, kt taps.
 struct ConvPlan {

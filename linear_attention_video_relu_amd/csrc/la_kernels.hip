@@ -35,6 +35,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "la_internal.h"
@@ -2557,6 +2558,39 @@ int launch_backward(const Plan& p, const void* q, const void* k, const void* v, 
                      static_cast<u32x4*>(dq), static_cast<u32x4*>(dk), static_cast<u32x4*>(dv), n16,
                      grad_bf16 ? 0x7fc07fc0u : 0x7fc00000u);
   return (int)hipGetLastError();
+}
+
+// ------------------------------------------------- allocation-free workspace
+//
+// The workspace of la_block_causal_forward_noalloc: a file-scope device array,
+// one copy per GPU the library runs on, held until the process ends.  In host
+// code `scratch` names a host-side stand-in, not the device memory: its device
+// address on each GPU comes from hipGetSymbolAddress, looked up once per device
+// with that device current, and only that address reaches the kernels.
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+int noalloc_workspace(void* stream, void** ws) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> addr[kMaxDevices];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return LAVR_NOALLOC_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return LAVR_NOALLOC_UNSUPPORTED;
+  if (stream != nullptr) {
+    int sdev = -1;
+    e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+    if (e != hipSuccess) return LAVR_NOALLOC_HIP;
+    if (sdev != dev) return LAVR_NOALLOC_WRONG_DEVICE;   // the stream must belong to the current device
+  }
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) return LAVR_NOALLOC_HIP;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  *ws = p;
+  return 0;
 }
 
 }  // namespace lavr

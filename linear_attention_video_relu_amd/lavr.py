@@ -56,6 +56,9 @@ def _load():
                                                   c_int, c_int, c_int, c_int, c_int, c_int,
                                                   ctypes.POINTER(LaRope), c_float, c_vp, c_size,
                                                   c_vp, ctypes.POINTER(c_vp)]),
+        "la_block_causal_forward_noalloc": (c_int, [c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int,
+                                                    c_int, c_int, c_int, c_int, c_int,
+                                                    ctypes.POINTER(LaRope), c_float, c_vp]),
         "la_backward_workspace_bytes": (c_size, [c_int] * 7 + [ctypes.POINTER(LaRope)]),
         "la_block_causal_backward": (c_int, [c_vp] * 7 + [c_int] * 9 + [ctypes.POINTER(LaRope), c_float,
                                                                          c_vp, c_size, c_vp]),
@@ -89,7 +92,7 @@ def _load():
 lib = _load()
 
 EXPORTS = ("rope_table_bytes", "rope_table_build", "la_workspace_bytes", "la_block_causal_forward",
-           "la_block_causal_forward_timed", "la_backward_workspace_bytes", "la_block_causal_backward",
+           "la_block_causal_forward_timed", "la_block_causal_forward_noalloc", "la_backward_workspace_bytes", "la_block_causal_backward",
            "la_block_causal_backward_from_forward",
            "la_qkv_workspace_bytes", "la_block_causal_forward_qkv", "la_stream_block_qkv",
            "la_temporal_conv", "la_conv_state_init", "la_temporal_conv_stream_block",
@@ -221,6 +224,26 @@ def block_causal_forward(q, k, v, block_frames, tokens_per_frame, rope=None, eps
                                        int(tokens_per_frame), int(block_frames), f0, _rope_ptr(rope),
                                        float(eps), _ptr(ws), ws.numel() * ws.element_size(),
                                        _stream(q.device)), "la_block_causal_forward")
+    return out
+
+
+def block_causal_forward_noalloc(q, k, v, block_frames, tokens_per_frame, rope=None, eps=EPS_DEFAULT, *,
+                                 out, out_dtype=None, first_block_frames=None):
+    """la_block_causal_forward_noalloc: the one-shot forward with the library's
+    fixed per-GPU workspace instead of a caller buffer.  `out` (contiguous, q's
+    shape, out_dtype) is required, so that the call allocates nothing."""
+    _check_qkv(q, k, v)
+    B, N, H, d = q.shape
+    if N % tokens_per_frame:
+        raise ValueError("N must be a multiple of tokens_per_frame")
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out.shape != q.shape or out.dtype != out_dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor of q's shape and out_dtype on q's device")
+    _check(lib.la_block_causal_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(q.dtype),
+                                               _dtype_code(out_dtype), B, H, d, N // tokens_per_frame,
+                                               int(tokens_per_frame), int(block_frames),
+                                               int(first_block_frames or 0), _rope_ptr(rope), float(eps),
+                                               _stream(q.device)), "la_block_causal_forward_noalloc")
     return out
 
 

@@ -389,3 +389,19 @@ def test_workspace_query_plans_with_the_rotary_window(lavr):
     # a description the call would reject sizes to 0
     bad = lavr.LaRope(16, 30, 0, 0, frames, 1, 1)             # sections do not sum to head_dim
     assert lavr.lib.la_workspace_bytes(B, H, d, frames, tpf, bf, 0, ctypes.byref(bad)) == 0
+
+
+def test_noalloc_forward_rejects_shapes_beyond_its_workspace(lavr):
+    """The allocation-free forward's workspace is a fixed 64 MiB array: a shape
+    that needs more (ten minute-length clips' worth of frames) is refused with
+    LA_ERR_UNSUPPORTED before any HIP call (placeholder device addresses)."""
+    B, H, d, frames, tpf, bf = 1, 70, 32, 2400, 1560, 8
+    assert lavr.lib.la_workspace_bytes(B, H, d, frames, tpf, bf, 0, None) > 64 << 20
+    q, k, v, out = (ctypes.c_void_p(i << 40) for i in range(1, 5))
+    rc = lavr.lib.la_block_causal_forward_noalloc(q, k, v, out, lavr.LA_BF16, lavr.LA_BF16, B, H, d, frames, tpf,
+                                                  bf, 0, None, 1e-8, None)
+    assert rc == lavr.LA_ERR_UNSUPPORTED
+    # argument checks come first, as for every call
+    rc = lavr.lib.la_block_causal_forward_noalloc(None, k, v, out, lavr.LA_BF16, lavr.LA_BF16, 1, H, d, 240, tpf,
+                                                  bf, 0, None, 1e-8, None)
+    assert rc == lavr.LA_ERR_INVALID_ARG
