@@ -134,20 +134,26 @@ def cpu_baseline(cfg, arrs, n_heads):
 
 # ------------------------------------------------------------------- GPU timing
 
+# Timing events are created with the default flags: each record is a small
+# command between two kernels (a few microseconds of the timeline), so the
+# timed steps record only the two points around the readout kernel; the
+# split of the rest into block state and prefix comes from a short pass with
+# all four points after the timed region.
 class HipEvents:
-    def __init__(self, n):
+    def __init__(self, n, flags=0):
         self.hip = ctypes.CDLL("libamdhip64.so")
         self.ev = (ctypes.c_void_p * n)()
         for i in range(n):
             e = ctypes.c_void_p()
-            rc = self.hip.hipEventCreate(ctypes.byref(e))
+            rc = self.hip.hipEventCreateWithFlags(ctypes.byref(e), ctypes.c_uint(flags))
             if rc != 0:
                 raise RuntimeError(f"hipEventCreate failed: {rc}")
             self.ev[i] = e.value
 
-    def ptr(self, i):
-        return ctypes.cast(ctypes.byref(self.ev, i * ctypes.sizeof(ctypes.c_void_p)),
-                           ctypes.POINTER(ctypes.c_void_p))
+    def marks(self, *slots):
+        """The four-entry event array of one timed forward call: slot numbers, or None
+        for a point that is not recorded."""
+        return (ctypes.c_void_p * 4)(*(None if i is None else self.ev[i] for i in slots))
 
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
@@ -218,13 +224,18 @@ def main():
         if rc:
             raise RuntimeError(lavr.status_string(rc))
 
-    ev = HipEvents(4 * args.steps)
+    K = args.steps
+    # timed steps: slot 2i before step i's readout, 2i+1 after it, 2K before step 0
+    ev = HipEvents(2 * K + 1)
+    marks = [ev.marks(2 * K if i == 0 else None, None, 2 * i, 2 * i + 1) for i in range(K)]
+    n_split = min(K, 10)
+    ev_split = HipEvents(4 * n_split)
+    marks_split = [ev_split.marks(4 * i, 4 * i + 1, 4 * i + 2, 4 * i + 3) for i in range(n_split)]
 
-    def fwd_timed(i):
+    def fwd_timed(m):
         rc = lavr.lib.la_block_causal_forward_timed(*ptrs, code, code, B, H, d, cfg["frames"], tpf,
                                                     bf, 0, ctypes.byref(rope.desc), 1e-8,
-                                                    ctypes.c_void_p(ws.data_ptr()), need, stream,
-                                                    ev.ptr(4 * i))
+                                                    ctypes.c_void_p(ws.data_ptr()), need, stream, m)
         if rc:
             raise RuntimeError(lavr.status_string(rc))
 
@@ -240,14 +251,24 @@ def main():
     torch.cuda.synchronize(dev)
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        fwd_timed(i)
+    for i in range(K):
+        fwd_timed(marks[i])
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-    ph = np.array([[ev.elapsed_ms(4 * i + a, 4 * i + a + 1) for a in range(3)] for i in range(args.steps)])
-    ev_step = np.array([ev.elapsed_ms(4 * i, 4 * i + 3) for i in range(args.steps)])
-    k_state, k_prefix, k_read = (float(x) for x in ph.mean(axis=0))
+    ms_step = wall * 1e3 / K
+    # readout: its own two points; block state + prefix (+ the gaps between the
+    # kernels): from the end of one step's readout to the start of the next one's
+    t_read = np.array([ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(K)])
+    t_rest = np.array([ev.elapsed_ms(2 * K if i == 0 else 2 * i - 1, 2 * i) for i in range(K)])
+    ev_total = ev.elapsed_ms(2 * K, 2 * K - 1)
+    for i in range(n_split):
+        fwd_timed(marks_split[i])
+    torch.cuda.synchronize(dev)
+    split = np.array([[ev_split.elapsed_ms(4 * i + a, 4 * i + a + 1) for a in range(3)]
+                      for i in range(n_split)])
+    k_state, k_prefix, k_read_split = (float(x) for x in split.mean(axis=0))
+    k_read = float(t_read.mean())
+    print(f"[bench] timed {K} steps: {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
 
     th = B * N * H
     esz = 2 if dt == torch.bfloat16 else 4
@@ -257,12 +278,15 @@ def main():
     bytes_read = 2 * th * d * esz + state_io            # Q read, O written; block prefixes in
     bytes_step = 4 * th * d * esz + 2 * state_io
     kernels = {
+        # block state and prefix from the four-point pass after the timed steps
         "k_block_state": {"ms": k_state, "alg_bytes": bytes_state,
-                          "gbs": bytes_state / (k_state * 1e6)},
-        "k_prefix": {"ms": k_prefix},
-        "k_readout": {"ms": k_read, "alg_bytes": bytes_read, "gbs": bytes_read / (k_read * 1e6)},
+                          "gbs": bytes_state / (k_state * 1e6), "source": f"{n_split} steps after"},
+        "k_prefix": {"ms": k_prefix, "source": f"{n_split} steps after"},
+        "k_readout": {"ms": k_read, "alg_bytes": bytes_read, "gbs": bytes_read / (k_read * 1e6),
+                      "source": "timed steps"},
+        "k_block_state+k_prefix+gaps": {"ms": float(t_rest.mean()), "source": "timed steps"},
     }
-    dom = "k_block_state" if k_state >= k_read else "k_readout"
+    dom = "k_block_state" if k_state >= k_read_split else "k_readout"
     ach = kernels[dom]["gbs"]
 
     result = {
@@ -287,13 +311,13 @@ def main():
                      "traffic": measured_traffic(cfg["name"], dom)},
         "step_hbm_gbs": bytes_step / (ms_step * 1e6),
         "step_frac_of_peak": bytes_step / (ms_step * 1e6) / HBM_PEAK_GBS,
-        "event_ms_per_step": float(ev_step.mean()),
+        "event_ms_per_step": ev_total / K,
         "kernels": kernels,
-        # per timed step, HIP-event ms of each kernel: the shader clock dips
-        # when the heavy load starts and recovers over ~40 ms, and the trend
-        # shows how much of the timed region falls in that ramp
-        "step_trend": {name: [round(float(x), 4) for x in ph[:, i]]
-                       for i, name in enumerate(("k_block_state", "k_prefix", "k_readout"))},
+        # per timed step, HIP-event ms of the readout and of the rest of the step:
+        # the shader clock dips when the heavy load starts and recovers over
+        # ~40 ms, and the trend shows how much of the timed region falls in that ramp
+        "step_trend": {"k_readout": [round(float(x), 4) for x in t_read],
+                       "k_block_state+k_prefix+gaps": [round(float(x), 4) for x in t_rest]},
         "cpu_baseline": cpu,
     }
 

@@ -149,10 +149,13 @@ int la_block_causal_forward(const void* q, const void* k, const void* v, void* o
                             int block_frames, int first_block_frames, const la_rope* rope,
                             float eps, void* ws, size_t ws_bytes, void* stream);
 
-/* la_block_causal_forward that also records four caller-created hipEvent_t
- * events[0..3] on `stream`: before the block-state kernel, after it, after
- * the prefix kernel and after the readout kernel, so a caller can time each
- * phase with hipEventElapsedTime.  events must not be NULL. */
+/* la_block_causal_forward that also records caller-created hipEvent_t events
+ * on `stream` at four points: events[0] before the block-state kernel,
+ * events[1] after it, events[2] after the prefix kernel (before the readout)
+ * and events[3] after the readout, so a caller can time each phase with
+ * hipEventElapsedTime.  events must not be NULL; an entry that is NULL is not
+ * recorded (every record adds a few microseconds between the kernels, so a
+ * caller timing a long run records only the points it needs). */
 int la_block_causal_forward_timed(const void* q, const void* k, const void* v, void* out,
                                   la_dtype in_dt, la_dtype out_dt,
                                   int B, int H, int head_dim, int frames, int tokens_per_frame,

@@ -153,9 +153,12 @@ int make_plan(Plan* p, int B, int H, int head_dim, int frames, int tpf, int bloc
   p->mag_gw = (uint64_t)(kTwo42 / gw_div) + 1;
   const long long row_bytes = (long long)p->row_in * 4;
   const long long min_n = cdiv(kMinWg, (long long)B * p->hg * p->nb);
-  // Block-state chunks stage (cos, sin) pairs (8 bytes); readout tiles may
-  // stage them as rope_words (16 bytes).
-  if (!split_block(Lmax, kStateMax, min_n, kStep, rope, tpf, row_bytes, 8, kTabLdsMax, &p->cpb, &p->Tc))
+  // Rotary windows are staged as (cos, sin) pairs (8 bytes), or as rope_words
+  // (16 bytes) by the readout tiles and, for bf16 inputs, the block-state chunks.
+  const bool bf16_in = in_dt == LA_BF16;
+  const int state_entry = bf16_in ? 16 : 8;
+  if (!split_block(Lmax, kStateMax, min_n, kStep, rope, tpf, row_bytes, state_entry,
+                   bf16_in ? kTabLdsMax16 : kTabLdsMax, &p->cpb, &p->Tc))
     return LA_ERR_UNSUPPORTED;
   if (!split_block(Lmax, kReadMax, min_n, 64, rope, tpf, row_bytes, 16, kTabLdsMax16, &p->rpb, &p->Tr))
     return LA_ERR_UNSUPPORTED;
@@ -175,7 +178,7 @@ int make_plan(Plan* p, int B, int H, int head_dim, int frames, int tpf, int bloc
   }
   const int tiles = (in_dt == LA_BF16 ? 3 : 2) * kStep * 64 * esize(in_dt);   // 64 channels per row
   p->tab_state = (int)(tab_pairs(rope, tpf, p->Tc) * 8);
-  p->lds_state = lavr::kStateTileSets * tiles + p->tab_state;
+  p->lds_state = lavr::kStateTileSets * tiles + (int)(tab_pairs(rope, tpf, p->Tc) * state_entry);
   p->lds_read = (int)(tab_pairs(rope, tpf, p->Tr) * 8);
   p->lds_read16 = 2 * p->lds_read;
 
@@ -410,7 +413,7 @@ int la_block_causal_forward_timed(const void* q, const void* k, const void* v, v
                                   int frames, int tokens_per_frame, int block_frames,
                                   int first_block_frames, const la_rope* rope, float eps,
                                   void* ws, size_t ws_bytes, void* stream, void* const* events) {
-  if (!events || !events[0] || !events[1] || !events[2] || !events[3]) return LA_ERR_INVALID_ARG;
+  if (!events) return LA_ERR_INVALID_ARG;
   if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return LA_ERR_INVALID_ARG;
   if (!std::isfinite(eps) || eps < 0.f) return LA_ERR_INVALID_ARG;
   Plan p;

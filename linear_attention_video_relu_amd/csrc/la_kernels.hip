@@ -171,17 +171,27 @@ __device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
   }
 }
 
-// split8 with h << 16 formed by a byte permute: written as a shift, the
-// compiler forms it with a second conversion of x[2i] (one more instruction
-// per pair).  Used where the instruction count matters (the readout's packed
-// path); elsewhere the shift form needs fewer registers.
-__device__ __forceinline__ void split8p(const float* x, u32x4& hi, u32x4& lo) {
+// split8 with the remainders formed by v_dot2c_f32_bf16: x - hi is the dot
+// product of the packed hi pair with (-1, 0) or (0, -1), accumulated onto x.
+// The products are exact and x - hi is representable in fp32, so the result
+// is the exact remainder in one instruction, where a subtraction needs the hi
+// part widened first: four instructions per pair instead of six.  Used where
+// the instruction count matters (the readout's packed path).
+//
+// The unused half of each multiplier is -0, not +0: a pair with a zero high
+// half is encoded as an inline constant, which v_dot2c reads as the fp32 value
+// (1.0 -> 0x3f800000, the pair (0, 1)); a literal is read bit for bit.  x - h
+// plus -0 * h' is still exactly x - h.
+__device__ __forceinline__ void split8d(const float* x, u32x4& hi, u32x4& lo) {
+  const bf16x2 m0 = __builtin_bit_cast(bf16x2, 0x8000bf80u);   // (-1, -0)
+  const bf16x2 m1 = __builtin_bit_cast(bf16x2, 0xbf808000u);   // (-0, -1)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t h = pack_bf16(x[2 * i], x[2 * i + 1]);
     hi[i] = h;
-    const uint32_t h0 = __builtin_amdgcn_perm(h, h, 0x01000c0cu);
-    lo[i] = pack_bf16(x[2 * i] - __uint_as_float(h0), x[2 * i + 1] - __uint_as_float(h & 0xffff0000u));
+    const bf16x2 hb = __builtin_bit_cast(bf16x2, h);
+    lo[i] = pack_bf16(__builtin_amdgcn_fdot2_f32_bf16(hb, m0, x[2 * i], false),
+                      __builtin_amdgcn_fdot2_f32_bf16(hb, m1, x[2 * i + 1], false));
   }
 }
 
@@ -501,6 +511,15 @@ struct TabStage {
     }
     for (int i = threadIdx.x + PER * NT; i < tot; i += NT) lds[i] = i < nt ? tsrc[i] : hwsrc[i - nt];
   }
+  // The same window written as rope_words (16 bytes per pair).
+  __device__ void commit16(u32x4* lds) const {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = threadIdx.x + k * NT;
+      if (i < tot) lds[i] = rope_words(v[k]);
+    }
+    for (int i = threadIdx.x + PER * NT; i < tot; i += NT) lds[i] = rope_words(i < nt ? tsrc[i] : hwsrc[i - nt]);
+  }
 };
 
 // --------------------------------------------------------- k_block_state
@@ -532,6 +551,9 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? ((P2 && DH == 32 && !NRM && 
   constexpr int W16 = 16 / ES;           // elements per 16 bytes
   constexpr int PF = (BF && P2 && !W64 && !NRM) ? LAVR_STATE_PF : 2;   // steps of loads in flight
   static_assert(PF == 2 || PF == 3, "block-state prefetch depth: two or three register buffers");
+  // bf16 keys that are not normalised stay packed: ReLU on the packed pairs,
+  // key sums and rotation by v_dot2_f32_bf16 against a rope_words window.
+  constexpr bool PK = BF && !NRM;
 
   extern __shared__ __align__(16) unsigned char smem[];
   // Tile set in use (two sets alternate per step when double buffered).
@@ -539,6 +561,7 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? ((P2 && DH == 32 && !NRM && 
   TIn* tK = tV + TILE_ELEMS;
   TIn* tKl = tK + TILE_ELEMS;            // bf16 only
   float2* tab = reinterpret_cast<float2*>(smem + kStateTileSets * TILE_BYTES);
+  u32x4* tab16 = reinterpret_cast<u32x4*>(smem + kStateTileSets * TILE_BYTES);
 
   const int g = blockIdx.x % a.hg;
   const int ci = blockIdx.x / a.hg;
@@ -600,7 +623,8 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? ((P2 && DH == 32 && !NRM && 
   load_step(b1);
   if constexpr (PF > 2) load_step(b2);
 
-  ts.commit(tab);
+  if constexpr (PK) ts.commit16(tab16);
+  else ts.commit(tab);
   RopeLane<P2> rl, rl1;                  // rl1: the second half at head dim 64
   TokPos tp;
   if (rope_on) {
@@ -621,7 +645,43 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? ((P2 && DH == 32 && !NRM && 
   const int hb = W64 ? (w & 1) : hh;     // half of the channels feeding B (R phi(K), columns f)
   const int rbase = W64 ? 0 : th * 32;   // first token row of the wave's share of a step
 
+  auto run_step_pk = [&](const Buf& bf) {
+    u32x4 T[4], T1[4];
+    if (rope_on) {
+      rl.fetch16(tab16, tp, win, T);
+      if constexpr (W64) rl1.fetch16(tab16, tp, win, T1);
+      tp.advance(a.pos);
+    }
+    // (1, -0) and (-0, 1): literals, not inline constants (as in split8d)
+    const bf16x2 one0 = __builtin_bit_cast(bf16x2, 0x80003f80u);
+    const bf16x2 one1 = __builtin_bit_cast(bf16x2, 0x3f808000u);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x4 kp = relu_pk(bf.k[h].r[0]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x2 kb = __builtin_bit_cast(bf16x2, (uint32_t)kp[i]);
+        zacc[h][2 * i] = __builtin_amdgcn_fdot2_f32_bf16(kb, one0, zacc[h][2 * i], false);
+        zacc[h][2 * i + 1] = __builtin_amdgcn_fdot2_f32_bf16(kb, one1, zacc[h][2 * i + 1], false);
+      }
+      const int col = (h * D + 8 * lc) ^ (((lrow >> 3) & 1) << 5);
+      *reinterpret_cast<u32x4*>(tV + lrow * TCOLS + col) = bf.v[h].r[0];
+      u32x4 hi = kp, lo = {0u, 0u, 0u, 0u};
+      if (rope_on) {
+        float x[8];
+        rotate_pk(kp, (W64 && h == 1) ? T1 : T, x);
+        split8d(x, hi, lo);
+      }
+      *reinterpret_cast<u32x4*>(tK + lrow * TCOLS + col) = hi;
+      *reinterpret_cast<u32x4*>(tKl + lrow * TCOLS + col) = lo;
+    }
+  };
+
   auto run_step = [&](const Buf& bf) {
+    if constexpr (PK) {
+      run_step_pk(bf);
+      return;
+    }
     float2 cs[4], cs1[4];
     if (rope_on) {
       rl.fetch(tab, tp, win, cs);
@@ -985,7 +1045,11 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH ==
   u32x4 zh[2], zl[2];
   u32x4 Ah[NA], Al[NA];
   float As[NA][8];
+  // Tiles in LDS are split and written by one wave each (wave i mod 4).
   auto take_tile = [&](int i, const float* srow) {
+    if constexpr (A_LDS) {
+      if (w != (i & 3)) return;
+    }
     const f32x4 s0 = *reinterpret_cast<const f32x4*>(srow);
     const f32x4 s1 = *reinterpret_cast<const f32x4*>(srow + 4);
     float sv[8];
@@ -993,11 +1057,9 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH ==
     for (int k = 0; k < 4; ++k) { sv[k] = s0[k]; sv[4 + k] = s1[k]; }
     if constexpr (A_LDS) {
       u32x4 hi, lo;
-      split8(sv, hi, lo);
-      if (w == 0) {
-        lds_a[(2 * i) * 64 + lane] = hi;
-        lds_a[(2 * i + 1) * 64 + lane] = lo;
-      }
+      split8d(sv, hi, lo);
+      lds_a[(2 * i) * 64 + lane] = hi;
+      lds_a[(2 * i + 1) * 64 + lane] = lo;
     } else if constexpr (BF) {
       split8(sv, Ah[i], Al[i]);
     } else {
@@ -1014,14 +1076,16 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH ==
     const f32x4 z1 = *reinterpret_cast<const f32x4*>(zp + 4);
 #pragma unroll
     for (int i = 0; i < 4; ++i) { zb[h][i] = z0[i]; zb[h][4 + i] = z1[i]; }
-    if constexpr (FAST) {
-      split8(zb[h], zh[h], zl[h]);
-      if constexpr (Z_LDS) {
-        if (w == 0 && tl == 0) {
+    if constexpr (Z_LDS) {
+      if (w == 0) {
+        split8d(zb[h], zh[h], zl[h]);
+        if (tl == 0) {
           lds_z[(2 * h) * 4 + ch] = zh[h];
           lds_z[(2 * h + 1) * 4 + ch] = zl[h];
         }
       }
+    } else if constexpr (FAST) {
+      split8(zb[h], zh[h], zl[h]);
     }
     if constexpr (W64) {
       // this h: output rows 32h .. 32h+31 = tiles et = 2h, 2h+1
@@ -1142,7 +1206,9 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH ==
         if constexpr (RO) {
           float x[8];
           rotate_pk(qp[h], h ? T1 : T, x);
-          split8p(x, bh[h], bl[h]);
+          // (the dot2c form needs more registers: with fp32 outputs it spills)
+          if constexpr (EO == 2) split8d(x, bh[h], bl[h]);
+          else split8(x, bh[h], bl[h]);
         } else {
           bh[h] = qp[h];
         }
@@ -1188,7 +1254,7 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH ==
           float x[8];
           rotate_pk(qp, T, x);
           u32x4 bh, bl;
-          split8p(x, bh, bl);
+          split8d(x, bh, bl);
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
             const u32x4 ah = lds_a[(2 * (2 * h + hf)) * 64 + aslot];
@@ -2378,7 +2444,7 @@ int launch_forward(const Plan& p, const void* q, const void* k, const void* v, v
                    void* stream, void* const* events, const Prologue* pro) {
   hipStream_t s = (hipStream_t)stream;
   auto mark = [&](int i) -> hipError_t {
-    return events ? hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), s) : hipSuccess;
+    return events && events[i] ? hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), s) : hipSuccess;
   };
   hipError_t e = mark(0);
   if (e != hipSuccess) return (int)e;

@@ -200,3 +200,46 @@ def test_rope_window_sized_workspace(lavr):
     e = oracle.rel_err(to_f64_torch(out), oracle_fwd(cfg, arrs))
     say(f"  f32 out err {e:.3e}")
     assert e <= TOL_BF16
+
+
+def test_timed_forward_records_only_the_given_points(lavr):
+    """la_block_causal_forward_timed writes the same output as the plain forward,
+    bit for bit, whether it records all four points or only some (NULL entries
+    are skipped), and the recorded points are in stream order."""
+    import ctypes
+    cfg = rounds_cfg(frames=32)
+    say("case timed forward, all and some event points")
+    _, (q, k, v) = device_inputs(cfg, DEV)
+    rope = rope_for(lavr, cfg)
+    bf, tpf = cfg["block_frames"], cfg["tokens_per_frame"]
+    B, H, d = cfg["B"], cfg["H"], cfg["head_dim"]
+    need = lavr.workspace_bytes(B, H, cfg["frames"], tpf, bf, rope=rope)
+    ws = lavr.new_workspace(need, DEV)
+    ref = lavr.block_causal_forward(q, k, v, bf, tpf, rope, workspace=ws)
+    hip = ctypes.CDLL("libamdhip64.so")
+    evs = []
+    for _ in range(4):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        evs.append(e.value)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(DEV).cuda_stream)
+    code = lavr._dtype_code(q.dtype)
+    try:
+        for pick in ((0, 1, 2, 3), (2, 3)):
+            out = torch.empty_like(q)
+            marks = (ctypes.c_void_p * 4)(*(evs[i] if i in pick else None for i in range(4)))
+            rc = lavr.lib.la_block_causal_forward_timed(
+                *(ctypes.c_void_p(x.data_ptr()) for x in (q, k, v, out)), code, code, B, H, d,
+                cfg["frames"], tpf, bf, 0, ctypes.byref(rope.desc), 1e-8,
+                ctypes.c_void_p(ws.data_ptr()), need, stream, marks)
+            assert rc == 0, lavr.status_string(rc)
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref)
+            for a, b in zip(pick[:-1], pick[1:]):
+                ms = ctypes.c_float()
+                assert hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(evs[a]),
+                                               ctypes.c_void_p(evs[b])) == 0
+                assert ms.value >= 0.0
+    finally:
+        for e in evs:
+            hip.hipEventDestroy(ctypes.c_void_p(e))
