@@ -360,12 +360,16 @@ struct TokPos {
   }
 };
 
-// Per lookup: table index = base + fl * sf + row * sr + col * sc, where only
-// the stride of the lookup's own section is non-zero (no per-lane branches).
+// Per lookup: byte offset in the staged window = base + fl * sf + row * sr +
+// col * sc, where only the stride of the lookup's own section is non-zero (no
+// per-lane branches); ESZ is the window's entry size (8 bytes for (cos, sin)
+// pairs, 16 for rope_words), folded into base and the strides so that a
+// lookup is three 24-bit multiply-adds.
 // P2: every section has an even number of pairs, so the pairs (4c, 4c+1) and
-// (4c+2, 4c+3) share a section, sit side by side in the table, and one
-// 16-byte LDS read fetches a couple; otherwise each pair is read on its own.
-template <bool P2>
+// (4c+2, 4c+3) share a section, sit side by side in the table, and one LDS
+// read fetches a couple (two for rope_words); otherwise each pair is read on
+// its own.
+template <bool P2, int ESZ = 8>
 struct RopeLane {
   static constexpr int NL = P2 ? 2 : 4;   // lookups per lane
   int base[NL], sf[NL], sr[NL], sc[NL];
@@ -375,26 +379,32 @@ struct RopeLane {
     for (int i = 0; i < NL; ++i) {
       const int gp = 4 * c + (P2 ? 2 * i : i);
       const bool in_t = gp < r.pt, in_h = !in_t && gp < r.pt + r.ph, in_w = !in_t && !in_h;
-      base[i] = in_t ? gp : (in_h ? w.nf * r.pt + (gp - r.pt) : w.nf * r.pt + r.gh * r.ph + (gp - r.pt - r.ph));
-      sf[i] = in_t ? r.pt : 0;
-      sr[i] = in_h ? r.ph : 0;
-      sc[i] = in_w ? r.pw : 0;
+      base[i] = ESZ * (in_t ? gp : (in_h ? w.nf * r.pt + (gp - r.pt) : w.nf * r.pt + r.gh * r.ph + (gp - r.pt - r.ph)));
+      sf[i] = in_t ? ESZ * r.pt : 0;
+      sr[i] = in_h ? ESZ * r.ph : 0;
+      sc[i] = in_w ? ESZ * r.pw : 0;
     }
+  }
+
+  __device__ int off(int i, int fl, const TokPos& tp) const {
+    return __umul24(fl, sf[i]) + (__umul24(tp.row, sr[i]) + (__umul24(tp.col, sc[i]) + base[i]));
   }
 
   // (cos, sin) of the lane's 4 pairs at the token's local frame (clamped into
   // the staged window, so tokens past the range read valid rows), row and column.
   __device__ void fetch(const float2* lds, const TokPos& tp, const TabWindow& w, float2* cs) const {
+    static_assert(ESZ == 8, "a (cos, sin) window has 8-byte entries");
     const int fl = min(tp.f - w.f_lo, w.nf - 1);
+    const char* base_p = reinterpret_cast<const char*>(lds);
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      const int idx = base[i] + __umul24(fl, sf[i]) + __umul24(tp.row, sr[i]) + __umul24(tp.col, sc[i]);
+      const char* e = base_p + off(i, fl, tp);
       if constexpr (P2) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(lds + idx);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(e);
         cs[2 * i] = make_float2(v[0], v[1]);
         cs[2 * i + 1] = make_float2(v[2], v[3]);
       } else {
-        cs[i] = lds[idx];
+        cs[i] = *reinterpret_cast<const float2*>(e);
       }
     }
   }
@@ -402,15 +412,17 @@ struct RopeLane {
   // The same lookups in a table staged by stage_table16: T[p] holds the
   // rope_words of the lane's pair p.
   __device__ void fetch16(const u32x4* lds, const TokPos& tp, const TabWindow& w, u32x4* T) const {
+    static_assert(ESZ == 16, "a rope_words window has 16-byte entries");
     const int fl = min(tp.f - w.f_lo, w.nf - 1);
+    const char* base_p = reinterpret_cast<const char*>(lds);
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      const int idx = base[i] + __umul24(fl, sf[i]) + __umul24(tp.row, sr[i]) + __umul24(tp.col, sc[i]);
+      const u32x4* e = reinterpret_cast<const u32x4*>(base_p + off(i, fl, tp));
       if constexpr (P2) {
-        T[2 * i] = lds[idx];
-        T[2 * i + 1] = lds[idx + 1];
+        T[2 * i] = e[0];
+        T[2 * i + 1] = e[1];
       } else {
-        T[i] = lds[idx];
+        T[i] = e[0];
       }
     }
   }
@@ -625,7 +637,7 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? ((P2 && DH == 32 && !NRM && 
 
   if constexpr (PK) ts.commit16(tab16);
   else ts.commit(tab);
-  RopeLane<P2> rl, rl1;                  // rl1: the second half at head dim 64
+  RopeLane<P2, PK ? 16 : 8> rl, rl1;    // rl1: the second half at head dim 64
   TokPos tp;
   if (rope_on) {
     rl.init(a.rope, win, lc);
@@ -645,7 +657,7 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? ((P2 && DH == 32 && !NRM && 
   const int hb = W64 ? (w & 1) : hh;     // half of the channels feeding B (R phi(K), columns f)
   const int rbase = W64 ? 0 : th * 32;   // first token row of the wave's share of a step
 
-  auto run_step_pk = [&](const Buf& bf) {
+  auto run_step_pk = [&](const auto& bf) {   // generic: instantiated only where called
     u32x4 T[4], T1[4];
     if (rope_on) {
       rl.fetch16(tab16, tp, win, T);
@@ -677,11 +689,7 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? ((P2 && DH == 32 && !NRM && 
     }
   };
 
-  auto run_step = [&](const Buf& bf) {
-    if constexpr (PK) {
-      run_step_pk(bf);
-      return;
-    }
+  auto run_step_wide = [&](const auto& bf) {   // generic: instantiated only where called
     float2 cs[4], cs1[4];
     if (rope_on) {
       rl.fetch(tab, tp, win, cs);
@@ -711,6 +719,11 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? ((P2 && DH == 32 && !NRM && 
         dk[1] = f32x4{x[4], x[5], x[6], x[7]};
       }
     }
+  };
+
+  auto run_step = [&](const Buf& bf) {
+    if constexpr (PK) run_step_pk(bf);
+    else run_step_wide(bf);
   };
 
   auto mfma_step = [&]() {
@@ -960,7 +973,7 @@ __global__ __launch_bounds__(256) void k_prefix1(PrefixArgs a) {
 // RO: RoPE on, a compile-time switch so the loop carries no branch on it.
 
 template <typename TIn, typename TOut, bool P2, int DH, bool NRM, bool RO>
-__global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH == 32 && P2) ? 3 : 2) void k_readout(
+__global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? ((DH == 64 && sizeof(TOut) == 4) ? 3 : 4) : (!NRM && DH == 32 && P2) ? 3 : 2) void k_readout(
     ReadArgs a) {
   constexpr bool BF = sizeof(TIn) == 2;
   constexpr bool W64 = DH == 64;
@@ -1027,7 +1040,7 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH ==
   // Prologue order: rotary window, then the prefix state, then the first Q
   // loads, so that no wait before the loop drains the Q prefetch.
   TabWindow win{0, 0};
-  RopeLane<P2> rl, rl1;                  // rl1: the second half at head dim 64
+  RopeLane<P2, FAST ? 16 : 8> rl, rl1;  // rl1: the second half at head dim 64
   TokPos tp;
   if constexpr (RO) {
     if constexpr (FAST) win = stage_table16(tab16, a.rope, a.pos.t0, t0, t1, a.pos.mag_tpf);
@@ -1186,7 +1199,7 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH ==
   };
 
   // One 16-token group, packed bf16 path.
-  auto run_fast = [&](const Buf& bf) {
+  auto run_fast = [&](const auto& bf) {   // generic: instantiated only where called
     u32x4 T[4], T1[4];
     if constexpr (RO) {
       rl.fetch16(tab16, tp, win, T);
@@ -1283,7 +1296,7 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH ==
   };
 
   // One 16-token group, fp32 path (fp32 or normalised inputs).
-  auto run_wide = [&](const Buf& bf) {
+  auto run_wide = [&](const auto& bf) {   // generic: instantiated only where called
     float2 cs[4], cs1[4];
     if constexpr (RO) {
       rl.fetch(tab, tp, win, cs);
