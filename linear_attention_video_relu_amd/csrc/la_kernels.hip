@@ -472,6 +472,15 @@ __device__ __forceinline__ void rotate8(float* x, const float2* cs) {
   }
 }
 
+// Normaliser of the packed readout path: the MFMA's A operand holds zbar's hi
+// part in rows 0-7 and its lo part in rows 8-15, so lane l (rows 4(l/16)..)
+// holds hi . phi(q) below lane 32 and lo . phi(q) from lane 32 on, for token
+// l mod 16; their sum (the same in both lanes) is the token's zbar . phi(q).
+__device__ __forceinline__ float den_rows(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+
 // Sum over the four lanes l, l^16, l^32, l^48 that hold one token's chunks.
 __device__ __forceinline__ float sum4_lanes(float v) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -960,9 +969,11 @@ __global__ __launch_bounds__(256) void k_prefix1(PrefixArgs a) {
 // read as zeros and their stores are dropped by the buffer range check.
 //
 // bf16 inputs that are not normalised take the packed path: phi(q) stays
-// packed bf16 (exact) and feeds two MFMAs whose A operands repeat zbar's hi and
-// lo bf16 parts in every row, so each output lane receives its own token's
-// normaliser zbar . phi(q) with no cross-lane sum; the rotation is
+// packed bf16 (exact) and feeds the normaliser's MFMA, whose A operand holds
+// zbar's hi bf16 part in rows 0-7 and its lo part in rows 8-15 at head dim 32
+// (one MFMA per head, the two row halves added across lanes l and l ^ 32), and
+// repeats hi and lo in every row of two MFMAs at 64, so each output lane
+// receives its own token's normaliser zbar . phi(q); the rotation is
 // v_dot2_f32_bf16 on the packed pairs against the rope_words table, so phi(q)
 // is never widened.  This path spends about a third fewer VALU instructions
 // per token than widening to fp32, which matters because the kernel's time
@@ -1253,15 +1264,14 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? ((DH == 64 && size
     } else {
       // Sbar and zbar operands from LDS in every group: opaque copies of the
       // lane index and row keep the compiler from hoisting them into registers.
-      int zrow = ch, aslot = lane;
+      int zrow = ch + ((tl >> 3) << 2), aslot = lane;
       asm volatile("" : "+v"(zrow), "+v"(aslot));
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const u32x4 qp = relu_pk(bf.x[h].r[0]);
-        const u32x4 zhh = lds_z[(2 * h) * 4 + zrow], zlh = lds_z[(2 * h + 1) * 4 + zrow];
+        const u32x4 zs = lds_z[8 * h + zrow];
         f32x4 dd = {0.f, 0.f, 0.f, 0.f};
-        dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(zhh), as_bf16x8(qp), dd, 0, 0, 0);
-        dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(zlh), as_bf16x8(qp), dd, 0, 0, 0);
+        dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(zs), as_bf16x8(qp), dd, 0, 0, 0);
         f32x4 o[2];
         if constexpr (RO) {
           float x[8];
@@ -1289,7 +1299,7 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? ((DH == 64 && size
             o[hf] = cc;
           }
         }
-        emit(h, o, __builtin_amdgcn_rcpf(dd[0] + a.eps), pk);
+        emit(h, o, __builtin_amdgcn_rcpf(den_rows(dd[0]) + a.eps), pk);
       }
     }
     store_pk(pk);
