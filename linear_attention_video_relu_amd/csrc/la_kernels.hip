@@ -1788,6 +1788,11 @@ __global__ __launch_bounds__(NT, 2) void k_bw_q(BwQArgs a) {
   u32x4* ops = reinterpret_cast<u32x4*>(smem + 4 * WAVE_BYTES);   // [NB blocks][4 slots][64 lanes]
   float* zred = reinterpret_cast<float*>(ops + NB * OPS_BLOCK);    // [4 waves][2 halves][32]
   float* zl = zred + 4 * 2 * D;                                     // zbar of the block (head dim 64)
+  // bf16 at head dim 32: the normaliser zbar . phi(q) on MFMA; zbar's hi and lo
+  // bf16 parts as its A operand ([head][part][lane row], 256 bytes) take the
+  // slot that holds zbar at 64.
+  constexpr bool PKD = BF && !W64;
+  u32x4* zsel = reinterpret_cast<u32x4*>(zl);
   float2* tab = reinterpret_cast<float2*>(zl + 2 * D);
   float* red = reinterpret_cast<float*>(smem);       // after the loop, over tiles + operands
 
@@ -1844,6 +1849,14 @@ __global__ __launch_bounds__(NT, 2) void k_bw_q(BwQArgs a) {
       const float* zp = (h == 0 ? rec0 : rec1) + D * D;
 #pragma unroll
       for (int i = 0; i < 8; ++i) zb[h][i] = zp[8 * ch + i];
+      if constexpr (PKD) {
+        if (w == 0 && tl == 0) {
+          u32x4 hi, lo;
+          split8d(zb[h], hi, lo);
+          zsel[(2 * h) * 4 + ch] = hi;
+          zsel[(2 * h + 1) * 4 + ch] = lo;
+        }
+      }
     }
   }
 
@@ -1928,6 +1941,11 @@ __global__ __launch_bounds__(NT, 2) void k_bw_q(BwQArgs a) {
     // u = Sbar^T g per output half (at 64 both input halves contribute), then
     // u . r and z . phi(q)
     float u[2][8], ur[2], den_h[2];
+    // PKD: a lane's A operand is zbar's hi part for output rows 0-7 (tl < 8)
+    // and its lo part for rows 8-15; an opaque copy of the row index keeps the
+    // compiler from hoisting the reads into registers.
+    int zrow = ch + ((tl >> 3) << 2);
+    if constexpr (PKD) asm volatile("" : "+v"(zrow));
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       f32x4 cc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -1940,9 +1958,15 @@ __global__ __launch_bounds__(NT, 2) void k_bw_q(BwQArgs a) {
       ur[h] = 0.f;
       den_h[h] = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        ur[h] += u[h][i] * rr[h][i];
-        den_h[h] += zb[h][i] * p[h][i];
+      for (int i = 0; i < 8; ++i) ur[h] += u[h][i] * rr[h][i];
+      if constexpr (PKD) {
+        const f32x4 dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(zsel[8 * h + zrow]),
+                                                                 as_bf16x8(relu_pk(bf.q[h].r[0])),
+                                                                 f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        den_h[h] = den_rows(dd[0]);             // the whole head's sum
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) den_h[h] += zb[h][i] * p[h][i];
       }
     }
     // 1/den and beta: per head at 32, over both halves at 64 (v_rcp_f32, as in the readout)
@@ -1957,7 +1981,7 @@ __global__ __launch_bounds__(NT, 2) void k_bw_q(BwQArgs a) {
     } else {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const float dsum = sum4_lanes(den_h[h]), usum = sum4_lanes(ur[h]);
+        const float dsum = PKD ? den_h[h] : sum4_lanes(den_h[h]), usum = sum4_lanes(ur[h]);
         inv[h] = live ? __builtin_amdgcn_rcpf(dsum + a.eps) : 0.f;
         beta[h] = -usum * (inv[h] * inv[h]);
       }
@@ -1971,7 +1995,7 @@ __global__ __launch_bounds__(NT, 2) void k_bw_q(BwQArgs a) {
       for (int i = 0; i < 8; ++i) rs[i] = rr[h][i] * inv[h];
       if constexpr (BF) {
         u32x4 hi, lo;
-        split8(rs, hi, lo);
+        split8d(rs, hi, lo);
         tile_put16(1, h, hi);
         tile_put16(2, h, lo);
       } else {
