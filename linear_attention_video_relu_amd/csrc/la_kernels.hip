@@ -46,7 +46,7 @@ namespace {
 constexpr int D = 32;                // channels of one lane chunk's half (a head at head dim 32)
 constexpr int NT = 256;              // threads of the state and readout workgroups
 constexpr int kReadAlBytes = 2 * 8 * 64 * 16;   // head dim 64, bf16: Sbar hi and lo tiles of a readout workgroup
-constexpr int kReadZBytes = 2 * 2 * 4 * 16;     // head dim 32, packed path: zbar hi and lo slices of a readout workgroup
+constexpr int kReadZBytes = 2 * 2 * 4 * 16;     // packed path: zbar hi and lo slices of a readout workgroup (2 heads or halves)
 constexpr int STEP = 64;             // tokens per step of the state kernel
 constexpr int TCOLS = 2 * D;         // an LDS tile row holds two heads
 constexpr int RSRC_WORD3 = 0x00020000;  // gfx9 raw buffer: 32-bit data, range checked
@@ -472,10 +472,10 @@ __device__ __forceinline__ void rotate8(float* x, const float2* cs) {
   }
 }
 
-// Normaliser of the packed readout path: the MFMA's A operand holds zbar's hi
-// part in rows 0-7 and its lo part in rows 8-15, so lane l (rows 4(l/16)..)
-// holds hi . phi(q) below lane 32 and lo . phi(q) from lane 32 on, for token
-// l mod 16; their sum (the same in both lanes) is the token's zbar . phi(q).
+// Normaliser of the packed paths: the MFMA's A operand holds zbar's hi part in
+// rows 0-7 and its lo part in rows 8-15, so lane l (rows 4(l/16)..) holds
+// hi . phi(q) below lane 32 and lo . phi(q) from lane 32 on, for token l mod
+// 16; their sum (the same in both lanes) is the token's zbar . phi(q).
 __device__ __forceinline__ float den_rows(float v) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(a[0]) + __uint_as_float(a[1]);
@@ -969,11 +969,11 @@ __global__ __launch_bounds__(256) void k_prefix1(PrefixArgs a) {
 // read as zeros and their stores are dropped by the buffer range check.
 //
 // bf16 inputs that are not normalised take the packed path: phi(q) stays
-// packed bf16 (exact) and feeds the normaliser's MFMA, whose A operand holds
-// zbar's hi bf16 part in rows 0-7 and its lo part in rows 8-15 at head dim 32
-// (one MFMA per head, the two row halves added across lanes l and l ^ 32), and
-// repeats hi and lo in every row of two MFMAs at 64, so each output lane
-// receives its own token's normaliser zbar . phi(q); the rotation is
+// packed bf16 (exact) and feeds the normaliser's MFMA, whose A operand (from
+// LDS) holds zbar's hi bf16 part in rows 0-7 and its lo part in rows 8-15 (one
+// MFMA per 32-channel half; the two row halves are added across lanes l and
+// l ^ 32), so each output lane receives its own token's normaliser
+// zbar . phi(q); the rotation is
 // v_dot2_f32_bf16 on the packed pairs against the rope_words table, so phi(q)
 // is never widened.  This path spends about a third fewer VALU instructions
 // per token than widening to fp32, which matters because the kernel's time
@@ -984,7 +984,7 @@ __global__ __launch_bounds__(256) void k_prefix1(PrefixArgs a) {
 // RO: RoPE on, a compile-time switch so the loop carries no branch on it.
 
 template <typename TIn, typename TOut, bool P2, int DH, bool NRM, bool RO>
-__global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? ((DH == 64 && sizeof(TOut) == 4) ? 3 : 4) : (!NRM && DH == 32 && P2) ? 3 : 2) void k_readout(
+__global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH == 32 && P2) ? 3 : 2) void k_readout(
     ReadArgs a) {
   constexpr bool BF = sizeof(TIn) == 2;
   constexpr bool W64 = DH == 64;
@@ -995,11 +995,11 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? ((DH == 64 && size
   extern __shared__ __align__(16) unsigned char smem[];
   // bf16 at head dim 64, and the packed path: the hi and lo parts of the Sbar
   // tiles live in LDS (one copy per workgroup, lane-major: slot (2 i + part) *
-  // 64 + lane), and on the packed path at head dim 32 zbar's bf16 parts too
-  // ([head][part][lane row] slices), which keeps the kernel within 128
-  // registers without spills.
+  // 64 + lane), and on the packed path zbar's bf16 parts too ([head or half]
+  // [part][lane row] slices), which keeps the kernel within 128 registers
+  // without spills.
   constexpr bool A_LDS = BF && (W64 || FAST);
-  constexpr bool Z_LDS = FAST && !W64;
+  constexpr bool Z_LDS = FAST;
   constexpr int A_BYTES = A_LDS ? 2 * NA * 64 * 16 : 0;
   constexpr int PRE = A_BYTES + (Z_LDS ? kReadZBytes : 0);
   u32x4* lds_a = reinterpret_cast<u32x4*>(smem);
@@ -1108,8 +1108,6 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? ((DH == 64 && size
           lds_z[(2 * h + 1) * 4 + ch] = zl[h];
         }
       }
-    } else if constexpr (FAST) {
-      split8(zb[h], zh[h], zl[h]);
     }
     if constexpr (W64) {
       // this h: output rows 32h .. 32h+31 = tiles et = 2h, 2h+1
@@ -1219,14 +1217,17 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? ((DH == 64 && size
     }
     u32x4 pk[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
     if constexpr (W64) {
-      // one head: den over both halves, every output tile from both halves
+      // one head: den over both halves, every output tile from both halves;
+      // the normaliser's A operand holds zbar's hi part in rows 0-7 and its lo
+      // part in rows 8-15 (one MFMA per half, read from LDS)
       u32x4 qp[2], bh[2], bl[2];
       f32x4 dd = {0.f, 0.f, 0.f, 0.f};
+      int zrow = ch + ((tl >> 3) << 2);
+      asm volatile("" : "+v"(zrow));
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         qp[h] = relu_pk(bf.x[h].r[0]);
-        dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(zh[h]), as_bf16x8(qp[h]), dd, 0, 0, 0);
-        dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(zl[h]), as_bf16x8(qp[h]), dd, 0, 0, 0);
+        dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(lds_z[8 * h + zrow]), as_bf16x8(qp[h]), dd, 0, 0, 0);
         if constexpr (RO) {
           float x[8];
           rotate_pk(qp[h], h ? T1 : T, x);
@@ -1237,7 +1238,7 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? ((DH == 64 && size
           bh[h] = qp[h];
         }
       }
-      const float inv = __builtin_amdgcn_rcpf(dd[0] + a.eps);
+      const float inv = __builtin_amdgcn_rcpf(den_rows(dd[0]) + a.eps);
       // The Sbar operands are read from LDS in every group: an opaque copy of
       // the lane index keeps the compiler from hoisting them into registers.
       int aslot = lane;
@@ -2556,7 +2557,8 @@ int launch_forward(const Plan& p, const void* q, const void* k, const void* v, v
   // bytes per pair instead of 8)
   const bool packed = in_bf16 && !nq;
   const int lds_tab = packed ? p.lds_read16 : p.lds_read;
-  e = p.D == 64 ? launch_readouts<64>(ra, in_bf16, out_bf16, p2, gr, lds_tab + (in_bf16 ? kReadAlBytes : 0), s)
+  e = p.D == 64 ? launch_readouts<64>(ra, in_bf16, out_bf16, p2, gr,
+                                     lds_tab + (in_bf16 ? kReadAlBytes : 0) + (packed ? kReadZBytes : 0), s)
                 : launch_readouts<32>(ra, in_bf16, out_bf16, p2, gr,
                                       lds_tab + (packed ? kReadAlBytes / 2 + kReadZBytes : 0), s);
   if (e == hipSuccess) e = mark(3);
