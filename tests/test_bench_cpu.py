@@ -57,3 +57,19 @@ def test_digest_covers_the_kernel_sources():
     d = bench.kernel_source_digest()
     assert re.fullmatch(r"[0-9a-f]{64}", d)
     assert set(bench.KERNEL_SOURCES) == {"la_kernels.hip", "la_internal.h", "la_api.cpp"}
+
+
+def test_cpu_baseline_reports_the_oracle_and_the_host():
+    """The cpu_baseline object of the bench line: the oracle timed on a bounded
+    sample, with the worker count, the host's core count and CPU model beside it."""
+    from linear_attention_video_relu_amd import workloads as W
+    cfg = W.workload("tiny_f32")
+    arrs = {x: W.draw(cfg, x) for x in W.TENSORS}
+    r = bench.cpu_baseline(cfg, arrs, 2)
+    assert r["kind"] == "oracle"
+    assert r["unit"] == "tokens·heads/s" and r["value"] > 0
+    assert r["workers"] == r["cores"] == min(2, r["host_cores"], bench.MAX_CPU_WORKERS)
+    assert r["host_cores"] == len(os.sched_getaffinity(0))
+    assert r["cpu_model"] is None or isinstance(r["cpu_model"], str)
+    assert "2 of 2 (batch, head) streams of tiny_f32" in r["sample"]
+    assert r["cpu_seconds"] >= 0 and r["wall_seconds"] > 0
