@@ -179,6 +179,7 @@ int make_plan(Plan* p, int B, int H, int head_dim, int frames, int tpf, int bloc
   const int tiles = (in_dt == LA_BF16 ? 3 : 2) * kStep * 64 * esize(in_dt);   // 64 channels per row
   p->tab_state = (int)(tab_pairs(rope, tpf, p->Tc) * 8);
   p->lds_state = lavr::kStateTileSets * tiles + (int)(tab_pairs(rope, tpf, p->Tc) * state_entry);
+  p->lds_state1 = tiles + (int)(tab_pairs(rope, tpf, p->Tc) * state_entry);
   p->lds_read = (int)(tab_pairs(rope, tpf, p->Tr) * 8);
   p->lds_read16 = 2 * p->lds_read;
 

@@ -52,6 +52,7 @@ struct Plan {
   uint64_t mag_gw;      // floor(2^42 / gw_div) + 1
   RopeDev rope;
   int lds_state;        // dynamic LDS bytes of the block-state kernel
+  int lds_state1;       // the same with one tile set (single-round launches)
   int tab_state;        // of which the rotary window of a chunk
   int lds_read;         // dynamic LDS bytes of the readout kernel's rotary window ((cos, sin) pairs)
   int lds_read16;       // the same window as rope_words (16 bytes per pair)

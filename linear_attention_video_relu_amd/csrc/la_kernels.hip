@@ -560,8 +560,10 @@ struct TabStage {
 // swapped, so the two half-waves read disjoint LDS banks.  Tokens past the
 // chunk read as zeros (buffer range check) and add nothing.
 
-template <typename TIn, bool P2, int DH, bool NRM>
-__global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? ((P2 && DH == 32 && !NRM && kStateTileSets == 1) ? 4 : (NRM && DH == 64) ? 2 : 3) : 2) void k_block_state(StateArgs a) {
+// TS: LDS tile sets (2: double buffered, one barrier per step; 1: single
+// buffered, so that more workgroups fit per CU for launches of one round).
+template <typename TIn, bool P2, int DH, bool NRM, int TS>
+__global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? ((P2 && DH == 32 && !NRM && TS == 1) ? 4 : (NRM && DH == 64) ? 2 : 3) : 2) void k_block_state(StateArgs a) {
   constexpr bool BF = sizeof(TIn) == 2;
   constexpr bool W64 = DH == 64;
   constexpr int RECN = DH * DH + DH;
@@ -581,8 +583,8 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? ((P2 && DH == 32 && !NRM && 
   TIn* tV = reinterpret_cast<TIn*>(smem);
   TIn* tK = tV + TILE_ELEMS;
   TIn* tKl = tK + TILE_ELEMS;            // bf16 only
-  float2* tab = reinterpret_cast<float2*>(smem + kStateTileSets * TILE_BYTES);
-  u32x4* tab16 = reinterpret_cast<u32x4*>(smem + kStateTileSets * TILE_BYTES);
+  float2* tab = reinterpret_cast<float2*>(smem + TS * TILE_BYTES);
+  u32x4* tab16 = reinterpret_cast<u32x4*>(smem + TS * TILE_BYTES);
 
   const int g = blockIdx.x % a.hg;
   const int ci = blockIdx.x / a.hg;
@@ -779,7 +781,7 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? ((P2 && DH == 32 && !NRM && 
     __syncthreads();
     load_step(bf);
     mfma_step();
-    if constexpr (kStateTileSets == 2) {
+    if constexpr (TS == 2) {
       const int off = (tV == reinterpret_cast<TIn*>(smem)) ? TILE_BYTES : 0;
       tV = reinterpret_cast<TIn*>(smem + off);
       tK = tV + TILE_ELEMS;
@@ -794,7 +796,7 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? ((P2 && DH == 32 && !NRM && 
     if constexpr (PF > 2) one_step(b2);
   }
 
-  if constexpr (kStateTileSets == 2) __syncthreads();   // last MFMA reads before red reuses the tiles
+  if constexpr (TS == 2) __syncthreads();   // last MFMA reads before red reuses the tiles
 
   // Head dim 32: combine the two waves of each head through LDS.  Key sums:
   // first across the 16 lanes of a wave that hold the same channel chunk
@@ -2350,18 +2352,27 @@ hipError_t launch_readout(const ReadArgs& ra, bool p2, dim3 grid, int lds, hipSt
 }
 
 template <int DH, bool NRM>
-hipError_t launch_state_n(const StateArgs& sa, bool in_bf16, bool p2, dim3 grid, int lds, hipStream_t s) {
-  if (in_bf16 && p2) hipLaunchKernelGGL((k_block_state<uint16_t, true, DH, NRM>), grid, dim3(NT), lds, s, sa);
-  else if (in_bf16) hipLaunchKernelGGL((k_block_state<uint16_t, false, DH, NRM>), grid, dim3(NT), lds, s, sa);
-  else if (p2) hipLaunchKernelGGL((k_block_state<float, true, DH, NRM>), grid, dim3(NT), lds, s, sa);
-  else hipLaunchKernelGGL((k_block_state<float, false, DH, NRM>), grid, dim3(NT), lds, s, sa);
+hipError_t launch_state_n(const StateArgs& sa, bool in_bf16, bool p2, dim3 grid, int lds, int lds1, hipStream_t s) {
+  // Packed bf16 at head dim 32: a launch of at most one round at four
+  // workgroups per CU takes single-buffered tiles (lds1 bytes), so that it runs
+  // as one round; longer launches keep two tile sets per workgroup.
+  if constexpr (DH == 32 && !NRM) {
+    if (in_bf16 && p2 && (long long)grid.x * grid.y <= 4LL * 256) {
+      hipLaunchKernelGGL((k_block_state<uint16_t, true, DH, NRM, 1>), grid, dim3(NT), lds1, s, sa);
+      return hipGetLastError();
+    }
+  }
+  if (in_bf16 && p2) hipLaunchKernelGGL((k_block_state<uint16_t, true, DH, NRM, kStateTileSets>), grid, dim3(NT), lds, s, sa);
+  else if (in_bf16) hipLaunchKernelGGL((k_block_state<uint16_t, false, DH, NRM, kStateTileSets>), grid, dim3(NT), lds, s, sa);
+  else if (p2) hipLaunchKernelGGL((k_block_state<float, true, DH, NRM, kStateTileSets>), grid, dim3(NT), lds, s, sa);
+  else hipLaunchKernelGGL((k_block_state<float, false, DH, NRM, kStateTileSets>), grid, dim3(NT), lds, s, sa);
   return hipGetLastError();
 }
 
 template <int DH>
-hipError_t launch_state(const StateArgs& sa, bool in_bf16, bool p2, dim3 grid, int lds, hipStream_t s) {
-  return sa.scale != nullptr ? launch_state_n<DH, true>(sa, in_bf16, p2, grid, lds, s)
-                             : launch_state_n<DH, false>(sa, in_bf16, p2, grid, lds, s);
+hipError_t launch_state(const StateArgs& sa, bool in_bf16, bool p2, dim3 grid, int lds, int lds1, hipStream_t s) {
+  return sa.scale != nullptr ? launch_state_n<DH, true>(sa, in_bf16, p2, grid, lds, lds1, s)
+                             : launch_state_n<DH, false>(sa, in_bf16, p2, grid, lds, lds1, s);
 }
 
 template <int DH, bool NRM>
@@ -2531,8 +2542,8 @@ int launch_forward(const Plan& p, const void* q, const void* k, const void* v, v
   prefix_fingerprint(p, k, v, in_bf16, nk ? pro : nullptr, &sa.fp0, &sa.fp1);
   const dim3 gs((unsigned)(p.hg * p.nb * p.cpb), (unsigned)p.B);
   const bool p2 = ((p.rope.pt | p.rope.ph | p.rope.pw) & 1) == 0;
-  e = p.D == 64 ? launch_state<64>(sa, in_bf16, p2, gs, p.lds_state, s)
-                : launch_state<32>(sa, in_bf16, p2, gs, p.lds_state, s);
+  e = p.D == 64 ? launch_state<64>(sa, in_bf16, p2, gs, p.lds_state, p.lds_state1, s)
+                : launch_state<32>(sa, in_bf16, p2, gs, p.lds_state, p.lds_state1, s);
   if (e == hipSuccess) e = mark(1);
   if (e != hipSuccess) return (int)e;
 
@@ -2626,8 +2637,8 @@ int launch_backward(const Plan& p, const void* q, const void* k, const void* v, 
   pa.S_save = nullptr; pa.z_save = nullptr; pa.H = p.H; pa.nb = p.nb; pa.cpb = p.cpb;
   pa.hd = p.D; pa.rec = p.rec; pa.rev = 0;
   if (!have_prefix) {
-    e = p.D == 64 ? launch_state<64>(sa, in_bf16, p2, gs, p.lds_state, s)
-                  : launch_state<32>(sa, in_bf16, p2, gs, p.lds_state, s);
+    e = p.D == 64 ? launch_state<64>(sa, in_bf16, p2, gs, p.lds_state, p.lds_state1, s)
+                  : launch_state<32>(sa, in_bf16, p2, gs, p.lds_state, p.lds_state1, s);
     if (e == hipSuccess) e = launch_prefix(pa, p, s);
     if (e != hipSuccess) return (int)e;
   }
