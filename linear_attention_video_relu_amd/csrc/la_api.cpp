@@ -35,7 +35,9 @@ namespace {
 constexpr int kStateMax = LAVR_STATE_MAX;
 constexpr int kReadMax = LAVR_READ_MAX;
 constexpr int kMinWg = LAVR_MIN_WG;
-constexpr long long kReadSlots = 4 * 256;   // readout workgroups resident at once (4 per CU)
+// readout workgroups resident at once on the packed path: kReadOcc per CU at
+// head dim 32, four (register-bound) at 64
+constexpr long long kReadSlots32 = lavr::kReadOcc * 256, kReadSlots64 = 4 * 256;
 constexpr int kTabLdsMax = 32768;      // LDS bytes for a staged rotary window ((cos, sin) pairs)
 constexpr int kTabLdsMax16 = 49152;    // the same for a readout tile's rope_words (with the 16 KB Sbar
                                        // copy at head dim 64, at most 64 KB per workgroup)
@@ -162,7 +164,7 @@ int make_plan(Plan* p, int B, int H, int head_dim, int frames, int tpf, int bloc
     return LA_ERR_UNSUPPORTED;
   if (!split_block(Lmax, kReadMax, min_n, 64, rope, tpf, row_bytes, 16, kTabLdsMax16, &p->rpb, &p->Tr))
     return LA_ERR_UNSUPPORTED;
-  fit_rounds(Lmax, kReadMax, (long long)B * p->hg * p->nb, kReadSlots, 64, rope, tpf, row_bytes, 16, kTabLdsMax16,
+  fit_rounds(Lmax, kReadMax, (long long)B * p->hg * p->nb, head_dim == 32 ? kReadSlots32 : kReadSlots64, 64, rope, tpf, row_bytes, 16, kTabLdsMax16,
              &p->rpb, &p->Tr);
   if ((long long)p->hg * p->nb * p->cpb > 0x7fffffffLL || (long long)p->hg * p->nb * p->rpb > 0x7fffffffLL)
     return LA_ERR_UNSUPPORTED;

@@ -24,6 +24,21 @@ constexpr size_t kWsHeader = 256;
 #endif
 constexpr int kStateTileSets = LAVR_STATE_DB == 2 ? 2 : 1;
 
+// Readout workgroups resident per CU on the packed bf16 path at head dim 32.
+// Its registers allow four; the launch asks for enough LDS that only kReadOcc
+// fit, because the readout streams Q in and the output out at once, and with
+// three per CU the HBM serves that mix faster than with four (fewer requests
+// in flight).  At head dim 64 four per CU measured faster, so that launch
+// keeps its register-bound occupancy.
+#ifndef LAVR_READ_OCC
+#define LAVR_READ_OCC 3
+#endif
+constexpr int kReadOcc = LAVR_READ_OCC;
+constexpr int kCuLds = 160 * 1024;   // LDS bytes per CU (gfx950)
+// Dynamic LDS floor of a packed readout workgroup: one more would not fit.
+constexpr int kReadOccLds = kCuLds / (kReadOcc + 1) + 256;
+static_assert(kReadOcc * kReadOccLds <= kCuLds, "readout occupancy floor");
+
 // Rotary table as the kernels see it.
 struct RopeDev {
   const float* table;   // (cos, sin) pairs; nullptr = RoPE off

@@ -1050,78 +1050,48 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH ==
   const int o_pair = (two || tl < 8) ? (tl & 7) * RO_ + ((tl >> 3) * D + co) * EO : kDrop;
   const int o_half1 = two ? D * EO : kDrop;   // fp32 stores: offset of half 1
 
-  // Prologue order: rotary window, then the prefix state, then the first Q
-  // loads, so that no wait before the loop drains the Q prefetch.
-  TabWindow win{0, 0};
+  // Prologue: the rotary window and the prefix record (zbar and the Sbar
+  // tiles) are loaded together, so that their latencies overlap, and the
+  // first Q groups follow once both are in LDS.  (Issuing the Q loads before
+  // those waits measured slower at the minute-length workload.)
+  TabStage ts;
+  if constexpr (RO) ts.issue(a.rope, a.pos.t0, t0, t1, a.pos.mag_tpf);
+  else ts.w = TabWindow{0, 0};
+  const TabWindow win = ts.w;
   RopeLane<P2, FAST ? 16 : 8> rl, rl1;  // rl1: the second half at head dim 64
-  TokPos tp;
-  if constexpr (RO) {
-    if constexpr (FAST) win = stage_table16(tab16, a.rope, a.pos.t0, t0, t1, a.pos.mag_tpf);
-    else win = stage_table(tab, a.rope, a.pos.t0, t0, t1, a.pos.mag_tpf);
-    rl.init(a.rope, win, ch);
-    if constexpr (W64) rl1.init(a.rope, win, ch + 4);
-    tp.init(t0 + w * 16 + tl, a.pos);
-  }
 
   // Key-sum slices zb[h] (channels 32h + 8ch .. +7 of the half's z; packed
   // path: their bf16 parts zh, zl) and Sbar tiles.  Head dim 32: tile 2h + hf
   // = rows 16hf + tl, channels 8ch .. +7 of head h.  Head dim 64: tile
   // 2et + kt = rows 16et + tl, channels 32kt + 8ch .. +7.
-  float zb[2][8];
-  u32x4 zh[2], zl[2];
-  u32x4 Ah[NA], Al[NA];
-  float As[NA][8];
-  // Tiles in LDS are split and written by one wave each (wave i mod 4).
-  auto take_tile = [&](int i, const float* srow) {
-    if constexpr (A_LDS) {
-      if (w != (i & 3)) return;
-    }
-    const f32x4 s0 = *reinterpret_cast<const f32x4*>(srow);
-    const f32x4 s1 = *reinterpret_cast<const f32x4*>(srow + 4);
-    float sv[8];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) { sv[k] = s0[k]; sv[4 + k] = s1[k]; }
-    if constexpr (A_LDS) {
-      u32x4 hi, lo;
-      split8d(sv, hi, lo);
-      lds_a[(2 * i) * 64 + lane] = hi;
-      lds_a[(2 * i + 1) * 64 + lane] = lo;
-    } else if constexpr (BF) {
-      split8(sv, Ah[i], Al[i]);
-    } else {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) As[i][k] = sv[k];
-    }
-  };
+  const float* pre[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int hd = W64 ? 0 : min(h, nh - 1);
-    const float* pre = a.prefix + ((size_t)(b * a.H + h0 + hd) * a.nb + j) * RECN;
-    const float* zp = pre + DH * DH + (W64 ? h * D : 0) + 8 * ch;
-    const f32x4 z0 = *reinterpret_cast<const f32x4*>(zp);
-    const f32x4 z1 = *reinterpret_cast<const f32x4*>(zp + 4);
+    pre[h] = a.prefix + ((size_t)(b * a.H + h0 + hd) * a.nb + j) * RECN;
+  }
+  auto tile_src = [&](int i) -> const float* {
+    if constexpr (W64) return pre[0] + (16 * (i >> 1) + tl) * DH + (i & 1) * D + 8 * ch;
+    else return ((i >> 1) ? pre[1] : pre[0]) + (16 * (i & 1) + tl) * D + 8 * ch;
+  };
+  float zb[2][8];
+  f32x4 zr[2][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { zb[h][i] = z0[i]; zb[h][4 + i] = z1[i]; }
-    if constexpr (Z_LDS) {
-      if (w == 0) {
-        split8d(zb[h], zh[h], zl[h]);
-        if (tl == 0) {
-          lds_z[(2 * h) * 4 + ch] = zh[h];
-          lds_z[(2 * h + 1) * 4 + ch] = zl[h];
-        }
-      }
-    }
-    if constexpr (W64) {
-      // this h: output rows 32h .. 32h+31 = tiles et = 2h, 2h+1
+  for (int h = 0; h < 2; ++h) {
+    const float* zp = pre[h] + DH * DH + (W64 ? h * D : 0) + 8 * ch;
+    zr[h][0] = *reinterpret_cast<const f32x4*>(zp);
+    zr[h][1] = *reinterpret_cast<const f32x4*>(zp + 4);
+  }
+  // Tiles in LDS are split and written by one wave each (wave i mod 4), so a
+  // wave loads only tiles w, w + 4, ...; register tiles are loaded by every wave.
+  constexpr int NL = A_LDS ? NA / 4 : NA;
+  auto tile_of = [&](int m) { return A_LDS ? w + 4 * m : m; };
+  f32x4 tr[NL][2];
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-          take_tile((2 * h + hf) * 2 + kt, pre + (16 * (2 * h + hf) + tl) * DH + kt * D + 8 * ch);
-    } else {
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) take_tile(2 * h + hf, pre + (16 * hf + tl) * D + 8 * ch);
-    }
+  for (int m = 0; m < NL; ++m) {
+    const float* src = tile_src(tile_of(m));
+    tr[m][0] = *reinterpret_cast<const f32x4*>(src);
+    tr[m][1] = *reinterpret_cast<const f32x4*>(src + 4);
   }
 
   // Normalised q: token scales of the tile (0 past it) and the lane's weights.
@@ -1154,6 +1124,49 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH ==
   constexpr int RPF = BF ? LAVR_READ_PF : 2;
   static_assert(RPF == 2 || RPF == 3, "readout prefetch depth: two or three buffers");
   Buf b0, b1, b2;
+
+  // The waits, oldest loads first: the window, then the record.
+  TokPos tp;
+  if constexpr (RO) {
+    if constexpr (FAST) ts.commit16(tab16);
+    else ts.commit(tab);
+    rl.init(a.rope, win, ch);
+    if constexpr (W64) rl1.init(a.rope, win, ch + 4);
+    tp.init(t0 + w * 16 + tl, a.pos);
+  }
+  u32x4 zh[2], zl[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { zb[h][i] = zr[h][0][i]; zb[h][4 + i] = zr[h][1][i]; }
+    if constexpr (Z_LDS) {
+      split8d(zb[h], zh[h], zl[h]);
+      if (w == 0 && tl == 0) {
+        lds_z[(2 * h) * 4 + ch] = zh[h];
+        lds_z[(2 * h + 1) * 4 + ch] = zl[h];
+      }
+    }
+  }
+  u32x4 Ah[NA], Al[NA];
+  float As[NA][8];
+#pragma unroll
+  for (int m = 0; m < NL; ++m) {
+    float sv[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) { sv[k] = tr[m][0][k]; sv[4 + k] = tr[m][1][k]; }
+    if constexpr (A_LDS) {
+      const int i = tile_of(m);
+      u32x4 hi, lo;
+      split8d(sv, hi, lo);
+      lds_a[(2 * i) * 64 + lane] = hi;
+      lds_a[(2 * i + 1) * 64 + lane] = lo;
+    } else if constexpr (BF) {
+      split8(sv, Ah[m], Al[m]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) As[m][k] = sv[k];
+    }
+  }
   load_group(b0);
   load_group(b1);
   if constexpr (RPF > 2) load_group(b2);
@@ -2497,6 +2510,10 @@ void prefix_fingerprint(const Plan& p, const void* k, const void* v, int in_bf16
   *f1 = b.h;
 }
 
+// Dynamic LDS of a readout launch: the packed path at head dim 32 asks for at
+// least the occupancy floor, so that kReadOcc workgroups share a CU.
+int read_lds(bool floor, int bytes) { return floor && bytes < kReadOccLds ? kReadOccLds : bytes; }
+
 int launch_forward(const Plan& p, const void* q, const void* k, const void* v, void* out,
                    int in_bf16, int out_bf16, float eps, void* ws,
                    const float* S_init, const float* z_init, float* S_save, float* z_save,
@@ -2569,9 +2586,9 @@ int launch_forward(const Plan& p, const void* q, const void* k, const void* v, v
   const bool packed = in_bf16 && !nq;
   const int lds_tab = packed ? p.lds_read16 : p.lds_read;
   e = p.D == 64 ? launch_readouts<64>(ra, in_bf16, out_bf16, p2, gr,
-                                     lds_tab + (in_bf16 ? kReadAlBytes : 0) + (packed ? kReadZBytes : 0), s)
+                                     read_lds(false, lds_tab + (in_bf16 ? kReadAlBytes : 0) + (packed ? kReadZBytes : 0)), s)
                 : launch_readouts<32>(ra, in_bf16, out_bf16, p2, gr,
-                                      lds_tab + (packed ? kReadAlBytes / 2 + kReadZBytes : 0), s);
+                                      read_lds(packed, lds_tab + (packed ? kReadAlBytes / 2 + kReadZBytes : 0)), s);
   if (e == hipSuccess) e = mark(3);
   return (int)e;
 }
