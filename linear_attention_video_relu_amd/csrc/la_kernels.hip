@@ -294,21 +294,6 @@ struct TabWindow {
   int nf;     // frames staged
 };
 
-__device__ __forceinline__ TabWindow stage_table(float2* lds, const RopeDev& r, long long t0,
-                                                 int n0, int n1, uint64_t mag_tpf) {
-  TabWindow w{0, 0};
-  if (r.table == nullptr || n1 <= n0) return w;
-  w.f_lo = (int)fast_div((uint32_t)n0, mag_tpf);
-  w.nf = (int)fast_div((uint32_t)(n1 - 1), mag_tpf) - w.f_lo + 1;
-  const float2* tab = reinterpret_cast<const float2*>(r.table);
-  const float2* tsrc = tab + (size_t)(t0 + w.f_lo) * r.pt;
-  const float2* hwsrc = tab + (size_t)r.max_frames * r.pt;
-  const int nt = w.nf * r.pt;
-  const int tot = nt + r.gh * r.ph + r.gw * r.pw;
-  for (int i = threadIdx.x; i < tot; i += blockDim.x) lds[i] = i < nt ? tsrc[i] : hwsrc[i - nt];
-  return w;
-}
-
 // Rotary entry for rotating a packed bf16 pair (a, b) = (x_2i, x_2i+1) with
 // v_dot2_f32_bf16 (exact bf16 products, fp32 sum).  cos and sin are split into
 // bf16 parts c = ch + cl, s = sh + sl (ch, sh rounded to nearest, cl, sl the
@@ -321,22 +306,6 @@ __device__ __forceinline__ u32x4 rope_words(float2 cs) {
   const float ch = bf16_round(cs.x), sh = bf16_round(cs.y);
   const float cl = cs.x - ch, sl = cs.y - sh;
   return u32x4{pack_bf16(ch, -sh), pack_bf16(cl, -sl), pack_bf16(sh, ch), pack_bf16(sl, cl)};
-}
-
-// stage_table with every (cos, sin) pair stored as its four rope_words.
-__device__ __forceinline__ TabWindow stage_table16(u32x4* lds, const RopeDev& r, long long t0,
-                                                   int n0, int n1, uint64_t mag_tpf) {
-  TabWindow w{0, 0};
-  if (r.table == nullptr || n1 <= n0) return w;
-  w.f_lo = (int)fast_div((uint32_t)n0, mag_tpf);
-  w.nf = (int)fast_div((uint32_t)(n1 - 1), mag_tpf) - w.f_lo + 1;
-  const float2* tab = reinterpret_cast<const float2*>(r.table);
-  const float2* tsrc = tab + (size_t)(t0 + w.f_lo) * r.pt;
-  const float2* hwsrc = tab + (size_t)r.max_frames * r.pt;
-  const int nt = w.nf * r.pt;
-  const int tot = nt + r.gh * r.ph + r.gw * r.pw;
-  for (int i = threadIdx.x; i < tot; i += blockDim.x) lds[i] = rope_words(i < nt ? tsrc[i] : hwsrc[i - nt]);
-  return w;
 }
 
 // (frame, row, col) of a lane's token, advanced 64 tokens at a time without
@@ -409,7 +378,7 @@ struct RopeLane {
     }
   }
 
-  // The same lookups in a table staged by stage_table16: T[p] holds the
+  // The same lookups in a window staged as rope_words: T[p] holds the
   // rope_words of the lane's pair p.
   __device__ void fetch16(const u32x4* lds, const TokPos& tp, const TabWindow& w, u32x4* T) const {
     static_assert(ESZ == 16, "a rope_words window has 16-byte entries");
@@ -498,7 +467,10 @@ __device__ __forceinline__ float sum16_lanes_mod4(float v) {
 }
 
 // Rotary window staged in two phases: the global reads go to registers
-// first, so K/V loads can be issued before the LDS writes wait for them.
+// first, so that a prologue can issue its other loads before the LDS writes
+// wait for these (with at most PER entries per thread in registers; a larger
+// window loads the rest in commit).  commit() writes (cos, sin) pairs,
+// commit16() the same pairs as rope_words.
 struct TabStage {
   static constexpr int PER = 4;   // entries a thread holds in registers
   float2 v[PER];
@@ -1500,32 +1472,6 @@ __device__ __forceinline__ void widen8(const Raw8<float>& r, float* x) {
 // 8ch + 4t .. +3: with both tiles, exactly the channels its inputs hold.
 __device__ __forceinline__ int perm_row(int t, int i) { return 8 * (i >> 2) + 4 * t + (i & 3); }
 
-// Operand tiles of one 32 x 32 block of an fp32 matrix m with row stride ld
-// (element [r][c] = m[r * ld + c]), or of the block's transpose (TR: [r][c] =
-// m[c * ld + r]), for both 16-row tiles, parked in LDS: slot (tile * 2 + part)
-// of `op` holds, per lane, the bf16 hi (part 0) and lo (part 1) of the lane's 8
-// values, or for fp32 values 0-3 (part 0) and 4-7 (part 1).  16-byte slots
-// per lane keep the reads conflict-free.
-template <bool BF, bool TR>
-__device__ __forceinline__ void put_block_ops(const float* m, int ld, int lane, u32x4* op) {
-  const int i = lane & 15, kc = lane >> 4;
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int row = perm_row(t, i);
-    float sv[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) sv[s] = TR ? m[(8 * kc + s) * ld + row] : m[row * ld + 8 * kc + s];
-    if constexpr (BF) {
-      u32x4 hi, lo;
-      split8(sv, hi, lo);
-      op[(t * 2) * 64 + lane] = hi;
-      op[(t * 2 + 1) * 64 + lane] = lo;
-    } else {
-      op[(t * 2) * 64 + lane] = __builtin_bit_cast(u32x4, f32x4{sv[0], sv[1], sv[2], sv[3]});
-      op[(t * 2 + 1) * 64 + lane] = __builtin_bit_cast(u32x4, f32x4{sv[4], sv[5], sv[6], sv[7]});
-    }
-  }
-}
 constexpr int OPS_BLOCK = 4 * 64;                   // u32x4 slots of one block's operand tiles
 
 // c[t] += (block, tile t) x for the lane's token; x as bf16 hi/lo (xl may be
@@ -1562,30 +1508,75 @@ __device__ __forceinline__ void take8(const f32x4* c, float* y) {
 // per head of the pair, at 64 the four quadrants (a, b) of the head's 64 x 64
 // matrix (block 2a + b maps input half b to output half a).  NMAT = 2: blocks
 // 0 .. NB-1 hold the matrix, NB .. 2NB-1 its transpose; NMAT = 1: blocks 0 ..
-// NB-1 hold the transpose only.  The four waves form them.
+// NB-1 hold the transpose only.  The four waves form them: block bo by wave
+// bo mod 4.  A block's operand tiles (both 16-row tiles), parked in LDS: slot
+// (tile * 2 + part) holds, per lane, the bf16 hi (part 0) and lo (part 1) of
+// the lane's 8 values, or for fp32 values 0-3 (part 0) and 4-7 (part 1);
+// 16-byte slots per lane keep the reads conflict-free.  In two steps, so that
+// a prologue issues these loads with its others and waits for them later:
+// issue() loads the wave's values into registers, commit() writes the tiles.
 template <bool BF, bool W64, int NMAT>
-__device__ __forceinline__ void form_ops(u32x4* ops, const float* rec0, const float* rec1, int w, int lane) {
-  constexpr int NB = W64 ? 4 : 2;
-  constexpr int TOT = NMAT * NB;
+struct OpsStage {
+  static constexpr int NB = W64 ? 4 : 2;
+  static constexpr int TOT = NMAT * NB;
+  static constexpr int K = (TOT + 3) / 4;   // blocks per wave (at most)
+  float sv[K][2][8];
+
+  __device__ void issue(const float* rec0, const float* rec1, int w, int lane) {
+    const int i = lane & 15, kc = lane >> 4;
 #pragma unroll
-  for (int k = 0; k < (TOT + 3) / 4; ++k) {
-    const int bo = w + 4 * k;
-    if (bo >= TOT) break;
-    const int tr = NMAT == 2 ? bo / NB : 1, blk = bo % NB;
-    u32x4* op = ops + bo * OPS_BLOCK;
-    if constexpr (W64) {
-      const int qa = blk >> 1, qb = blk & 1;
-      // block (qa, qb) of M: rows 32qa.., columns 32qb..; of M^T: the
-      // transpose of M's block (qb, qa)
-      if (tr == 0) put_block_ops<BF, false>(rec0 + (32 * qa) * 64 + 32 * qb, 64, lane, op);
-      else put_block_ops<BF, true>(rec0 + (32 * qb) * 64 + 32 * qa, 64, lane, op);
-    } else {
-      const float* m = blk == 0 ? rec0 : rec1;
-      if (tr == 0) put_block_ops<BF, false>(m, 32, lane, op);
-      else put_block_ops<BF, true>(m, 32, lane, op);
+    for (int k = 0; k < K; ++k) {
+      const int bo = w + 4 * k;
+      if (bo >= TOT) break;
+      const bool tr = NMAT == 2 ? bo >= NB : true;
+      const int blk = bo % NB;
+      // Element [r][c] of the block is m[r * ld + c], of its transpose
+      // m[c * ld + r].  At 64, block (qa, qb) of M: rows 32qa.., columns
+      // 32qb..; of M^T: the transpose of M's block (qb, qa).
+      const float* m;
+      int ld;
+      if constexpr (W64) {
+        const int qa = blk >> 1, qb = blk & 1;
+        m = tr ? rec0 + (32 * qb) * 64 + 32 * qa : rec0 + (32 * qa) * 64 + 32 * qb;
+        ld = 64;
+      } else {
+        m = blk == 0 ? rec0 : rec1;
+        ld = 32;
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int row = perm_row(t, i);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sv[k][t][e] = m[tr ? (8 * kc + e) * ld + row : row * ld + 8 * kc + e];
+      }
     }
   }
-}
+
+  __device__ void commit(u32x4* ops, int w, int lane) const {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int bo = w + 4 * k;
+      if (bo >= TOT) break;
+      u32x4* op = ops + bo * OPS_BLOCK;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const float* v = sv[k][t];
+        if constexpr (BF) {
+          u32x4 hi, lo;
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = v[e];
+          split8(x, hi, lo);
+          op[(t * 2) * 64 + lane] = hi;
+          op[(t * 2 + 1) * 64 + lane] = lo;
+        } else {
+          op[(t * 2) * 64 + lane] = __builtin_bit_cast(u32x4, f32x4{v[0], v[1], v[2], v[3]});
+          op[(t * 2 + 1) * 64 + lane] = __builtin_bit_cast(u32x4, f32x4{v[4], v[5], v[6], v[7]});
+        }
+      }
+    }
+  }
+};
 
 // Store the 8 channels y of the lane's token for half h: bf16 pieces are
 // collected in pk for the paired store; fp32 goes out at once.
@@ -1673,19 +1664,18 @@ __global__ __launch_bounds__(NT, 2) void k_bw_kv(BwKVArgs a) {
   const int o_one = tl * RO + 8 * ch * EO;
   const int o_pair = (tl & 7) * RO + ((tl >> 3) * D + 8 * ch) * EO;
 
-  const TabWindow win = stage_table(tab, a.rope, a.pos.t0, t0, t1, a.pos.mag_tpf);
-  RopeLane<P2> rl, rl1;                  // rl1: the second half at head dim 64
-  TokPos tp;
-  if (rope_on) {
-    rl.init(a.rope, win, ch);
-    if constexpr (W64) rl1.init(a.rope, win, ch + 4);
-    tp.init(t0 + w * 16 + tl, a.pos);
-  }
+  // Prologue: the rotary window and the block's suffix record (dS, dz) are
+  // loaded together, so that one memory latency covers both, then the window
+  // and the operand blocks go to LDS, then the first K/V groups are loaded.
+  TabStage ts;
+  ts.issue(a.rope, a.pos.t0, t0, t1, a.pos.mag_tpf);
+  const TabWindow win = ts.w;
 
   // dS and dS^T operand blocks of block j in LDS; dz slices per half.
   const float* rec0 = a.suffix + ((size_t)(b * a.H + h0) * a.nb + j) * RECN;
   const float* rec1 = a.suffix + ((size_t)(b * a.H + h0 + (nh - 1)) * a.nb + j) * RECN;
-  form_ops<BF, W64, 2>(ops, rec0, rec1, w, lane);
+  OpsStage<BF, W64, 2> os;
+  os.issue(rec0, rec1, w, lane);
   float dzb[2][8];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -1693,6 +1683,16 @@ __global__ __launch_bounds__(NT, 2) void k_bw_kv(BwKVArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) dzb[h][i] = zp[8 * ch + i];
   }
+
+  ts.commit(tab);
+  RopeLane<P2> rl, rl1;                  // rl1: the second half at head dim 64
+  TokPos tp;
+  if (rope_on) {
+    rl.init(a.rope, win, ch);
+    if constexpr (W64) rl1.init(a.rope, win, ch + 4);
+    tp.init(t0 + w * 16 + tl, a.pos);
+  }
+  os.commit(ops, w, lane);
 
   struct Buf { Raw8<TIn> k[2], v[2]; };
   auto load_group = [&](Buf& bf) {
@@ -1841,7 +1841,35 @@ __global__ __launch_bounds__(NT, 2) void k_bw_q(BwQArgs a) {
   const int o_one = tl * RO + 8 * ch * EO;
   const int o_pair = (tl & 7) * RO + ((tl >> 3) * D + 8 * ch) * EO;
 
-  const TabWindow win = stage_table(tab, a.rope, a.pos.t0, c0, c1, a.pos.mag_tpf);
+  // Prologue: the rotary window and the block's prefix record (Sbar, zbar)
+  // are loaded together, so that one memory latency covers both, then the
+  // window and the operand blocks go to LDS, then the first q/g groups are
+  // loaded.
+  TabStage ts;
+  ts.issue(a.rope, a.pos.t0, c0, c1, a.pos.mag_tpf);
+  const TabWindow win = ts.w;
+
+  // Sbar^T operand blocks of block j in LDS (the same for every wave); zbar
+  // slices per half: in registers at 32, at 64 in LDS, read per group
+  // (registers are the limit there).
+  const float* rec0 = a.prefix + ((size_t)(b * a.H + h0) * a.nb + j) * RECN;
+  const float* rec1 = a.prefix + ((size_t)(b * a.H + h0 + (nh - 1)) * a.nb + j) * RECN;
+  OpsStage<BF, W64, 1> os;
+  os.issue(rec0, rec1, w, lane);
+  float zb[2][8];
+  float z64 = 0.f;
+  if constexpr (W64) {
+    z64 = rec0[DH * DH + (threadIdx.x & (DH - 1))];
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float* zp = (h == 0 ? rec0 : rec1) + D * D;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) zb[h][i] = zp[8 * ch + i];
+    }
+  }
+
+  ts.commit(tab);
   RopeLane<P2> rl, rl1;                  // rl1: the second half at head dim 64
   TokPos tp;
   if (rope_on) {
@@ -1849,29 +1877,17 @@ __global__ __launch_bounds__(NT, 2) void k_bw_q(BwQArgs a) {
     if constexpr (W64) rl1.init(a.rope, win, ch + 4);
     tp.init(c0 + w * 16 + tl, a.pos);
   }
-
-  // Sbar^T operand blocks of block j in LDS (the same for every wave); zbar
-  // slices per half: in registers at 32, at 64 in LDS, read per group
-  // (registers are the limit there).
-  const float* rec0 = a.prefix + ((size_t)(b * a.H + h0) * a.nb + j) * RECN;
-  const float* rec1 = a.prefix + ((size_t)(b * a.H + h0 + (nh - 1)) * a.nb + j) * RECN;
-  form_ops<BF, W64, 1>(ops, rec0, rec1, w, lane);
-  float zb[2][8];
+  os.commit(ops, w, lane);
   if constexpr (W64) {
-    if (threadIdx.x < DH) zl[threadIdx.x] = rec0[DH * DH + threadIdx.x];
-  } else {
+    if (threadIdx.x < DH) zl[threadIdx.x] = z64;
+  } else if constexpr (PKD) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const float* zp = (h == 0 ? rec0 : rec1) + D * D;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) zb[h][i] = zp[8 * ch + i];
-      if constexpr (PKD) {
-        if (w == 0 && tl == 0) {
-          u32x4 hi, lo;
-          split8d(zb[h], hi, lo);
-          zsel[(2 * h) * 4 + ch] = hi;
-          zsel[(2 * h + 1) * 4 + ch] = lo;
-        }
+      if (w == 0 && tl == 0) {
+        u32x4 hi, lo;
+        split8d(zb[h], hi, lo);
+        zsel[(2 * h) * 4 + ch] = hi;
+        zsel[(2 * h + 1) * 4 + ch] = lo;
       }
     }
   }
