@@ -20,20 +20,25 @@ namespace {
 // workgroups, so that a single streamed block still fills 256 CUs.  kMinWg is
 // about one resident round of the block-state kernel (3 workgroups per CU);
 // measured on a streamed 3-frame block (B = 2, 70 heads): 1024 -> 56-57 us,
-// 700 -> 54 us, 1536 -> 59 us per call.  Readout tiles of at most 640 tokens
-// (20 per 8-frame block of the minute-long clip): 0.636 ms against 0.641 ms
-// at 1024 (13 tiles), 0.656 at 2048 and 0.725 at 320.
+// 700 -> 54 us, 1536 -> 59 us per call.  Readout tiles of at most 512 tokens
+// at head dim 32 (25 per 8-frame block of the minute-long clip), whose
+// prologue overlaps its loads: 0.599-0.603 ms against 0.605-0.614 at 640,
+// 0.623-0.626 at 448 and 896, 0.604 at 384, 0.643 at 1280; at head dim 64,
+// 640 (0.651-0.653 ms against 0.657 at 512).
 #ifndef LAVR_STATE_MAX
 #define LAVR_STATE_MAX 4200
 #endif
 #ifndef LAVR_READ_MAX
-#define LAVR_READ_MAX 640
+#define LAVR_READ_MAX 512
+#endif
+#ifndef LAVR_READ_MAX64
+#define LAVR_READ_MAX64 640
 #endif
 #ifndef LAVR_MIN_WG
 #define LAVR_MIN_WG 700
 #endif
 constexpr int kStateMax = LAVR_STATE_MAX;
-constexpr int kReadMax = LAVR_READ_MAX;
+constexpr int kReadMax = LAVR_READ_MAX, kReadMax64 = LAVR_READ_MAX64;
 constexpr int kMinWg = LAVR_MIN_WG;
 // readout workgroups resident at once on the packed path: kReadOcc per CU at
 // head dim 32, four (register-bound) at 64
@@ -162,9 +167,10 @@ int make_plan(Plan* p, int B, int H, int head_dim, int frames, int tpf, int bloc
   if (!split_block(Lmax, kStateMax, min_n, kStep, rope, tpf, row_bytes, state_entry,
                    bf16_in ? kTabLdsMax16 : kTabLdsMax, &p->cpb, &p->Tc))
     return LA_ERR_UNSUPPORTED;
-  if (!split_block(Lmax, kReadMax, min_n, 64, rope, tpf, row_bytes, 16, kTabLdsMax16, &p->rpb, &p->Tr))
+  const int read_max = head_dim == 32 ? kReadMax : kReadMax64;
+  if (!split_block(Lmax, read_max, min_n, 64, rope, tpf, row_bytes, 16, kTabLdsMax16, &p->rpb, &p->Tr))
     return LA_ERR_UNSUPPORTED;
-  fit_rounds(Lmax, kReadMax, (long long)B * p->hg * p->nb, head_dim == 32 ? kReadSlots32 : kReadSlots64, 64, rope, tpf, row_bytes, 16, kTabLdsMax16,
+  fit_rounds(Lmax, read_max, (long long)B * p->hg * p->nb, head_dim == 32 ? kReadSlots32 : kReadSlots64, 64, rope, tpf, row_bytes, 16, kTabLdsMax16,
              &p->rpb, &p->Tr);
   if ((long long)p->hg * p->nb * p->cpb > 0x7fffffffLL || (long long)p->hg * p->nb * p->rpb > 0x7fffffffLL)
     return LA_ERR_UNSUPPORTED;
