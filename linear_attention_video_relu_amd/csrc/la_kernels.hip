@@ -544,8 +544,10 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? ((P2 && DH == 32 && !NRM && 
   constexpr int TILE_ELEMS = STEP * TCOLS;
   constexpr int TILE_BYTES = NTILE * TILE_ELEMS * ES;
   constexpr int W16 = 16 / ES;           // elements per 16 bytes
-  constexpr int PF = (BF && P2 && !W64 && !NRM) ? LAVR_STATE_PF : 2;   // steps of loads in flight
-  static_assert(PF == 2 || PF == 3, "block-state prefetch depth: two or three register buffers");
+  // Steps of loads in flight: a launch of one resident round (single-buffered
+  // tiles, four workgroups per CU) runs faster with one; longer launches keep two.
+  constexpr int PF = (BF && P2 && !W64 && !NRM) ? (TS == 1 ? 1 : LAVR_STATE_PF) : 2;
+  static_assert(PF >= 1 && PF <= 3, "block-state prefetch depth: one to three register buffers");
   // bf16 keys that are not normalised stay packed: ReLU on the packed pairs,
   // key sums and rotation by v_dot2_f32_bf16 against a rope_words window.
   constexpr bool PK = BF && !NRM;
@@ -615,7 +617,7 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? ((P2 && DH == 32 && !NRM && 
   // oldest step.
   Buf b0, b1, b2;
   load_step(b0);
-  load_step(b1);
+  if constexpr (PF > 1) load_step(b1);
   if constexpr (PF > 2) load_step(b2);
 
   if constexpr (PK) ts.commit16(tab16);
@@ -764,7 +766,7 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? ((P2 && DH == 32 && !NRM && 
   };
   for (int s0 = c0; s0 < c1; s0 += PF * STEP) {
     one_step(b0);
-    one_step(b1);
+    if constexpr (PF > 1) one_step(b1);
     if constexpr (PF > 2) one_step(b2);
   }
 
@@ -957,7 +959,9 @@ __global__ __launch_bounds__(256) void k_prefix1(PrefixArgs a) {
 //
 // RO: RoPE on, a compile-time switch so the loop carries no branch on it.
 
-template <typename TIn, typename TOut, bool P2, int DH, bool NRM, bool RO>
+// R1: a launch of one resident round (the packed path at head dim 32), which
+// runs faster with one group of loads in flight per wave than with two.
+template <typename TIn, typename TOut, bool P2, int DH, bool NRM, bool RO, bool R1>
 __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH == 32 && P2) ? 3 : 2) void k_readout(
     ReadArgs a) {
   constexpr bool BF = sizeof(TIn) == 2;
@@ -1093,8 +1097,9 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH ==
   // Register buffers: loads run RPF groups ahead of the arithmetic.  Every
   // load is issued, also past the tile (those read zeros and touch no memory),
   // so the number of loads in flight is fixed.
-  constexpr int RPF = BF ? LAVR_READ_PF : 2;
-  static_assert(RPF == 2 || RPF == 3, "readout prefetch depth: two or three buffers");
+  static_assert(!R1 || (BF && !NRM && DH == 32), "one-round readout launches: packed path at head dim 32");
+  constexpr int RPF = R1 ? 1 : BF ? LAVR_READ_PF : 2;
+  static_assert(RPF >= 1 && RPF <= 3, "readout prefetch depth: one to three buffers");
   Buf b0, b1, b2;
 
   // The waits, oldest loads first: the window, then the record.
@@ -1140,7 +1145,7 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH ==
     }
   }
   load_group(b0);
-  load_group(b1);
+  if constexpr (RPF > 1) load_group(b1);
   if constexpr (RPF > 2) load_group(b2);
 
   __syncthreads();
@@ -1397,8 +1402,10 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH ==
   for (int gi = w; gi < ngroups; gi += 4 * RPF) {
     run_group(b0);
     load_group(b0);
-    run_group(b1);
-    load_group(b1);
+    if constexpr (RPF > 1) {
+      run_group(b1);
+      load_group(b1);
+    }
     if constexpr (RPF > 2) {
       run_group(b2);
       load_group(b2);
@@ -2374,9 +2381,17 @@ __global__ __launch_bounds__(NT) void k_qk_rms(RmsArgs a) {
 
 template <typename TIn, typename TOut, int DH, bool NRM>
 hipError_t launch_readout(const ReadArgs& ra, bool p2, dim3 grid, int lds, hipStream_t s) {
-  if (ra.rope.table == nullptr) hipLaunchKernelGGL((k_readout<TIn, TOut, true, DH, NRM, false>), grid, dim3(NT), lds, s, ra);
-  else if (p2) hipLaunchKernelGGL((k_readout<TIn, TOut, true, DH, NRM, true>), grid, dim3(NT), lds, s, ra);
-  else hipLaunchKernelGGL((k_readout<TIn, TOut, false, DH, NRM, true>), grid, dim3(NT), lds, s, ra);
+  if constexpr (sizeof(TIn) == 2 && !NRM && DH == 32) {
+    if ((long long)grid.x * grid.y <= (long long)kReadOcc * 256) {   // one resident round
+      if (ra.rope.table == nullptr) hipLaunchKernelGGL((k_readout<TIn, TOut, true, DH, NRM, false, true>), grid, dim3(NT), lds, s, ra);
+      else if (p2) hipLaunchKernelGGL((k_readout<TIn, TOut, true, DH, NRM, true, true>), grid, dim3(NT), lds, s, ra);
+      else hipLaunchKernelGGL((k_readout<TIn, TOut, false, DH, NRM, true, true>), grid, dim3(NT), lds, s, ra);
+      return hipGetLastError();
+    }
+  }
+  if (ra.rope.table == nullptr) hipLaunchKernelGGL((k_readout<TIn, TOut, true, DH, NRM, false, false>), grid, dim3(NT), lds, s, ra);
+  else if (p2) hipLaunchKernelGGL((k_readout<TIn, TOut, true, DH, NRM, true, false>), grid, dim3(NT), lds, s, ra);
+  else hipLaunchKernelGGL((k_readout<TIn, TOut, false, DH, NRM, true, false>), grid, dim3(NT), lds, s, ra);
   return hipGetLastError();
 }
 
