@@ -40,8 +40,8 @@ namespace {
 constexpr int kStateMax = LAVR_STATE_MAX;
 constexpr int kReadMax = LAVR_READ_MAX, kReadMax64 = LAVR_READ_MAX64;
 constexpr int kMinWg = LAVR_MIN_WG;
-// readout workgroups resident at once on the packed path: kReadOcc per CU at
-// head dim 32, four (register-bound) at 64
+// readout workgroups resident in one round on the packed path: kReadOcc per CU
+// at head dim 32 (the occupancy a launch of one round takes), four at 64
 constexpr long long kReadSlots32 = lavr::kReadOcc * 256, kReadSlots64 = 4 * 256;
 constexpr int kTabLdsMax = 32768;      // LDS bytes for a staged rotary window ((cos, sin) pairs)
 constexpr int kTabLdsMax16 = 49152;    // the same for a readout tile's rope_words (with the 16 KB Sbar

@@ -24,20 +24,20 @@ constexpr size_t kWsHeader = 256;
 #endif
 constexpr int kStateTileSets = LAVR_STATE_DB == 2 ? 2 : 1;
 
-// Readout workgroups resident per CU on the packed bf16 path at head dim 32.
-// Its registers allow four; the launch asks for enough LDS that only kReadOcc
-// fit, because the readout streams Q in and the output out at once, and with
-// three per CU the HBM serves that mix faster than with four (fewer requests
-// in flight).  At head dim 64 four per CU measured faster, so that launch
-// keeps its register-bound occupancy.
-#ifndef LAVR_READ_OCC
-#define LAVR_READ_OCC 3
-#endif
-constexpr int kReadOcc = LAVR_READ_OCC;
+// Readout workgroups resident per CU on the packed bf16 path at head dim 32,
+// set by an LDS floor (its registers would allow six).  The readout streams Q
+// in and the output out at once, and the HBM serves that mix best with few
+// requests in flight: each wave keeps one 16-token group of loads in flight,
+// four workgroups share a CU in a launch of several rounds, and a launch that
+// fits one round at three per CU runs at three.  At head dim 64 the launch
+// keeps its register-bound four per CU and two groups in flight.
+constexpr int kReadOcc = 3;    // one-round launches (at most kReadOcc * 256 workgroups)
+constexpr int kReadOccN = 4;   // longer launches
 constexpr int kCuLds = 160 * 1024;   // LDS bytes per CU (gfx950)
-// Dynamic LDS floor of a packed readout workgroup: one more would not fit.
+// Dynamic LDS floors of a packed readout workgroup: one more would not fit.
 constexpr int kReadOccLds = kCuLds / (kReadOcc + 1) + 256;
-static_assert(kReadOcc * kReadOccLds <= kCuLds, "readout occupancy floor");
+constexpr int kReadOccLdsN = kCuLds / (kReadOccN + 1) + 256;
+static_assert(kReadOcc * kReadOccLds <= kCuLds && kReadOccN * kReadOccLdsN <= kCuLds, "readout occupancy floors");
 
 // Rotary table as the kernels see it.
 struct RopeDev {

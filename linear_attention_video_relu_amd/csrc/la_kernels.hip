@@ -959,9 +959,7 @@ __global__ __launch_bounds__(256) void k_prefix1(PrefixArgs a) {
 //
 // RO: RoPE on, a compile-time switch so the loop carries no branch on it.
 
-// R1: a launch of one resident round (the packed path at head dim 32), which
-// runs faster with one group of loads in flight per wave than with two.
-template <typename TIn, typename TOut, bool P2, int DH, bool NRM, bool RO, bool R1>
+template <typename TIn, typename TOut, bool P2, int DH, bool NRM, bool RO>
 __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH == 32 && P2) ? 3 : 2) void k_readout(
     ReadArgs a) {
   constexpr bool BF = sizeof(TIn) == 2;
@@ -1097,8 +1095,9 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH ==
   // Register buffers: loads run RPF groups ahead of the arithmetic.  Every
   // load is issued, also past the tile (those read zeros and touch no memory),
   // so the number of loads in flight is fixed.
-  static_assert(!R1 || (BF && !NRM && DH == 32), "one-round readout launches: packed path at head dim 32");
-  constexpr int RPF = R1 ? 1 : BF ? LAVR_READ_PF : 2;
+  // One group in flight on the packed path at head dim 32 (with more
+  // workgroups per CU: see kReadOccN), two or three elsewhere.
+  constexpr int RPF = (FAST && !W64) ? 1 : BF ? LAVR_READ_PF : 2;
   static_assert(RPF >= 1 && RPF <= 3, "readout prefetch depth: one to three buffers");
   Buf b0, b1, b2;
 
@@ -2381,17 +2380,9 @@ __global__ __launch_bounds__(NT) void k_qk_rms(RmsArgs a) {
 
 template <typename TIn, typename TOut, int DH, bool NRM>
 hipError_t launch_readout(const ReadArgs& ra, bool p2, dim3 grid, int lds, hipStream_t s) {
-  if constexpr (sizeof(TIn) == 2 && !NRM && DH == 32) {
-    if ((long long)grid.x * grid.y <= (long long)kReadOcc * 256) {   // one resident round
-      if (ra.rope.table == nullptr) hipLaunchKernelGGL((k_readout<TIn, TOut, true, DH, NRM, false, true>), grid, dim3(NT), lds, s, ra);
-      else if (p2) hipLaunchKernelGGL((k_readout<TIn, TOut, true, DH, NRM, true, true>), grid, dim3(NT), lds, s, ra);
-      else hipLaunchKernelGGL((k_readout<TIn, TOut, false, DH, NRM, true, true>), grid, dim3(NT), lds, s, ra);
-      return hipGetLastError();
-    }
-  }
-  if (ra.rope.table == nullptr) hipLaunchKernelGGL((k_readout<TIn, TOut, true, DH, NRM, false, false>), grid, dim3(NT), lds, s, ra);
-  else if (p2) hipLaunchKernelGGL((k_readout<TIn, TOut, true, DH, NRM, true, false>), grid, dim3(NT), lds, s, ra);
-  else hipLaunchKernelGGL((k_readout<TIn, TOut, false, DH, NRM, true, false>), grid, dim3(NT), lds, s, ra);
+  if (ra.rope.table == nullptr) hipLaunchKernelGGL((k_readout<TIn, TOut, true, DH, NRM, false>), grid, dim3(NT), lds, s, ra);
+  else if (p2) hipLaunchKernelGGL((k_readout<TIn, TOut, true, DH, NRM, true>), grid, dim3(NT), lds, s, ra);
+  else hipLaunchKernelGGL((k_readout<TIn, TOut, false, DH, NRM, true>), grid, dim3(NT), lds, s, ra);
   return hipGetLastError();
 }
 
@@ -2541,9 +2532,14 @@ void prefix_fingerprint(const Plan& p, const void* k, const void* v, int in_bf16
   *f1 = b.h;
 }
 
-// Dynamic LDS of a readout launch: the packed path at head dim 32 asks for at
-// least the occupancy floor, so that kReadOcc workgroups share a CU.
-int read_lds(bool floor, int bytes) { return floor && bytes < kReadOccLds ? kReadOccLds : bytes; }
+// Dynamic LDS of a readout launch of `wgs` workgroups: the packed path at head
+// dim 32 asks for at least the occupancy floor, so that kReadOcc workgroups
+// share a CU in a launch of one such round and kReadOccN in a longer one.
+int read_lds(bool floor, long long wgs, int bytes) {
+  if (!floor) return bytes;
+  const int f = wgs <= (long long)kReadOcc * 256 ? kReadOccLds : kReadOccLdsN;
+  return bytes < f ? f : bytes;
+}
 
 int launch_forward(const Plan& p, const void* q, const void* k, const void* v, void* out,
                    int in_bf16, int out_bf16, float eps, void* ws,
@@ -2617,9 +2613,9 @@ int launch_forward(const Plan& p, const void* q, const void* k, const void* v, v
   const bool packed = in_bf16 && !nq;
   const int lds_tab = packed ? p.lds_read16 : p.lds_read;
   e = p.D == 64 ? launch_readouts<64>(ra, in_bf16, out_bf16, p2, gr,
-                                     read_lds(false, lds_tab + (in_bf16 ? kReadAlBytes : 0) + (packed ? kReadZBytes : 0)), s)
+                                     read_lds(false, 0, lds_tab + (in_bf16 ? kReadAlBytes : 0) + (packed ? kReadZBytes : 0)), s)
                 : launch_readouts<32>(ra, in_bf16, out_bf16, p2, gr,
-                                      read_lds(packed, lds_tab + (packed ? kReadAlBytes / 2 + kReadZBytes : 0)), s);
+                                      read_lds(packed, (long long)gr.x * gr.y, lds_tab + (packed ? kReadAlBytes / 2 + kReadZBytes : 0)), s);
   if (e == hipSuccess) e = mark(3);
   return (int)e;
 }
