@@ -134,13 +134,17 @@ def cpu_baseline(cfg, arrs, n_heads):
 
 # ------------------------------------------------------------------- GPU timing
 
-# Timing events are created with the default flags: each record is a small
-# command between two kernels (a few microseconds of the timeline), so the
-# timed steps record only the two points around the readout kernel; the
-# split of the rest into block state and prefix comes from a short pass with
-# all four points after the timed region.
+# Timing events: la_block_causal_forward_timed binds them to the kernels' own
+# dispatches (start and end of the block-state kernel and of the readout), so
+# they put no command between the kernels.  They are created without the
+# system-scope fence (hipEventDisableSystemFence): an event that completes
+# with that fence writes back and invalidates the caches, which would perturb
+# the next kernel.  The timed region still ends with a device synchronize.
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
 class HipEvents:
-    def __init__(self, n, flags=0):
+    def __init__(self, n, flags=HIP_EVENT_DISABLE_SYSTEM_FENCE):
         self.hip = ctypes.CDLL("libamdhip64.so")
         self.ev = (ctypes.c_void_p * n)()
         for i in range(n):
@@ -151,8 +155,9 @@ class HipEvents:
             self.ev[i] = e.value
 
     def marks(self, *slots):
-        """The four-entry event array of one timed forward call: slot numbers, or None
-        for a point that is not recorded."""
+        """The four-entry event array of one timed forward call (block-state start
+        and end, readout start and end): slot numbers, or None for a point that is
+        not recorded."""
         return (ctypes.c_void_p * 4)(*(None if i is None else self.ev[i] for i in slots))
 
     def elapsed_ms(self, a, b):
@@ -225,9 +230,14 @@ def main():
             raise RuntimeError(lavr.status_string(rc))
 
     K = args.steps
-    # timed steps: slot 2i before step i's readout, 2i+1 after it, 2K before step 0
-    ev = HipEvents(2 * K + 1)
-    marks = [ev.marks(2 * K if i == 0 else None, None, 2 * i, 2 * i + 1) for i in range(K)]
+    # Timed step i binds two events, slots 2i and 2i+1, to its readout's start
+    # and end.  Each bound event still costs ~1.5 us of the timeline (20-step
+    # runs at the steady clock: 1.1765 ms with no events, 1.1794 with the
+    # readout's two, 1.1848 with all four), so the split of the rest of the step
+    # into block state and prefix comes from a pass with all four after the
+    # timed steps.
+    ev = HipEvents(2 * K)
+    marks = [ev.marks(None, None, 2 * i, 2 * i + 1) for i in range(K)]
     n_split = min(K, 10)
     ev_split = HipEvents(4 * n_split)
     marks_split = [ev_split.marks(4 * i, 4 * i + 1, 4 * i + 2, 4 * i + 3) for i in range(n_split)]
@@ -256,11 +266,11 @@ def main():
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / K
-    # readout: its own two points; block state + prefix (+ the gaps between the
-    # kernels): from the end of one step's readout to the start of the next one's
+    # readout: its own two points; the rest of the step (block state, prefix and
+    # the launch boundaries): from one readout's end to the next one's start
     t_read = np.array([ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(K)])
-    t_rest = np.array([ev.elapsed_ms(2 * K if i == 0 else 2 * i - 1, 2 * i) for i in range(K)])
-    ev_total = ev.elapsed_ms(2 * K, 2 * K - 1)
+    t_rest = np.array([ev.elapsed_ms(2 * i - 1, 2 * i) for i in range(1, K)])
+    ev_span = ev.elapsed_ms(0, 2 * K - 1)      # readout 0 start .. readout K-1 end
     for i in range(n_split):
         fwd_timed(marks_split[i])
     torch.cuda.synchronize(dev)
@@ -281,10 +291,11 @@ def main():
         # block state and prefix from the four-point pass after the timed steps
         "k_block_state": {"ms": k_state, "alg_bytes": bytes_state,
                           "gbs": bytes_state / (k_state * 1e6), "source": f"{n_split} steps after"},
-        "k_prefix": {"ms": k_prefix, "source": f"{n_split} steps after"},
+        "k_prefix+boundaries": {"ms": k_prefix, "source": f"{n_split} steps after"},
         "k_readout": {"ms": k_read, "alg_bytes": bytes_read, "gbs": bytes_read / (k_read * 1e6),
                       "source": "timed steps"},
-        "k_block_state+k_prefix+gaps": {"ms": float(t_rest.mean()), "source": "timed steps"},
+        "k_block_state+k_prefix+boundaries": {"ms": float(t_rest.mean()) if K > 1 else None,
+                                              "source": "timed steps"},
     }
     dom = "k_block_state" if k_state >= k_read_split else "k_readout"
     ach = kernels[dom]["gbs"]
@@ -311,13 +322,15 @@ def main():
                      "traffic": measured_traffic(cfg["name"], dom)},
         "step_hbm_gbs": bytes_step / (ms_step * 1e6),
         "step_frac_of_peak": bytes_step / (ms_step * 1e6) / HBM_PEAK_GBS,
-        "event_ms_per_step": ev_total / K,
+        # first readout's start to last readout's end, per step (K - 1 whole steps
+        # plus one readout)
+        "event_ms_per_step": (ev_span + float(t_rest.mean() if K > 1 else 0.0)) / K,
         "kernels": kernels,
-        # per timed step, HIP-event ms of the readout and of the rest of the step:
-        # the shader clock dips when the heavy load starts and recovers over
-        # ~40 ms, and the trend shows how much of the timed region falls in that ramp
+        # per timed step, HIP-event ms of each kernel: the shader clock dips when
+        # the heavy load starts and recovers over ~40 ms, and the trend shows how
+        # much of the timed region falls in that ramp
         "step_trend": {"k_readout": [round(float(x), 4) for x in t_read],
-                       "k_block_state+k_prefix+gaps": [round(float(x), 4) for x in t_rest]},
+                       "k_block_state+k_prefix+boundaries": [round(float(x), 4) for x in t_rest]},
         "cpu_baseline": cpu,
     }
 

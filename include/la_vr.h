@@ -149,13 +149,16 @@ int la_block_causal_forward(const void* q, const void* k, const void* v, void* o
                             int block_frames, int first_block_frames, const la_rope* rope,
                             float eps, void* ws, size_t ws_bytes, void* stream);
 
-/* la_block_causal_forward that also records caller-created hipEvent_t events
- * on `stream` at four points: events[0] before the block-state kernel,
- * events[1] after it, events[2] after the prefix kernel (before the readout)
- * and events[3] after the readout, so a caller can time each phase with
- * hipEventElapsedTime.  events must not be NULL; an entry that is NULL is not
- * recorded (every record adds a few microseconds between the kernels, so a
- * caller timing a long run records only the points it needs). */
+/* la_block_causal_forward that also times its two large kernels with
+ * caller-created hipEvent_t events: events[0] and events[1] take the start and
+ * end of the block-state kernel, events[2] and events[3] the start and end of
+ * the readout, so hipEventElapsedTime gives each kernel's duration, and the
+ * span from events[1] to events[2] the prefix kernel with the launch
+ * boundaries around it.  The events are bound to the kernels' own dispatches
+ * (hipExtLaunchKernel), so they add no command between the kernels and the
+ * timed call runs the same timeline as la_block_causal_forward.  events must
+ * not be NULL; an entry that is NULL is not recorded.  Not for HIP graph
+ * capture (use la_block_causal_forward there). */
 int la_block_causal_forward_timed(const void* q, const void* k, const void* v, void* out,
                                   la_dtype in_dt, la_dtype out_dt,
                                   int B, int H, int head_dim, int frames, int tokens_per_frame,

@@ -31,6 +31,7 @@
 // carries ~17 significant bits instead of 8.
 // fp32 inputs use the fp32 MFMA (v_mfma_f32_*_f32) and are exact fp32 products.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -827,8 +828,9 @@ __global__ __launch_bounds__(NT, sizeof(TIn) == 2 ? ((P2 && DH == 32 && !NRM && 
 // Grid: x = element group (17 x 64 covers the 1056 floats of a record),
 // y = head, z = batch; 256 threads.  For each run of 32 blocks, the four waves
 // form block sums p_0 + p_1 + ... (chunk order) for blocks w, w+4, ... of the
-// run into LDS, reading the (block, chunk) partials of a wave eight at a time
-// so that their latencies overlap; then wave 0 walks the run in block order:
+// run into LDS, reading the (block, chunk) partials of a wave 24 at a time so
+// that their latencies overlap (all of them at once for 8 blocks of 3 chunks,
+// the minute-length clip's 30 blocks); then wave 0 walks the run in block order:
 // prefix = previous prefix + block sum.  A streaming call starts from the
 // carried cache, so one block streamed on top of a cache adds exactly as the
 // one-shot prefix does.
@@ -850,7 +852,7 @@ __global__ __launch_bounds__(PFX_NT) void k_prefix(PrefixArgs a) {
   float acc = 0.f;
   if (w == 0 && ok && a.S_init != nullptr)
     acc = el < a.hd * a.hd ? a.S_init[bh * a.hd * a.hd + el] : a.z_init[bh * a.hd + el - a.hd * a.hd];
-  constexpr int BATCH = 8;
+  constexpr int BATCH = 24;
   for (int r0 = 0; r0 < a.nb; r0 += PFX_RUN) {
     const int nr = min(PFX_RUN, a.nb - r0);
     // Items of this wave: (block bi, chunk c) for its blocks r0 + w + 4 bi, in
@@ -860,7 +862,7 @@ __global__ __launch_bounds__(PFX_NT) void k_prefix(PrefixArgs a) {
     int bi = 0, c = 0;                    // (block, chunk) of the next item to add
     for (int q0 = 0; q0 < items; q0 += BATCH) {
       // Unconditional loads (items past the end reread the last one) keep the
-      // eight in flight together.
+      // batch in flight together.
       float v[BATCH];
       int lb = bi, lcn = c;               // (block, chunk) of the next item to load
 #pragma unroll
@@ -940,16 +942,16 @@ __global__ __launch_bounds__(256) void k_prefix1(PrefixArgs a) {
 // (f), B = 32 channels (f) x tokens: lane l holds channels 8(l>>4) .. +7 of
 // each 32-channel half of token (l & 15), one 16-byte load of bf16 q per half.
 // At head dim 32 each half is a head; at 64 every 16-row tile of the output
-// sums the products of both halves.  The output lane holds channels
-// 4(l>>4) .. +3 of each 16-row tile for token (l & 15).  Tokens past the tile
+// sums the products of both halves.  The Sbar rows are staged so that the
+// output lane holds channels 8(l>>4) .. +7 of each 32-channel half for token
+// (l & 15) (four from each of the half's two tiles).  Tokens past the tile
 // read as zeros and their stores are dropped by the buffer range check.
 //
 // bf16 inputs that are not normalised take the packed path: phi(q) stays
 // packed bf16 (exact) and feeds the normaliser's MFMA, whose A operand (from
-// LDS) holds zbar's hi bf16 part in rows 0-7 and its lo part in rows 8-15 (one
-// MFMA per 32-channel half; the two row halves are added across lanes l and
-// l ^ 32), so each output lane receives its own token's normaliser
-// zbar . phi(q); the rotation is
+// LDS) holds zbar's hi bf16 part in the even rows and its lo part in the odd
+// rows (one MFMA per 32-channel half), so each output lane receives its own
+// token's hi and lo parts of zbar . phi(q) side by side; the rotation is
 // v_dot2_f32_bf16 on the packed pairs against the rope_words table, so phi(q)
 // is never widened.  This path spends about a third fewer VALU instructions
 // per token than widening to fp32, which matters because the kernel's time
@@ -994,26 +996,35 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH ==
   const int t1 = min(t0 + a.Tr, blk1);
   if (t0 >= t1) return;
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  // the wave index is uniform across the wave: kept in a scalar register, so
+  // that the group loop and the per-group buffer resources below are scalar work
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int tl = lane & 15, ch = lane >> 4;
   const int h0 = W64 ? g : 2 * g;        // first head of the group
   const int nh = W64 ? 2 : min(2, a.H - h0);   // 32-channel halves that hold data
   const int ngroups = (t1 - t0 + 15) >> 4;
 
+  // Q, the token scales and out are reached through one buffer resource per
+  // 16-token group, starting at the group's first row and ending at the
+  // tile's end (no bytes past it: a group past the end reads zeros and drops
+  // its stores).  The resources are formed in scalar registers, and a lane's
+  // offsets inside them stay fixed, so advancing a group costs no vector
+  // instruction.
   const int RB = a.row_in * ES, RO_ = a.H * DH * EO;
-  const __amdgpu_buffer_rsrc_t rq =
-      make_rsrc(static_cast<const char*>(a.q) + ((size_t)b * a.N + t0) * RB, (uint32_t)(t1 - t0) * RB);
-  const __amdgpu_buffer_rsrc_t ro =
-      make_rsrc(static_cast<char*>(a.out) + ((size_t)b * a.N + t0) * RO_, (uint32_t)(t1 - t0) * RO_);
-  int qoff = (w * 16 + tl) * RB + (g * 64 + 8 * ch) * ES;
-  int ooff = (w * 16) * RO_ + g * 64 * EO;
-  // Output offsets of this lane.  fp32: channels 4ch..+3 of each 16-channel
-  // tile of token tl.  bf16 (after the exchange in store_pk): a 16-byte piece
-  // of channels co..co+7; with both halves present, tokens tl & 7 (first store)
-  // and 8 + (tl & 7) (second store) of half tl >> 3, so each store instruction
-  // writes whole 128-byte lines (8 tokens x the group's 64 channels).
-  const int co = 4 * ch + ((ch & 1) ? 12 : 0);
-  const int o_one = tl * RO_ + (EO == 2 ? co : 4 * ch) * EO;
+  const char* q_tile = static_cast<const char*>(a.q) + ((size_t)b * a.N + t0) * RB;
+  char* o_tile = static_cast<char*>(a.out) + ((size_t)b * a.N + t0) * RO_;
+  const int n_tok = t1 - t0;
+  auto q_rsrc = [&](int gr) { return make_rsrc(q_tile + (size_t)(16 * gr) * RB, (uint32_t)max(n_tok - 16 * gr, 0) * RB); };
+  auto o_rsrc = [&](int gr) { return make_rsrc(o_tile + (size_t)(16 * gr) * RO_, (uint32_t)max(n_tok - 16 * gr, 0) * RO_); };
+  const int qlane = tl * RB + (g * 64 + 8 * ch) * ES;
+  // Output offsets of this lane: channels 8ch .. 8ch+7 of each 32-channel half
+  // of token tl (the Sbar rows are staged in the order that puts them there).
+  // fp32: stored as two 16-byte pieces per half.  bf16 (after the exchange in
+  // store_pk): tokens tl & 7 (first store) and 8 + (tl & 7) (second store) of
+  // half tl >> 3, so each store instruction writes whole 128-byte lines
+  // (8 tokens x the group's 64 channels).
+  const int o_one = tl * RO_ + (g * 64 + 8 * ch) * EO;
   // The last group of an odd head count (head dim 32) holds one head: its
   // second half is computed on whatever the loads return, and every store of
   // that half is sent past the buffer range, where the hardware drops it (an
@@ -1021,7 +1032,8 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH ==
   // then serves every group.
   const bool two = W64 || nh == 2;
   constexpr int kDrop = (int)0x80000000u;
-  const int o_pair = (two || tl < 8) ? (tl & 7) * RO_ + ((tl >> 3) * D + co) * EO : kDrop;
+  const int o_pair = (two || tl < 8) ? (tl & 7) * RO_ + (g * 64 + (tl >> 3) * D + 8 * ch) * EO : kDrop;
+  const int o_pair2 = o_pair + 8 * RO_;       // second bf16 store: tokens 8 .. 15
   const int o_half1 = two ? D * EO : kDrop;   // fp32 stores: offset of half 1
 
   // Prologue: the rotary window and the prefix record (zbar and the Sbar
@@ -1035,18 +1047,23 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH ==
   RopeLane<P2, FAST ? 16 : 8> rl, rl1;  // rl1: the second half at head dim 64
 
   // Key-sum slices zb[h] (channels 32h + 8ch .. +7 of the half's z; packed
-  // path: their bf16 parts zh, zl) and Sbar tiles.  Head dim 32: tile 2h + hf
-  // = rows 16hf + tl, channels 8ch .. +7 of head h.  Head dim 64: tile
-  // 2et + kt = rows 16et + tl, channels 32kt + 8ch .. +7.
+  // path: their bf16 parts zh, zl) and Sbar tiles.  A tile is 16 rows of one
+  // 32-row half of Sbar: tile row m of the half's tile hf is Sbar row
+  // 8 (m / 4) + 4 hf + m % 4 of the half, so that the MFMA's output lane
+  // (rows 4 (l / 16) .. +3 of each tile) receives rows 8 (l / 16) .. +7, eight
+  // consecutive channels of its token, with no exchange between lanes.  Head
+  // dim 32: tile 2h + hf of head h, channels 8ch .. +7.  Head dim 64: tile
+  // 2et + kt = half et >> 1, tile et & 1, channels 32kt + 8ch .. +7.
   const float* pre[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int hd = W64 ? 0 : min(h, nh - 1);
     pre[h] = a.prefix + ((size_t)(b * a.H + h0 + hd) * a.nb + j) * RECN;
   }
+  auto tile_row = [&](int hf) { return 8 * (tl >> 2) + 4 * hf + (tl & 3); };
   auto tile_src = [&](int i) -> const float* {
-    if constexpr (W64) return pre[0] + (16 * (i >> 1) + tl) * DH + (i & 1) * D + 8 * ch;
-    else return ((i >> 1) ? pre[1] : pre[0]) + (16 * (i & 1) + tl) * D + 8 * ch;
+    if constexpr (W64) return pre[0] + (32 * (i >> 2) + tile_row((i >> 1) & 1)) * DH + (i & 1) * D + 8 * ch;
+    else return ((i >> 1) ? pre[1] : pre[0]) + tile_row(i & 1) * D + 8 * ch;
   };
   float zb[2][8];
   f32x4 zr[2][2];
@@ -1069,9 +1086,8 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH ==
   }
 
   // Normalised q: token scales of the tile (0 past it) and the lane's weights.
-  const __amdgpu_buffer_rsrc_t rs =
-      make_rsrc(NRM ? a.scale + (size_t)b * a.N + t0 : nullptr, NRM ? (uint32_t)(t1 - t0) * 4 : 0u);
-  int soff = (w * 16 + tl) * 4;
+  const float* s_tile = NRM ? a.scale + (size_t)b * a.N + t0 : nullptr;
+  auto s_rsrc = [&](int gr) { return make_rsrc(s_tile + 16 * gr, NRM ? (uint32_t)max(n_tok - 16 * gr, 0) * 4 : 0u); };
   float gam[2][8];
   if constexpr (NRM) {
 #pragma unroll
@@ -1079,14 +1095,13 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH ==
   }
 
   struct Buf { Raw8<TIn> x[2]; float s; };
+  int gload = w;                         // next group to load (uniform)
   auto load_group = [&](Buf& bf) {
+    const __amdgpu_buffer_rsrc_t rq = q_rsrc(gload);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) bf.x[h] = bload8<TIn>(rq, qoff + h * D * ES);
-    qoff += 64 * RB;
-    if constexpr (NRM) {
-      bf.s = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, soff, 0, 0));
-      soff += 64 * 4;
-    }
+    for (int h = 0; h < 2; ++h) bf.x[h] = bload8<TIn>(rq, qlane + h * D * ES);
+    if constexpr (NRM) bf.s = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(s_rsrc(gload), tl * 4, 0, 0));
+    gload += 4;
   };
   auto widen_q = [&](const Buf& bf, int h, float* x) {
     if constexpr (NRM) norm_relu_widen(bf.x[h], gam[h], bf.s, x);
@@ -1149,39 +1164,30 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH ==
 
   __syncthreads();
 
-  // Output of one 32-channel half h (o: its two 16-row tiles) scaled by inv:
-  // bf16 pieces go to pk[h] for the paired store, fp32 is stored at once.
-  auto emit = [&](int h, const f32x4* o, float inv, u32x4* pk) {
+  // Output of one 32-channel half h (o: its two 16-row tiles, channels
+  // 8ch .. 8ch+3 and 8ch+4 .. 8ch+7 of token tl) scaled by inv: bf16 pieces go
+  // to pk[h] for the paired store, fp32 is stored at once.
+  auto emit = [&](int h, const f32x4* o, float inv, u32x4* pk, __amdgpu_buffer_rsrc_t ro) {
     if constexpr (EO == 2) {
-      // Lane row ch holds channels 4ch..4ch+3 of each 16-channel tile.  One
-      // permlane16 swap per dword trades the tiles between rows ch and ch^1,
-      // so an even row ends up with channels 4ch..4ch+7 and an odd row with
-      // 12+4ch..19+4ch: one 16-byte store per lane.
-      const uint32_t p00 = pack_bf16(o[0][0] * inv, o[0][1] * inv);
-      const uint32_t p01 = pack_bf16(o[0][2] * inv, o[0][3] * inv);
-      const uint32_t p10 = pack_bf16(o[1][0] * inv, o[1][1] * inv);
-      const uint32_t p11 = pack_bf16(o[1][2] * inv, o[1][3] * inv);
-      const auto s0 = __builtin_amdgcn_permlane16_swap(p00, p10, false, false);
-      const auto s1 = __builtin_amdgcn_permlane16_swap(p01, p11, false, false);
-      pk[h] = u32x4{s0[0], s1[0], s0[1], s1[1]};
+      pk[h] = u32x4{pack_bf16(o[0][0] * inv, o[0][1] * inv), pack_bf16(o[0][2] * inv, o[0][3] * inv),
+                    pack_bf16(o[1][0] * inv, o[1][1] * inv), pack_bf16(o[1][2] * inv, o[1][3] * inv)};
     } else {
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const f32x4 ov = o[hf] * inv;
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ov), ro,
-                                               ooff + o_one + (h ? o_half1 : 0) + 16 * hf * EO, 0,
-                                               LAVR_STORE_CPOL);
+                                               o_one + (h ? o_half1 : 0) + 4 * hf * EO, 0, LAVR_STORE_CPOL);
       }
     }
   };
 
-  // bf16 stores of a group, then the next group's offset.  Lanes tl and
+  // bf16 stores of a group.  Lanes tl and
   // tl ^ 8 (DPP row rotate by 8 inside each 16-lane row) trade one piece: the
   // low lane keeps half 0 of tokens tl and tl + 8, the high lane half 1 of
   // tokens tl - 8 and tl.  The bank masks limit each rotated move to the lanes
   // that take the partner's piece (banks 2-3 = lanes 8-15 of a row, banks 0-1
   // = lanes 0-7); the other lanes keep their own.
-  auto store_pk = [&](const u32x4* pk) {
+  auto store_pk = [&](const u32x4* pk, __amdgpu_buffer_rsrc_t ro) {
     if constexpr (EO == 2) {
       uint32_t first[4], second[4];
 #pragma unroll
@@ -1191,15 +1197,22 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH ==
         second[i] = (uint32_t)__builtin_amdgcn_update_dpp((int)p1, (int)p0, 0x128, 0xf, 0x3, false);
       }
       __builtin_amdgcn_raw_buffer_store_b128(u32x4{first[0], first[1], first[2], first[3]}, ro,
-                                             ooff + o_pair, 0, LAVR_STORE_CPOL);
+                                             o_pair, 0, LAVR_STORE_CPOL);
       __builtin_amdgcn_raw_buffer_store_b128(u32x4{second[0], second[1], second[2], second[3]}, ro,
-                                             ooff + o_pair + 8 * RO_, 0, LAVR_STORE_CPOL);
+                                             o_pair2, 0, LAVR_STORE_CPOL);
     }
-    ooff += 64 * RO_;
   };
 
-  // One 16-token group, packed bf16 path.
-  auto run_fast = [&](const auto& bf) {   // generic: instantiated only where called
+  // Normaliser of the packed path: the MFMA's A operand holds zbar's hi part
+  // in the tile rows m with m % 2 == 0 and its lo part in the odd rows (lane
+  // tl supplies row tl), so each output lane's elements 0 and 1 are its
+  // token's hi . phi(q) and lo . phi(q), and the accumulator starts at
+  // (eps, 0, 0, 0): den = dd[0] + dd[1] with no exchange between lanes.
+  const f32x4 dd_init = {a.eps, 0.f, 0.f, 0.f};
+
+  // One 16-token group (gc: its index in the tile), packed bf16 path.
+  auto run_fast = [&](const auto& bf, int gc) {   // generic: instantiated only where called
+    const __amdgpu_buffer_rsrc_t ro = o_rsrc(gc);
     u32x4 T[4], T1[4];
     if constexpr (RO) {
       rl.fetch16(tab16, tp, win, T);
@@ -1208,12 +1221,11 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH ==
     }
     u32x4 pk[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
     if constexpr (W64) {
-      // one head: den over both halves, every output tile from both halves;
-      // the normaliser's A operand holds zbar's hi part in rows 0-7 and its lo
-      // part in rows 8-15 (one MFMA per half, read from LDS)
+      // one head: den over both halves, every output tile from both halves
+      // (one normaliser MFMA per half, A operand read from LDS)
       u32x4 qp[2], bh[2], bl[2];
-      f32x4 dd = {0.f, 0.f, 0.f, 0.f};
-      int zrow = ch + ((tl >> 3) << 2);
+      f32x4 dd = dd_init;
+      int zrow = ch + ((tl & 1) << 2);
       asm volatile("" : "+v"(zrow));
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -1229,7 +1241,7 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH ==
           bh[h] = qp[h];
         }
       }
-      const float inv = __builtin_amdgcn_rcpf(den_rows(dd[0]) + a.eps);
+      const float inv = __builtin_amdgcn_rcpf(dd[0] + dd[1]);
       // The Sbar operands are read from LDS in every group: an opaque copy of
       // the lane index keeps the compiler from hoisting them into registers.
       int aslot = lane;
@@ -1251,19 +1263,20 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH ==
           }
           o[hf] = cc;
         }
-        emit(h, o, inv, pk);
+        emit(h, o, inv, pk, ro);
       }
     } else {
       // Sbar and zbar operands from LDS in every group: opaque copies of the
-      // lane index and row keep the compiler from hoisting them into registers.
-      int zrow = ch + ((tl >> 3) << 2), aslot = lane;
-      asm volatile("" : "+v"(zrow), "+v"(aslot));
+      // lane's byte offsets keep the compiler from hoisting them into registers.
+      int zb_off = 16 * (ch + ((tl & 1) << 2)), ab_off = 16 * lane;
+      asm volatile("" : "+v"(zb_off), "+v"(ab_off));
+      const u32x4* zsl = reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(lds_z) + zb_off);
+      const u32x4* asl = reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(lds_a) + ab_off);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const u32x4 qp = relu_pk(bf.x[h].r[0]);
-        const u32x4 zs = lds_z[8 * h + zrow];
-        f32x4 dd = {0.f, 0.f, 0.f, 0.f};
-        dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(zs), as_bf16x8(qp), dd, 0, 0, 0);
+        const u32x4 zs = zsl[8 * h];
+        const f32x4 dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(zs), as_bf16x8(qp), dd_init, 0, 0, 0);
         f32x4 o[2];
         if constexpr (RO) {
           float x[8];
@@ -1272,8 +1285,8 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH ==
           split8d(x, bh, bl);
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
-            const u32x4 ah = lds_a[(2 * (2 * h + hf)) * 64 + aslot];
-            const u32x4 al = lds_a[(2 * (2 * h + hf) + 1) * 64 + aslot];
+            const u32x4 ah = asl[(2 * (2 * h + hf)) * 64];
+            const u32x4 al = asl[(2 * (2 * h + hf) + 1) * 64];
             f32x4 cc = {0.f, 0.f, 0.f, 0.f};
             cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah), as_bf16x8(bh), cc, 0, 0, 0);
             cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah), as_bf16x8(bl), cc, 0, 0, 0);
@@ -1283,22 +1296,24 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH ==
         } else {
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
-            const u32x4 ah = lds_a[(2 * (2 * h + hf)) * 64 + aslot];
-            const u32x4 al = lds_a[(2 * (2 * h + hf) + 1) * 64 + aslot];
+            const u32x4 ah = asl[(2 * (2 * h + hf)) * 64];
+            const u32x4 al = asl[(2 * (2 * h + hf) + 1) * 64];
             f32x4 cc = {0.f, 0.f, 0.f, 0.f};
             cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah), as_bf16x8(qp), cc, 0, 0, 0);
             cc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al), as_bf16x8(qp), cc, 0, 0, 0);
             o[hf] = cc;
           }
         }
-        emit(h, o, __builtin_amdgcn_rcpf(den_rows(dd[0]) + a.eps), pk);
+        emit(h, o, __builtin_amdgcn_rcpf(dd[0] + dd[1]), pk, ro);
       }
     }
-    store_pk(pk);
+    store_pk(pk, ro);
   };
 
-  // One 16-token group, fp32 path (fp32 or normalised inputs).
-  auto run_wide = [&](const auto& bf) {   // generic: instantiated only where called
+  // One 16-token group (gc: its index in the tile), fp32 path (fp32 or
+  // normalised inputs).
+  auto run_wide = [&](const auto& bf, int gc) {   // generic: instantiated only where called
+    const __amdgpu_buffer_rsrc_t ro = o_rsrc(gc);
     float2 cs[4], cs1[4];
     if constexpr (RO) {
       rl.fetch(tab, tp, win, cs);
@@ -1352,7 +1367,7 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH ==
           }
           o[hf] = cc;
         }
-        emit(h, o, inv, pk);
+        emit(h, o, inv, pk, ro);
       }
     } else {
 #pragma unroll
@@ -1385,28 +1400,28 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH ==
           }
         }
         den = sum4_lanes(den);
-        emit(h, o, __builtin_amdgcn_rcpf(den + a.eps), pk);
+        emit(h, o, __builtin_amdgcn_rcpf(den + a.eps), pk, ro);
       }
     }
-    store_pk(pk);
+    store_pk(pk, ro);
   };
 
-  auto run_group = [&](const Buf& bf) {
-    if constexpr (FAST) run_fast(bf);
-    else run_wide(bf);
+  auto run_group = [&](const Buf& bf, int gc) {
+    if constexpr (FAST) run_fast(bf, gc);
+    else run_wide(bf, gc);
   };
 
   // Whole rounds of RPF groups; groups past the tile read zeros and their
   // stores are dropped by the range check.
   for (int gi = w; gi < ngroups; gi += 4 * RPF) {
-    run_group(b0);
+    run_group(b0, gi);
     load_group(b0);
     if constexpr (RPF > 1) {
-      run_group(b1);
+      run_group(b1, gi + 4);
       load_group(b1);
     }
     if constexpr (RPF > 2) {
-      run_group(b2);
+      run_group(b2, gi + 8);
       load_group(b2);
     }
   }
@@ -2378,52 +2393,69 @@ __global__ __launch_bounds__(NT) void k_qk_rms(RmsArgs a) {
   }
 }
 
+// Timing events of one launch.  A caller's events are bound to the kernel's
+// own dispatch (hipExtLaunchKernel): they take its start and end times and add
+// no command to the stream, where an event record between two kernels leaves
+// a gap of several microseconds in the timeline.
+struct KEv {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool any() const { return start != nullptr || stop != nullptr; }
+};
+
+#define LAVR_LAUNCH(KER, GRID, LDS, S, EV, ARG)                                            \
+  do {                                                                                     \
+    if ((EV).any()) hipExtLaunchKernelGGL(KER, GRID, dim3(NT), LDS, S, (EV).start, (EV).stop, 0u, ARG); \
+    else hipLaunchKernelGGL(KER, GRID, dim3(NT), LDS, S, ARG);                             \
+  } while (0)
+
 template <typename TIn, typename TOut, int DH, bool NRM>
-hipError_t launch_readout(const ReadArgs& ra, bool p2, dim3 grid, int lds, hipStream_t s) {
-  if (ra.rope.table == nullptr) hipLaunchKernelGGL((k_readout<TIn, TOut, true, DH, NRM, false>), grid, dim3(NT), lds, s, ra);
-  else if (p2) hipLaunchKernelGGL((k_readout<TIn, TOut, true, DH, NRM, true>), grid, dim3(NT), lds, s, ra);
-  else hipLaunchKernelGGL((k_readout<TIn, TOut, false, DH, NRM, true>), grid, dim3(NT), lds, s, ra);
+hipError_t launch_readout(const ReadArgs& ra, bool p2, dim3 grid, int lds, hipStream_t s, KEv ev) {
+  if (ra.rope.table == nullptr) LAVR_LAUNCH((k_readout<TIn, TOut, true, DH, NRM, false>), grid, lds, s, ev, ra);
+  else if (p2) LAVR_LAUNCH((k_readout<TIn, TOut, true, DH, NRM, true>), grid, lds, s, ev, ra);
+  else LAVR_LAUNCH((k_readout<TIn, TOut, false, DH, NRM, true>), grid, lds, s, ev, ra);
   return hipGetLastError();
 }
 
 template <int DH, bool NRM>
-hipError_t launch_state_n(const StateArgs& sa, bool in_bf16, bool p2, dim3 grid, int lds, int lds1, hipStream_t s) {
+hipError_t launch_state_n(const StateArgs& sa, bool in_bf16, bool p2, dim3 grid, int lds, int lds1, hipStream_t s,
+                          KEv ev) {
   // Packed bf16 at head dim 32: a launch of at most one round at four
   // workgroups per CU takes single-buffered tiles (lds1 bytes), so that it runs
   // as one round; longer launches keep two tile sets per workgroup.
   if constexpr (DH == 32 && !NRM) {
     if (in_bf16 && p2 && (long long)grid.x * grid.y <= 4LL * 256) {
-      hipLaunchKernelGGL((k_block_state<uint16_t, true, DH, NRM, 1>), grid, dim3(NT), lds1, s, sa);
+      LAVR_LAUNCH((k_block_state<uint16_t, true, DH, NRM, 1>), grid, lds1, s, ev, sa);
       return hipGetLastError();
     }
   }
-  if (in_bf16 && p2) hipLaunchKernelGGL((k_block_state<uint16_t, true, DH, NRM, kStateTileSets>), grid, dim3(NT), lds, s, sa);
-  else if (in_bf16) hipLaunchKernelGGL((k_block_state<uint16_t, false, DH, NRM, kStateTileSets>), grid, dim3(NT), lds, s, sa);
-  else if (p2) hipLaunchKernelGGL((k_block_state<float, true, DH, NRM, kStateTileSets>), grid, dim3(NT), lds, s, sa);
-  else hipLaunchKernelGGL((k_block_state<float, false, DH, NRM, kStateTileSets>), grid, dim3(NT), lds, s, sa);
+  if (in_bf16 && p2) LAVR_LAUNCH((k_block_state<uint16_t, true, DH, NRM, kStateTileSets>), grid, lds, s, ev, sa);
+  else if (in_bf16) LAVR_LAUNCH((k_block_state<uint16_t, false, DH, NRM, kStateTileSets>), grid, lds, s, ev, sa);
+  else if (p2) LAVR_LAUNCH((k_block_state<float, true, DH, NRM, kStateTileSets>), grid, lds, s, ev, sa);
+  else LAVR_LAUNCH((k_block_state<float, false, DH, NRM, kStateTileSets>), grid, lds, s, ev, sa);
   return hipGetLastError();
 }
 
 template <int DH>
-hipError_t launch_state(const StateArgs& sa, bool in_bf16, bool p2, dim3 grid, int lds, int lds1, hipStream_t s) {
-  return sa.scale != nullptr ? launch_state_n<DH, true>(sa, in_bf16, p2, grid, lds, lds1, s)
-                             : launch_state_n<DH, false>(sa, in_bf16, p2, grid, lds, lds1, s);
+hipError_t launch_state(const StateArgs& sa, bool in_bf16, bool p2, dim3 grid, int lds, int lds1, hipStream_t s,
+                        KEv ev = {}) {
+  return sa.scale != nullptr ? launch_state_n<DH, true>(sa, in_bf16, p2, grid, lds, lds1, s, ev)
+                             : launch_state_n<DH, false>(sa, in_bf16, p2, grid, lds, lds1, s, ev);
 }
 
 template <int DH, bool NRM>
 hipError_t launch_readouts_n(const ReadArgs& ra, bool in_bf16, bool out_bf16, bool p2, dim3 grid, int lds,
-                             hipStream_t s) {
-  if (in_bf16 && out_bf16) return launch_readout<uint16_t, uint16_t, DH, NRM>(ra, p2, grid, lds, s);
-  if (in_bf16) return launch_readout<uint16_t, float, DH, NRM>(ra, p2, grid, lds, s);
-  if (out_bf16) return launch_readout<float, uint16_t, DH, NRM>(ra, p2, grid, lds, s);
-  return launch_readout<float, float, DH, NRM>(ra, p2, grid, lds, s);
+                             hipStream_t s, KEv ev) {
+  if (in_bf16 && out_bf16) return launch_readout<uint16_t, uint16_t, DH, NRM>(ra, p2, grid, lds, s, ev);
+  if (in_bf16) return launch_readout<uint16_t, float, DH, NRM>(ra, p2, grid, lds, s, ev);
+  if (out_bf16) return launch_readout<float, uint16_t, DH, NRM>(ra, p2, grid, lds, s, ev);
+  return launch_readout<float, float, DH, NRM>(ra, p2, grid, lds, s, ev);
 }
 
 template <int DH>
 hipError_t launch_readouts(const ReadArgs& ra, bool in_bf16, bool out_bf16, bool p2, dim3 grid, int lds,
-                           hipStream_t s) {
-  return ra.scale != nullptr ? launch_readouts_n<DH, true>(ra, in_bf16, out_bf16, p2, grid, lds, s)
-                             : launch_readouts_n<DH, false>(ra, in_bf16, out_bf16, p2, grid, lds, s);
+                           hipStream_t s, KEv ev = {}) {
+  return ra.scale != nullptr ? launch_readouts_n<DH, true>(ra, in_bf16, out_bf16, p2, grid, lds, s, ev)
+                             : launch_readouts_n<DH, false>(ra, in_bf16, out_bf16, p2, grid, lds, s, ev);
 }
 
 PosArgs pos_args(const Plan& p) {
@@ -2546,11 +2578,11 @@ int launch_forward(const Plan& p, const void* q, const void* k, const void* v, v
                    const float* S_init, const float* z_init, float* S_save, float* z_save,
                    void* stream, void* const* events, const Prologue* pro) {
   hipStream_t s = (hipStream_t)stream;
-  auto mark = [&](int i) -> hipError_t {
-    return events && events[i] ? hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), s) : hipSuccess;
-  };
-  hipError_t e = mark(0);
-  if (e != hipSuccess) return (int)e;
+  // events[0] / [1]: start and end of the block-state kernel, [2] / [3]: of the
+  // readout, each bound to the kernel's dispatch
+  auto ev = [&](int i) -> hipEvent_t { return events ? reinterpret_cast<hipEvent_t>(events[i]) : nullptr; };
+  const KEv ev_state{ev(0), ev(1)}, ev_read{ev(2), ev(3)};
+  hipError_t e = hipSuccess;
   const bool nq = pro != nullptr && pro->q_gamma != nullptr;
   const bool nk = pro != nullptr && pro->k_gamma != nullptr;
   if (nq || nk) {
@@ -2586,9 +2618,8 @@ int launch_forward(const Plan& p, const void* q, const void* k, const void* v, v
   prefix_fingerprint(p, k, v, in_bf16, nk ? pro : nullptr, &sa.fp0, &sa.fp1);
   const dim3 gs((unsigned)(p.hg * p.nb * p.cpb), (unsigned)p.B);
   const bool p2 = ((p.rope.pt | p.rope.ph | p.rope.pw) & 1) == 0;
-  e = p.D == 64 ? launch_state<64>(sa, in_bf16, p2, gs, p.lds_state, p.lds_state1, s)
-                : launch_state<32>(sa, in_bf16, p2, gs, p.lds_state, p.lds_state1, s);
-  if (e == hipSuccess) e = mark(1);
+  e = p.D == 64 ? launch_state<64>(sa, in_bf16, p2, gs, p.lds_state, p.lds_state1, s, ev_state)
+                : launch_state<32>(sa, in_bf16, p2, gs, p.lds_state, p.lds_state1, s, ev_state);
   if (e != hipSuccess) return (int)e;
 
   PrefixArgs pa;
@@ -2596,7 +2627,6 @@ int launch_forward(const Plan& p, const void* q, const void* k, const void* v, v
   pa.S_save = S_save; pa.z_save = z_save; pa.H = p.H; pa.nb = p.nb; pa.cpb = p.cpb;
   pa.hd = p.D; pa.rec = p.rec; pa.rev = 0;
   e = launch_prefix(pa, p, s);
-  if (e == hipSuccess) e = mark(2);
   if (e != hipSuccess) return (int)e;
 
   ReadArgs ra;
@@ -2613,10 +2643,11 @@ int launch_forward(const Plan& p, const void* q, const void* k, const void* v, v
   const bool packed = in_bf16 && !nq;
   const int lds_tab = packed ? p.lds_read16 : p.lds_read;
   e = p.D == 64 ? launch_readouts<64>(ra, in_bf16, out_bf16, p2, gr,
-                                     read_lds(false, 0, lds_tab + (in_bf16 ? kReadAlBytes : 0) + (packed ? kReadZBytes : 0)), s)
+                                     read_lds(false, 0, lds_tab + (in_bf16 ? kReadAlBytes : 0) + (packed ? kReadZBytes : 0)), s,
+                                     ev_read)
                 : launch_readouts<32>(ra, in_bf16, out_bf16, p2, gr,
-                                      read_lds(packed, (long long)gr.x * gr.y, lds_tab + (packed ? kReadAlBytes / 2 + kReadZBytes : 0)), s);
-  if (e == hipSuccess) e = mark(3);
+                                      read_lds(packed, (long long)gr.x * gr.y, lds_tab + (packed ? kReadAlBytes / 2 + kReadZBytes : 0)), s,
+                                      ev_read);
   return (int)e;
 }
 
