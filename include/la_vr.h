@@ -80,7 +80,8 @@ typedef enum {
 typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
 
 /* Description of a rotary table built by rope_table_build.  table == NULL turns
- * RoPE off (identity rotation). */
+ * RoPE off (identity rotation).  A table of 2^31 or more (cos, sin) pairs is
+ * rejected (LA_ERR_INVALID_ARG): the kernels index it with 32-bit integers. */
 typedef struct {
   const float* table;          /* device; (cos, sin) float pairs, see rope_table_bytes */
   int d_t, d_h, d_w;           /* even section widths, d_t + d_h + d_w == head_dim */

@@ -74,6 +74,10 @@ int check_rope(const la_rope* r, int head_dim, int tpf, long long t0, long long 
   if (r->max_frames < 1 || r->grid_h < 1 || r->grid_w < 1) return LA_ERR_INVALID_ARG;
   if (r->d_h + r->d_w > 0 && (long long)r->grid_h * r->grid_w != tpf) return LA_ERR_INVALID_ARG;
   if (t0 < 0 || t0 + frames > r->max_frames) return LA_ERR_INVALID_ARG;
+  // the kernels index the table's (cos, sin) pairs with 32-bit integers
+  const long long pairs = (long long)r->max_frames * (r->d_t / 2) + (long long)r->grid_h * (r->d_h / 2) +
+                          (long long)r->grid_w * (r->d_w / 2);
+  if (pairs >= (1LL << 31)) return LA_ERR_INVALID_ARG;
   return LA_OK;
 }
 

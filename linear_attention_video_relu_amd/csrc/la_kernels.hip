@@ -134,6 +134,7 @@ struct ReadArgs {
   float eps;
   int H, N, L, L0, nb, rpb, Tr, hg;   // L0: tokens of the first block
   int row_in;                // elements from one token row of q to the next
+  uint64_t mag_hg, mag_rpb;  // floor(2^42 / hg) + 1, floor(2^42 / rpb) + 1 (fast_div)
   PosArgs pos;
   RopeDev rope;
 };
@@ -477,8 +478,10 @@ struct TabStage {
   float2 v[PER];
   int nt, tot;
   TabWindow w;
-  const float2* tsrc;
-  const float2* hwsrc;
+  const float2* tab;
+  int tb, hb;                     // table index of the window's first t row, of the h/w rows
+  // Table index of window entry i (the t rows, then the h and w sections).
+  __device__ int src(int i) const { return i + (i < nt ? tb : hb - nt); }
 
   __device__ void issue(const RopeDev& r, long long t0, int n0, int n1, uint64_t mag_tpf) {
     w = TabWindow{0, 0};
@@ -486,15 +489,15 @@ struct TabStage {
     if (r.table == nullptr || n1 <= n0) return;
     w.f_lo = (int)fast_div((uint32_t)n0, mag_tpf);
     w.nf = (int)fast_div((uint32_t)(n1 - 1), mag_tpf) - w.f_lo + 1;
-    const float2* tab = reinterpret_cast<const float2*>(r.table);
-    tsrc = tab + (size_t)(t0 + w.f_lo) * r.pt;
-    hwsrc = tab + (size_t)r.max_frames * r.pt;
+    tab = reinterpret_cast<const float2*>(r.table);
+    tb = (int)(t0 + w.f_lo) * r.pt;
+    hb = r.max_frames * r.pt;
     nt = w.nf * r.pt;
     tot = nt + r.gh * r.ph + r.gw * r.pw;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int i = threadIdx.x + k * NT;
-      if (i < tot) v[k] = i < nt ? tsrc[i] : hwsrc[i - nt];
+      if (i < tot) v[k] = tab[src(i)];
     }
   }
   __device__ void commit(float2* lds) const {
@@ -503,7 +506,7 @@ struct TabStage {
       const int i = threadIdx.x + k * NT;
       if (i < tot) lds[i] = v[k];
     }
-    for (int i = threadIdx.x + PER * NT; i < tot; i += NT) lds[i] = i < nt ? tsrc[i] : hwsrc[i - nt];
+    for (int i = threadIdx.x + PER * NT; i < tot; i += NT) lds[i] = tab[src(i)];
   }
   // The same window written as rope_words (16 bytes per pair).
   __device__ void commit16(u32x4* lds) const {
@@ -512,7 +515,7 @@ struct TabStage {
       const int i = threadIdx.x + k * NT;
       if (i < tot) lds[i] = rope_words(v[k]);
     }
-    for (int i = threadIdx.x + PER * NT; i < tot; i += NT) lds[i] = rope_words(i < nt ? tsrc[i] : hwsrc[i - nt]);
+    for (int i = threadIdx.x + PER * NT; i < tot; i += NT) lds[i] = rope_words(tab[src(i)]);
   }
 };
 
@@ -985,10 +988,12 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH ==
   float2* tab = reinterpret_cast<float2*>(smem + PRE);
   u32x4* tab16 = reinterpret_cast<u32x4*>(smem + PRE);
 
-  const int g = blockIdx.x % a.hg;
-  const int ti = blockIdx.x / a.hg;
+  // (tile, head group) and (block, tile in block) from the workgroup index by
+  // multiply-shift divisions (fast_div) instead of the compiler's division
+  const int ti = (int)fast_div(blockIdx.x, a.mag_hg);
+  const int g = blockIdx.x - ti * a.hg;
   const int b = blockIdx.y;
-  const int j = ti / a.rpb;
+  const int j = (int)fast_div((uint32_t)ti, a.mag_rpb);
   const int r = ti - j * a.rpb;
   const int blk0 = block_start(j, a.L0, a.L);
   const int blk1 = min(blk0 + (j == 0 ? a.L0 : a.L), a.N);
@@ -1131,10 +1136,12 @@ __global__ __launch_bounds__(NT, (sizeof(TIn) == 2 && !NRM) ? 4 : (!NRM && DH ==
 #pragma unroll
     for (int i = 0; i < 4; ++i) { zb[h][i] = zr[h][0][i]; zb[h][4 + i] = zr[h][1][i]; }
     if constexpr (Z_LDS) {
-      split8d(zb[h], zh[h], zl[h]);
-      if (w == 0 && tl == 0) {
-        lds_z[(2 * h) * 4 + ch] = zh[h];
-        lds_z[(2 * h + 1) * 4 + ch] = zl[h];
+      if (w == 0) {                      // uniform: only wave 0 stores the slices
+        split8d(zb[h], zh[h], zl[h]);
+        if (tl == 0) {
+          lds_z[(2 * h) * 4 + ch] = zh[h];
+          lds_z[(2 * h + 1) * 4 + ch] = zl[h];
+        }
       }
     }
   }
@@ -2635,6 +2642,8 @@ int launch_forward(const Plan& p, const void* q, const void* k, const void* v, v
   ra.gamma = nq ? pro->q_gamma : nullptr;
   ra.H = p.H; ra.N = p.N; ra.L = p.L; ra.L0 = p.L0; ra.nb = p.nb; ra.rpb = p.rpb; ra.Tr = p.Tr; ra.hg = p.hg;
   ra.row_in = p.row_in;
+  ra.mag_hg = (uint64_t)((1LL << 42) / p.hg) + 1;
+  ra.mag_rpb = (uint64_t)((1LL << 42) / p.rpb) + 1;
   ra.pos = pa_pos;
   ra.rope = p.rope;
   const dim3 gr((unsigned)(p.hg * p.nb * p.rpb), (unsigned)p.B);
