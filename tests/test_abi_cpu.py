@@ -157,6 +157,19 @@ def test_forward_rejects_bad_rope(lavr, kw):
     assert call_forward(lavr, rope=ctypes.byref(r)) == lavr.LA_ERR_INVALID_ARG
 
 
+def test_rope_table_pair_count_fits_32_bits(lavr):
+    """The kernels index the rotary table's (cos, sin) pairs with 32-bit integers: a
+    description of 2^31 pairs or more is refused by the planner (workspace query 0)."""
+    def ws(max_frames):
+        r = rope_desc(lavr, max_frames=max_frames, d_t=16, d_h=8, d_w=8)
+        return lavr.lib.la_workspace_bytes(1, 2, 32, 4, 6, 2, 0, ctypes.byref(r))
+    # 8 t pairs per frame plus 2 * 4 + 3 * 4 h/w pairs
+    assert ws(1 << 27) > 0                                   # 2^30 + 20 pairs
+    assert ws(((1 << 31) - 20) // 8) > 0                     # just below 2^31
+    assert ws(((1 << 31) - 20) // 8 + 1) == 0                # 2^31 + 4
+    assert ws(1 << 28) == 0
+
+
 def test_forward_rejects_shared_memory(lavr):
     """The workspace may not share bytes with the tensors or the rotary table,
     nor the output with the table (checked before anything is launched)."""
