@@ -150,6 +150,31 @@ int la_block_causal_forward(const void* q, const void* k, const void* v, void* o
                             int block_frames, int first_block_frames, const la_rope* rope,
                             float eps, void* ws, size_t ws_bytes, void* stream);
 
+/* Workspace bytes of la_block_causal_forward_replay (0 if the shape is invalid,
+ * including frames not a multiple of block_frames). */
+size_t la_replay_workspace_bytes(int B, int H, int head_dim, int frames, int tokens_per_frame,
+                                 int block_frames, const la_rope* rope);
+
+/* One-shot forward for deterministic replay ("Block Causal Linear Attention",
+ * happyin.space, "Integration Contract" and "Acceptance Checks": streaming must
+ * reproduce the one-shot result).  Its output equals, bit for bit, the outputs
+ * of streaming the same clip block by block with la_stream_block (save = 1,
+ * from a zeroed state, the same B, H, head_dim, block_frames, tokens_per_frame,
+ * rotary table, eps and output dtype).  la_block_causal_forward splits each
+ * block into chunks sized for the whole clip's launch, a streamed call into
+ * chunks sized for one block, and the fp32 block sums then round differently
+ * (about one bf16 step apart); this entry point takes the streamed split for
+ * every block, at the cost of more, shorter chunks on long clips.  The clip
+ * must consist of whole blocks (frames a multiple of block_frames, else
+ * LA_ERR_INVALID_ARG); arguments and errors are otherwise those of
+ * la_block_causal_forward, with ws sized by la_replay_workspace_bytes.  Its
+ * workspace is not one that la_block_causal_backward_from_forward accepts. */
+int la_block_causal_forward_replay(const void* q, const void* k, const void* v, void* out,
+                                   la_dtype in_dt, la_dtype out_dt, int B, int H, int head_dim,
+                                   int frames, int tokens_per_frame, int block_frames,
+                                   const la_rope* rope, float eps, void* ws, size_t ws_bytes,
+                                   void* stream);
+
 /* la_block_causal_forward that also times its two large kernels with
  * caller-created hipEvent_t events: events[0] and events[1] take the start and
  * end of the block-state kernel, events[2] and events[3] the start and end of

@@ -129,9 +129,12 @@ void fit_rounds(int L, int max_tokens, long long rows, long long slots, int mult
 
 // first_block_frames: frames of the first block (0 = block_frames).  row_mult:
 // input token rows hold row_mult * H * head_dim elements (3 for fused q|k|v).
+// stream_chunks: split every block into the chunks a streamed call of that one
+// block takes (the chunk count is planned as for a launch of one block), so that
+// the block states, and every output, equal the streamed ones bit for bit.
 int make_plan(Plan* p, int B, int H, int head_dim, int frames, int tpf, int block_frames,
               int first_block_frames, const la_rope* rope, long long t0, la_dtype in_dt,
-              int row_mult = 1) {
+              int row_mult = 1, bool stream_chunks = false) {
   if (B < 1 || H < 1 || head_dim < 1 || frames < 1 || tpf < 1 || block_frames < 1 ||
       first_block_frames < 0)
     return LA_ERR_INVALID_ARG;
@@ -163,7 +166,7 @@ int make_plan(Plan* p, int B, int H, int head_dim, int frames, int tpf, int bloc
   p->mag_tpf = (uint64_t)(kTwo42 / tpf) + 1;
   p->mag_gw = (uint64_t)(kTwo42 / gw_div) + 1;
   const long long row_bytes = (long long)p->row_in * 4;
-  const long long min_n = cdiv(kMinWg, (long long)B * p->hg * p->nb);
+  const long long min_n = cdiv(kMinWg, (long long)B * p->hg * (stream_chunks ? 1 : p->nb));
   // Rotary windows are staged as (cos, sin) pairs (8 bytes), or as rope_words
   // (16 bytes) by the readout tiles and, for bf16 inputs, the block-state chunks.
   const bool bf16_in = in_dt == LA_BF16;
@@ -410,6 +413,38 @@ int la_block_causal_forward(const void* q, const void* k, const void* v, void* o
   Plan p;
   int st = make_plan(&p, B, H, head_dim, frames, tokens_per_frame, block_frames, first_block_frames,
                      rope, 0, in_dt);
+  if (st != LA_OK) return st;
+  st = check_tensors(q, k, v, out, in_dt, out_dt, p);
+  if (st != LA_OK) return st;
+  if (!ws || !aligned(ws, 256) || ws_bytes < p.ws_total) return LA_ERR_INVALID_ARG;
+  const size_t nin = tensor_bytes(p, in_dt), nout = tensor_bytes(p, out_dt);
+  st = check_scratch(p, ws, p.ws_total, {out, nout}, {{q, nin}, {k, nin}, {v, nin}}, rope);
+  if (st != LA_OK) return st;
+  return hip_status(lavr::launch_forward(p, q, k, v, out, in_dt == LA_BF16, out_dt == LA_BF16, eps,
+                                         ws, nullptr, nullptr, nullptr, nullptr, stream));
+}
+
+size_t la_replay_workspace_bytes(int B, int H, int head_dim, int frames, int tokens_per_frame,
+                                 int block_frames, const la_rope* rope) {
+  if (block_frames < 1 || frames < 1 || frames % block_frames != 0) return 0;
+  Plan p;
+  if (make_plan(&p, B, H, head_dim, frames, tokens_per_frame, block_frames, 0, rope, 0, LA_BF16, 1,
+                true) != LA_OK)
+    return 0;
+  return p.ws_total;
+}
+
+int la_block_causal_forward_replay(const void* q, const void* k, const void* v, void* out,
+                                   la_dtype in_dt, la_dtype out_dt, int B, int H, int head_dim,
+                                   int frames, int tokens_per_frame, int block_frames,
+                                   const la_rope* rope, float eps, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return LA_ERR_INVALID_ARG;
+  if (!std::isfinite(eps) || eps < 0.f) return LA_ERR_INVALID_ARG;
+  if (block_frames < 1 || frames < 1 || frames % block_frames != 0) return LA_ERR_INVALID_ARG;
+  Plan p;
+  int st = make_plan(&p, B, H, head_dim, frames, tokens_per_frame, block_frames, 0, rope, 0, in_dt, 1,
+                     true);
   if (st != LA_OK) return st;
   st = check_tensors(q, k, v, out, in_dt, out_dt, p);
   if (st != LA_OK) return st;
@@ -669,6 +704,6 @@ const char* la_status_string(int status) {
   }
 }
 
-const char* la_version(void) { return "0.4.0"; }
+const char* la_version(void) { return "0.5.0"; }
 
 }  // extern "C"

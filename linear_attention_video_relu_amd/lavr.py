@@ -52,6 +52,10 @@ def _load():
         "la_block_causal_forward": (c_int, [c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int,
                                             c_int, c_int, c_int, c_int, c_int,
                                             ctypes.POINTER(LaRope), c_float, c_vp, c_size, c_vp]),
+        "la_replay_workspace_bytes": (c_size, [c_int] * 6 + [ctypes.POINTER(LaRope)]),
+        "la_block_causal_forward_replay": (c_int, [c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int,
+                                                   c_int, c_int, c_int, c_int,
+                                                   ctypes.POINTER(LaRope), c_float, c_vp, c_size, c_vp]),
         "la_block_causal_forward_timed": (c_int, [c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int,
                                                   c_int, c_int, c_int, c_int, c_int, c_int,
                                                   ctypes.POINTER(LaRope), c_float, c_vp, c_size,
@@ -92,7 +96,7 @@ def _load():
 lib = _load()
 
 EXPORTS = ("rope_table_bytes", "rope_table_build", "la_workspace_bytes", "la_block_causal_forward",
-           "la_block_causal_forward_timed", "la_block_causal_forward_noalloc", "la_backward_workspace_bytes", "la_block_causal_backward",
+           "la_replay_workspace_bytes", "la_block_causal_forward_replay", "la_block_causal_forward_timed", "la_block_causal_forward_noalloc", "la_backward_workspace_bytes", "la_block_causal_backward",
            "la_block_causal_backward_from_forward",
            "la_qkv_workspace_bytes", "la_block_causal_forward_qkv", "la_stream_block_qkv",
            "la_temporal_conv", "la_conv_state_init", "la_temporal_conv_stream_block",
@@ -224,6 +228,40 @@ def block_causal_forward(q, k, v, block_frames, tokens_per_frame, rope=None, eps
                                        int(tokens_per_frame), int(block_frames), f0, _rope_ptr(rope),
                                        float(eps), _ptr(ws), ws.numel() * ws.element_size(),
                                        _stream(q.device)), "la_block_causal_forward")
+    return out
+
+
+def replay_workspace_bytes(B, H, frames, tokens_per_frame, block_frames, head_dim=HEAD_DIM, rope=None):
+    """Workspace bytes of block_causal_forward_replay."""
+    n = lib.la_replay_workspace_bytes(int(B), int(H), int(head_dim), int(frames), int(tokens_per_frame),
+                                      int(block_frames), _rope_ptr(rope))
+    if n == 0:
+        raise ValueError("invalid shape for la_replay_workspace_bytes (whole blocks required)")
+    return n
+
+
+def block_causal_forward_replay(q, k, v, block_frames, tokens_per_frame, rope=None, eps=EPS_DEFAULT,
+                                out=None, out_dtype=None, workspace=None):
+    """la_block_causal_forward_replay: the one-shot forward whose output equals,
+    bit for bit, streaming the clip block by block with StreamState.step (save=True,
+    from a fresh state).  The clip must be whole blocks of block_frames frames."""
+    _check_qkv(q, k, v)
+    B, N, H, d = q.shape
+    if N % tokens_per_frame:
+        raise ValueError("N must be a multiple of tokens_per_frame")
+    frames = N // tokens_per_frame
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, N, H, d), dtype=out_dtype, device=q.device)
+    elif out.shape != q.shape or out.dtype != out_dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor of q's shape and out_dtype on q's device")
+    need = replay_workspace_bytes(B, H, frames, tokens_per_frame, block_frames, d, rope)
+    ws = _workspace(q.device, need) if workspace is None else workspace
+    _check(lib.la_block_causal_forward_replay(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(q.dtype),
+                                              _dtype_code(out_dtype), B, H, d, frames,
+                                              int(tokens_per_frame), int(block_frames), _rope_ptr(rope),
+                                              float(eps), _ptr(ws), ws.numel() * ws.element_size(),
+                                              _stream(q.device)), "la_block_causal_forward_replay")
     return out
 
 

@@ -56,7 +56,7 @@ def test_calls_only_enqueue_kernels():
 
 
 def test_version_and_status_strings(lavr):
-    assert lavr.lib.la_version() == b"0.4.0"
+    assert lavr.lib.la_version() == b"0.5.0"
     for code in range(5):
         assert lavr.status_string(code).startswith("LA_")
     assert "unknown" in lavr.status_string(99)
@@ -155,6 +155,26 @@ def rope_desc(lavr, **kw):
 def test_forward_rejects_bad_rope(lavr, kw):
     r = rope_desc(lavr, **kw)
     assert call_forward(lavr, rope=ctypes.byref(r)) == lavr.LA_ERR_INVALID_ARG
+
+
+def test_replay_workspace_and_whole_blocks(lavr):
+    """The replay forward plans every block as a streamed call of one block: on a
+    clip of many blocks that is more, shorter chunks (a larger workspace than the
+    plain forward's), and the clip must be whole blocks."""
+    r = rope_desc(lavr, max_frames=120, grid_h=30, grid_w=52)
+    plain = lavr.lib.la_workspace_bytes(2, 70, 32, 120, 1560, 3, 0, ctypes.byref(r))
+    replay = lavr.lib.la_replay_workspace_bytes(2, 70, 32, 120, 1560, 3, ctypes.byref(r))
+    assert replay > plain > 0
+    # one block: the replay plan is the streamed one
+    one = lavr.lib.la_workspace_bytes(2, 70, 32, 3, 1560, 3, 0, ctypes.byref(r))
+    assert lavr.lib.la_replay_workspace_bytes(2, 70, 32, 3, 1560, 3, ctypes.byref(r)) == one
+    assert lavr.lib.la_replay_workspace_bytes(2, 70, 32, 119, 1560, 3, ctypes.byref(r)) == 0
+    assert lavr.lib.la_replay_workspace_bytes(2, 70, 32, 120, 1560, 0, ctypes.byref(r)) == 0
+    rc = lavr.lib.la_block_causal_forward_replay(
+        ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 0x1000000), ctypes.c_void_p(FAKE + 0x2000000),
+        ctypes.c_void_p(FAKE + 0x3000000), lavr.LA_BF16, lavr.LA_BF16, 1, 2, 32, 5, 6, 2, None, 1e-8,
+        ctypes.c_void_p(FAKE + 0x4000000), 1 << 30, None)
+    assert rc == lavr.LA_ERR_INVALID_ARG          # 5 frames are not whole blocks of 2
 
 
 def test_rope_table_pair_count_fits_32_bits(lavr):
