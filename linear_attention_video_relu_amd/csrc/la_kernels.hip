@@ -914,6 +914,12 @@ __global__ __launch_bounds__(256) void k_prefix1(PrefixArgs a) {
   const size_t bh = (size_t)blockIdx.z * a.H + blockIdx.y;
   const size_t cstride = (size_t)gridDim.z * a.H * REC;   // from one chunk's record to the next
   const float* part = a.part + bh * REC + el;
+  const bool inS = el < a.hd * a.hd;
+  const size_t si = bh * a.hd * a.hd + el, zi = bh * a.hd + el - a.hd * a.hd;
+  // the carried state is read first, so that its load is in flight with the
+  // partials' (one memory latency for the whole kernel)
+  float acc = 0.f;
+  if (a.S_init != nullptr) acc = inS ? a.S_init[si] : a.z_init[zi];
   constexpr int BATCH = 16;
   float s = 0.f;
   for (int c0 = 0; c0 < a.cpb; c0 += BATCH) {
@@ -924,10 +930,6 @@ __global__ __launch_bounds__(256) void k_prefix1(PrefixArgs a) {
     for (int i = 0; i < BATCH; ++i)
       if (c0 + i < a.cpb) s += v[i];
   }
-  const bool inS = el < a.hd * a.hd;
-  const size_t si = bh * a.hd * a.hd + el, zi = bh * a.hd + el - a.hd * a.hd;
-  float acc = 0.f;
-  if (a.S_init != nullptr) acc = inS ? a.S_init[si] : a.z_init[zi];
   acc += s;
   a.prefix[bh * REC + el] = acc;
   if (a.S_save != nullptr) {

@@ -542,8 +542,9 @@ class StreamState:
             out = torch.empty((B, N, H, d), dtype=out_dtype, device=q.device)
         elif out.shape != q.shape or out.dtype != out_dtype or not out.is_contiguous():
             raise ValueError("out must be a contiguous tensor of q's shape and out_dtype")
-        need = lib.la_workspace_bytes(B, H, d, frames, int(tokens_per_frame), frames, 0, _rope_ptr(rope))
-        ws = _workspace(q.device, need) if workspace is None else workspace
+        # (a caller's workspace is sized by the library's own check)
+        ws = workspace if workspace is not None else _workspace(
+            q.device, lib.la_workspace_bytes(B, H, d, frames, int(tokens_per_frame), frames, 0, _rope_ptr(rope)))
         _check(lib.la_stream_block(ctypes.byref(self.desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                    _dtype_code(q.dtype), _dtype_code(out_dtype), B, H, d, frames,
                                    int(tokens_per_frame), _rope_ptr(rope), float(eps), int(bool(save)),
@@ -566,8 +567,9 @@ class StreamState:
             out = torch.empty((B, N, H, d), dtype=out_dtype, device=qkv.device)
         elif out.shape != (B, N, H, d) or out.dtype != out_dtype or not out.is_contiguous():
             raise ValueError("out must be a contiguous (B, N, H, head_dim) tensor of out_dtype")
-        need = lib.la_qkv_workspace_bytes(B, H, d, frames, int(tokens_per_frame), frames, 0, _rope_ptr(rope))
-        ws = _workspace(qkv.device, need) if workspace is None else workspace
+        ws = workspace if workspace is not None else _workspace(
+            qkv.device, lib.la_qkv_workspace_bytes(B, H, d, frames, int(tokens_per_frame), frames, 0,
+                                                   _rope_ptr(rope)))
         _check(lib.la_stream_block_qkv(ctypes.byref(self.desc), _ptr(qkv), _ptr(out), _dtype_code(qkv.dtype),
                                        _dtype_code(out_dtype), B, H, d, frames, int(tokens_per_frame),
                                        _rope_ptr(rope), float(eps), _gptr(q_gamma), _gptr(k_gamma),
