@@ -54,7 +54,7 @@ def measured_traffic(workload, kernel):
 
     The summary under profiles/ carries a JSON block with the digest of the kernel
     sources the counters were taken on; when the sources have changed since, the
-    figure no longer describes this build and None is returned."""
+    figure no longer describes the built kernels and None is returned."""
     path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
     if not os.path.exists(path):
         return None
@@ -189,7 +189,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the path is measured on a single MI355X "
-              "(--gpus 1); multi-GPU runs are not part of this build.", file=sys.stderr)
+              "(--gpus 1); runs on several GPUs are not measured by this benchmark.", file=sys.stderr)
         sys.exit(2)
 
     cfg = W.workload(args.workload)
